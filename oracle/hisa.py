@@ -1,0 +1,120 @@
+"""Oracle: HISA hierarchical indexer (block-pooled coarse filter, token refinement).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): plain, slow, fp64.
+
+The HISA abstract describes the path: a DSA-style lightweight indexer scores
+every past token for the query and keeps a token-level top-k; HISA replaces the
+flat scan by (1) a block-level coarse filter that scores pooled block
+representatives and drops the rest, then (2) the original indexer applied only
+inside the remaining blocks, giving an exact token-level top-k among them.
+
+Readings where the pages are silent:
+  * indexer score of token t: sum_h w_h * ReLU(q_h . k_t) with non-negative
+    per-head weights w_h (the DSA lightweight-indexer form);
+  * pooled representative of a block: the mean of its valid (dequantized) keys;
+  * the block score uses the same indexer formula on the representative;
+  * fp8 storage: OCP e4m3fn codes with one positive f32 scale per row,
+    dequantized value = scale * e4m3fn(code);
+  * ties: larger score first, then lower block / token index;
+  * "exact" top-k means exact within the kept blocks (the coarse stage is a
+    heuristic; its agreement with the flat indexer is measured by IoU).
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Value of OCP fp8 e4m3fn bytes: sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0.
+
+    Exponent field 0 is subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN; there is no infinity.
+    """
+    u = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = (u >> 7) & 1
+    exp = (u >> 3) & 0xF
+    man = u & 0x7
+    mag = np.where(exp == 0, (man / 8.0) * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(exp - 7.0))
+    mag = np.where((exp == 0xF) & (man == 0x7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def dequantize(codes, scale) -> np.ndarray:
+    """Rows of fp8 codes times their per-row scale."""
+    return _f64(scale)[..., None] * e4m3fn_decode(codes)
+
+
+def pooled_reps(keys, block: int) -> np.ndarray:
+    """Mean of each block's valid keys: keys [L][d] (valid rows only) -> [ceil(L/block)][d]."""
+    keys = _f64(keys)
+    L = keys.shape[0]
+    nb = -(-L // block)
+    reps = np.empty((nb, keys.shape[1]))
+    for b in range(nb):
+        reps[b] = keys[b * block: min((b + 1) * block, L)].mean(axis=0)
+    return reps
+
+
+def indexer_scores(q, w, x) -> np.ndarray:
+    """sum_h w_h * ReLU(q_h . x_t) for every row x_t."""
+    q = _f64(q)
+    w = _f64(w)
+    x = _f64(x)
+    total = np.zeros(x.shape[0])
+    for h in range(q.shape[0]):
+        total += w[h] * np.maximum(x @ q[h], 0.0)
+    return total
+
+
+def top_largest(scores, ids, k: int) -> np.ndarray:
+    """First min(k, n) ids in (score descending, id ascending) order, returned ascending."""
+    s = _f64(scores)
+    ids = np.asarray(ids, dtype=np.int64)
+    order = np.lexsort((ids, -s))
+    return np.sort(ids[order[:k]])
+
+
+def select(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, keep_blocks: int,
+           top_k: int) -> Dict[str, np.ndarray]:
+    """HISA selection for one query from raw fp8 inputs."""
+    q = dequantize(q8, q_scale)
+    keys = dequantize(np.asarray(k8)[:seq_len], np.asarray(k_scale)[:seq_len])
+    reps = pooled_reps(keys, block)
+    S = indexer_scores(q, w, reps)
+    blocks = top_largest(S, np.arange(reps.shape[0]), keep_blocks)
+    cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    cand = cand[cand < seq_len]
+    s = indexer_scores(q, w, keys[cand])
+    sel = top_largest(s, cand, top_k)
+    return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s, sel=sel)
+
+
+def select_in_blocks(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, blocks,
+                     top_k: int) -> Dict[str, np.ndarray]:
+    """Fine stage alone, on given kept blocks."""
+    q = dequantize(q8, q_scale)
+    blocks = np.asarray(blocks, dtype=np.int64)
+    cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    cand = cand[cand < seq_len]
+    keys = dequantize(np.asarray(k8)[cand], np.asarray(k_scale)[cand])
+    s = indexer_scores(q, w, keys)
+    return dict(cand=cand, token_scores=s, sel=top_largest(s, cand, top_k))
+
+
+def flat_select(q8, q_scale, w, k8, k_scale, seq_len: int, top_k: int) -> np.ndarray:
+    """The flat DSA-style indexer: exact top-k over every valid token."""
+    q = dequantize(q8, q_scale)
+    keys = dequantize(np.asarray(k8)[:seq_len], np.asarray(k_scale)[:seq_len])
+    return top_largest(indexer_scores(q, w, keys), np.arange(seq_len), top_k)
+
+
+def iou(a, b) -> float:
+    a = np.asarray(a)
+    b = np.asarray(b)
+    union = np.union1d(a, b).size
+    return 1.0 if union == 0 else np.intersect1d(a, b).size / union

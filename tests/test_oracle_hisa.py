@@ -1,0 +1,94 @@
+"""Pins for the HISA oracle: library fp8 decode, special cases that reduce to the flat indexer,
+the ReLU scale factoring, and brute-force ordering."""
+import numpy as np
+import pytest
+
+from oracle import hisa as O
+from hash_hierarchical_top_amd import synth
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def test_e4m3fn_decode_matches_library_for_all_256_codes():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = O.e4m3fn_decode(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+    # worked values: 0x38 = 1.0, 0x7E = 448 (largest finite), 0x01 = 2^-9, 0xB8 = -1.0
+    assert O.e4m3fn_decode(np.array([0x38, 0x7E, 0x01, 0xB8], np.uint8)).tolist() == \
+        [1.0, 448.0, 2.0 ** -9, -1.0]
+
+
+def test_pooled_reps_worked_and_special_cases():
+    keys = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 9.0], [7.0, -1.0], [2.0, 2.0]])
+    # blocks of 2 over 5 rows: means (2,3), (6,4), (2,2) -- the last block has one valid row
+    assert O.pooled_reps(keys, 2).tolist() == [[2.0, 3.0], [6.0, 4.0], [2.0, 2.0]]
+    assert np.array_equal(O.pooled_reps(keys, 1), keys)
+
+
+def test_indexer_scores_worked_example_and_relu_factoring():
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w = np.array([0.5, 2.0])
+    x = np.array([[2.0, -3.0], [-1.0, 1.0]])
+    # t0: 0.5*relu(2) + 2*relu(-3) = 1.0 ; t1: 0.5*relu(-1) + 2*relu(1) = 2.0
+    assert O.indexer_scores(q, w, x).tolist() == [1.0, 2.0]
+    rng = _rng(1)
+    q = rng.standard_normal((8, 16))
+    w = rng.random(8)
+    x = rng.standard_normal((30, 16))
+    base = O.indexer_scores(q, w, x)
+    assert np.allclose(O.indexer_scores(3.0 * q, w, x), 3.0 * base)
+    assert np.allclose(O.indexer_scores(q, w, 0.25 * x), 0.25 * base)
+    assert np.all(base >= 0)
+
+
+def _brute_top_largest(scores, ids, k):
+    keep = []
+    for i in range(len(ids)):
+        better = sum(1 for j in range(len(ids))
+                     if scores[j] > scores[i] or (scores[j] == scores[i] and ids[j] < ids[i]))
+        if better < k:
+            keep.append(ids[i])
+    return sorted(keep)
+
+
+def test_top_largest_brute_force():
+    rng = _rng(2)
+    for _ in range(40):
+        n = int(rng.integers(1, 50))
+        s = rng.integers(0, 4, n).astype(float)
+        ids = np.arange(n) * 3
+        for k in (1, n // 2 + 1, n + 2):
+            assert O.top_largest(s, ids, k).tolist() == _brute_top_largest(list(s), list(ids), k)
+
+
+def _small_inputs(ctx, seed):
+    return synth.make_hisa_inputs(8, ctx, ctx, 4, seed, head_dim=32, make_kv=False)
+
+
+def test_keep_all_blocks_equals_flat_indexer():
+    inp = _small_inputs(1000, 3)
+    args = (inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], 1000)
+    res = O.select(*args, block=64, keep_blocks=16, top_k=100)
+    flat = O.flat_select(*args, top_k=100)
+    assert res["sel"].tolist() == flat.tolist()
+    assert O.iou(res["sel"], flat) == 1.0
+
+
+def test_block_size_one_coarse_equals_fine():
+    inp = _small_inputs(300, 4)
+    args = (inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], 300)
+    res = O.select(*args, block=1, keep_blocks=40, top_k=40)
+    assert res["blocks"].tolist() == res["sel"].tolist()
+    assert res["sel"].tolist() == O.flat_select(*args, top_k=40).tolist()
+
+
+def test_iou_definition():
+    assert O.iou([1, 2, 3], [2, 3, 4]) == pytest.approx(0.5)
+    assert O.iou([], []) == 1.0
