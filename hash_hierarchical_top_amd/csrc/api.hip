@@ -1,0 +1,591 @@
+// extern "C" entry points of libhhr.so: host-side argument checks, workspace
+// layout, and stream-ordered dispatch of the gfx950 kernels.  Every check runs
+// before anything is enqueued, and none of the checks touches the HIP runtime,
+// so the error paths are usable (and tested) on a machine without a GPU.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "hhr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hhr_status fail(hhr_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hhr_status ok() {
+  g_err[0] = '\0';
+  return HHR_OK;
+}
+
+hhr_status hip_fail(hipError_t e, const char* where) {
+  return fail(HHR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HHR_TRY(expr)                    \
+  do {                                   \
+    hhr_status _st = (expr);             \
+    if (_st != HHR_OK) return _st;       \
+  } while (0)
+
+#define HHR_LAUNCH(expr, where)                        \
+  do {                                                 \
+    hipError_t _e = (expr);                            \
+    if (_e != hipSuccess) return hip_fail(_e, where);  \
+  } while (0)
+
+hhr_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(HHR_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 15u)
+    return fail(HHR_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return HHR_OK;
+}
+
+hhr_status check_opt_ptr(const void* p, const char* name) {
+  return p == nullptr ? HHR_OK : check_ptr(p, name);
+}
+
+hhr_status check_shape(const hhr_shape* s) {
+  if (s == nullptr) return fail(HHR_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(HHR_ERR_INVALID_ARG, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(HHR_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads / s->n_kv_heads > hhr::kMaxG)
+    return fail(HHR_ERR_UNSUPPORTED, "query heads per KV head must be <= %d", hhr::kMaxG);
+  if (s->head_dim != hhr::kD) return fail(HHR_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (s->code_bits != 128) return fail(HHR_ERR_UNSUPPORTED, "code_bits must be 128");
+  if (s->page_size != hhr::kPS) return fail(HHR_ERR_UNSUPPORTED, "page_size must be 16");
+  if (s->max_ctx < hhr::kPS || s->max_ctx % hhr::kPS != 0)
+    return fail(HHR_ERR_INVALID_ARG, "max_ctx must be a positive multiple of 16");
+  if (s->max_ctx > hhr::kMaxCtx)
+    return fail(HHR_ERR_UNSUPPORTED, "max_ctx must be <= %d", hhr::kMaxCtx);
+  if (s->kv_dtype != HHR_F32 && s->kv_dtype != HHR_BF16)
+    return fail(HHR_ERR_INVALID_ARG, "kv_dtype must be HHR_F32 or HHR_BF16");
+  if ((long long)s->batch * s->n_kv_heads > 65535 || (long long)s->batch * s->n_q_heads > 1 << 30)
+    return fail(HHR_ERR_UNSUPPORTED, "batch * n_kv_heads must be <= 65535");
+  return HHR_OK;
+}
+
+hhr_status check_keep(int32_t keep_num, int32_t keep_den, int32_t keep_abs) {
+  if (keep_abs > 0) return HHR_OK;
+  if (keep_abs < 0) return fail(HHR_ERR_INVALID_ARG, "keep_pages_abs must be >= 0");
+  if (keep_num < 1 || keep_den < 1 || keep_num > keep_den)
+    return fail(HHR_ERR_INVALID_ARG,
+                "keep ratio must satisfy 1 <= keep_num <= keep_den (got %d/%d)", keep_num,
+                keep_den);
+  return HHR_OK;
+}
+
+hhr_status check_top_k(int32_t top_k) {
+  if (top_k < 1) return fail(HHR_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (top_k > hhr::kMaxCand) return fail(HHR_ERR_UNSUPPORTED, "top_k must be <= %d", hhr::kMaxCand);
+  return HHR_OK;
+}
+
+int32_t keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den, int32_t keep_abs) {
+  if (n_pages <= 0) return 0;
+  if (keep_abs > 0) return n_pages < keep_abs ? n_pages : keep_abs;
+  if (keep_num < 1 || keep_den < 1) return 0;
+  long long p = ((long long)keep_num * n_pages + keep_den - 1) / keep_den;
+  if (p < 1) p = 1;
+  return (int32_t)(p < n_pages ? p : n_pages);
+}
+
+hhr_status check_p_max(int32_t p_max) {
+  if ((long long)p_max * hhr::kPS > hhr::kMaxCand)
+    return fail(HHR_ERR_UNSUPPORTED,
+                "at most %d candidate keys per (sequence, KV head): kept pages x 16 = %lld",
+                hhr::kMaxCand, (long long)p_max * hhr::kPS);
+  return HHR_OK;
+}
+
+size_t attn_part_bytes(const hhr_shape& s, int32_t n_split) {
+  return (size_t)s.batch * s.n_kv_heads * n_split * hhr::kMaxG * (hhr::kD + 2) * sizeof(float);
+}
+
+int32_t n_split_for(int32_t top_k) { return (top_k + hhr::kAttnChunk - 1) / hhr::kAttnChunk; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int kHisaMaxHeads = 64;
+constexpr int kHisaMaxCand = 16384;
+
+hhr_status check_hisa_shape(const hhr_hisa_shape* s) {
+  if (s == nullptr) return fail(HHR_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->batch > 65535)
+    return fail(HHR_ERR_INVALID_ARG, "batch must be in [1, 65535]");
+  if (s->n_index_heads < 1) return fail(HHR_ERR_INVALID_ARG, "n_index_heads must be >= 1");
+  if (s->n_index_heads > kHisaMaxHeads)
+    return fail(HHR_ERR_UNSUPPORTED, "n_index_heads must be <= %d", kHisaMaxHeads);
+  if (s->head_dim != hhr::kD) return fail(HHR_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (s->block < 16 || s->block > 1024 || s->block % 16 != 0)
+    return fail(HHR_ERR_UNSUPPORTED, "block must be a multiple of 16 in [16, 1024]");
+  if (s->max_ctx < s->block || s->max_ctx % s->block != 0)
+    return fail(HHR_ERR_INVALID_ARG, "max_ctx must be a positive multiple of block");
+  if (s->max_ctx / s->block > kHisaMaxCand || s->max_ctx > (1 << 24))
+    return fail(HHR_ERR_UNSUPPORTED, "max_ctx / block must be <= %d and max_ctx <= 2^24",
+                kHisaMaxCand);
+  return HHR_OK;
+}
+
+hhr_status check_hisa_sel(const hhr_hisa_shape* s, int32_t keep_blocks, int32_t top_k) {
+  if (keep_blocks < 1) return fail(HHR_ERR_INVALID_ARG, "keep_blocks must be >= 1");
+  if ((long long)keep_blocks * s->block > kHisaMaxCand)
+    return fail(HHR_ERR_UNSUPPORTED, "keep_blocks * block must be <= %d", kHisaMaxCand);
+  if (top_k < 1) return fail(HHR_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (top_k > kHisaMaxCand) return fail(HHR_ERR_UNSUPPORTED, "top_k must be <= %d", kHisaMaxCand);
+  return HHR_OK;
+}
+
+uint32_t* status_of(void* workspace) { return reinterpret_cast<uint32_t*>(workspace); }
+
+}  // namespace
+
+namespace hhr {
+
+bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int32_t keep_abs,
+                    int32_t top_k, Workspace* ws) {
+  Workspace w;
+  const int NpCap = s.max_ctx / kPS;
+  w.p_max = keep_count(NpCap, keep_num, keep_den, keep_abs);
+  w.n_split = n_split_for(top_k);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t BHq = (size_t)s.batch * s.n_q_heads;
+  const size_t BHkv = (size_t)s.batch * s.n_kv_heads;
+  w.ctrl = take(kAlign);
+  w.q_rot = take(BHq * kD * sizeof(float));
+  w.q_codes = take(BHq * kNW * sizeof(uint32_t));
+  w.scores = take(BHkv * NpCap * sizeof(float));
+  w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
+  w.kept_count = take(BHkv * sizeof(int32_t));
+  w.dist = 0;
+  w.attn_part = take(attn_part_bytes(s, w.n_split));
+  w.total = off;
+  *ws = w;
+  return true;
+}
+
+bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t top_k,
+                         HisaWorkspace* ws) {
+  (void)top_k;
+  HisaWorkspace w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t B = (size_t)s.batch;
+  w.ctrl = take(kAlign);
+  w.block_scores = take(B * (s.max_ctx / s.block) * sizeof(float));
+  w.kept_blocks = take(B * keep_blocks * sizeof(int32_t));
+  w.kept_count = take(B * sizeof(int32_t));
+  w.token_scores = take(B * (size_t)keep_blocks * s.block * sizeof(float));
+  w.total = off;
+  *ws = w;
+  return true;
+}
+
+}  // namespace hhr
+
+extern "C" {
+
+const char* hhr_status_string(int32_t status) {
+  switch (status) {
+    case HHR_OK: return "HHR_OK";
+    case HHR_ERR_INVALID_ARG: return "HHR_ERR_INVALID_ARG";
+    case HHR_ERR_UNSUPPORTED: return "HHR_ERR_UNSUPPORTED";
+    case HHR_ERR_WORKSPACE: return "HHR_ERR_WORKSPACE";
+    case HHR_ERR_HIP: return "HHR_ERR_HIP";
+    default: return "HHR_ERR_UNKNOWN";
+  }
+}
+
+const char* hhr_last_error(void) { return g_err; }
+
+int32_t hhr_abi_version(void) { return 1; }
+
+int32_t hhr_keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den,
+                       int32_t keep_pages_abs) {
+  return keep_count(n_pages, keep_num, keep_den, keep_pages_abs);
+}
+
+size_t hhr_workspace_size(const hhr_shape* shape, int32_t keep_num, int32_t keep_den,
+                          int32_t keep_pages_abs, int32_t top_k) {
+  if (check_shape(shape) != HHR_OK || check_keep(keep_num, keep_den, keep_pages_abs) != HHR_OK ||
+      check_top_k(top_k) != HHR_OK)
+    return 0;
+  hhr::Workspace ws;
+  hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &ws);
+  if (check_p_max(ws.p_max) != HHR_OK) return 0;
+  return ws.total;
+}
+
+hhr_status hhr_read_device_status(void* workspace, void* stream, uint32_t* flags) {
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  if (flags == nullptr) return fail(HHR_ERR_INVALID_ARG, "flags is NULL");
+  HHR_LAUNCH(hipStreamSynchronize(as_stream(stream)), "hipStreamSynchronize");
+  uint32_t v = 0;
+  HHR_LAUNCH(hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost), "hipMemcpy");
+  const uint32_t zero = 0;
+  HHR_LAUNCH(hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice), "hipMemcpy");
+  *flags = v;
+  return ok();
+}
+
+hhr_status hhr_append_keys(const hhr_shape* shape, const void* k_cache, const int32_t* start,
+                           const int32_t* n_new, int32_t max_new, const float* R,
+                           const float* W, uint32_t* codes, float* page_meta,
+                           uint32_t* status_word, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_ptr(k_cache, "k_cache"));
+  HHR_TRY(check_ptr(start, "start"));
+  HHR_TRY(check_ptr(n_new, "n_new"));
+  HHR_TRY(check_ptr(R, "R"));
+  HHR_TRY(check_ptr(W, "W"));
+  HHR_TRY(check_ptr(codes, "codes"));
+  HHR_TRY(check_ptr(page_meta, "page_meta"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  if (max_new < 0 || max_new > shape->max_ctx)
+    return fail(HHR_ERR_INVALID_ARG, "max_new must be in [0, max_ctx]");
+  HHR_LAUNCH(hhr::launch_append_keys(*shape, k_cache, start, n_new, max_new, R, W, codes,
+                                     page_meta, status_word, as_stream(stream)),
+             "append_keys launch");
+  return ok();
+}
+
+hhr_status hhr_encode_queries(const hhr_shape* shape, const float* q, const float* R,
+                              const float* W, float* q_rot, uint32_t* q_codes, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_ptr(q, "q"));
+  HHR_TRY(check_ptr(R, "R"));
+  HHR_TRY(check_ptr(W, "W"));
+  HHR_TRY(check_ptr(q_rot, "q_rot"));
+  HHR_TRY(check_ptr(q_codes, "q_codes"));
+  HHR_LAUNCH(hhr::launch_encode_queries(*shape, q, R, W, q_rot, q_codes, as_stream(stream)),
+             "encode_queries launch");
+  return ok();
+}
+
+hhr_status hhr_page_scores(const hhr_shape* shape, const float* q_rot, const int32_t* seq_len,
+                           const float* page_meta, float* scores, uint32_t* status_word,
+                           void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_ptr(q_rot, "q_rot"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(page_meta, "page_meta"));
+  HHR_TRY(check_ptr(scores, "scores"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  HHR_LAUNCH(hhr::launch_page_scores(*shape, q_rot, seq_len, page_meta, scores, status_word,
+                                     as_stream(stream)),
+             "page_scores launch");
+  return ok();
+}
+
+hhr_status hhr_top_pages(const hhr_shape* shape, const float* scores, const int32_t* seq_len,
+                         int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                         int32_t* kept, int32_t* kept_count, uint32_t* status_word,
+                         void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_keep(keep_num, keep_den, keep_pages_abs));
+  HHR_TRY(check_ptr(scores, "scores"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(kept, "kept"));
+  HHR_TRY(check_ptr(kept_count, "kept_count"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  const int32_t p_max = keep_count(shape->max_ctx / hhr::kPS, keep_num, keep_den, keep_pages_abs);
+  HHR_LAUNCH(hhr::launch_top_pages(*shape, scores, seq_len, keep_num, keep_den, keep_pages_abs,
+                                   p_max, kept, kept_count, status_word, as_stream(stream)),
+             "top_pages launch");
+  return ok();
+}
+
+hhr_status hhr_hamming_topk(const hhr_shape* shape, const uint32_t* q_codes,
+                            const uint32_t* codes, const int32_t* seq_len, const int32_t* kept,
+                            const int32_t* kept_count, int32_t p_max, int32_t top_k,
+                            int32_t* sel_idx, int32_t* sel_count, uint16_t* dist,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_top_k(top_k));
+  HHR_TRY(check_ptr(q_codes, "q_codes"));
+  HHR_TRY(check_ptr(codes, "codes"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(kept, "kept"));
+  HHR_TRY(check_ptr(kept_count, "kept_count"));
+  HHR_TRY(check_ptr(sel_idx, "sel_idx"));
+  HHR_TRY(check_ptr(sel_count, "sel_count"));
+  HHR_TRY(check_opt_ptr(dist, "dist"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  if (p_max < 1 || p_max > shape->max_ctx / hhr::kPS)
+    return fail(HHR_ERR_INVALID_ARG, "p_max must be in [1, max_ctx / 16]");
+  HHR_TRY(check_p_max(p_max));
+  if (workspace_bytes < hhr::kAlign) return fail(HHR_ERR_WORKSPACE, "workspace too small");
+  HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count, p_max,
+                                      top_k, sel_idx, sel_count, dist, status_of(workspace),
+                                      as_stream(stream)),
+             "hamming_topk launch");
+  return ok();
+}
+
+hhr_status hhr_sparse_decode(const hhr_shape* shape, const float* q, const void* k_cache,
+                             const void* v_cache, const int32_t* sel_idx,
+                             const int32_t* sel_count, int32_t top_k, float scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_top_k(top_k));
+  HHR_TRY(check_ptr(q, "q"));
+  HHR_TRY(check_ptr(k_cache, "k_cache"));
+  HHR_TRY(check_ptr(v_cache, "v_cache"));
+  HHR_TRY(check_ptr(sel_idx, "sel_idx"));
+  HHR_TRY(check_ptr(sel_count, "sel_count"));
+  HHR_TRY(check_ptr(out, "out"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
+  const int32_t n_split = n_split_for(top_k);
+  const size_t need = hhr::kAlign + attn_part_bytes(*shape, n_split);
+  if (workspace_bytes < need)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, sparse decode needs %zu",
+                workspace_bytes, need);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + hhr::kAlign);
+  HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
+                                       scale, out, part, n_split, status_of(workspace),
+                                       as_stream(stream)),
+             "sparse_decode launch");
+  return ok();
+}
+
+static hhr_status select_impl(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                              const float* R, const float* W, const uint32_t* codes,
+                              const float* page_meta, int32_t keep_num, int32_t keep_den,
+                              int32_t keep_abs, int32_t top_k, int32_t* sel_idx,
+                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hhr::Workspace* layout) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_keep(keep_num, keep_den, keep_abs));
+  HHR_TRY(check_top_k(top_k));
+  HHR_TRY(check_ptr(q, "q"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(R, "R"));
+  HHR_TRY(check_ptr(W, "W"));
+  HHR_TRY(check_ptr(codes, "codes"));
+  HHR_TRY(check_ptr(page_meta, "page_meta"));
+  HHR_TRY(check_ptr(sel_idx, "sel_idx"));
+  HHR_TRY(check_ptr(sel_count, "sel_count"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  hhr::Workspace ws;
+  hhr::make_workspace(*shape, keep_num, keep_den, keep_abs, top_k, &ws);
+  HHR_TRY(check_p_max(ws.p_max));
+  if (workspace_bytes < ws.total)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                ws.total);
+  char* base = static_cast<char*>(workspace);
+  uint32_t* status = status_of(workspace);
+  float* q_rot = reinterpret_cast<float*>(base + ws.q_rot);
+  uint32_t* q_codes = reinterpret_cast<uint32_t*>(base + ws.q_codes);
+  float* scores = reinterpret_cast<float*>(base + ws.scores);
+  int32_t* kept = reinterpret_cast<int32_t*>(base + ws.kept);
+  int32_t* kept_count = reinterpret_cast<int32_t*>(base + ws.kept_count);
+  HHR_LAUNCH(hhr::launch_encode_queries(*shape, q, R, W, q_rot, q_codes, stream),
+             "encode_queries launch");
+  HHR_LAUNCH(hhr::launch_page_scores(*shape, q_rot, seq_len, page_meta, scores, status, stream),
+             "page_scores launch");
+  HHR_LAUNCH(hhr::launch_top_pages(*shape, scores, seq_len, keep_num, keep_den, keep_abs,
+                                   ws.p_max, kept, kept_count, status, stream),
+             "top_pages launch");
+  HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count,
+                                      ws.p_max, top_k, sel_idx, sel_count, nullptr, status,
+                                      stream),
+             "hamming_topk launch");
+  *layout = ws;
+  return HHR_OK;
+}
+
+hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                      const float* R, const float* W, const uint32_t* codes,
+                      const float* page_meta, int32_t keep_num, int32_t keep_den,
+                      int32_t keep_pages_abs, int32_t top_k, int32_t* sel_idx,
+                      int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  hhr::Workspace ws;
+  HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
+                      keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
+                      as_stream(stream), &ws));
+  return ok();
+}
+
+hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                      const float* R, const float* W, const uint32_t* codes,
+                      const float* page_meta, const void* k_cache, const void* v_cache,
+                      int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
+                      float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_ptr(k_cache, "k_cache"));
+  HHR_TRY(check_ptr(v_cache, "v_cache"));
+  HHR_TRY(check_ptr(out, "out"));
+  if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
+  hhr::Workspace ws;
+  HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
+                      keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
+                      as_stream(stream), &ws));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.attn_part);
+  HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
+                                       scale, out, part, ws.n_split, status_of(workspace),
+                                       as_stream(stream)),
+             "sparse_decode launch");
+  return ok();
+}
+
+
+// ------------------------------------------------------------------ HISA
+size_t hhr_hisa_workspace_size(const hhr_hisa_shape* shape, int32_t keep_blocks, int32_t top_k) {
+  if (check_hisa_shape(shape) != HHR_OK || check_hisa_sel(shape, keep_blocks, top_k) != HHR_OK)
+    return 0;
+  hhr::HisaWorkspace ws;
+  hhr::make_hisa_workspace(*shape, keep_blocks, top_k, &ws);
+  return ws.total;
+}
+
+hhr_status hhr_hisa_pool_keys(const hhr_hisa_shape* shape, const uint8_t* k8,
+                              const float* k_scale, const int32_t* start, const int32_t* n_new,
+                              int32_t max_new, float* reps, uint32_t* status_word, void* stream) {
+  HHR_TRY(check_hisa_shape(shape));
+  HHR_TRY(check_ptr(k8, "k8"));
+  HHR_TRY(check_ptr(k_scale, "k_scale"));
+  HHR_TRY(check_ptr(start, "start"));
+  HHR_TRY(check_ptr(n_new, "n_new"));
+  HHR_TRY(check_ptr(reps, "reps"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  if (max_new < 0 || max_new > shape->max_ctx)
+    return fail(HHR_ERR_INVALID_ARG, "max_new must be in [0, max_ctx]");
+  HHR_LAUNCH(hhr::launch_hisa_pool(*shape, k8, k_scale, start, n_new, max_new, reps, status_word,
+                                   as_stream(stream)),
+             "hisa_pool launch");
+  return ok();
+}
+
+hhr_status hhr_hisa_block_scores(const hhr_hisa_shape* shape, const uint8_t* q8,
+                                 const float* q_scale, const float* w, const float* reps,
+                                 const int32_t* seq_len, float* block_scores,
+                                 uint32_t* status_word, void* stream) {
+  HHR_TRY(check_hisa_shape(shape));
+  HHR_TRY(check_ptr(q8, "q8"));
+  HHR_TRY(check_ptr(q_scale, "q_scale"));
+  HHR_TRY(check_ptr(w, "w"));
+  HHR_TRY(check_ptr(reps, "reps"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(block_scores, "block_scores"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, block_scores,
+                                           status_word, as_stream(stream)),
+             "hisa_block_scores launch");
+  return ok();
+}
+
+hhr_status hhr_hisa_top_blocks(const hhr_hisa_shape* shape, const float* block_scores,
+                               const int32_t* seq_len, int32_t keep_blocks,
+                               int32_t* kept_blocks, int32_t* kept_count,
+                               uint32_t* status_word, void* stream) {
+  HHR_TRY(check_hisa_shape(shape));
+  HHR_TRY(check_hisa_sel(shape, keep_blocks, 1));
+  HHR_TRY(check_ptr(block_scores, "block_scores"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(kept_blocks, "kept_blocks"));
+  HHR_TRY(check_ptr(kept_count, "kept_count"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, block_scores, seq_len, keep_blocks, kept_blocks,
+                                         kept_count, status_word, as_stream(stream)),
+             "hisa_top_blocks launch");
+  return ok();
+}
+
+hhr_status hhr_hisa_token_topk(const hhr_hisa_shape* shape, const uint8_t* q8,
+                               const float* q_scale, const float* w, const uint8_t* k8,
+                               const float* k_scale, const int32_t* seq_len,
+                               const int32_t* kept_blocks, const int32_t* kept_count,
+                               int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
+                               int32_t* sel_count, float* token_scores, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_hisa_shape(shape));
+  HHR_TRY(check_hisa_sel(shape, keep_blocks, top_k));
+  HHR_TRY(check_ptr(q8, "q8"));
+  HHR_TRY(check_ptr(q_scale, "q_scale"));
+  HHR_TRY(check_ptr(w, "w"));
+  HHR_TRY(check_ptr(k8, "k8"));
+  HHR_TRY(check_ptr(k_scale, "k_scale"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(kept_blocks, "kept_blocks"));
+  HHR_TRY(check_ptr(kept_count, "kept_count"));
+  HHR_TRY(check_ptr(sel_idx, "sel_idx"));
+  HHR_TRY(check_ptr(sel_count, "sel_count"));
+  HHR_TRY(check_opt_ptr(token_scores, "token_scores"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  hhr::HisaWorkspace ws;
+  hhr::make_hisa_workspace(*shape, keep_blocks, top_k, &ws);
+  if (workspace_bytes < ws.total)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                ws.total);
+  float* ts = token_scores ? token_scores
+                           : reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.token_scores);
+  HHR_LAUNCH(hhr::launch_hisa_token_topk(*shape, q8, q_scale, w, k8, k_scale, seq_len,
+                                         kept_blocks, kept_count, keep_blocks, top_k, sel_idx,
+                                         sel_count, ts, status_of(workspace), as_stream(stream)),
+             "hisa_token_topk launch");
+  return ok();
+}
+
+hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const float* q_scale,
+                           const float* w, const uint8_t* k8, const float* k_scale,
+                           const float* reps, const int32_t* seq_len, int32_t keep_blocks,
+                           int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_hisa_shape(shape));
+  HHR_TRY(check_hisa_sel(shape, keep_blocks, top_k));
+  HHR_TRY(check_ptr(q8, "q8"));
+  HHR_TRY(check_ptr(q_scale, "q_scale"));
+  HHR_TRY(check_ptr(w, "w"));
+  HHR_TRY(check_ptr(k8, "k8"));
+  HHR_TRY(check_ptr(k_scale, "k_scale"));
+  HHR_TRY(check_ptr(reps, "reps"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(sel_idx, "sel_idx"));
+  HHR_TRY(check_ptr(sel_count, "sel_count"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  hhr::HisaWorkspace ws;
+  hhr::make_hisa_workspace(*shape, keep_blocks, top_k, &ws);
+  if (workspace_bytes < ws.total)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                ws.total);
+  char* base = static_cast<char*>(workspace);
+  uint32_t* status = status_of(workspace);
+  float* bs = reinterpret_cast<float*>(base + ws.block_scores);
+  int32_t* kept = reinterpret_cast<int32_t*>(base + ws.kept_blocks);
+  int32_t* kc = reinterpret_cast<int32_t*>(base + ws.kept_count);
+  float* ts = reinterpret_cast<float*>(base + ws.token_scores);
+  hipStream_t st = as_stream(stream);
+  HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status, st),
+             "hisa_block_scores launch");
+  HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, bs, seq_len, keep_blocks, kept, kc, status, st),
+             "hisa_top_blocks launch");
+  HHR_LAUNCH(hhr::launch_hisa_token_topk(*shape, q8, q_scale, w, k8, k_scale, seq_len, kept, kc,
+                                         keep_blocks, top_k, sel_idx, sel_count, ts, status, st),
+             "hisa_token_topk launch");
+  return ok();
+}
+
+}  // extern "C"

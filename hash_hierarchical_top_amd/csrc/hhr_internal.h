@@ -1,0 +1,82 @@
+// Host-side internals of libhhr: kernel launchers and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hhr.h"
+#include "hhr_consts.h"
+
+namespace hhr {
+
+constexpr int kMaxCtx = 262144;            // Lcap limit (NpCap <= 16384)
+constexpr int kMaxCand = 32768;            // kept candidates per (b, g): p_max * 16
+constexpr int kAttnChunk = 64;             // selected keys per split-K workgroup
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of the decode workspace regions.  Region 0 (the control block)
+// holds the device status word at offset 0.
+struct Workspace {
+  size_t ctrl = 0, q_rot = 0, q_codes = 0, scores = 0, kept = 0, kept_count = 0, dist = 0,
+         attn_part = 0, total = 0;
+  int32_t p_max = 0, n_split = 0;
+};
+
+bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int32_t keep_abs,
+                    int32_t top_k, Workspace* ws);
+
+// ---- launchers (all asynchronous on `stream`) ----
+hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int32_t* start,
+                              const int32_t* n_new, int32_t max_new, const float* R,
+                              const float* W, uint32_t* codes, float* meta, uint32_t* status,
+                              hipStream_t stream);
+hipError_t launch_encode_queries(const hhr_shape& s, const float* q, const float* R,
+                                 const float* W, float* q_rot, uint32_t* q_codes,
+                                 hipStream_t stream);
+hipError_t launch_page_scores(const hhr_shape& s, const float* q_rot, const int32_t* seq_len,
+                              const float* meta, float* scores, uint32_t* status,
+                              hipStream_t stream);
+hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32_t* seq_len,
+                            int32_t keep_num, int32_t keep_den, int32_t keep_abs, int32_t p_max,
+                            int32_t* kept, int32_t* kept_count, uint32_t* status,
+                            hipStream_t stream);
+hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
+                               const int32_t* seq_len, const int32_t* kept,
+                               const int32_t* kept_count, int32_t p_max, int32_t top_k,
+                               int32_t* sel_idx, int32_t* sel_count, uint16_t* dist,
+                               uint32_t* status, hipStream_t stream);
+hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* k_cache,
+                                const void* v_cache, const int32_t* sel_idx,
+                                const int32_t* sel_count, int32_t top_k, float scale, float* out,
+                                float* part, int32_t n_split, uint32_t* status,
+                                hipStream_t stream);
+
+// ---- HISA ----
+struct HisaWorkspace {
+  size_t ctrl = 0, block_scores = 0, kept_blocks = 0, kept_count = 0, token_scores = 0, total = 0;
+};
+bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t top_k,
+                         HisaWorkspace* ws);
+
+hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const float* k_scale,
+                            const int32_t* start, const int32_t* n_new, int32_t max_new,
+                            float* reps, uint32_t* status, hipStream_t stream);
+hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
+                                    const float* q_scale, const float* w, const float* reps,
+                                    const int32_t* seq_len, float* block_scores,
+                                    uint32_t* status, hipStream_t stream);
+hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_scores,
+                                  const int32_t* seq_len, int32_t keep_blocks, int32_t* kept,
+                                  int32_t* kept_count, uint32_t* status, hipStream_t stream);
+hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
+                                  const float* q_scale, const float* w, const uint8_t* k8,
+                                  const float* k_scale, const int32_t* seq_len,
+                                  const int32_t* kept, const int32_t* kept_count,
+                                  int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
+                                  int32_t* sel_count, float* token_scores, uint32_t* status,
+                                  hipStream_t stream);
+
+}  // namespace hhr
