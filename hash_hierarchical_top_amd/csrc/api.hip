@@ -153,6 +153,18 @@ uint32_t* status_of(void* workspace) { return reinterpret_cast<uint32_t*>(worksp
 
 namespace hhr {
 
+size_t ctrl_bytes(const hhr_shape& s) {
+  return kAlign + align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+}
+
+AttnWorkspace attn_workspace(const hhr_shape& s, int32_t top_k) {
+  AttnWorkspace a;
+  a.tickets = kAlign;
+  a.part = ctrl_bytes(s);
+  a.total = a.part + align_up(attn_part_bytes(s, n_split_for(top_k)));
+  return a;
+}
+
 bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int32_t keep_abs,
                     int32_t top_k, Workspace* ws) {
   Workspace w;
@@ -167,13 +179,14 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   };
   const size_t BHq = (size_t)s.batch * s.n_q_heads;
   const size_t BHkv = (size_t)s.batch * s.n_kv_heads;
+  // control block: status word, then the split-K tickets (same offsets in every layout)
   w.ctrl = take(kAlign);
+  w.attn_tickets = take(BHkv * sizeof(uint32_t));
   w.q_rot = take(BHq * kD * sizeof(float));
   w.q_codes = take(BHq * kNW * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
-  w.dist = 0;
   w.attn_part = take(attn_part_bytes(s, w.n_split));
   w.total = off;
   *ws = w;
@@ -357,14 +370,14 @@ hhr_status hhr_sparse_decode(const hhr_shape* shape, const float* q, const void*
   HHR_TRY(check_ptr(workspace, "workspace"));
   if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
   const int32_t n_split = n_split_for(top_k);
-  const size_t need = hhr::kAlign + attn_part_bytes(*shape, n_split);
-  if (workspace_bytes < need)
+  const hhr::AttnWorkspace aw = hhr::attn_workspace(*shape, top_k);
+  if (workspace_bytes < aw.total)
     return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, sparse decode needs %zu",
-                workspace_bytes, need);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + hhr::kAlign);
+                workspace_bytes, aw.total);
+  char* base = static_cast<char*>(workspace);
   HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
-                                       scale, out, part, n_split, status_of(workspace),
-                                       as_stream(stream)),
+                                       scale, out, reinterpret_cast<float*>(base + aw.part),
+                                       n_split, status_of(workspace), as_stream(stream)),
              "sparse_decode launch");
   return ok();
 }
@@ -443,10 +456,10 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
                       as_stream(stream), &ws));
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.attn_part);
+  char* base = static_cast<char*>(workspace);
   HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
-                                       scale, out, part, ws.n_split, status_of(workspace),
-                                       as_stream(stream)),
+                                       scale, out, reinterpret_cast<float*>(base + ws.attn_part),
+                                       ws.n_split, status_of(workspace), as_stream(stream)),
              "sparse_decode launch");
   return ok();
 }

@@ -20,10 +20,17 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Byte offsets of the decode workspace regions.  Region 0 (the control block)
 // holds the device status word at offset 0.
 struct Workspace {
-  size_t ctrl = 0, q_rot = 0, q_codes = 0, scores = 0, kept = 0, kept_count = 0, dist = 0,
-         attn_part = 0, total = 0;
+  size_t ctrl = 0, q_rot = 0, q_codes = 0, scores = 0, kept = 0, kept_count = 0,
+         attn_tickets = 0, attn_part = 0, total = 0;
   int32_t p_max = 0, n_split = 0;
 };
+
+// Workspace of hhr_sparse_decode alone: control block, tickets, partials.
+struct AttnWorkspace {
+  size_t tickets = 0, part = 0, total = 0;
+};
+AttnWorkspace attn_workspace(const hhr_shape& s, int32_t top_k);
+size_t ctrl_bytes(const hhr_shape& s);
 
 bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int32_t keep_abs,
                     int32_t top_k, Workspace* ws);

@@ -18,6 +18,7 @@ namespace {
 constexpr int kMaxIndexHeads = 64;
 constexpr int kHisaThreads = 1024;
 constexpr int kHisaItems = 16;  // candidates per thread: <= 16384 per query
+constexpr int kHisaMaxCand = kHisaThreads * kHisaItems;
 
 // OCP fp8 e4m3fn -> f32: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
 // 2..0; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN; no infinities.
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void k_hisa_block_scores(
   if (hg == 0 && blk0 + bl < Nb) block_scores[(size_t)b * NbCap + blk0 + bl] = part;
 }
 
-// H3: exact top keep_blocks blocks of one query.
+// H3: exact top keep_blocks blocks of one query (block c = i*1024 + tid in slot i).
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
     const float* __restrict__ block_scores, const int32_t* __restrict__ seq_len,
     int keep_blocks, int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
@@ -128,15 +129,17 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   const int NbCap = Lcap / block;
   const int tid = threadIdx.x;
   int32_t* out = kept + (size_t)b * keep_blocks;
-  const int items = (Nb + kHisaThreads - 1) / kHisaThreads;
-  const int i0 = tid * items;
   const float* sc = block_scores + (size_t)b * NbCap;
-  uint32_t key[kHisaItems];
+  float x[kHisaItems];
+  bool pr[kHisaItems];
 #pragma unroll
-  for (int i = 0; i < kHisaItems; ++i)
-    key[i] = (i < items && i0 + i < Nb) ? orderable_key(sc[i0 + i]) : 0u;
-  const int cnt = top_largest_ordered<kHisaThreads, kHisaItems>(
-      key, items, keep_blocks, sh, [&](int pos, int c) { out[pos] = c; });
+  for (int i = 0; i < kHisaItems; ++i) {
+    const int c = i * kHisaThreads + tid;
+    x[i] = sc[min(c, max(Nb - 1, 0))];
+    pr[i] = c < Nb;
+  }
+  const int cnt = top_largest_strided<kHisaThreads, kHisaItems>(
+      x, pr, keep_blocks, sh, [&](int pos, int c) { out[pos] = c; });
   for (int i = cnt + tid; i < keep_blocks; i += kHisaThreads) out[i] = -1;
   if (tid == 0) kept_count[b] = cnt;
 }
@@ -214,37 +217,39 @@ __global__ __launch_bounds__(256) void k_hisa_token_scores(
   }
 }
 
-// H5: exact top-k over the kept blocks' valid tokens by (larger s, lower t).
+// H5: exact top-k over the kept blocks' valid tokens by (larger s, lower t);
+// candidate c = (kept slot c / block, row c % block) sits in slot c / 1024 of
+// thread c % 1024.  Kept blocks are ascending, so candidate order is position
+// order and ties go to the lower position.
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
     const float* __restrict__ token_scores, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
     int top_k, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int Lcap,
     int block) {
   __shared__ TopScratch sh;
+  __shared__ int skept[kHisaMaxCand / 16];
   const int b = blockIdx.x;
   int L = seq_len[b];
   if (L < 0 || L > Lcap) L = 0;
   const int kc = L > 0 ? min(kept_count[b], keep_blocks) : 0;
   const int ncand = kc * block;
   const int tid = threadIdx.x;
-  const int items = (ncand + kHisaThreads - 1) / kHisaThreads;
-  const int i0 = tid * items;
-  const int32_t* kb = kept + (size_t)b * keep_blocks;
+  for (int i = tid; i < kc; i += kHisaThreads) skept[i] = kept[(size_t)b * keep_blocks + i];
+  __syncthreads();
   const float* ts = token_scores + (size_t)b * keep_blocks * block;
-  uint32_t key[kHisaItems];
+  float x[kHisaItems];
+  bool pr[kHisaItems];
 #pragma unroll
   for (int i = 0; i < kHisaItems; ++i) {
-    key[i] = 0u;
-    const int c = i0 + i;
-    if (i < items && c < ncand) {
-      const int blk = kb[c / block];
-      const int t = blk * block + c % block;
-      if (blk >= 0 && t < L) key[i] = orderable_key(ts[c]);
-    }
+    const int c = i * kHisaThreads + tid;
+    const int cc = min(c, max(ncand - 1, 0));
+    x[i] = ts[cc];
+    const int blk = skept[cc / block];
+    pr[i] = c < ncand && blk >= 0 && blk * block + c % block < L;
   }
   int32_t* out = sel_idx + (size_t)b * top_k;
-  const int cnt = top_largest_ordered<kHisaThreads, kHisaItems>(
-      key, items, top_k, sh, [&](int pos, int c) { out[pos] = kb[c / block] * block + c % block; });
+  const int cnt = top_largest_strided<kHisaThreads, kHisaItems>(
+      x, pr, top_k, sh, [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; });
   for (int i = cnt + tid; i < top_k; i += kHisaThreads) out[i] = -1;
   if (tid == 0) sel_count[b] = cnt;
 }

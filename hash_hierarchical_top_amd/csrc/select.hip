@@ -30,19 +30,23 @@ __device__ __forceinline__ int checked_len(const int32_t* seq_len, int b, int Lc
 // dimension the group reduces to A_d = sum_h max(q'_hd, 0) and
 // B_d = sum_h min(q'_hd, 0), and s(p) = sum_d (A_d mx_pd + B_d mn_pd).
 //
-// One wave streams 16 pages at a time: lane l reads dims {2l, 2l+1} of each
-// page (16 bytes; the wave reads the page's 1 KiB in one coalesced load),
-// keeps 16 partial sums, and a butterfly reduce-scatter leaves the sum of
-// page 8*b5 + 4*b4 + 2*b3 + b2 (b_i = bit i of the lane id) in every lane.
+// A wave takes a batch of 16 consecutive pages.  Lane (row r = l/16,
+// sub = l%16) handles pages pb + 4j + r (j = 0..3) and, in each, the 16-byte
+// pieces k = 0..3 at byte 256k + 16 sub (dims 2(sub + 16k) and +1), so every
+// load instruction reads four whole 256-byte runs.  All 16 loads are issued
+// before anything that depends on the query (addresses are clamped, not
+// branched on, so nothing serialises them); a 4-value reduce-scatter over the
+// 16 lanes of a row then leaves page pb + 4j + r in lanes with j = 2 b3 + b2.
 constexpr int kScoreWaves = 4;
-constexpr int kPagesPerWaveIter = 16;
+constexpr int kScorePagesPerWave = 16;
+constexpr int kScorePagesPerWg = kScoreWaves * kScorePagesPerWave;  // 64
 
 __global__ __launch_bounds__(256) void k_page_scores(const float* __restrict__ q_rot,
                                                      const int32_t* __restrict__ seq_len,
                                                      const float* __restrict__ meta,
                                                      float* __restrict__ scores,
                                                      uint32_t* __restrict__ status, int Hq,
-                                                     int Hkv, int Lcap, int pages_per_wg) {
+                                                     int Hkv, int Lcap) {
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
@@ -50,76 +54,74 @@ __global__ __launch_bounds__(256) void k_page_scores(const float* __restrict__ q
   const int NpCap = Lcap / kPS;
   const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
   const int Np = (L + kPS - 1) / kPS;
-  const int p_begin = blockIdx.x * pages_per_wg;
-  if (p_begin >= Np) return;
-  const int p_end = min(Np, p_begin + pages_per_wg);
-
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
-  float A0 = 0.f, B0 = 0.f, A1 = 0.f, B1 = 0.f;
-  const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD + 2 * l;
-  for (int h = 0; h < G; ++h) {
-    const float2 v = *(const float2*)(qr + (size_t)h * kD);
-    A0 += fmaxf(v.x, 0.f);
-    B0 += fminf(v.x, 0.f);
-    A1 += fmaxf(v.y, 0.f);
-    B1 += fminf(v.y, 0.f);
-  }
-  const float* mbase = meta + (size_t)bg * NpCap * kD * 2 + 4 * l;
-  float* sbase = scores + (size_t)bg * NpCap;
+  const int pb = blockIdx.x * kScorePagesPerWg + w * kScorePagesPerWave;
+  if (pb >= Np) return;
+  const int r = l >> 4;
+  const int sub = l & 15;
 
-  for (int pb = p_begin + w * kPagesPerWaveIter; pb < p_end;
-       pb += kScoreWaves * kPagesPerWaveIter) {
-    float v[16];
+  const float* mbase = meta + (size_t)bg * NpCap * kD * 2 + 4 * sub;
+  floatx4 m[4][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = pb + i;
-      v[i] = 0.f;
-      if (p < p_end) {
-        const floatx4 m = __builtin_nontemporal_load((const floatx4*)(mbase + (size_t)p * kD * 2));
-        // m = {mn[2l], mx[2l], mn[2l+1], mx[2l+1]}
-        v[i] = A0 * m[1] + B0 * m[0] + A1 * m[3] + B1 * m[2];
-      }
-    }
-    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8, b2 = l & 4;
+  for (int j = 0; j < 4; ++j) {
+    const int p = min(pb + 4 * j + r, Np - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = b5 ? v[i] : v[i + 8];
-      const float keep = b5 ? v[i + 8] : v[i];
-      v[i] = keep + __shfl_xor(send, 32);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = b4 ? v[i] : v[i + 4];
-      const float keep = b4 ? v[i + 4] : v[i];
-      v[i] = keep + __shfl_xor(send, 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = b3 ? v[i] : v[i + 2];
-      const float keep = b3 ? v[i + 2] : v[i];
-      v[i] = keep + __shfl_xor(send, 8);
-    }
-    {
-      const float send = b2 ? v[0] : v[1];
-      const float keep = b2 ? v[1] : v[0];
-      v[0] = keep + __shfl_xor(send, 4);
-    }
-    v[0] += __shfl_xor(v[0], 2);
-    v[0] += __shfl_xor(v[0], 1);
-    const int idx = (b5 ? 8 : 0) + (b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0);
-    if ((l & 3) == 0 && pb + idx < p_end) sbase[pb + idx] = v[0];
+    for (int k = 0; k < 4; ++k)
+      m[j][k] = __builtin_nontemporal_load((const floatx4*)(mbase + (size_t)p * kD * 2 + 64 * k));
   }
+  float A[4][2], B[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) A[k][0] = A[k][1] = B[k][0] = B[k][1] = 0.f;
+  const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD + 2 * sub;
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 v = *(const float2*)(qr + (size_t)h * kD + 32 * k);
+      A[k][0] += fmaxf(v.x, 0.f);
+      B[k][0] += fminf(v.x, 0.f);
+      A[k][1] += fmaxf(v.y, 0.f);
+      B[k][1] += fminf(v.y, 0.f);
+    }
+  }
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // m = {mn[d0], mx[d0], mn[d1], mx[d1]}
+      x += A[k][0] * m[j][k][1] + B[k][0] * m[j][k][0] + A[k][1] * m[j][k][3] +
+           B[k][1] * m[j][k][2];
+    v[j] = x;
+  }
+  const bool b3 = l & 8, b2 = l & 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float send = b3 ? v[i] : v[i + 2];
+    const float keep = b3 ? v[i + 2] : v[i];
+    v[i] = keep + __shfl_xor(send, 8);
+  }
+  {
+    const float send = b2 ? v[0] : v[1];
+    const float keep = b2 ? v[1] : v[0];
+    v[0] = keep + __shfl_xor(send, 4);
+  }
+  v[0] += __shfl_xor(v[0], 2);
+  v[0] += __shfl_xor(v[0], 1);
+  const int p = pb + 4 * ((b3 ? 2 : 0) + (b2 ? 1 : 0)) + r;
+  if ((l & 3) == 0 && p < Np) scores[(size_t)bg * NpCap + p] = v[0];
 }
 
 // ------------------------------------------------------------------ S4
-// Exact top-P of the page scores of one (b, g) in one 1024-thread workgroup
-// (radix select on orderable float keys, then an ordered block scan), kept
-// pages written ascending.
+// Exact top-P of the page scores of one (b, g) in one workgroup: page
+// p = i*512 + tid sits in slot i of thread tid (coalesced loads); the cut-off
+// comes from a value-linear histogram, and the kept pages are written
+// ascending by an ordered compaction.
+constexpr int kTopPThreads = 512;
+constexpr int kTopPItems = kMaxCtx / kPS / kTopPThreads;  // 32: NpCap <= 16384
 constexpr int kSelThreads = 1024;
-constexpr int kTopPItems = 16;  // NpCap <= 16384
 
-__global__ __launch_bounds__(kSelThreads) void k_top_pages(
+__global__ __launch_bounds__(kTopPThreads) void k_top_pages(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_len, int keep_num,
     int keep_den, int keep_abs, int p_max, int Hkv, int Lcap, int32_t* __restrict__ kept,
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ status) {
@@ -136,31 +138,37 @@ __global__ __launch_bounds__(kSelThreads) void k_top_pages(
   }
   const int tid = threadIdx.x;
   int32_t* out = kept + (size_t)bg * p_max;
-  for (int i = P + tid; i < p_max; i += kSelThreads) out[i] = -1;
+  for (int i = P + tid; i < p_max; i += kTopPThreads) out[i] = -1;
   if (tid == 0) kept_count[bg] = P;
   if (P == 0) return;
 
-  const int items = (Np + kSelThreads - 1) / kSelThreads;
-  const int i0 = tid * items;
   const float* sc = scores + (size_t)bg * NpCap;
-  uint32_t key[kTopPItems];
+  float x[kTopPItems];
+  bool pr[kTopPItems];
 #pragma unroll
-  for (int i = 0; i < kTopPItems; ++i)
-    key[i] = (i < items && i0 + i < Np) ? orderable_key(sc[i0 + i]) : 0u;
-  top_largest_ordered<kSelThreads, kTopPItems>(key, items, P, sh,
-                                               [&](int pos, int c) { out[pos] = c; });
+  for (int i = 0; i < kTopPItems; ++i) {
+    const int c = i * kTopPThreads + tid;
+    x[i] = sc[min(c, Np - 1)];  // clamped, not branched: the loads overlap
+    pr[i] = c < Np;
+  }
+  top_largest_strided<kTopPThreads, kTopPItems>(x, pr, P, sh,
+                                                [&](int pos, int c) { out[pos] = c; });
 }
 
 // ------------------------------------------------------------------ S5+S6
 // Candidates are the rows of the kept pages in kept order, which is ascending
-// position order: candidate c = (kept slot c/16, row c%16).  Candidate
-// c = i*1024 + tid is held by thread tid in register slot i.
-//   pass 1: H for every candidate (coalesced 16-byte code loads), LDS histogram;
-//   threshold: the smallest H value T whose cumulative count reaches top_k;
-//   pass 2: ordered selection -- H < T, or H == T among the first `need` --
-//           with positions from wave ballots plus a scan over (slot, wave).
+// position order: candidate c = (kept slot c/16, row c%16), held by thread
+// c % 1024 in register slot c / 1024.
+//   pass 1: H for every candidate -- the kept list is staged in LDS and the
+//           16-byte code loads are issued 16 at a time (clamped rows, no
+//           branches) -- into an LDS histogram (4 copies spread same-bin atomics);
+//   threshold: the smallest H value T whose cumulative count reaches top_k,
+//           and how many candidates with H == T are taken (need);
+//   pass 2: ordered compaction on key = 4096 - H (larger key = smaller H).
 constexpr int kHamItems = kMaxCand / kSelThreads;  // 32
 constexpr int kHamBins = 128 * kMaxG + 1;           // 2049
+constexpr int kHistCopies = 4;
+constexpr int kHamBatch = 16;
 
 __global__ __launch_bounds__(kSelThreads) void k_hamming_topk(
     const uint32_t* __restrict__ q_codes, const uint32_t* __restrict__ codes,
@@ -168,11 +176,12 @@ __global__ __launch_bounds__(kSelThreads) void k_hamming_topk(
     const int32_t* __restrict__ kept_count, int p_max, int top_k, int Hq, int Hkv, int Lcap,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, uint16_t* __restrict__ dist,
     uint32_t* __restrict__ status) {
-  __shared__ int hist[kHamBins];
+  __shared__ int hist[kHistCopies][kHamBins];
+  __shared__ int skept[kMaxCand / kPS];
   __shared__ uint32_t sq[kMaxG * kNW];
-  __shared__ int cnt_lt[kHamItems * 16], cnt_eq[kHamItems * 16];
-  __shared__ int s_T, s_need;
+  __shared__ int s_T, s_need, s_valid;
   __shared__ int scan_lds[kSelThreads / kWave + 1];
+  __shared__ TopScratch sh;
 
   const int bg = blockIdx.x;
   const int b = bg / Hkv;
@@ -180,53 +189,72 @@ __global__ __launch_bounds__(kSelThreads) void k_hamming_topk(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
-  const int l = tid & 63;
   const int L = checked_len(seq_len, b, Lcap, g == 0 ? status : nullptr);
   const int P = L > 0 ? min(kept_count[bg], p_max) : 0;
   const int ncand = P * kPS;
   const int nbins = 128 * G + 1;
 
   if (tid < G * kNW) sq[tid] = q_codes[((size_t)b * Hq + (size_t)g * G) * kNW + tid];
-  for (int i = tid; i < nbins; i += kSelThreads) hist[i] = 0;
+  for (int i = tid; i < P; i += kSelThreads) skept[i] = kept[(size_t)bg * p_max + i];
+  for (int i = tid; i < kHistCopies * kHamBins; i += kSelThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
 
-  const int32_t* kp = kept + (size_t)bg * p_max;
   const uint32_t* cb = codes + (size_t)bg * Lcap * kNW;
   const int items = (ncand + kSelThreads - 1) / kSelThreads;
-  // distances (<= 2048, or 0xFFFF for absent candidates) packed two per register
-  uint32_t Hp[kHamItems / 2];
+  int* my_hist = hist[w & (kHistCopies - 1)];
+  int H[kHamItems];
 #pragma unroll
-  for (int i = 0; i < kHamItems / 2; ++i) Hp[i] = 0xFFFFFFFFu;
-#define HHR_H(i) ((int)((Hp[(i) >> 1] >> (16 * ((i) & 1))) & 0xFFFFu))
+  for (int i = 0; i < kHamItems; ++i) H[i] = -1;  // absent
 #pragma unroll
-  for (int i = 0; i < kHamItems; ++i) {
-    const int c = i * kSelThreads + tid;
-    if (i < items && c < ncand) {
-      const int page = kp[c >> 4];
-      const int t = page * kPS + (c & 15);
-      if (page >= 0 && t < L) {
-        const u32x4 code = *(const u32x4*)(cb + (size_t)t * kNW);
-        int h = 0;
-        for (int qh = 0; qh < G; ++qh) {
-          h += __popc(code[0] ^ sq[qh * kNW + 0]) + __popc(code[1] ^ sq[qh * kNW + 1]) +
-               __popc(code[2] ^ sq[qh * kNW + 2]) + __popc(code[3] ^ sq[qh * kNW + 3]);
-        }
-        Hp[i >> 1] = (Hp[i >> 1] & ~(0xFFFFu << (16 * (i & 1)))) | ((uint32_t)h << (16 * (i & 1)));
-        atomicAdd(&hist[h], 1);
+  for (int i0 = 0; i0 < kHamItems; i0 += kHamBatch) {
+    if (i0 < items) {
+      u32x4 code[kHamBatch];
+      bool ok[kHamBatch];
+#pragma unroll
+      for (int j = 0; j < kHamBatch; ++j) {
+        const int c = (i0 + j) * kSelThreads + tid;
+        const int page = skept[min(c, ncand - 1) >> 4];
+        const int t = page * kPS + (c & 15);
+        ok[j] = c < ncand && page >= 0 && t < L;
+        code[j] = *(const u32x4*)(cb + (size_t)(ok[j] ? t : 0) * kNW);
       }
-      if (dist) dist[(size_t)bg * p_max * kPS + c] = (uint16_t)HHR_H(i);
+#pragma unroll
+      for (int j = 0; j < kHamBatch; ++j) {
+        if (ok[j]) {
+          int h = 0;
+          for (int qh = 0; qh < G; ++qh) {
+            h += __popc(code[j][0] ^ sq[qh * kNW + 0]) + __popc(code[j][1] ^ sq[qh * kNW + 1]) +
+                 __popc(code[j][2] ^ sq[qh * kNW + 2]) + __popc(code[j][3] ^ sq[qh * kNW + 3]);
+          }
+          H[i0 + j] = h;
+          atomicAdd(&my_hist[h], 1);
+        }
+      }
+    }
+  }
+  if (dist) {
+#pragma unroll
+    for (int i = 0; i < kHamItems; ++i) {
+      const int c = i * kSelThreads + tid;
+      if (c < ncand) dist[(size_t)bg * p_max * kPS + c] = H[i] < 0 ? (uint16_t)0xFFFF : (uint16_t)H[i];
     }
   }
   __syncthreads();
 
   // threshold over bins in ascending H
-  __shared__ int s_valid;
   {
     const int per = (nbins + kSelThreads - 1) / kSelThreads;  // <= 3
     const int b0 = tid * per;
     int local = 0;
-    for (int i = 0; i < per; ++i)
-      if (b0 + i < nbins) local += hist[b0 + i];
+    for (int i = 0; i < per; ++i) {
+      if (b0 + i < nbins) {
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < kHistCopies; ++k) c += hist[k][b0 + i];
+        hist[0][b0 + i] = c;
+        local += c;
+      }
+    }
     int total;
     const int ex = block_exclusive_scan<kSelThreads, int>(local, scan_lds, &total);
     if (tid == 0) {
@@ -239,7 +267,7 @@ __global__ __launch_bounds__(kSelThreads) void k_hamming_topk(
       int run = ex;
       for (int i = 0; i < per; ++i) {
         if (b0 + i < nbins) {
-          const int c = hist[b0 + i];
+          const int c = hist[0][b0 + i];
           if (run < top_k && run + c >= top_k) {
             s_T = b0 + i;
             s_need = top_k - run;
@@ -250,68 +278,17 @@ __global__ __launch_bounds__(kSelThreads) void k_hamming_topk(
     }
     __syncthreads();
   }
-  const int T = s_T;
-  const int need = s_need;
   const int count = min(top_k, s_valid);
-
-  // pass 2: per (slot i, wave w) counts of H < T and H == T
+  uint32_t key[kHamItems];
 #pragma unroll
-  for (int i = 0; i < kHamItems; ++i) {
-    if (i < items) {
-      const uint64_t blt = __ballot(HHR_H(i) < T);
-      const uint64_t beq = __ballot(HHR_H(i) == T);
-      if (l == 0) {
-        cnt_lt[i * 16 + w] = popc64(blt);
-        cnt_eq[i * 16 + w] = popc64(beq);
-      }
-    }
-  }
-  __syncthreads();
-  if (w == 0) {
-    // exclusive scan over the (slot i, wave w) sequence, 16 waves per slot
-    const int n = items * 16;
-    const int per = (n + kWave - 1) / kWave;
-    int a = 0, e2 = 0;
-    for (int k = 0; k < per; ++k) {
-      const int j = l * per + k;
-      if (j < n) {
-        a += cnt_lt[j];
-        e2 += cnt_eq[j];
-      }
-    }
-    int ra = wave_inclusive_scan(a) - a;
-    int re = wave_inclusive_scan(e2) - e2;
-    for (int k = 0; k < per; ++k) {
-      const int j = l * per + k;
-      if (j < n) {
-        const int ta = cnt_lt[j], te = cnt_eq[j];
-        cnt_lt[j] = ra;
-        cnt_eq[j] = re;
-        ra += ta;
-        re += te;
-      }
-    }
-  }
-  __syncthreads();
-
+  for (int i = 0; i < kHamItems; ++i) key[i] = H[i] < 0 ? 0u : (uint32_t)(4096 - H[i]);
+  const uint32_t T = s_T == nbins ? 0u : (uint32_t)(4096 - s_T);
   int32_t* out = sel_idx + (size_t)bg * top_k;
-  const uint64_t mlt = lanemask_lt();
-#pragma unroll
-  for (int i = 0; i < kHamItems; ++i) {
-    if (i < items) {
-      const int Hi = HHR_H(i);
-      const uint64_t blt = __ballot(Hi < T);
-      const uint64_t beq = __ballot(Hi == T);
-      const int c = i * kSelThreads + tid;
-      const int lt_before = cnt_lt[i * 16 + w] + popc64(blt & mlt);
-      const int eq_before = cnt_eq[i * 16 + w] + popc64(beq & mlt);
-      const bool take = Hi < T || (Hi == T && eq_before < need);
-      if (take) out[lt_before + min(eq_before, need)] = kp[c >> 4] * kPS + (c & 15);
-    }
-  }
+  compact_strided<kSelThreads, kHamItems>(key, T, s_need, sh, [&](int pos, int c) {
+    out[pos] = skept[c >> 4] * kPS + (c & 15);
+  });
   for (int i = count + tid; i < top_k; i += kSelThreads) out[i] = -1;
   if (tid == 0) sel_count[bg] = count;
-#undef HHR_H
 }
 
 }  // namespace
@@ -320,10 +297,9 @@ hipError_t launch_page_scores(const hhr_shape& s, const float* q_rot, const int3
                               const float* meta, float* scores, uint32_t* status,
                               hipStream_t stream) {
   const int NpCap = s.max_ctx / kPS;
-  const int pages_per_wg = 128;
-  dim3 grid((NpCap + pages_per_wg - 1) / pages_per_wg, s.batch * s.n_kv_heads);
+  dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, s.batch * s.n_kv_heads);
   hipLaunchKernelGGL(k_page_scores, grid, dim3(256), 0, stream, q_rot, seq_len, meta, scores,
-                     status, s.n_q_heads, s.n_kv_heads, s.max_ctx, pages_per_wg);
+                     status, s.n_q_heads, s.n_kv_heads, s.max_ctx);
   return hipGetLastError();
 }
 
@@ -331,7 +307,7 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
                             int32_t keep_num, int32_t keep_den, int32_t keep_abs, int32_t p_max,
                             int32_t* kept, int32_t* kept_count, uint32_t* status,
                             hipStream_t stream) {
-  hipLaunchKernelGGL(k_top_pages, dim3(s.batch * s.n_kv_heads), dim3(kSelThreads), 0, stream,
+  hipLaunchKernelGGL(k_top_pages, dim3(s.batch * s.n_kv_heads), dim3(kTopPThreads), 0, stream,
                      scores, seq_len, keep_num, keep_den, keep_abs, p_max, s.n_kv_heads,
                      s.max_ctx, kept, kept_count, status);
   return hipGetLastError();

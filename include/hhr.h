@@ -42,6 +42,16 @@
  *     workspace status word (read it with hhr_read_device_status).
  *   - Results are deterministic: repeated calls on the same inputs give
  *     bit-identical outputs.
+ *   - Workspace: device memory of at least the size the matching
+ *     *_workspace_size() function returns.  It starts with a control block
+ *     (the device status word at offset 0, then one split-K ticket counter
+ *     per (b, g) at offset 256) that must be zero before the workspace is
+ *     first used -- allocate it zero-filled.  Every call leaves the tickets
+ *     zero again; the status word keeps its error bits until
+ *     hhr_read_device_status clears it.  The control block sits at the same
+ *     offsets in every layout, so one workspace may serve every entry point.
+ *     Calls that share a workspace must not overlap in time (order them on
+ *     one stream).
  */
 #ifndef HHR_H_
 #define HHR_H_
