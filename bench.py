@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="replay the rotation as one HIP graph")
+    ap.add_argument("--path", choices=("decode", "staged"), default="decode",
+                    help="decode: one hhr_decode call per step; staged: hhr_select then "
+                         "hhr_sparse_decode")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -126,8 +129,13 @@ def main():
 
     def step(i):
         lay = layers[i % args.layers]
-        hhr.hhr_decode(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"], lay["K"],
-                       lay["V"], *keep, top_k, scale, sel, cnt, out, ws)
+        if args.path == "decode":
+            hhr.hhr_decode(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"],
+                           lay["K"], lay["V"], *keep, top_k, scale, sel, cnt, out, ws)
+        else:
+            hhr.hhr_select(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"], *keep,
+                           top_k, sel, cnt, ws)
+            hhr.hhr_sparse_decode(shape, q, lay["K"], lay["V"], sel, cnt, top_k, scale, out, ws)
 
     for i in range(args.warmup):
         step(i)
@@ -243,7 +251,9 @@ def main():
         "config": {"workload": args.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "ctx": int(seq_np.max()), "page_size": 16, "code_bits": 128,
                    "keep": f"{keep[0]}/{keep[1]}" if keep[2] == 0 else keep[2], "top_k": top_k,
-                   "layers_rotated": args.layers, "hip_graph": bool(graph is not None)},
+                   "layers_rotated": args.layers, "hip_graph": bool(graph is not None),
+                   "entry": "hhr_decode" if args.path == "decode"
+                   else "hhr_select+hhr_sparse_decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "step_algorithmic_bytes": step_bytes,

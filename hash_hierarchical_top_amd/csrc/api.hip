@@ -154,7 +154,17 @@ uint32_t* status_of(void* workspace) { return reinterpret_cast<uint32_t*>(worksp
 namespace hhr {
 
 size_t ctrl_bytes(const hhr_shape& s) {
-  return kAlign + align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+  return kAlign + align_up(kCountersPerGroup * (size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+}
+
+HamScratch ham_scratch(const hhr_shape& s, int32_t p_max) {
+  const size_t BG = (size_t)s.batch * s.n_kv_heads;
+  const size_t G = (size_t)(s.n_q_heads / s.n_kv_heads);
+  HamScratch h;
+  h.dist = ctrl_bytes(s);
+  h.hist = h.dist + align_up(BG * (size_t)p_max * kPS * sizeof(uint16_t));
+  h.end = h.hist + align_up(BG * (size_t)ham_chunks(p_max) * (128 * G + 1) * sizeof(int));
+  return h;
 }
 
 AttnWorkspace attn_workspace(const hhr_shape& s, int32_t top_k) {
@@ -179,9 +189,14 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   };
   const size_t BHq = (size_t)s.batch * s.n_q_heads;
   const size_t BHkv = (size_t)s.batch * s.n_kv_heads;
-  // control block: status word, then the split-K tickets (same offsets in every layout)
+  // control block: status word and group tickets, then kCountersPerGroup
+  // counters per (b, g)
+  // (same offsets in every layout)
   w.ctrl = take(kAlign);
-  w.attn_tickets = take(BHkv * sizeof(uint32_t));
+  w.counters = take(kCountersPerGroup * BHkv * sizeof(uint32_t));
+  const HamScratch hs = ham_scratch(s, w.p_max);
+  w.ham_dist = take(hs.hist - hs.dist);
+  w.ham_hist = take(hs.end - hs.hist);
   w.q_rot = take(BHq * kD * sizeof(float));
   w.q_codes = take(BHq * kNW * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
@@ -347,10 +362,15 @@ hhr_status hhr_hamming_topk(const hhr_shape* shape, const uint32_t* q_codes,
   if (p_max < 1 || p_max > shape->max_ctx / hhr::kPS)
     return fail(HHR_ERR_INVALID_ARG, "p_max must be in [1, max_ctx / 16]");
   HHR_TRY(check_p_max(p_max));
-  if (workspace_bytes < hhr::kAlign) return fail(HHR_ERR_WORKSPACE, "workspace too small");
+  const hhr::HamScratch hs = hhr::ham_scratch(*shape, p_max);
+  if (workspace_bytes < hs.end)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, hs.end);
+  char* base = static_cast<char*>(workspace);
+  uint16_t* d = dist != nullptr ? dist : reinterpret_cast<uint16_t*>(base + hs.dist);
   HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count, p_max,
-                                      top_k, sel_idx, sel_count, dist, status_of(workspace),
-                                      as_stream(stream)),
+                                      top_k, sel_idx, sel_count, d,
+                                      reinterpret_cast<int*>(base + hs.hist),
+                                      status_of(workspace), as_stream(stream)),
              "hamming_topk launch");
   return ok();
 }
@@ -421,7 +441,9 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
                                    ws.p_max, kept, kept_count, status, stream),
              "top_pages launch");
   HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count,
-                                      ws.p_max, top_k, sel_idx, sel_count, nullptr, status,
+                                      ws.p_max, top_k, sel_idx, sel_count,
+                                      reinterpret_cast<uint16_t*>(base + ws.ham_dist),
+                                      reinterpret_cast<int*>(base + ws.ham_hist), status,
                                       stream),
              "hamming_topk launch");
   *layout = ws;

@@ -9,6 +9,7 @@
 
 #include "hhr_device.h"
 #include "hhr_internal.h"
+#include "stages.h"
 
 namespace hhr {
 
@@ -201,76 +202,13 @@ __global__ __launch_bounds__(256) void k_append_encode(
   }
 }
 
-// S2: one workgroup (512 threads) per (b, KV head) encodes the G queries of the
-// group.  Thread t owns columns 4*(t%64) .. +3 of [R | W] (256 columns) over
-// the 16 input dims 16*(t/64) .. +15: it issues its 16 float4 loads at once,
-// keeps them in registers, and forms partial dot products for 4 query heads
-// at a time; the 8 partials of each output are summed in LDS in fixed order.
-// Outputs: q' = q R (columns < 128) and the sign bits of q W (packed by ballot).
-constexpr int kQeThreads = 512;
-
+// S2: one workgroup (512 threads) per (b, KV head) encodes the G queries of the group.
 __global__ __launch_bounds__(kQeThreads) void k_encode_queries(
     const float* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
     float* __restrict__ q_rot, uint32_t* __restrict__ q_codes, int Hq, int Hkv) {
-  __shared__ float sq[kMaxG][kD];
-  __shared__ float red[8][4][2 * kD];
+  __shared__ QencSmem sm;
   const int bg = blockIdx.x;
-  const int b = bg / Hkv;
-  const int g = bg % Hkv;
-  const int G = Hq / Hkv;
-  const int tid = threadIdx.x;
-  const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
-  for (int i = tid; i < G * kD; i += kQeThreads) sq[i / kD][i % kD] = q[qbase + i];
-
-  const int cg = tid & 63;
-  const int dg = tid >> 6;
-  const int c0 = 4 * cg;  // column in [0, 256)
-  const float* M = (c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kD + (c0 - kD));
-  floatx4 m[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) m[j] = *(const floatx4*)(M + (size_t)(16 * dg + j) * kD);
-  __syncthreads();
-
-  for (int hc = 0; hc < G; hc += 4) {
-    floatx4 acc[4];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      acc[hh] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (hc + hh < G) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float x = sq[hc + hh][16 * dg + j];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[hh][k] = fmaf(x, m[j][k], acc[hh][k]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) red[dg][hh][c0 + k] = acc[hh][k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int o = tid + kQeThreads * pass;  // (head hh, column col) of this chunk
-      const int hh = o >> 8;
-      const int col = o & 255;
-      float v = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v += red[k][hh][col];
-      const int h = hc + hh;
-      if (col < kD) {
-        if (h < G) q_rot[qbase + (size_t)hh * kD + (size_t)hc * kD + col] = v;
-      } else {
-        const uint64_t bits = __ballot(v >= 0.0f);
-        if ((tid & 63) == 0 && h < G) {
-          const int word = (col - kD) >> 5;  // col is the wave's first column here
-          uint32_t* dst = q_codes + ((size_t)b * Hq + (size_t)g * G + h) * kNW + word;
-          dst[0] = (uint32_t)bits;
-          dst[1] = (uint32_t)(bits >> 32);
-        }
-      }
-    }
-    __syncthreads();
-  }
+  qenc_group<false>(bg / Hkv, bg % Hkv, Hq, Hkv, q, R, W, q_rot, q_codes, sm);
 }
 
 }  // namespace

@@ -9,4 +9,8 @@ constexpr int kPS = 16;    // page size
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kMaxG = 16;  // query heads per KV head
 
+// Fine top-k distance chunks: 64 kept pages (1024 candidates) per workgroup.
+constexpr int kHamChunkPages = 64;
+constexpr int ham_chunks(int pages) { return (pages + kHamChunkPages - 1) / kHamChunkPages; }
+
 }  // namespace hhr

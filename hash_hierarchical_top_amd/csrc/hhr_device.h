@@ -43,16 +43,91 @@ __device__ __forceinline__ uint32_t orderable_key(float x) {
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Cross-lane exchanges use DPP (a VALU operand modifier, a few cycles) rather
+// than __shfl (an LDS permute, ~100 cycles).  gfx9 DPP controls: quad_perm,
+// row_shr:n (lane i of a 16-lane row reads lane i-n, zero past the row
+// start), row_half_mirror / row_mirror (lane j of 8 / 16 reads lane 7-j /
+// 15-j), row_bcast:15 / :31 (lane 15 / 31 feeds the following rows).  Every
+// wave op here needs all 64 lanes active.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowShr = 0x110;   // + n, 1 <= n <= 15
+constexpr int kRowMirror = 0x140;
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Butterfly inside each 16-lane row, then the four row results combined in
+// scalar registers; every lane returns the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v += dpp_f<dpp::kQuadXor1>(v);
+  v += dpp_f<dpp::kQuadXor2>(v);
+  v += dpp_f<dpp::kRowHalfMirror>(v);
+  v += dpp_f<dpp::kRowMirror>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Sum over the 16 lanes of each row; every lane of the row gets the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<dpp::kQuadXor1>(v);
+  v += dpp_f<dpp::kQuadXor2>(v);
+  v += dpp_f<dpp::kRowHalfMirror>(v);
+  v += dpp_f<dpp::kRowMirror>(v);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_f<dpp::kQuadXor1>(v));
+  v = fmaxf(v, dpp_f<dpp::kQuadXor2>(v));
+  v = fmaxf(v, dpp_f<dpp::kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<dpp::kRowMirror>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+__device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<dpp::kQuadXor1>(v);
+  v += dpp_i<dpp::kQuadXor2>(v);
+  v += dpp_i<dpp::kRowHalfMirror>(v);
+  v += dpp_i<dpp::kRowMirror>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  int x = (int)v;
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<dpp::kQuadXor1>(x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<dpp::kQuadXor2>(x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<dpp::kRowHalfMirror>(x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<dpp::kRowMirror>(x));
+  return min(min((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  int x = (int)v;
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<dpp::kQuadXor1>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<dpp::kQuadXor2>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<dpp::kRowHalfMirror>(x));
+  x = (int)max((uint32_t)x, (uint32_t)dpp_i<dpp::kRowMirror>(x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
 }
 
 // Lanes below this one in the wave.
@@ -63,16 +138,20 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
 
-// Inclusive scan across the wave.
+// Inclusive scan across the wave (32-bit integers): Hillis-Steele inside
+// each 16-lane row with row_shr 1, 2, 4, 8, then row totals carried forward
+// with row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3).
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    T t = __shfl_up(x, off);
-    if (l >= off) x += t;
-  }
-  return x;
+  static_assert(sizeof(T) == 4, "32-bit scan");
+  int v = __builtin_bit_cast(int, x);
+  v += dpp_i<dpp::kRowShr + 1>(v);
+  v += dpp_i<dpp::kRowShr + 2>(v);
+  v += dpp_i<dpp::kRowShr + 4>(v);
+  v += dpp_i<dpp::kRowShr + 8>(v);
+  v += dpp_i<dpp::kRowBcast15, 0xA>(v);
+  v += dpp_i<dpp::kRowBcast31, 0xC>(v);
+  return __builtin_bit_cast(T, v);
 }
 
 // Exclusive scan over a whole workgroup of NT threads (NT/64 waves <= 64).
@@ -98,4 +177,39 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* lds, T* total) {
   return lds[w] + inc - v;
 }
 
+// ---------------------------------------------------------------- coherence
+// Data handed from one workgroup to another inside a kernel crosses XCDs,
+// whose L2 caches are not coherent with each other.  A device-scope fence
+// (__threadfence) writes back and invalidates a whole L2, which costs tens of
+// microseconds when every workgroup does it; instead such data is written
+// and read with agent-scope (sc1) accesses, which the L2 does not hold stale,
+// and a producer publishes with s_waitcnt(0) + a relaxed agent-scope atomic.
+// Mem<false> is the plain path for data that only crosses kernel boundaries.
+template <bool COH>
+struct Mem {
+  template <typename T>
+  static __device__ __forceinline__ T ld(const T* p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+  }
+  template <typename T>
+  static __device__ __forceinline__ void st(T* p, T v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+  }
+};
+
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
 }  // namespace hhr
+

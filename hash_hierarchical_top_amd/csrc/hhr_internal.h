@@ -20,10 +20,18 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Byte offsets of the decode workspace regions.  Region 0 (the control block)
 // holds the device status word at offset 0.
 struct Workspace {
-  size_t ctrl = 0, q_rot = 0, q_codes = 0, scores = 0, kept = 0, kept_count = 0,
-         attn_tickets = 0, attn_part = 0, total = 0;
+  size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, q_rot = 0, q_codes = 0, scores = 0,
+         kept = 0, kept_count = 0, attn_part = 0, total = 0;
   int32_t p_max = 0, n_split = 0;
 };
+
+// Scratch of the fine top-k (distances, chunk histograms), at offsets that
+// depend only on the shape and p_max, right after the control block.
+struct HamScratch {
+  size_t dist = 0, hist = 0, end = 0;
+};
+HamScratch ham_scratch(const hhr_shape& s, int32_t p_max);
+constexpr int kCountersPerGroup = 8;  // control words per (b, g) after the first 256 bytes
 
 // Workspace of hhr_sparse_decode alone: control block, tickets, partials.
 struct AttnWorkspace {
@@ -53,13 +61,17 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                                const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
-                               int32_t* sel_idx, int32_t* sel_count, uint16_t* dist,
+                               int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* chist,
                                uint32_t* status, hipStream_t stream);
 hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* k_cache,
                                 const void* v_cache, const int32_t* sel_idx,
                                 const int32_t* sel_count, int32_t top_k, float scale, float* out,
                                 float* part, int32_t n_split, uint32_t* status,
                                 hipStream_t stream);
+
+// Control block: status word at byte 0; bytes 64..255 and kCountersPerGroup
+// words per (b, g) from byte 256 are reserved for cross-workgroup scheduling.
+constexpr size_t kCtrlTicketsOffset = 64;
 
 // ---- HISA ----
 struct HisaWorkspace {

@@ -110,14 +110,11 @@ __global__ __launch_bounds__(256) void k_hisa_block_scores(
       part = fmaf(w[(size_t)b * Hi + h], fmaxf(dot, 0.f), part);
     }
   }
-  part += __shfl_xor(part, 8);
-  part += __shfl_xor(part, 4);
-  part += __shfl_xor(part, 2);
-  part += __shfl_xor(part, 1);
+  part = row_sum16(part);
   if (hg == 0 && blk0 + bl < Nb) block_scores[(size_t)b * NbCap + blk0 + bl] = part;
 }
 
-// H3: exact top keep_blocks blocks of one query (block c = i*1024 + tid in slot i).
+// H3: exact top keep_blocks blocks of one query (thread tid takes a run of consecutive blocks).
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
     const float* __restrict__ block_scores, const int32_t* __restrict__ seq_len,
     int keep_blocks, int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
@@ -130,16 +127,16 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   const int tid = threadIdx.x;
   int32_t* out = kept + (size_t)b * keep_blocks;
   const float* sc = block_scores + (size_t)b * NbCap;
-  float x[kHisaItems];
-  bool pr[kHisaItems];
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
 #pragma unroll
   for (int i = 0; i < kHisaItems; ++i) {
     const int c = i * kHisaThreads + tid;
-    x[i] = sc[min(c, max(Nb - 1, 0))];
-    pr[i] = c < Nb;
+    sbuf[c] = sc[min(c, max(Nb - 1, 0))];
   }
-  const int cnt = top_largest_strided<kHisaThreads, kHisaItems>(
-      x, pr, keep_blocks, sh, [&](int pos, int c) { out[pos] = c; });
+  __syncthreads();
+  const int cnt = top_largest_lds<kHisaThreads>(
+      sbuf, Nb, [](int) { return true; }, keep_blocks, sh,
+      [&](int pos, int c) { out[pos] = c; });
   for (int i = cnt + tid; i < keep_blocks; i += kHisaThreads) out[i] = -1;
   if (tid == 0) kept_count[b] = cnt;
 }
@@ -208,19 +205,16 @@ __global__ __launch_bounds__(256) void k_hisa_token_scores(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         part = fmaf(wq[nt], fmaxf(acc[nt][j] * (sqh[nt] * sk), 0.f), part);
-      part += __shfl_xor(part, 8);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 1);
+      part = row_sum16(part);
       if (lrow == 0) ts[16 * mt + 4 * lgrp + j] = tt < L ? part : -__builtin_huge_valf();
     }
   }
 }
 
 // H5: exact top-k over the kept blocks' valid tokens by (larger s, lower t);
-// candidate c = (kept slot c / block, row c % block) sits in slot c / 1024 of
-// thread c % 1024.  Kept blocks are ascending, so candidate order is position
-// order and ties go to the lower position.
+// candidate c = (kept slot c / block, row c % block).  Kept blocks are
+// ascending, so candidate order is position order and ties go to the lower
+// position.
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
     const float* __restrict__ token_scores, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
@@ -237,19 +231,21 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
   for (int i = tid; i < kc; i += kHisaThreads) skept[i] = kept[(size_t)b * keep_blocks + i];
   __syncthreads();
   const float* ts = token_scores + (size_t)b * keep_blocks * block;
-  float x[kHisaItems];
-  bool pr[kHisaItems];
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
 #pragma unroll
   for (int i = 0; i < kHisaItems; ++i) {
     const int c = i * kHisaThreads + tid;
-    const int cc = min(c, max(ncand - 1, 0));
-    x[i] = ts[cc];
-    const int blk = skept[cc / block];
-    pr[i] = c < ncand && blk >= 0 && blk * block + c % block < L;
+    sbuf[c] = ts[min(c, max(ncand - 1, 0))];
   }
+  __syncthreads();
+  auto present = [&](int c) {
+    const int blk = skept[c / block];
+    return blk >= 0 && blk * block + c % block < L;
+  };
   int32_t* out = sel_idx + (size_t)b * top_k;
-  const int cnt = top_largest_strided<kHisaThreads, kHisaItems>(
-      x, pr, top_k, sh, [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; });
+  const int cnt = top_largest_lds<kHisaThreads>(
+      sbuf, ncand, present, top_k, sh,
+      [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; });
   for (int i = cnt + tid; i < top_k; i += kHisaThreads) out[i] = -1;
   if (tid == 0) sel_count[b] = cnt;
 }

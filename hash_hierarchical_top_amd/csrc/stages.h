@@ -1,0 +1,701 @@
+// Device functions of the decode steps S2..S7, shared by the kernels behind
+// the entry points, so every composition computes bit-identical results.
+// Internal header.
+//
+// COH selects agent-scope (sc1) accesses, for kernels in which one workgroup
+// consumes data that another workgroup of the same launch produced (see Mem<>
+// in hhr_device.h); COH = false is the plain path between launches.
+#pragma once
+
+#include <type_traits>
+
+#include "hhr_device.h"
+#include "hhr_internal.h"
+#include "topk_device.h"
+
+namespace hhr {
+
+constexpr uint32_t kSpinLimit = 1u << 18;  // polls (each up to ~1000 cycles apart): well under a second
+
+// One lane waits until *flag >= target (agent-scope polls).  On timeout it sets
+// HHR_DEV_TIMEOUT and returns, and once that bit is set every other wait gives
+// up at its next check, so a kernel always terminates promptly.
+__device__ __forceinline__ void spin_until_geq(const uint32_t* flag, uint32_t target,
+                                               uint32_t* status) {
+  // exponential back-off up to ~1000 cycles keeps hundreds of waiting
+  // workgroups from hammering the few cache lines that hold the counters
+  uint32_t n = 0, nap = 1;
+  while (ld_agent_u32(flag) < target) {
+    ++n;
+    if ((n & 63u) == 0u && status && (ld_agent_u32(status) & HHR_DEV_TIMEOUT)) return;
+    if (n >= kSpinLimit) {
+      if (status) atomicOr(status, HHR_DEV_TIMEOUT);
+      return;
+    }
+    for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(1);
+    if (nap < 16u) nap <<= 1;
+  }
+}
+
+// ============================================================== S2: query
+// Thread t < 512 owns columns 4*(t%64) .. +3 of [R | W] (256 columns) over the
+// 16 input dims 16*((t/64)%8) .. +15: it issues its 16 float4 loads at once,
+// keeps them in registers and forms partial dot products for 4 query heads at
+// a time; the 8 partials of each output are summed in LDS in fixed order.
+// Outputs q' = q R (columns < 128) and the sign bits of q W (packed by ballot).
+// Every thread of the workgroup must call (it contains barriers); threads
+// >= 512 only take part in the barriers.
+constexpr int kQeThreads = 512;
+
+struct QencSmem {
+  float sq[kMaxG][kD];
+  float red[8][4][2 * kD];
+};
+
+template <bool COH>
+__device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
+                           const float* __restrict__ R, const float* __restrict__ W,
+                           float* q_rot, uint32_t* q_codes, QencSmem& sm) {
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const bool act = tid < kQeThreads;
+  const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
+  if (act)
+    for (int i = tid; i < G * kD; i += kQeThreads) sm.sq[i / kD][i % kD] = q[qbase + i];
+  const int cg = tid & 63;
+  const int dg = (tid >> 6) & 7;
+  const int c0 = 4 * cg;  // column in [0, 256)
+  const float* M = (c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kD + (c0 - kD));
+  floatx4 m[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    m[j] = act ? *(const floatx4*)(M + (size_t)(16 * dg + j) * kD) : floatx4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int hc = 0; hc < G; hc += 4) {
+    if (act) {
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (hc + hh < G) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float x = sm.sq[hc + hh][16 * dg + j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = fmaf(x, m[j][k], acc[k]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sm.red[dg][hh][c0 + k] = acc[k];
+      }
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int o = tid + kQeThreads * pass;  // (head hh, column col) of this chunk
+        const int hh = o >> 8;
+        const int col = o & 255;
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += sm.red[k][hh][col];
+        const int h = hc + hh;
+        if (col < kD) {
+          if (h < G) Mem<COH>::st(q_rot + qbase + (size_t)h * kD + col, v);
+        } else {
+          const uint64_t bits = __ballot(v >= 0.0f);
+          if ((tid & 63) == 0 && h < G) {
+            const int word = (col - kD) >> 5;  // col is the wave's first column here
+            uint32_t* dst = q_codes + ((size_t)b * Hq + (size_t)g * G + h) * kNW + word;
+            Mem<COH>::st(dst, (uint32_t)bits);
+            Mem<COH>::st(dst + 1, (uint32_t)(bits >> 32));
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================== S3: bound
+// s(p) = sum_h sum_d max(q'_hd mn_pd, q'_hd mx_pd).  Because mn <= mx,
+// max(q mn, q mx) = max(q,0) mx + min(q,0) mn, so per dimension the group
+// reduces to A_d = sum_h max(q'_hd, 0) and B_d = sum_h min(q'_hd, 0), and
+// s(p) = sum_d (A_d mx_pd + B_d mn_pd).
+//
+// One wave scores pages pb .. pb+15 (those < Np).  Lane (row r = l/16,
+// sub = l%16) handles pages pb + 4j + r (j = 0..3) and, in each, the 16-byte
+// pieces k = 0..3 at byte 256k + 16 sub (dims 2(sub + 16k) and +1), so every
+// load instruction reads four whole 256-byte runs.  All 16 loads are issued
+// first (addresses clamped, not branched on); if `ready` is given, lane 0 then
+// waits for the query encoding; a 4-value reduce-scatter over the 16 lanes of
+// a row leaves page pb + 4j + r in lanes with j = 2 b3 + b2.  The whole wave
+// must be active (cross-lane DPP exchanges).
+constexpr int kScorePagesPerWave = 16;
+
+template <bool COH, int NB = 1>
+__device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, int pb,
+                            const float* q_rot, const float* __restrict__ meta, float* scores,
+                            const uint32_t* ready, uint32_t* status) {
+  // NB consecutive 16-page batches pb, pb + 16, ...; every load of every batch
+  // is issued before any of them is used.
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  const int l = threadIdx.x & 63;
+  const int r = l >> 4;
+  const int sub = l & 15;
+  const float* mbase = meta + (size_t)bg * NpCap * kD * 2 + 4 * sub;
+  floatx4 m[NB][4][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = min(pb + kScorePagesPerWave * nb + 4 * j + r, Np - 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        m[nb][j][k] =
+            __builtin_nontemporal_load((const floatx4*)(mbase + (size_t)p * kD * 2 + 64 * k));
+    }
+  if (ready != nullptr && l == 0) spin_until_geq(ready, 1u, status);
+  float A[4][2], B[4][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) A[k][0] = A[k][1] = B[k][0] = B[k][1] = 0.f;
+  const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD + 2 * sub;
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float vx = Mem<COH>::ld(qr + (size_t)h * kD + 32 * k);
+      const float vy = Mem<COH>::ld(qr + (size_t)h * kD + 32 * k + 1);
+      A[k][0] += fmaxf(vx, 0.f);
+      B[k][0] += fminf(vx, 0.f);
+      A[k][1] += fmaxf(vy, 0.f);
+      B[k][1] += fminf(vy, 0.f);
+    }
+  }
+  const bool b3 = l & 8, b2 = l & 4;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)  // m = {mn[d0], mx[d0], mn[d1], mx[d1]}
+        x += A[k][0] * m[nb][j][k][1] + B[k][0] * m[nb][j][k][0] + A[k][1] * m[nb][j][k][3] +
+             B[k][1] * m[nb][j][k][2];
+      v[j] = x;
+    }
+    // partner lanes: 15 - sub (other 8-lane half), then 7 - (sub % 8) (other
+    // quad of the half), then the quad's own butterfly
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = b3 ? v[i] : v[i + 2];
+      const float keep = b3 ? v[i + 2] : v[i];
+      v[i] = keep + dpp_f<dpp::kRowMirror>(send);
+    }
+    {
+      const float send = b2 ? v[0] : v[1];
+      const float keep = b2 ? v[1] : v[0];
+      v[0] = keep + dpp_f<dpp::kRowHalfMirror>(send);
+    }
+    v[0] += dpp_f<dpp::kQuadXor2>(v[0]);
+    v[0] += dpp_f<dpp::kQuadXor1>(v[0]);
+    const int p = pb + kScorePagesPerWave * nb + 4 * ((b3 ? 2 : 0) + (b2 ? 1 : 0)) + r;
+    if ((l & 3) == 0 && p < Np) Mem<COH>::st(scores + (size_t)bg * NpCap + p, v[0]);
+  }
+}
+
+// ============================================================== S4: prune
+// Exact top-P of Np page scores in one workgroup of NT threads.  The scores
+// are first staged into LDS with coalesced loads (page c = i*NT + tid, eight
+// loads in flight per thread, addresses clamped instead of branched); the
+// selection then reads each thread's run of pages from there.  sbuf holds
+// kMaxCtx / kPS floats.  emit(pos, page) with pos ascending in page.
+template <int NT, bool COH, typename Emit>
+__device__ int top_pages_core(const float* sc, int Np, int P, float* sbuf, TopScratch& sh,
+                              Emit emit) {
+  constexpr int kB = 8;
+  const int tid = threadIdx.x;
+  const int last = max(Np - 1, 0);
+#pragma unroll 1
+  for (int c0 = 0; c0 < Np; c0 += kB * NT) {
+    float x[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) x[j] = Mem<COH>::ld(sc + min(c0 + j * NT + tid, last));
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int c = c0 + j * NT + tid;
+      if (c < Np) sbuf[c] = x[j];
+    }
+  }
+  __syncthreads();
+  return top_largest_lds<NT>(sbuf, Np, [](int) { return true; }, P, sh, emit);
+}
+
+__device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
+  if (Np <= 0) return 0;
+  if (keep_abs > 0) return min(Np, keep_abs);
+  return min(Np, max(1, (int)(((long long)keep_num * Np + keep_den - 1) / keep_den)));
+}
+
+// ====================================================== S5 + S6: fine top-k
+// Candidates are the rows of the kept pages in kept order, which is ascending
+// position order: candidate c = (kept slot c/16, row c%16).  Two stages:
+//   distances (many workgroups): chunk k holds the candidates of kept slots
+//     [64k, 64k + 64); each workgroup computes H for its chunk, writes it
+//     (0xFFFF for a row past the sequence end) and its chunk's histogram
+//     over H = 0 .. 128 G.  Spreading this over many CUs matters: per
+//     candidate it costs a 16-byte gather and ~50 vector ops;
+//   selection (one workgroup per (b, g)): sums the chunk histograms, finds
+//     the smallest H value T whose cumulative count reaches top_k and how
+//     many candidates with H == T are taken, then compacts in candidate
+//     order.
+constexpr int kHamBins = 128 * kMaxG + 1;  // 2049
+constexpr int kHistCopies = 4;
+constexpr int kHamChunk = kHamChunkPages * kPS;  // 1024 candidates
+
+struct HamDistSmem {
+  int hist[kHistCopies][kHamBins];
+  int skept[kHamChunkPages];
+  __attribute__((aligned(16))) uint32_t sq[kMaxG * kNW];
+};
+
+// 16-byte load; the coherent form is four agent-scope dword loads.
+template <bool COH>
+__device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
+  if constexpr (COH) {
+    return u32x4{Mem<true>::ld(p), Mem<true>::ld(p + 1), Mem<true>::ld(p + 2),
+                 Mem<true>::ld(p + 3)};
+  } else {
+    return *(const u32x4*)p;
+  }
+}
+
+// Distances of chunk k of (b, g): candidates c in [1024k, 1024k + 1024) with
+// c < 16 P.  dist [B][Hkv][p_max*16] u16; chist [B][Hkv][nchk][128 G + 1].
+// All threads call; NT divides 1024.
+template <int NT, bool COH>
+__device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, int P, int k,
+                               int p_max, int nchk, const uint32_t* q_codes,
+                               const uint32_t* __restrict__ codes, const int32_t* kept,
+                               uint16_t* dist, int* chist, HamDistSmem& sm) {
+  constexpr int kItems = kHamChunk / NT;
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int nbins = 128 * G + 1;
+  const int Np = (L + kPS - 1) / kPS;
+  const int page0 = k * kHamChunkPages;
+  const int npg = min(kHamChunkPages, P - page0);
+  const int ncl = npg * kPS;  // candidates in this chunk
+  if (tid < npg) sm.skept[tid] = Mem<COH>::ld(kept + (size_t)bg * p_max + page0 + tid);
+  if (tid < G * kNW)
+    sm.sq[tid] = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * kNW + tid);
+  for (int i = tid; i < kHistCopies * nbins; i += NT) sm.hist[i / nbins][i % nbins] = 0;
+  __syncthreads();
+
+  const uint32_t* cb = codes + (size_t)bg * Lcap * kNW;
+  const u32x4* sq4 = reinterpret_cast<const u32x4*>(sm.sq);
+  const int lastc = max(ncl - 1, 0);
+  u32x4 code[kItems];
+  bool ok[kItems];
+  uint32_t h[kItems];
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int c = j * NT + tid;
+    const int page = sm.skept[min(c, lastc) >> 4];
+    const int t = page * kPS + (c & 15);
+    ok[j] = c < ncl && (unsigned)page < (unsigned)Np && t < L;
+    code[j] = *(const u32x4*)(cb + (size_t)(ok[j] ? t : 0) * kNW);
+    h[j] = 0u;
+  }
+  for (int qh = 0; qh < G; ++qh) {
+    const u32x4 q = sq4[qh];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+      h[j] += __popc(code[j][0] ^ q[0]) + __popc(code[j][1] ^ q[1]) + __popc(code[j][2] ^ q[2]) +
+              __popc(code[j][3] ^ q[3]);
+  }
+  int* my_hist = sm.hist[w & (kHistCopies - 1)];
+  uint16_t* dc = dist + (size_t)bg * p_max * kPS + (size_t)page0 * kPS;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int c = j * NT + tid;
+    if (ok[j]) atomicAdd(&my_hist[h[j]], 1);
+    if (c < ncl) Mem<COH>::st(dc + c, (uint16_t)(ok[j] ? h[j] : 0xFFFFu));
+  }
+  __syncthreads();
+  int* ch = chist + ((size_t)bg * nchk + k) * nbins;
+  for (int i = tid; i < nbins; i += NT) {
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < kHistCopies; ++r) c += sm.hist[r][i];
+    Mem<COH>::st(ch + i, c);
+  }
+}
+
+struct HamSmem {
+  int hist[kHamBins];
+  union {
+    __attribute__((aligned(16))) uint16_t hval[kMaxCand];      // H of candidate c
+    __attribute__((aligned(16))) float scores[kMaxCtx / kPS];  // page scores (S4)
+  };
+  int skept[kMaxCand / kPS];
+  int s_T, s_need, s_valid;
+  int scan[17];
+  TopScratch top;
+};
+
+// Selection of (b, g) from the distances and chunk histograms of its
+// ham_chunks(P) chunks.  If skept_ready, sm.skept already holds the kept
+// pages; otherwise they are read from kept.  All threads call.
+template <int NT, bool COH>
+__device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int p_max, int nchk,
+                           const int32_t* kept, bool skept_ready, const uint16_t* dist,
+                           const int* chist, int32_t* sel_idx, int32_t* sel_count,
+                           HamSmem& sm) {
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  const int tid = threadIdx.x;
+  const int ncand = P * kPS;
+  const int nbins = 128 * G + 1;
+  const int nch = ham_chunks(P);
+
+  // gather: kept pages, distances (8 per 16-byte load), summed histograms
+  if (!skept_ready)
+    for (int i = tid; i < P; i += NT) sm.skept[i] = Mem<COH>::ld(kept + (size_t)bg * p_max + i);
+  {
+    const uint32_t* d32 = reinterpret_cast<const uint32_t*>(dist + (size_t)bg * p_max * kPS);
+    const int nv8 = (ncand + 7) / 8;
+#pragma unroll 4
+    for (int i = tid; i < nv8; i += NT)
+      reinterpret_cast<u32x4*>(sm.hval)[i] = ld_u32x4<COH>(d32 + 4 * i);
+  }
+  const int* chb = chist + (size_t)bg * nchk * nbins;
+  for (int i = tid; i < nbins; i += NT) {
+    int c = 0;
+#pragma unroll 8
+    for (int k = 0; k < nch; ++k) c += Mem<COH>::ld(chb + (size_t)k * nbins + i);
+    sm.hist[i] = c;
+  }
+  __syncthreads();
+
+  // threshold over bins in ascending H
+  {
+    const int per = (nbins + NT - 1) / NT;  // <= 5
+    const int b0 = tid * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < nbins) local += sm.hist[b0 + i];
+    int total;
+    const int ex = block_exclusive_scan<NT, int>(local, sm.scan, &total);
+    if (tid == 0) {
+      sm.s_T = nbins;  // every valid H is < nbins: take all valid candidates
+      sm.s_need = 0;
+      sm.s_valid = total;
+    }
+    __syncthreads();
+    if (total > top_k) {
+      int run = ex;
+      for (int i = 0; i < per; ++i) {
+        if (b0 + i < nbins) {
+          const int c = sm.hist[b0 + i];
+          if (run < top_k && run + c >= top_k) {
+            sm.s_T = b0 + i;
+            sm.s_need = top_k - run;
+          }
+          run += c;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int count = min(top_k, sm.s_valid);
+  const uint32_t Th = (uint32_t)sm.s_T;
+  const int need_eq = sm.s_need;
+
+  // ordered compaction over each thread's run of candidates, read as 8
+  // distances per 16-byte LDS load in rolled loops
+  const int nv8 = (ncand + 8 * NT - 1) / (8 * NT);
+  const int c0 = 8 * nv8 * tid;
+  const u32x4* run8 = reinterpret_cast<const u32x4*>(sm.hval) + nv8 * tid;
+  auto cls_of = [&](const u32x4& hw, int e, int c) -> int {
+    const uint32_t word = hw[e >> 1];
+    uint32_t h = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+    if (c >= ncand) h = 0xFFFFu;
+    return h < Th ? 1 : (h == Th ? 2 : 0);
+  };
+  int gt = 0, eq = 0;
+#pragma unroll 1
+  for (int j = 0; j < nv8; ++j) {
+    const u32x4 hw = run8[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = cls_of(hw, e, c0 + 8 * j + e);
+      gt += k == 1;
+      eq += k == 2;
+    }
+  }
+  int gb, eb;
+  run_offsets<NT>(gt, eq, sm.top, gb, eb);
+  int32_t* out = sel_idx + (size_t)bg * top_k;
+  auto emit = [&](int pos, int c) { Mem<COH>::st(out + pos, sm.skept[c >> 4] * kPS + (c & 15)); };
+#pragma unroll 1
+  for (int j = 0; j < nv8; ++j) {
+    const u32x4 hw = run8[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + 8 * j + e;
+      emit_ordered(cls_of(hw, e, c), c, need_eq, gb, eb, emit);
+    }
+  }
+  for (int i = count + tid; i < top_k; i += NT) Mem<COH>::st(out + i, -1);
+  if (tid == 0) Mem<COH>::st(sel_count + bg, count);
+}
+
+// ============================================================== S7: attend
+// One 256-thread group takes a chunk of up to 64 selected keys of one (b, g)
+// for all G query heads.  It gathers the chunk's K and V rows with every load
+// in flight at once (row indices clamped, data masked), stages K in LDS for
+// the logits, then reuses the buffer for V; writes the unnormalised partial
+// (o~, m, l): o~_h = sum_i e^(x_hi - m_h) V_i, m_h = max_i x_hi,
+// l_h = sum_i e^(x_hi - m_h), x_hi = q_h . K_i * scale.
+// All threads of the workgroup must call (barriers); each 256-thread group
+// passes its own chunk (nk = 0 for an idle group).
+constexpr int kCh = kAttnChunk;      // 64 selected keys per chunk
+constexpr int kPartStride = kD + 2;  // o~[128], m, l
+constexpr int kRowPad = 8;           // LDS row padding (bank spread), in elements
+
+template <bool KF32>
+struct AttnSmem {
+  typedef typename std::conditional<KF32, float, uint16_t>::type ET;
+  __attribute__((aligned(16))) ET rows[kCh * (kD + kRowPad)];
+  float sq[kMaxG][kD];
+  float sp[kMaxG][kCh];
+  int sidx[kCh];
+  float sm[kMaxG], sl[kMaxG];
+};
+
+template <bool KF32, bool COH>
+__device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, int k0, int nk,
+                           float scale, const float* __restrict__ q,
+                           const void* __restrict__ kcache, const void* __restrict__ vcache,
+                           const int32_t* sel_idx, float* pout, uint32_t* status,
+                           AttnSmem<KF32>& sm) {
+  typedef typename AttnSmem<KF32>::ET ET;
+  constexpr int kStride = kD + kRowPad;
+  constexpr int kVec = 16 / sizeof(ET);              // elements per 16-byte load
+  constexpr int kChunksPerRow = kD / kVec;           // 16 (bf16) or 32 (f32)
+  constexpr int kLoads = kCh * kChunksPerRow / 256;  // per thread, per matrix: 4 or 8
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  const int tq = threadIdx.x & 255;
+  const int w = tq >> 6;
+  const int l = tq & 63;
+
+  if (tq < kCh) {
+    int idx = -1;
+    if (tq < nk) {
+      idx = Mem<COH>::ld(sel_idx + (size_t)bg * top_k + k0 + tq);
+      if (idx < 0 || idx >= Lcap) {
+        if (status) atomicOr(status, HHR_DEV_BAD_INDEX);
+        idx = -1;
+      }
+    }
+    sm.sidx[tq] = idx;
+  }
+  for (int i = tq; i < G * kD; i += 256)
+    sm.sq[i / kD][i % kD] = q[((size_t)b * Hq + (size_t)g * G) * kD + i];
+  __syncthreads();
+
+  // gather: every thread issues all of its K and V loads before storing any
+  const ET* kb = (const ET*)kcache + (size_t)bg * Lcap * kD;
+  const ET* vb = (const ET*)vcache + (size_t)bg * Lcap * kD;
+  u32x4 kreg[kLoads], vreg[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int c = tq + 256 * i;
+    const int r = c / kChunksPerRow;
+    const int cc = c % kChunksPerRow;
+    const int idx = max(sm.sidx[r], 0);
+    kreg[i] = *(const u32x4*)(kb + (size_t)idx * kD + cc * kVec);
+    vreg[i] = *(const u32x4*)(vb + (size_t)idx * kD + cc * kVec);
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int c = tq + 256 * i;
+    const int r = c / kChunksPerRow;
+    const int cc = c % kChunksPerRow;
+    if (sm.sidx[r] < 0) {
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    *(u32x4*)(sm.rows + r * kStride + cc * kVec) = kreg[i];
+  }
+  __syncthreads();
+
+  // logits: thread (key = l, head group w) -> heads w, w+4, ...
+  for (int h = w; h < G; h += 4) {
+    const ET* row = sm.rows + l * kStride;
+    float dot = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < kD / kVec; ++c) {
+      const u32x4 v = *(const u32x4*)(row + c * kVec);
+      if constexpr (KF32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dot = fmaf(sm.sq[h][4 * c + j], __uint_as_float(v[j]), dot);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dot = fmaf(sm.sq[h][8 * c + 2 * j], bf16_to_f32(v[j] & 0xFFFFu), dot);
+          dot = fmaf(sm.sq[h][8 * c + 2 * j + 1], bf16_to_f32(v[j] >> 16), dot);
+        }
+      }
+    }
+    sm.sp[h][l] = (l < nk && sm.sidx[l] >= 0) ? dot * scale : -__builtin_huge_valf();
+  }
+  __syncthreads();
+
+  // V rows replace K rows; chunk softmax numerators (one wave per head, lane = key)
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int c = tq + 256 * i;
+    *(u32x4*)(sm.rows + (c / kChunksPerRow) * kStride + (c % kChunksPerRow) * kVec) = vreg[i];
+  }
+  for (int h = w; h < G; h += 4) {
+    const float x = sm.sp[h][l];
+    const float m = wave_max(x);
+    const float p = (x == -__builtin_huge_valf()) ? 0.f : expf(x - m);
+    const float s = wave_sum(p);
+    sm.sp[h][l] = p;
+    if (l == 0) {
+      sm.sm[h] = m;
+      sm.sl[h] = s;
+    }
+  }
+  __syncthreads();
+
+  // partial o~_h[d] = sum_k p_h[k] V[k][d]: lane owns dims {2l, 2l+1}, wave w heads w, w+4, ...
+  if (nk > 0) {
+    for (int h = w; h < G; h += 4) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < kCh; ++k) {
+        const float p = sm.sp[h][k];
+        const ET* row = sm.rows + k * kStride;
+        float v0, v1;
+        if constexpr (KF32) {
+          v0 = row[2 * l];
+          v1 = row[2 * l + 1];
+        } else {
+          const uint32_t pair = *(const uint32_t*)(row + 2 * l);
+          v0 = bf16_to_f32(pair & 0xFFFFu);
+          v1 = bf16_to_f32(pair >> 16);
+        }
+        a0 = fmaf(p, v0, a0);
+        a1 = fmaf(p, v1, a1);
+      }
+      Mem<COH>::st(pout + h * kPartStride + 2 * l, a0);
+      Mem<COH>::st(pout + h * kPartStride + 2 * l + 1, a1);
+      if (l == 0) {
+        Mem<COH>::st(pout + h * kPartStride + kD, sm.sm[h]);
+        Mem<COH>::st(pout + h * kPartStride + kD + 1, sm.sl[h]);
+      }
+    }
+  }
+}
+
+// Merge the ns chunk partials of one (b, g) into o (1024 threads):
+//   M_h = max_s m_sh, f_sh = e^(m_sh - M_h), L_h = sum_s f_sh l_sh,
+//   o_h = sum_s f_sh o~_sh / L_h  (o = 0 when nothing was selected).
+// Thread (h, dim quad, s-group) sums chunks s = sgrp, sgrp + NSG, ...; the
+// s-groups are then added in order in LDS.
+constexpr int kCombThreads = 512;
+constexpr int kCombMaxChunks = kMaxCand / kCh;  // 512
+
+struct CombSmem {
+  float f[kMaxG][kCombMaxChunks];
+  float lsum[kMaxG];
+  floatx4 red[kCombThreads];
+};
+
+// kCombThreads threads (every caller uses this count, so all sum in the same
+// order).
+template <bool COH>
+__device__ void attn_combine(int b, int g, int Hq, int Hkv, int ns, int n_split,
+                             const float* part, float* __restrict__ out, CombSmem& sm) {
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const size_t sstride = (size_t)kMaxG * kPartStride;
+  const float* pb = part + (size_t)bg * n_split * sstride;
+  // chunk weights: one wave per head
+  for (int h = w; h < G; h += kCombThreads / kWave) {
+    float M = -__builtin_huge_valf();
+    for (int s = l; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(pb + s * sstride + h * kPartStride + kD));
+    M = wave_max(M);
+    float ls = 0.f;
+    for (int s = l; s < ns; s += kWave) {
+      const float* ps = pb + s * sstride + h * kPartStride;
+      const float ms = Mem<COH>::ld(ps + kD);
+      const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
+      sm.f[h][s] = f;
+      ls = fmaf(f, Mem<COH>::ld(ps + kD + 1), ls);
+    }
+    ls = wave_sum(ls);
+    if (l == 0) sm.lsum[h] = ls;
+  }
+  __syncthreads();
+  const int pairs = G * (kD / 4);                       // (head, dim quad)
+  const int nsg = max(1, kCombThreads / pairs);         // chunk groups
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int pair = tid % pairs;
+  const int sgrp = tid / pairs;
+  const int h = pair / (kD / 4);
+  const int d4 = pair % (kD / 4);
+  if (sgrp < nsg && ns > 0) {
+    // chunks s = sgrp, sgrp + nsg, ... in ascending order, eight loads in
+    // flight (indices clamped; a clamped slot gets weight 0)
+    constexpr int kB = 8;
+#pragma unroll 1
+    for (int s0 = sgrp; s0 < ns; s0 += kB * nsg) {
+      floatx4 v[kB];
+      float f[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int s = s0 + j * nsg;
+        const int sc = min(s, ns - 1);
+        const float* po = pb + sc * sstride + h * kPartStride + 4 * d4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] = Mem<COH>::ld(po + k);
+        f[j] = s < ns ? sm.f[h][sc] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = fmaf(f[j], v[j][k], acc[k]);
+    }
+  }
+  sm.red[tid] = acc;
+  __syncthreads();
+  // pairs may exceed the thread count (G = 16: 512 pairs, 2 groups): loop
+  for (int pp = tid; pp < pairs; pp += kCombThreads) {
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < nsg; ++k) {
+      const floatx4 r = sm.red[k * pairs + pp];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] += r[j];
+    }
+    const int hh = pp / (kD / 4);
+    const int dd = pp % (kD / 4);
+    const float L = sm.lsum[hh];
+    floatx4 res;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) res[j] = (ns > 0 && L > 0.f) ? o[j] / L : 0.f;
+    *(floatx4*)(out + ((size_t)b * Hq + (size_t)g * G + hh) * kD + 4 * dd) = res;
+  }
+}
+
+}  // namespace hhr

@@ -1,8 +1,9 @@
 // Ordered exact top-P inside one workgroup: the P largest scores, ties to the
 // lower candidate index, emitted in ascending candidate order.  Internal header.
 //
-// Layout: candidate c = i*NT + tid sits in register slot i of thread tid, so
-// a workgroup's loads of a contiguous score array are coalesced.
+// Layout: the scores sit in LDS; thread tid owns a run of consecutive
+// candidates, read as float4, so the whole selection works from registers and
+// the output order follows from one block scan.
 //
 // The selection is described by a cut-off (T, need_eq) on orderable keys:
 // candidate c is taken iff key > T, or key == T and fewer than need_eq keys
@@ -11,13 +12,15 @@
 //     bins the scores into 2048 bins linear in value -- bin(v) = (int)((v -
 //     vmin) * 2048 / (vmax - vmin)) is non-decreasing in v because each step
 //     of the float arithmetic is monotone, so a higher bin holds only larger
-//     scores -- and the threshold bin b* (count above < P <= count through
-//     b*) usually holds a handful of scores, whose exact value ranks give T;
-//   * radix select over orderable keys (when b* holds more than 1024 scores,
-//     e.g. many equal values): 11-bit digits of key - kmin from the highest
-//     bit in which keys differ.
-// Then an ordered compaction: wave ballots give ranks inside each (slot,
-// wave) group and one scan over the groups gives their offsets.
+//     scores.  If the whole threshold bin b* (count above < P <= count
+//     through b*) is taken, the cut is "bin >= b*"; otherwise b* usually
+//     holds a handful of scores, whose exact value ranks give T;
+//   * radix select over orderable keys (when b* holds more than
+//     kLinListMax scores, e.g. many equal values): 11-bit digits of
+//     key - kmin from the highest bit in which keys differ.
+// Then an ordered compaction over the per-thread runs: each thread counts
+// its taken candidates (strictly inside the cut, and on it) and one block
+// scan of the packed pair gives every run its output offset.
 #pragma once
 
 #include "hhr_device.h"
@@ -25,64 +28,56 @@
 namespace hhr {
 
 constexpr int kLinBins = 2048;
-constexpr int kLinListMax = 1024;
-constexpr int kTopMaxGroups = 1024;  // ITEMS * (NT / 64)
+constexpr int kLinListMax = 512;
 
 struct TopScratch {
   int hist[kLinBins];
   float list_v[kLinListMax];
   int list_n;
-  int grp_gt[kTopMaxGroups];
-  int grp_eq[kTopMaxGroups];
   float w_min[16], w_max[16];
   int w_n[16];
   uint32_t w_kmin[16], w_kmax[16];
-  float vmin, vmax;
   uint32_t kmin, kmax;
-  int n_valid, bstar, above, digit;
+  int bstar, above, digit;
   uint32_t T;
   int need_eq;
   int scan[17];
+  uint32_t uscan[17];
 };
 
 // Cut-off of the K largest present keys (key 0 = absent), 1 <= K < #present.
-template <int NT, int ITEMS>
-__device__ void radix_cutoff(const uint32_t (&key)[ITEMS], int K, TopScratch& sh) {
+// key_of(i) gives this thread's key i of n_items (the loops stay rolled: this
+// runs once per selection, so small code matters more than loop overhead).
+template <int NT, typename KeyOf>
+__device__ void radix_cutoff(KeyOf key_of, int n_items, int K, TopScratch& sh) {
   constexpr int NWAVES = NT / kWave;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = tid % kWave;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    if (key[i] != 0u) {
-      mn = min(mn, key[i]);
-      mx = max(mx, key[i]);
+#pragma unroll 1
+  for (int i = 0; i < n_items; ++i) {
+    const uint32_t k = key_of(i);
+    if (k != 0u) {
+      mn = min(mn, k);
+      mx = max(mx, k);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-  }
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
   __syncthreads();
   if (l == 0) {
     sh.w_kmin[w] = mn;
     sh.w_kmax[w] = mx;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t a = 0xFFFFFFFFu, z = 0u;
-    for (int k = 0; k < NWAVES; ++k) {
-      a = min(a, sh.w_kmin[k]);
-      z = max(z, sh.w_kmax[k]);
-    }
-    sh.kmin = a;
-    sh.kmax = z;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll 1
+  for (int k = 0; k < NWAVES; ++k) {
+    kmin = min(kmin, sh.w_kmin[k]);
+    kmax = max(kmax, sh.w_kmax[k]);
   }
-  __syncthreads();
-  const uint32_t kmin = sh.kmin;
-  const uint32_t range = sh.kmax - kmin;
+  const uint32_t range = kmax - kmin;
   if (range == 0u) {
     if (tid == 0) {
       sh.T = kmin;
@@ -94,6 +89,7 @@ __device__ void radix_cutoff(const uint32_t (&key)[ITEMS], int K, TopScratch& sh
   const int nbits = 32 - __clz((int)range);
   uint32_t prefix = 0, pmask = 0;
   int remaining = K;
+#pragma unroll 1
   for (int hi = nbits; hi > 0; hi -= 11) {
     const int width = hi < 11 ? hi : 11;
     const int shift = hi - width;
@@ -102,10 +98,11 @@ __device__ void radix_cutoff(const uint32_t (&key)[ITEMS], int K, TopScratch& sh
     __syncthreads();
     for (int i = tid; i < nb; i += NT) sh.hist[i] = 0;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      if (key[i] != 0u) {
-        const uint32_t rel = key[i] - kmin;
+#pragma unroll 1
+    for (int i = 0; i < n_items; ++i) {
+      const uint32_t k = key_of(i);
+      if (k != 0u) {
+        const uint32_t rel = k - kmin;
         if ((rel & pmask) == prefix) atomicAdd(&sh.hist[(rel >> shift) & dmask], 1);
       }
     }
@@ -142,92 +139,68 @@ __device__ void radix_cutoff(const uint32_t (&key)[ITEMS], int K, TopScratch& sh
   __syncthreads();
 }
 
-// Ordered compaction: emit(pos, c) for every taken candidate, pos ascending in c.
-template <int NT, int ITEMS, typename Emit>
-__device__ void compact_strided(const uint32_t (&key)[ITEMS], uint32_t T, int need_eq,
-                                TopScratch& sh, Emit emit) {
-  constexpr int NWAVES = NT / kWave;
-  static_assert(ITEMS * NWAVES <= kTopMaxGroups, "too many (slot, wave) groups");
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int l = tid % kWave;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint64_t bgt = __ballot(key[i] != 0u && key[i] > T);
-    const uint64_t beq = __ballot(key[i] != 0u && key[i] == T);
-    if (l == 0) {
-      sh.grp_gt[i * NWAVES + w] = popc64(bgt);
-      sh.grp_eq[i * NWAVES + w] = popc64(beq);
-    }
-  }
-  __syncthreads();
-  if (w == 0) {
-    constexpr int m = ITEMS * NWAVES;
-    constexpr int per = (m + kWave - 1) / kWave;
-    int a = 0, e = 0;
-#pragma unroll
-    for (int k = 0; k < per; ++k) {
-      const int j = l * per + k;
-      if (j < m) {
-        a += sh.grp_gt[j];
-        e += sh.grp_eq[j];
-      }
-    }
-    int ra = wave_inclusive_scan(a) - a;
-    int re = wave_inclusive_scan(e) - e;
-#pragma unroll
-    for (int k = 0; k < per; ++k) {
-      const int j = l * per + k;
-      if (j < m) {
-        const int ta = sh.grp_gt[j], te = sh.grp_eq[j];
-        sh.grp_gt[j] = ra;
-        sh.grp_eq[j] = re;
-        ra += ta;
-        re += te;
-      }
-    }
-  }
-  __syncthreads();
-  const uint64_t mlt = lanemask_lt();
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const bool gt = key[i] != 0u && key[i] > T;
-    const bool eq = key[i] != 0u && key[i] == T;
-    const uint64_t bgt = __ballot(gt);
-    const uint64_t beq = __ballot(eq);
-    const int gt_before = sh.grp_gt[i * NWAVES + w] + popc64(bgt & mlt);
-    const int eq_before = sh.grp_eq[i * NWAVES + w] + popc64(beq & mlt);
-    if (gt || (eq && eq_before < need_eq))
-      emit(gt_before + min(eq_before, need_eq), i * NT + tid);
-  }
+// Output offsets of this thread's run in an ordered compaction: gt and eq
+// count the run's candidates strictly inside the cut and on it; returns the
+// counts over all earlier runs (one block scan of gt | eq << 16: both totals
+// stay below 65536).
+template <int NT>
+__device__ __forceinline__ void run_offsets(int gt, int eq, TopScratch& sh, int& gt0, int& eq0) {
+  uint32_t tot;
+  const uint32_t ex =
+      block_exclusive_scan<NT, uint32_t>((uint32_t)gt | ((uint32_t)eq << 16), sh.uscan, &tot);
+  gt0 = (int)(ex & 0xFFFFu);
+  eq0 = (int)(ex >> 16);
 }
 
-// The min(P, #present) largest of the present scores x[i] (present[i]),
-// ties to the lower candidate c = i*NT + tid; emit(pos, c) in ascending c.
-// Returns the number selected.  Scores must be finite.
-template <int NT, int ITEMS, typename Emit>
-__device__ int top_largest_strided(const float (&x)[ITEMS], const bool (&present)[ITEMS], int P,
-                                   TopScratch& sh, Emit emit) {
+// Emits one candidate of a run in order: cls 1 = inside the cut (always
+// taken), 2 = on the cut (taken while fewer than need_eq on-cut candidates
+// precede it).  The output slot is the number of taken candidates before it.
+template <typename Emit>
+__device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& gb, int& eb,
+                                             Emit& emit) {
+  const bool take = cls == 1 || (cls == 2 && eb < need_eq);
+  if (take) emit(gb + min(eb, need_eq), c);
+  gb += cls == 1 ? 1 : 0;
+  eb += cls == 2 ? 1 : 0;
+}
+
+// The min(P, #present) largest present scores of sbuf[0..n), ties to the
+// lower index; emit(pos, c) for each taken candidate c, pos = its rank in
+// ascending c.  present(c) tells whether candidate c < n exists.  Thread tid
+// owns candidates [4*nv4*tid, 4*nv4*(tid+1)) with nv4 = ceil(n / (4*NT)),
+// read from LDS as float4 in rolled loops; sbuf must hold 4*NT*nv4 floats,
+// 16-byte aligned (slots past n are read but never used).  Scores must be
+// finite (-0 counts as +0).  Returns the number taken.  All threads call.
+template <int NT, typename Present, typename Emit>
+__device__ int top_largest_lds(const float* sbuf, int n, Present present, int P, TopScratch& sh,
+                               Emit emit) {
   constexpr int NWAVES = NT / kWave;
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = tid % kWave;
+  const int nv4 = (n + 4 * NT - 1) / (4 * NT);
+  const int c0 = 4 * nv4 * tid;
+  const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
+  auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
+  auto is_present = [&](int c) { return c < n && present(c); };
 
   float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
   int cnt = 0;
+#pragma unroll 1
+  for (int j = 0; j < nv4; ++j) {
+    const float4 t = run4[j];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    if (present[i]) {
-      mn = fminf(mn, x[i]);
-      mx = fmaxf(mx, x[i]);
-      ++cnt;
+    for (int e = 0; e < 4; ++e) {
+      if (is_present(c0 + 4 * j + e)) {
+        mn = fminf(mn, val(t, e));
+        mx = fmaxf(mx, val(t, e));
+        ++cnt;
+      }
     }
   }
-  mn = -wave_max(-mn);
+  mn = wave_min(mn);
   mx = wave_max(mx);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  cnt = wave_sum_i(cnt);
   if (l == 0) {
     sh.w_min[w] = mn;
     sh.w_max[w] = mx;
@@ -236,43 +209,35 @@ __device__ int top_largest_strided(const float (&x)[ITEMS], const bool (&present
   for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
-  if (w == 0) {
-    float a = l < NWAVES ? sh.w_min[l] : __builtin_huge_valf();
-    float z = l < NWAVES ? sh.w_max[l] : -__builtin_huge_valf();
-    int c = l < NWAVES ? sh.w_n[l] : 0;
-    a = -wave_max(-a);
-    z = wave_max(z);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-    if (l == 0) {
-      sh.vmin = a;
-      sh.vmax = z;
-      sh.n_valid = c;
-    }
+  float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
+  int n_valid = 0;
+#pragma unroll 1
+  for (int k = 0; k < NWAVES; ++k) {
+    vmin = fminf(vmin, sh.w_min[k]);
+    vmax = fmaxf(vmax, sh.w_max[k]);
+    n_valid += sh.w_n[k];
   }
-  __syncthreads();
-  const int n_valid = sh.n_valid;
   const int Pe = min(P, n_valid);
   if (Pe <= 0) return 0;
 
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) key[i] = present[i] ? orderable_key(x[i]) : 0u;
-
-  uint32_t T = 0u;  // Pe == n_valid: every present key (>= 0x007FFFFF) is > 0
-  int need_eq = 0;
+  // cut-off: mode 0 = every present candidate, 1 = bin >= bstar, 2 = keys
+  int mode = 0, bstar = 0, need_eq = 0;
+  uint32_t T = 0u;
+  const float range = vmax - vmin;
+  const float inv = range > 0.f ? (float)kLinBins / range : 0.f;
+  auto bin_of = [&](float x) {
+    const float f = (x - vmin) * inv;
+    const int bb = f < (float)kLinBins ? (int)f : kLinBins - 1;
+    return min(max(bb, 0), kLinBins - 1);
+  };
   if (Pe < n_valid) {
-    const float vmin = sh.vmin;
-    const float range = sh.vmax - vmin;
-    const float inv = range > 0.f ? (float)kLinBins / range : 0.f;
-    auto bin_of = [&](float v) {
-      const float f = (v - vmin) * inv;
-      const int bb = f < (float)kLinBins ? (int)f : kLinBins - 1;
-      return min(max(bb, 0), kLinBins - 1);
-    };
+#pragma unroll 1
+    for (int j = 0; j < nv4; ++j) {
+      const float4 t = run4[j];
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
-      if (present[i]) atomicAdd(&sh.hist[bin_of(x[i])], 1);
+      for (int e = 0; e < 4; ++e)
+        if (is_present(c0 + 4 * j + e)) atomicAdd(&sh.hist[bin_of(val(t, e))], 1);
+    }
     __syncthreads();
     {
       constexpr int PER = kLinBins / NT > 0 ? kLinBins / NT : 1;
@@ -298,22 +263,27 @@ __device__ int top_largest_strided(const float (&x)[ITEMS], const bool (&present
       }
     }
     __syncthreads();
-    const int bstar = sh.bstar;
+    bstar = sh.bstar;
     const int need = Pe - sh.above;  // 1 <= need <= hist[b*]
     const int cstar = sh.hist[bstar];
-    if (cstar <= kLinListMax) {
+    if (need == cstar) {
+      mode = 1;
+    } else if (cstar <= kLinListMax) {
+      mode = 2;
+#pragma unroll 1
+      for (int j = 0; j < nv4; ++j) {
+        const float4 t = run4[j];
 #pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        if (present[i] && bin_of(x[i]) == bstar) {
-          const int slot = atomicAdd(&sh.list_n, 1);
-          sh.list_v[slot] = x[i];
-        }
+        for (int e = 0; e < 4; ++e)
+          if (is_present(c0 + 4 * j + e) && bin_of(val(t, e)) == bstar)
+            sh.list_v[atomicAdd(&sh.list_n, 1)] = val(t, e);
       }
       __syncthreads();
       // T = the value with (#greater in b*) < need <= (#greater) + (#equal)
       for (int j = tid; j < cstar; j += NT) {
         const float vj = sh.list_v[j];
         int gtr = 0, eql = 0;
+#pragma unroll 1
         for (int k = 0; k < cstar; ++k) {
           const float vk = sh.list_v[k];
           gtr += vk > vj;
@@ -328,12 +298,46 @@ __device__ int top_largest_strided(const float (&x)[ITEMS], const bool (&present
       T = sh.T;
       need_eq = sh.need_eq;
     } else {
-      radix_cutoff<NT, ITEMS>(key, Pe, sh);
+      mode = 2;
+      radix_cutoff<NT>(
+          [&](int i) -> uint32_t {
+            const int c = c0 + i;
+            return is_present(c) ? orderable_key(sbuf[c]) : 0u;
+          },
+          4 * nv4, Pe, sh);
       T = sh.T;
       need_eq = sh.need_eq;
     }
   }
-  compact_strided<NT, ITEMS>(key, T, need_eq, sh, emit);
+  auto cls_of = [&](float x, int c) -> int {
+    const uint32_t k = orderable_key(x);
+    const int by_key = k > T ? 1 : (k == T ? 2 : 0);
+    const int by_bin = bin_of(x) >= bstar ? 1 : 0;
+    const int cls = mode == 0 ? 1 : (mode == 1 ? by_bin : by_key);
+    return is_present(c) ? cls : 0;
+  };
+  int gt = 0, eq = 0;
+#pragma unroll 1
+  for (int j = 0; j < nv4; ++j) {
+    const float4 t = run4[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = cls_of(val(t, e), c0 + 4 * j + e);
+      gt += k == 1;
+      eq += k == 2;
+    }
+  }
+  int gb, eb;
+  run_offsets<NT>(gt, eq, sh, gb, eb);
+#pragma unroll 1
+  for (int j = 0; j < nv4; ++j) {
+    const float4 t = run4[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c0 + 4 * j + e;
+      emit_ordered(cls_of(val(t, e), c), c, need_eq, gb, eb, emit);
+    }
+  }
   return Pe;
 }
 

@@ -44,14 +44,15 @@
  *     bit-identical outputs.
  *   - Workspace: device memory of at least the size the matching
  *     *_workspace_size() function returns.  It starts with a control block
- *     (the device status word at offset 0, then one split-K ticket counter
- *     per (b, g) at offset 256) that must be zero before the workspace is
- *     first used -- allocate it zero-filled.  Every call leaves the tickets
- *     zero again; the status word keeps its error bits until
- *     hhr_read_device_status clears it.  The control block sits at the same
- *     offsets in every layout, so one workspace may serve every entry point.
- *     Calls that share a workspace must not overlap in time (order them on
- *     one stream).
+ *     (the device status word at offset 0, hhr_decode's scheduling tickets at
+ *     offset 64, and eight counters per (b, g) at offset 256) that must be zero
+ *     before the workspace is first used -- allocate it zero-filled.  Every
+ *     call leaves tickets and counters zero again (after an
+ *     HHR_DEV_TIMEOUT, zero the workspace before reusing it); the status word
+ *     keeps its error bits until hhr_read_device_status clears it.  The
+ *     control block sits at the same offsets in every layout, so one
+ *     workspace may serve every entry point.  Calls that share a workspace
+ *     must not overlap in time (order them on one stream).
  */
 #ifndef HHR_H_
 #define HHR_H_
@@ -75,6 +76,8 @@ typedef enum {
 /* Device status bits (hhr_read_device_status). */
 #define HHR_DEV_BAD_SEQ_LEN 0x1u  /* a seq_len was < 0 or > max_ctx           */
 #define HHR_DEV_BAD_INDEX 0x2u    /* a selected position was outside [0,Lcap) */
+#define HHR_DEV_TIMEOUT 0x4u      /* hhr_decode: a wait between its workgroups gave up
+                                     (results of that call are unspecified) */
 
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
@@ -188,8 +191,9 @@ hhr_status hhr_top_pages(const hhr_shape* shape, const float* scores, const int3
  *   sel_count  [B][Hkv] int32         out: min(top_k, #valid candidates)
  *   dist       [B][Hkv][p_max*ps] uint16, out, or NULL: H of candidate
  *              i = (kept slot i/ps, row i%ps); 0xFFFF for rows >= seq_len
- *   workspace  >= hhr_workspace_size(...) bytes (scratch for the distances
- *              when dist is NULL) */
+ *   workspace  >= hhr_workspace_size(...) bytes for the keep parameters that
+ *              gave p_max (scratch for per-chunk H histograms, and for the
+ *              distances when dist is NULL); HHR_ERR_WORKSPACE if smaller */
 hhr_status hhr_hamming_topk(const hhr_shape* shape, const uint32_t* q_codes,
                             const uint32_t* codes, const int32_t* seq_len, const int32_t* kept,
                             const int32_t* kept_count, int32_t p_max, int32_t top_k,

@@ -161,6 +161,12 @@ def test_workspace_errors(H):
         H.HHR_ERR_WORKSPACE
     assert _status(H.hhr_sparse_decode, s, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 0.088, FAKE, FAKE,
                    workspace_bytes=512, stream=0) == H.HHR_ERR_WORKSPACE
+    # the fine top-k keeps per-chunk histograms (and, without dist, the
+    # distances) in the workspace: a control block alone is too small
+    p_max = H.hhr_keep_count(1024 // 16, 1, 4, 0)
+    for dist in (None, FAKE):
+        assert _status(H.hhr_hamming_topk, s, FAKE, FAKE, FAKE, FAKE, FAKE, p_max, 128, FAKE,
+                       FAKE, dist, FAKE, workspace_bytes=4096, stream=0) == H.HHR_ERR_WORKSPACE
 
 
 def test_hisa_errors(H):
