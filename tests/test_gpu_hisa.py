@@ -1,0 +1,278 @@
+"""GPU parity of the HISA indexer path (H1..H5) through the C ABI against the CPU
+oracle: pooled block representatives, block scores, top blocks, fp8 token
+scores and the exact token top-k inside the kept blocks, then attention over
+the selection (hhr_sparse_decode with one KV head).
+
+Stages downstream of a floating-point result are checked on the GPU's own
+upstream values (conditioned oracle), where the discrete results must be
+exact; the end-to-end selection from raw inputs may differ only where the
+oracle's score sits within 1e-4 (relative) of the cut-off score.  Cases span
+block sizes 16 / 64 / 128, ragged and one-token and empty sequences, top_k
+above the candidate count, and keep-all-blocks (which must equal the flat
+indexer).
+"""
+import numpy as np
+import pytest
+import torch
+
+from hash_hierarchical_top_amd import synth
+from oracle import hhr as OH
+from oracle import hisa as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SCORE_EXCUSE = 1e-4
+CASES = [
+    dict(name="hi64_blk128_ragged", n_index_heads=64, block=128, max_ctx=16384,
+         seq_lens=[10000, 16384], keep_blocks=16, top_k=1024, seed=21),
+    dict(name="hi8_blk16_tiny", n_index_heads=8, block=16, max_ctx=4096, seq_lens=[1000, 1, 0],
+         keep_blocks=20, top_k=200, seed=22),
+    dict(name="hi32_blk64_bigk", n_index_heads=32, block=64, max_ctx=2048, seq_lens=[777],
+         keep_blocks=8, top_k=2048, seed=23),
+]
+
+
+def _inputs(case):
+    """Per-sequence draws stacked along the batch: q8 [B][Hi][d], k8 [B][Lcap][d], ..."""
+    parts = [synth.make_hisa_inputs(case["n_index_heads"], L, case["max_ctx"], 4,
+                                    case["seed"] + 7 * b, block=case["block"], make_kv=False)
+             for b, L in enumerate(case["seq_lens"])]
+    return {k: np.stack([p[k] for p in parts]) if k != "seq_len"
+            else np.array([int(p[k][0]) for p in parts], dtype=np.int32)
+            for k in parts[0]}
+
+
+class HisaRun:
+    def __init__(self, H, case):
+        self.H, self.case = H, case
+        self.inp = _inputs(case)
+        B = len(case["seq_lens"])
+        self.B, self.block, self.Lcap = B, case["block"], case["max_ctx"]
+        self.keep, self.top_k = case["keep_blocks"], case["top_k"]
+        self.NbCap = self.Lcap // self.block
+        self.shape = H.make_hisa_shape(B, case["n_index_heads"], self.block, self.Lcap)
+        dv = U.dev()
+        self.d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dv) for k, v in self.inp.items()}
+        i32 = dict(dtype=torch.int32, device=dv)
+        f32 = dict(dtype=torch.float32, device=dv)
+        self.reps = torch.zeros((B, self.NbCap, 128), **f32)
+        self.block_scores = torch.full((B, self.NbCap), float("nan"), **f32)
+        self.kept = torch.zeros((B, self.keep), **i32)
+        self.kept_count = torch.zeros((B,), **i32)
+        self.token_scores = torch.full((B, self.keep * self.block), float("nan"), **f32)
+        self.sel = torch.zeros((B, self.top_k), **i32)
+        self.sel_count = torch.zeros((B,), **i32)
+        ws = H.hhr_hisa_workspace_size(self.shape, self.keep, self.top_k)
+        assert ws > 0
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=dv)
+        self.status = self.ws[:4].view(torch.int32)
+
+    def run_stages(self):
+        H, d = self.H, self.d
+        zero = torch.zeros(self.B, dtype=torch.int32, device=U.dev())
+        H.hhr_hisa_pool_keys(self.shape, d["k8"], d["k_scale"], zero, d["seq_len"],
+                             max(1, int(self.inp["seq_len"].max())), self.reps, self.status)
+        H.hhr_hisa_block_scores(self.shape, d["q8"], d["q_scale"], d["w"], self.reps,
+                                d["seq_len"], self.block_scores, self.status)
+        H.hhr_hisa_top_blocks(self.shape, self.block_scores, d["seq_len"], self.keep, self.kept,
+                              self.kept_count, self.status)
+        H.hhr_hisa_token_topk(self.shape, d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"],
+                              d["seq_len"], self.kept, self.kept_count, self.keep, self.top_k,
+                              self.sel, self.sel_count, self.token_scores, self.ws)
+        torch.cuda.synchronize()
+
+    # oracle-side views of one sequence
+    def L(self, b):
+        return int(self.inp["seq_len"][b])
+
+    def q(self, b):
+        return O.dequantize(self.inp["q8"][b], self.inp["q_scale"][b])
+
+    def keys(self, b):
+        L = self.L(b)
+        return O.dequantize(self.inp["k8"][b, :L], self.inp["k_scale"][b, :L])
+
+    def nb(self, b):
+        return -(-self.L(b) // self.block)
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[c["name"] for c in CASES])
+def run(request, gpu_lib):
+    case = request.param
+    print(f"\n[gpu hisa case] {case['name']}", flush=True)
+    r = HisaRun(gpu_lib, case)
+    r.run_stages()
+    return r
+
+
+def _abs_terms(q, w, x):
+    """sum_h w_h * sum_d |q_hd x_td| per row: the scale of the rounding in the indexer score."""
+    return (np.abs(x) @ np.abs(q).T) @ np.abs(np.asarray(w, dtype=np.float64))
+
+
+def test_pool_reps(run):
+    reps = run.reps.cpu().numpy().astype(np.float64)
+    for b in range(run.B):
+        if run.L(b) == 0:
+            continue
+        keys = run.keys(b)
+        want = O.pooled_reps(keys, run.block)
+        scale = np.stack([np.abs(keys[i * run.block:(i + 1) * run.block]).mean(0)
+                          for i in range(run.nb(b))])
+        assert np.all(np.abs(reps[b, :run.nb(b)] - want) <= 1e-5 * scale + 1e-30)
+
+
+def test_block_scores_conditioned(run):
+    got = run.block_scores.cpu().numpy().astype(np.float64)
+    reps = run.reps.cpu().numpy().astype(np.float64)
+    for b in range(run.B):
+        nb = run.nb(b)
+        q, w = run.q(b), run.inp["w"][b]
+        want = O.indexer_scores(q, w, reps[b, :nb])
+        tol = 1e-5 * _abs_terms(q, w, reps[b, :nb]) + 1e-30
+        assert np.all(np.abs(got[b, :nb] - want) <= tol)
+
+
+def test_top_blocks_conditioned_exact(run):
+    sc = run.block_scores.cpu().numpy()
+    kept = run.kept.cpu().numpy()
+    cnt = run.kept_count.cpu().numpy()
+    for b in range(run.B):
+        nb = run.nb(b)
+        want = O.top_largest(sc[b, :nb].astype(np.float64), np.arange(nb), run.keep)
+        assert cnt[b] == min(run.keep, nb)
+        np.testing.assert_array_equal(kept[b, :cnt[b]], want)
+        assert np.all(kept[b, cnt[b]:] == -1)
+
+
+def test_top_blocks_against_unconditioned_oracle(run):
+    """Raw inputs: a kept-block difference is allowed only within the excuse band."""
+    kept = run.kept.cpu().numpy()
+    cnt = run.kept_count.cpu().numpy()
+    for b in range(run.B):
+        if run.L(b) == 0:
+            assert cnt[b] == 0
+            continue
+        ref = O.select(run.inp["q8"][b], run.inp["q_scale"][b], run.inp["w"][b],
+                       run.inp["k8"][b], run.inp["k_scale"][b], run.L(b), run.block, run.keep,
+                       run.top_k)
+        S = ref["block_scores"]
+        cut = np.sort(S)[::-1][min(run.keep, S.size) - 1]
+        diff = np.setxor1d(kept[b, :cnt[b]], ref["blocks"])
+        for blk in diff:
+            assert abs(S[blk] - cut) <= SCORE_EXCUSE * abs(cut), (b, blk)
+
+
+def _candidates(run, b, kept_row, count):
+    blocks = kept_row[:count].astype(np.int64)
+    cand = (blocks[:, None] * run.block + np.arange(run.block)[None, :]).reshape(-1)
+    return cand  # slot-major: slot i, row r -> kept[i] * block + r
+
+
+def test_token_scores_conditioned(run):
+    ts = run.token_scores.cpu().numpy().astype(np.float64)
+    kept = run.kept.cpu().numpy()
+    cnt = run.kept_count.cpu().numpy()
+    for b in range(run.B):
+        cand = _candidates(run, b, kept[b], cnt[b])
+        valid = cand < run.L(b)
+        got = ts[b, :cand.size]
+        assert np.all(np.isneginf(got[~valid]))
+        c = cand[valid]
+        x = O.dequantize(run.inp["k8"][b, c], run.inp["k_scale"][b, c])
+        q, w = run.q(b), run.inp["w"][b]
+        want = O.indexer_scores(q, w, x)
+        tol = 1e-5 * _abs_terms(q, w, x) + 1e-30
+        assert np.all(np.abs(got[valid] - want) <= tol)
+
+
+def test_token_topk_conditioned_exact(run):
+    ts = run.token_scores.cpu().numpy()
+    kept = run.kept.cpu().numpy()
+    cnt = run.kept_count.cpu().numpy()
+    sel = run.sel.cpu().numpy()
+    sc = run.sel_count.cpu().numpy()
+    for b in range(run.B):
+        cand = _candidates(run, b, kept[b], cnt[b])
+        valid = cand < run.L(b)
+        want = O.top_largest(ts[b, :cand.size][valid].astype(np.float64), cand[valid], run.top_k)
+        assert sc[b] == want.size
+        np.testing.assert_array_equal(sel[b, :sc[b]], want)
+        assert np.all(sel[b, sc[b]:] == -1)
+
+
+def test_composite_equals_stages(run, gpu_lib):
+    H, d = gpu_lib, run.d
+    sel2 = torch.full_like(run.sel, 7)
+    cnt2 = torch.full_like(run.sel_count, 7)
+    H.hhr_hisa_select(run.shape, d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"], run.reps,
+                      d["seq_len"], run.keep, run.top_k, sel2, cnt2, run.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel2, run.sel) and torch.equal(cnt2, run.sel_count)
+    assert H.hhr_read_device_status(run.ws) == 0
+
+
+def test_keep_all_blocks_equals_flat_indexer(gpu_lib):
+    """Keeping every block, the selection is the flat indexer's exact top-k (IoU 1 against
+    the oracle's flat selection, up to the excuse band around the k-th score)."""
+    case = dict(CASES[1], name="keep_all", seq_lens=[3000, 4096], keep_blocks=4096 // 16,
+                top_k=300, seed=31)
+    r = HisaRun(gpu_lib, case)
+    r.run_stages()
+    ts = r.token_scores.cpu().numpy()
+    sel = r.sel.cpu().numpy()
+    sc = r.sel_count.cpu().numpy()
+    for b in range(r.B):
+        L = r.L(b)
+        # conditioned: every valid token is a candidate, in position order
+        np.testing.assert_array_equal(r.kept.cpu().numpy()[b, :r.nb(b)], np.arange(r.nb(b)))
+        want = O.top_largest(ts[b, :L].astype(np.float64), np.arange(L), r.top_k)
+        np.testing.assert_array_equal(sel[b, :sc[b]], want)
+        # unconditioned: the flat oracle
+        s = O.indexer_scores(r.q(b), r.inp["w"][b], r.keys(b))
+        flat = O.flat_select(r.inp["q8"][b], r.inp["q_scale"][b], r.inp["w"][b], r.inp["k8"][b],
+                             r.inp["k_scale"][b], L, r.top_k)
+        cut = np.sort(s)[::-1][r.top_k - 1]
+        for t in np.setxor1d(sel[b, :sc[b]], flat):
+            assert abs(s[t] - cut) <= SCORE_EXCUSE * abs(cut)
+
+
+def test_attention_over_hisa_selection(gpu_lib):
+    """H5: 16 attention heads on one bf16 KV head over the HISA selection."""
+    H = gpu_lib
+    case = dict(CASES[0], name="attn", seq_lens=[9000], seed=41)
+    r = HisaRun(H, case)
+    r.run_stages()
+    rng = np.random.Generator(np.random.PCG64(4242))
+    Lcap, Ha = r.Lcap, 16
+    K = synth.f32_to_bf16_bits(rng.standard_normal((1, 1, Lcap, 128), dtype=np.float32))
+    V = synth.f32_to_bf16_bits(rng.standard_normal((1, 1, Lcap, 128), dtype=np.float32))
+    q = synth.round_to_bf16(rng.standard_normal((1, Ha, 128), dtype=np.float32))
+    shape = H.make_shape(1, Ha, 1, Lcap, "bf16")
+    dv = U.dev()
+    out = torch.zeros((1, Ha, 128), dtype=torch.float32, device=dv)
+    ws = torch.zeros(H.hhr_workspace_size(shape, 1, 1, 0, r.top_k), dtype=torch.uint8, device=dv)
+    sel = r.sel.view(1, 1, r.top_k)
+    cnt = r.sel_count.view(1, 1)
+    H.hhr_sparse_decode(shape, torch.from_numpy(q).to(dv), U.kv_to_device(K, "bf16"),
+                        U.kv_to_device(V, "bf16"), sel, cnt, r.top_k, 1.0 / np.sqrt(128.0), out,
+                        ws)
+    torch.cuda.synchronize()
+    idx = r.sel.cpu().numpy()[0, :int(r.sel_count[0])]
+    Kf = synth.bf16_bits_to_f32(K[0, 0])
+    Vf = synth.bf16_bits_to_f32(V[0, 0])
+    want = OH.attend(q[0], Kf[idx], Vf[idx])
+    assert np.abs(out.cpu().numpy()[0].astype(np.float64) - want).max() <= 2e-3
+
+
+def test_bad_seq_len_sets_status_and_selects_nothing(gpu_lib):
+    case = dict(CASES[1], name="bad_len", seq_lens=[1000, 2000], seed=51)
+    r = HisaRun(gpu_lib, case)
+    r.d["seq_len"][1] = r.Lcap + 1
+    r.inp["seq_len"][1] = 0  # what the oracle should see: an empty sequence
+    r.run_stages()
+    assert gpu_lib.hhr_read_device_status(r.ws) & 0x1
+    assert int(r.sel_count[1]) == 0 and int(r.kept_count[1]) == 0
+    assert torch.all(r.sel[1] == -1)
+    assert int(r.sel_count[0]) == min(r.top_k, 1000)
