@@ -276,3 +276,37 @@ def test_bad_seq_len_sets_status_and_selects_nothing(gpu_lib):
     assert int(r.sel_count[1]) == 0 and int(r.kept_count[1]) == 0
     assert torch.all(r.sel[1] == -1)
     assert int(r.sel_count[0]) == min(r.top_k, 1000)
+
+
+def test_full_size_hisa_128k(gpu_lib):
+    """The full HISA decode workload: 131072 fp8 index keys, 64 index heads, 1024 blocks of 128,
+    top 64 blocks, token top-2048; every block score and token score of the kept blocks checked,
+    both selections exact on the GPU's scores, block selection within the excuse band on raw
+    inputs."""
+    w = synth.HISA_WORKLOADS["hisa_128k"]
+    case = dict(name="hisa_128k", n_index_heads=w.n_index_heads, block=w.block, max_ctx=w.ctx,
+                seq_lens=[w.ctx], keep_blocks=w.keep_blocks, top_k=w.top_k, seed=w.seed)
+    r = HisaRun(gpu_lib, case)
+    r.run_stages()
+    q, wt = r.q(0), r.inp["w"][0]
+    reps = r.reps.cpu().numpy().astype(np.float64)[0]
+    keys = r.keys(0)
+    want_reps = O.pooled_reps(keys, r.block)
+    scale = np.abs(keys).reshape(-1, r.block, 128).mean(1)
+    assert np.all(np.abs(reps - want_reps) <= 1e-5 * scale + 1e-30)
+    bs = r.block_scores.cpu().numpy().astype(np.float64)[0]
+    assert np.all(np.abs(bs - O.indexer_scores(q, wt, reps)) <= 1e-5 * _abs_terms(q, wt, reps))
+    kept = r.kept.cpu().numpy()[0]
+    np.testing.assert_array_equal(kept, O.top_largest(bs, np.arange(bs.size), r.keep))
+    S = O.indexer_scores(q, wt, want_reps)
+    cut = np.sort(S)[::-1][r.keep - 1]
+    for blk in np.setxor1d(kept, O.top_largest(S, np.arange(S.size), r.keep)):
+        assert abs(S[blk] - cut) <= SCORE_EXCUSE * abs(cut)
+    cand = _candidates(r, 0, kept, r.keep)
+    ts = r.token_scores.cpu().numpy().astype(np.float64)[0]
+    x = keys[cand]
+    assert np.all(np.abs(ts - O.indexer_scores(q, wt, x)) <= 1e-5 * _abs_terms(q, wt, x))
+    sel = r.sel.cpu().numpy()[0]
+    np.testing.assert_array_equal(sel, O.top_largest(ts, cand, r.top_k))
+    assert int(r.sel_count[0]) == r.top_k
+    assert gpu_lib.hhr_read_device_status(r.ws) == 0
