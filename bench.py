@@ -13,9 +13,11 @@ rotates through --layers independent copies of every per-layer buffer
 (K, V, codes, page metadata, R, W), about 4.8 GB at 8 layers.
 
 Prints one JSON line.  `roofline` is for the page-bound scorer, the kernel
-that moves most of the step's bytes; its duration is measured with HIP events
-around each launch on the stream it runs on, in a pass of its own over the
-same rotating layers.  `cpu_baseline` times the CPU oracle (numpy, 1 thread)
+that moves most of the step's bytes; its average launch duration is measured
+with one pair of HIP events on its stream around a pass of back-to-back
+launches over the same rotating layers; `traffic` is its counter-measured HBM
+bytes per launch from the committed profile, while the scorer's sources are
+unchanged since.  `cpu_baseline` times the CPU oracle (numpy, 1 thread)
 on whole decode steps of the same workload for a bounded number of seconds.
 """
 from __future__ import annotations
@@ -34,6 +36,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# Measured HBM traffic of the page-bound scorer comes from a committed counter
+# profile; it is reported only while the kernel sources that build that kernel
+# (the files below) are unchanged since the counters were taken.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "page_scores_llama8b_128k_hbm_traffic.md")
+SCORER_SOURCES = ["hash_hierarchical_top_amd/csrc/select.hip",
+                  "hash_hierarchical_top_amd/csrc/stages.h",
+                  "hash_hierarchical_top_amd/csrc/topk_device.h",
+                  "hash_hierarchical_top_amd/csrc/hhr_device.h",
+                  "hash_hierarchical_top_amd/csrc/hhr_internal.h",
+                  "hash_hierarchical_top_amd/csrc/hhr_consts.h"]
+
+
+def scorer_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in SCORER_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Calibrated HBM bytes per k_page_scores launch from the counter profile, or None if
+    there is none for this workload or the scorer's sources changed since."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != scorer_source_digest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -68,6 +105,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hhr.load()
     dev = torch.device("cuda", 0)
+    if args.workload in synth.HISA_WORKLOADS:
+        return main_hisa(args, torch, hhr, synth, dev)
     w = synth.WORKLOADS[args.workload]
     B, Hq, Hkv, Lcap, top_k = w.batch, w.n_q_heads, w.n_kv_heads, w.max_ctx, w.top_k
     keep = (w.keep_num, w.keep_den, w.keep_pages_abs)
@@ -199,22 +238,22 @@ def main():
     scores = torch.zeros((B, Hkv, NpCap), dtype=torch.float32, device=dev)
     hhr.hhr_encode_queries(shape, q, R0, W0, q_rot, q_codes)
     nk = min(args.steps, 400)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nk)]
     for i in range(args.layers):
         hhr.hhr_page_scores(shape, q_rot, seq, layers[i]["meta"], scores, ws)
     torch.cuda.synchronize()
-    for i in range(nk):
-        lay = layers[i % args.layers]
-        kev[i][0].record(stream)
-        hhr.hhr_page_scores(shape, q_rot, seq, lay["meta"], scores, ws)
-        kev[i][1].record(stream)
+    ke0 = torch.cuda.Event(enable_timing=True)
+    ke1 = torch.cuda.Event(enable_timing=True)
+    ke0.record(stream)
+    for i in range(nk):  # back to back on the scorer's stream, rotating layers
+        hhr.hhr_page_scores(shape, q_rot, seq, layers[i % args.layers]["meta"], scores, ws)
+    ke1.record(stream)
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    k_ms = ke0.elapsed_time(ke1) / nk
     k_bytes = meta_bytes + B * Hq * 128 * 4 + int(Np.sum()) * Hkv * 4
     roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload),
                 "kernel": "k_page_scores", "bytes_per_launch": k_bytes,
                 "avg_launch_us": round(k_ms * 1e3, 3)}
 
@@ -262,6 +301,192 @@ def main():
         "recall_topk_vs_exact": [round(r, 4) for r in recalls],
         "planted_hit_rate": [round(float(x), 3) for x in planted_hits],
         "encoder_prefill": enc,
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main_hisa(args, torch, hhr, synth, dev):
+    """HISA decode step: hhr_hisa_select (block scores, top blocks, fp8 token scores,
+    token top-k) then hhr_sparse_decode with the attention heads on one KV head."""
+    w = synth.HISA_WORKLOADS[args.workload]
+    t_gen = time.time()
+    inp = synth.make_hisa_workload_inputs(args.workload)
+    t_gen = time.time() - t_gen
+    L, Hi, Ha, blk = w.ctx, w.n_index_heads, w.n_attn_heads, w.block
+    hs = hhr.make_hisa_shape(1, Hi, blk, L)
+    ashape = hhr.make_shape(1, Ha, 1, L, "bf16")
+    scale = 1.0 / math.sqrt(128.0)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q8, q_scale, wt = t(inp["q8"][None]), t(inp["q_scale"][None]), t(inp["w"][None])
+    qa = t(inp["q_attn"][None])
+    seq = t(inp["seq_len"])
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    k80, ks0 = t(inp["k8"][None]), t(inp["k_scale"][None])
+    K0, V0 = t(inp["K"]).view(torch.bfloat16), t(inp["V"]).view(torch.bfloat16)
+    layers = []
+    for i in range(args.layers):
+        lay = dict(k8=k80 if i == 0 else k80.clone(), ks=ks0 if i == 0 else ks0.clone(),
+                   K=K0 if i == 0 else K0.clone(), V=V0 if i == 0 else V0.clone(),
+                   reps=torch.zeros((1, L // blk, 128), dtype=torch.float32, device=dev))
+        layers.append(lay)
+    ws_h = torch.zeros(hhr.hhr_hisa_workspace_size(hs, w.keep_blocks, w.top_k), dtype=torch.uint8,
+                       device=dev)
+    ws_a = torch.zeros(hhr.hhr_workspace_size(ashape, 0, 1, 1, w.top_k), dtype=torch.uint8,
+                       device=dev)  # attention only: the keep count does not matter
+    sel = torch.zeros((1, 1, w.top_k), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    out = torch.zeros((1, Ha, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- prefill-time pooling (H1), timed per layer
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pool_ms = []
+    for lay in layers:
+        pe[0].record(stream)
+        hhr.hhr_hisa_pool_keys(hs, lay["k8"], lay["ks"], zero, seq, L, lay["reps"], ws_h)
+        pe[1].record(stream)
+        torch.cuda.synchronize()
+        pool_ms.append(pe[0].elapsed_time(pe[1]))
+
+    def step(i):
+        lay = layers[i % args.layers]
+        hhr.hhr_hisa_select(hs, q8, q_scale, wt, lay["k8"], lay["ks"], lay["reps"], seq,
+                            w.keep_blocks, w.top_k, sel.view(1, w.top_k), cnt.view(1), ws_h)
+        hhr.hhr_sparse_decode(ashape, qa, lay["K"], lay["V"], sel, cnt, w.top_k, scale, out, ws_a)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            for i in range(args.layers):
+                step(i)
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.layers):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // args.layers)):
+            graph.replay()
+        torch.cuda.synchronize()
+    n_rep = -(-args.steps // args.layers) if graph is not None else 0
+    steps = n_rep * args.layers if graph is not None else args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    if graph is not None:
+        for _ in range(n_rep):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    assert hhr.hhr_read_device_status(ws_h) == 0 and hhr.hhr_read_device_status(ws_a) == 0
+
+    # algorithmic bytes per step: pooled reps, kept fp8 keys + scales, K/V rows, q and o
+    n_sel = int(cnt.item())
+    step_bytes = ((L // blk) * 128 * 4 + w.keep_blocks * blk * (128 + 4) + n_sel * 2 * 128 * 2
+                  + Hi * (128 + 8) + Ha * 128 * 4 * 2)
+    # dominant kernel by bytes: the fp8 token scorer + token top-k entry point, timed back to
+    # back on its stream over the rotating layers
+    kept = torch.zeros((1, w.keep_blocks), dtype=torch.int32, device=dev)
+    kc = torch.zeros((1,), dtype=torch.int32, device=dev)
+    bs = torch.zeros((1, L // blk), dtype=torch.float32, device=dev)
+    hhr.hhr_hisa_block_scores(hs, q8, q_scale, wt, layers[0]["reps"], seq, bs, ws_h)
+    hhr.hhr_hisa_top_blocks(hs, bs, seq, w.keep_blocks, kept, kc, ws_h)
+    nk = min(args.steps, 400)
+    ke0, ke1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ke0.record(stream)
+    for i in range(nk):
+        lay = layers[i % args.layers]
+        hhr.hhr_hisa_token_topk(hs, q8, q_scale, wt, lay["k8"], lay["ks"], seq, kept, kc,
+                                w.keep_blocks, w.top_k, sel.view(1, w.top_k), cnt.view(1), None,
+                                ws_h)
+    ke1.record(stream)
+    torch.cuda.synchronize()
+    k_ms = ke0.elapsed_time(ke1) / nk
+    k_bytes = w.keep_blocks * blk * (128 + 4) + Hi * (128 + 8) + w.keep_blocks * 4 + w.top_k * 4
+    roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 5), "traffic": None,
+                "kernel": "k_hisa_token_scores + k_hisa_topk (hhr_hisa_token_topk)",
+                "bytes_per_launch": k_bytes, "avg_launch_us": round(k_ms * 1e3, 3),
+                "note": "latency-bound: ~1 MB per launch"}
+
+    # ---- selection quality and CPU baseline (oracle select + attention, 1 thread)
+    from oracle import hhr as OH
+    from oracle import hisa as OS
+
+    sel_h = sel.cpu().numpy()[0, 0, :n_sel]
+    flat = OS.flat_select(inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], L,
+                          w.top_k)
+    iou = OS.iou(sel_h, flat)
+    # the same on the planted-block variant: 16 blocks whose keys lean towards the index
+    # queries' mean direction, i.e. data with block structure for the coarse stage to find
+    pin = synth.make_hisa_workload_inputs(args.workload, planted_blocks=16, make_kv=False)
+    pk8, pks = t(pin["k8"][None]), t(pin["k_scale"][None])
+    preps = torch.zeros((1, L // blk, 128), dtype=torch.float32, device=dev)
+    hhr.hhr_hisa_pool_keys(hs, pk8, pks, zero, seq, L, preps, ws_h)
+    hhr.hhr_hisa_select(hs, t(pin["q8"][None]), t(pin["q_scale"][None]), t(pin["w"][None]), pk8,
+                        pks, preps, seq, w.keep_blocks, w.top_k, sel.view(1, w.top_k),
+                        cnt.view(1), ws_h)
+    torch.cuda.synchronize()
+    iou_planted = OS.iou(sel.cpu().numpy()[0, 0, :int(cnt.item())],
+                         OS.flat_select(pin["q8"], pin["q_scale"], pin["w"], pin["k8"],
+                                        pin["k_scale"], L, w.top_k))
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        Kf = synth.bf16_bits_to_f32(inp["K"][0, 0])
+        Vf = synth.bf16_bits_to_f32(inp["V"][0, 0])
+        with threadpool_limits(limits=1):
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                r = OS.select(inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], L,
+                              blk, w.keep_blocks, w.top_k)
+                OH.attend(inp["q_attn"], Kf[r["sel"]], Vf[r["sel"]], scale)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        cpu = {"value": round(n / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} whole HISA decode steps of {w.name} (pooling included, "
+                         f"attention on {Ha} heads), {el:.1f} s, numpy fp64, BLAS 1 thread"}
+    line = {
+        "metric": "HISA decode queries/s (64 fp8 index heads + 16 attention heads) at 128K ctx",
+        "value": round(steps / (ms_per_step * steps / 1e3), 1), "unit": "queries/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3 index, bf16 K/V, f32 accumulate",
+        "data": "synthetic (seeded; N(0,1) index queries and keys quantised to e4m3)",
+        "config": {"workload": w.name, "ctx": L, "index_heads": Hi, "block": blk,
+                   "keep_blocks": w.keep_blocks, "top_k": w.top_k, "attn_heads": Ha,
+                   "layers_rotated": args.layers, "hip_graph": bool(graph is not None),
+                   "entry": "hhr_hisa_select+hhr_sparse_decode"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e6), 1),
+        "iou_vs_flat_indexer": round(float(iou), 4),
+        "iou_vs_flat_indexer_planted_blocks": round(float(iou_planted), 4),
+        "pool_prefill_ms": round(float(np.median(pool_ms[1:] if len(pool_ms) > 1 else pool_ms)), 4),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
     }

@@ -44,10 +44,10 @@
  *     bit-identical outputs.
  *   - Workspace: device memory of at least the size the matching
  *     *_workspace_size() function returns.  It starts with a control block
- *     (the device status word at offset 0, hhr_decode's scheduling tickets at
- *     offset 64, and eight counters per (b, g) at offset 256) that must be zero
- *     before the workspace is first used -- allocate it zero-filled.  Every
- *     call leaves tickets and counters zero again (after an
+ *     (the device status word at offset 0; bytes 64..255 and eight words per
+ *     (b, g) from offset 256 are reserved for cross-workgroup scheduling)
+ *     that must be zero before the workspace is first used -- allocate it
+ *     zero-filled.  Every call leaves the reserved words zero (after an
  *     HHR_DEV_TIMEOUT, zero the workspace before reusing it); the status word
  *     keeps its error bits until hhr_read_device_status clears it.  The
  *     control block sits at the same offsets in every layout, so one
@@ -76,8 +76,9 @@ typedef enum {
 /* Device status bits (hhr_read_device_status). */
 #define HHR_DEV_BAD_SEQ_LEN 0x1u  /* a seq_len was < 0 or > max_ctx           */
 #define HHR_DEV_BAD_INDEX 0x2u    /* a selected position was outside [0,Lcap) */
-#define HHR_DEV_TIMEOUT 0x4u      /* hhr_decode: a wait between its workgroups gave up
-                                     (results of that call are unspecified) */
+#define HHR_DEV_TIMEOUT 0x4u      /* a wait between workgroups of one launch gave up
+                                     (results of that call are unspecified); reserved:
+                                     no current kernel waits on another workgroup */
 
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
