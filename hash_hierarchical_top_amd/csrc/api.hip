@@ -153,17 +153,27 @@ uint32_t* status_of(void* workspace) { return reinterpret_cast<uint32_t*>(worksp
 
 namespace hhr {
 
-size_t ctrl_bytes(const hhr_shape& s) {
-  return kAlign + align_up(kCountersPerGroup * (size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+// Control block: status word and reserved words (256 B), kCountersPerGroup
+// counters per (b, g), then the fine top-k H histograms; all of it is zero
+// between calls, and every layout places its scratch after it.
+static size_t counters_bytes(const hhr_shape& s) {
+  return align_up(kCountersPerGroup * (size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
 }
+
+static size_t ham_hist_bytes(const hhr_shape& s) {
+  const size_t BG = (size_t)s.batch * s.n_kv_heads;
+  const size_t G = (size_t)(s.n_q_heads / s.n_kv_heads);
+  return align_up(BG * (128 * G + 1) * sizeof(int));
+}
+
+size_t ctrl_bytes(const hhr_shape& s) { return kAlign + counters_bytes(s) + ham_hist_bytes(s); }
 
 HamScratch ham_scratch(const hhr_shape& s, int32_t p_max) {
   const size_t BG = (size_t)s.batch * s.n_kv_heads;
-  const size_t G = (size_t)(s.n_q_heads / s.n_kv_heads);
   HamScratch h;
+  h.hist = kAlign + counters_bytes(s);
   h.dist = ctrl_bytes(s);
-  h.hist = h.dist + align_up(BG * (size_t)p_max * kPS * sizeof(uint16_t));
-  h.end = h.hist + align_up(BG * (size_t)ham_chunks(p_max) * (128 * G + 1) * sizeof(int));
+  h.end = h.dist + align_up(BG * (size_t)p_max * kPS * sizeof(uint16_t));
   return h;
 }
 
@@ -189,14 +199,13 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   };
   const size_t BHq = (size_t)s.batch * s.n_q_heads;
   const size_t BHkv = (size_t)s.batch * s.n_kv_heads;
-  // control block: status word and group tickets, then kCountersPerGroup
-  // counters per (b, g)
-  // (same offsets in every layout)
+  // control block (same offsets in every layout): status word and reserved
+  // words, counters per (b, g), fine top-k histograms
   w.ctrl = take(kAlign);
-  w.counters = take(kCountersPerGroup * BHkv * sizeof(uint32_t));
+  w.counters = take(counters_bytes(s));
+  w.ham_hist = take(ham_hist_bytes(s));
   const HamScratch hs = ham_scratch(s, w.p_max);
-  w.ham_dist = take(hs.hist - hs.dist);
-  w.ham_hist = take(hs.end - hs.hist);
+  w.ham_dist = take(hs.end - hs.dist);
   w.q_rot = take(BHq * kD * sizeof(float));
   w.q_codes = take(BHq * kNW * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
@@ -427,25 +436,19 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
     return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 ws.total);
   char* base = static_cast<char*>(workspace);
-  uint32_t* status = status_of(workspace);
-  float* q_rot = reinterpret_cast<float*>(base + ws.q_rot);
-  uint32_t* q_codes = reinterpret_cast<uint32_t*>(base + ws.q_codes);
-  float* scores = reinterpret_cast<float*>(base + ws.scores);
-  int32_t* kept = reinterpret_cast<int32_t*>(base + ws.kept);
-  int32_t* kept_count = reinterpret_cast<int32_t*>(base + ws.kept_count);
-  HHR_LAUNCH(hhr::launch_encode_queries(*shape, q, R, W, q_rot, q_codes, stream),
-             "encode_queries launch");
-  HHR_LAUNCH(hhr::launch_page_scores(*shape, q_rot, seq_len, page_meta, scores, status, stream),
-             "page_scores launch");
-  HHR_LAUNCH(hhr::launch_top_pages(*shape, scores, seq_len, keep_num, keep_den, keep_abs,
-                                   ws.p_max, kept, kept_count, status, stream),
-             "top_pages launch");
-  HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count,
-                                      ws.p_max, top_k, sel_idx, sel_count,
-                                      reinterpret_cast<uint16_t*>(base + ws.ham_dist),
-                                      reinterpret_cast<int*>(base + ws.ham_hist), status,
-                                      stream),
-             "hamming_topk launch");
+  hhr::CompositeBuffers buf;
+  buf.status = status_of(workspace);
+  buf.counters = reinterpret_cast<uint32_t*>(base + ws.counters);
+  buf.scores = reinterpret_cast<float*>(base + ws.scores);
+  buf.q_codes = reinterpret_cast<uint32_t*>(base + ws.q_codes);
+  buf.kept = reinterpret_cast<int32_t*>(base + ws.kept);
+  buf.kept_count = reinterpret_cast<int32_t*>(base + ws.kept_count);
+  buf.dist = reinterpret_cast<uint16_t*>(base + ws.ham_dist);
+  buf.chist = reinterpret_cast<int*>(base + ws.ham_hist);
+  HHR_LAUNCH(hhr::launch_select_composite(*shape, q, seq_len, R, W, codes, page_meta, keep_num,
+                                          keep_den, keep_abs, ws.p_max, top_k, sel_idx,
+                                          sel_count, buf, stream),
+             "select launch");
   *layout = ws;
   return HHR_OK;
 }

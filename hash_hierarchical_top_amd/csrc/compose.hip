@@ -1,0 +1,139 @@
+// The composite selection (hhr_select, and the selection part of hhr_decode):
+// S2 + S3 + S4 in one launch, then the fine top-k kernels.
+//
+// k_score_topp ends the page stage with the workgroup that finishes last:
+// every workgroup writes its bounds with agent-scope stores, waits for them
+// (s_waitcnt), and bumps a per-(b, g) counter with an agent-scope atomic; the
+// workgroup that brings the counter to the grid size resets it and runs top-P
+// on everyone's bounds (read with agent-scope loads).  Nobody waits for
+// anybody, so there is no scheduling hazard.  Each workgroup rotates its
+// group's queries itself, so no separate query-encoding launch precedes it.
+// (Measured: such a hand-off costs about as much as a kernel boundary, ~2 us;
+// the gain here is the query encoding off the critical path.)
+//
+// Every step calls the same device functions as the one-step kernels, with
+// the same thread counts where the order of floating-point sums depends on it,
+// so both compositions give bit-identical results.
+
+#include "hhr_device.h"
+#include "hhr_internal.h"
+#include "stages.h"
+
+namespace hhr {
+
+namespace {
+
+constexpr int kScoreThreads = 1024;
+constexpr int kScorePagesPerWg = (kScoreThreads / kWave) * kScorePagesPerWave;  // 256
+
+__device__ __forceinline__ int clamped_len(const int32_t* seq_len, int b, int Lcap,
+                                           uint32_t* status) {
+  const int L = seq_len[b];
+  if (L < 0 || L > Lcap) {
+    if (status && threadIdx.x == 0) atomicOr(status, HHR_DEV_BAD_SEQ_LEN);
+    return 0;
+  }
+  return L;
+}
+
+// Publishes this workgroup's stores and counts it in; true in the workgroup
+// that arrives last (which also re-zeroes the counter).  All threads call.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n_wg, int* s_last) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = add_agent_u32(counter, 1u);
+    *s_last = prev == n_wg - 1u;
+    if (*s_last) st_agent_u32(counter, 0u);
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
+
+struct ScoreTopSmem {
+  union {
+    struct {
+      QencSmem qe;
+      float qrot[kMaxG][kD];
+    } rot;
+    struct {
+      __attribute__((aligned(16))) float sbuf[kMaxCtx / kPS];
+      TopScratch top;
+    } sel;
+  };
+};
+
+// S2 + S3 + S4.  grid (ceil(NpCap / 256), B*Hkv), 1024 threads: 16 waves x 16
+// pages.  Each workgroup rotates its group's queries itself (64 KiB of R from
+// L2, issued after its metadata loads so both are in flight together);
+// workgroup 0 of each (b, g) also writes the query codes.
+__global__ __launch_bounds__(kScoreThreads) void k_score_topp(
+    const float* __restrict__ q, const int32_t* __restrict__ seq_len,
+    const float* __restrict__ R, const float* __restrict__ W, const float* __restrict__ meta,
+    int keep_num, int keep_den, int keep_abs, int p_max, int Hq, int Hkv, int Lcap,
+    float* __restrict__ scores, uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
+    int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
+    uint32_t* __restrict__ status) {
+  __shared__ ScoreTopSmem sm;
+  __shared__ int s_last;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv;
+  const int g = bg % Hkv;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int NpCap = Lcap / kPS;
+  const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
+  const int Np = (L + kPS - 1) / kPS;
+  const int pb = blockIdx.x * kScorePagesPerWg + (tid >> 6) * kScorePagesPerWave;
+  const bool wave_has = pb < Np;                                    // wave-uniform
+  const bool wg_has = (int)blockIdx.x * kScorePagesPerWg < Np;      // block-uniform
+  PageLoads<1> pl;
+  if (wave_has) score_load<1>(bg, NpCap, Np, pb, meta, pl);
+  auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
+  if (blockIdx.x == 0) {
+    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
+    qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
+                      [&](int h, int word, uint32_t bits) {
+                        q_codes[cbase + (size_t)h * kNW + word] = bits;
+                      });
+  } else if (wg_has) {
+    qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
+                                 [](int, int, uint32_t) {});
+  }
+  if (wave_has) {
+    float A[4][2], B[4][2];
+    score_ab(G, [&](int h, int d) { return sm.rot.qrot[h][d]; }, A, B);
+    score_finish<true, 1>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
+  }
+  if (!arrive_last(&counters[bg], gridDim.x, &s_last)) return;
+
+  const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
+  int32_t* out = kept + (size_t)bg * p_max;
+  for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
+  if (tid == 0) kept_count[bg] = P;
+  if (P == 0) return;
+  top_pages_core<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, sm.sel.sbuf,
+                                      sm.sel.top, [&](int pos, int c) { out[pos] = c; });
+}
+
+}  // namespace
+
+hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
+                                   const float* R, const float* W, const uint32_t* codes,
+                                   const float* meta, int32_t keep_num, int32_t keep_den,
+                                   int32_t keep_abs, int32_t p_max, int32_t top_k,
+                                   int32_t* sel_idx, int32_t* sel_count,
+                                   const CompositeBuffers& buf, hipStream_t stream) {
+  const int BG = s.batch * s.n_kv_heads;
+  const int NpCap = s.max_ctx / kPS;
+  hipLaunchKernelGGL(k_score_topp, dim3((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG),
+                     dim3(kScoreThreads), 0, stream, q, seq_len, R, W, meta, keep_num, keep_den,
+                     keep_abs, p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, buf.scores,
+                     buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
+                             top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status, stream);
+}
+
+}  // namespace hhr

@@ -25,10 +25,11 @@ struct Workspace {
   int32_t p_max = 0, n_split = 0;
 };
 
-// Scratch of the fine top-k (distances, chunk histograms), at offsets that
-// depend only on the shape and p_max, right after the control block.
+// Scratch of the fine top-k: the H histograms (zero between calls) are the
+// last part of the control block; the distances follow it.  Offsets depend
+// only on the shape and p_max.
 struct HamScratch {
-  size_t dist = 0, hist = 0, end = 0;
+  size_t hist = 0, dist = 0, end = 0;
 };
 HamScratch ham_scratch(const hhr_shape& s, int32_t p_max);
 constexpr int kCountersPerGroup = 8;  // control words per (b, g) after the first 256 bytes
@@ -68,6 +69,27 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
                                 const int32_t* sel_count, int32_t top_k, float scale, float* out,
                                 float* part, int32_t n_split, uint32_t* status,
                                 hipStream_t stream);
+
+// Composite selection (hhr_select, hhr_decode): S2..S4 in one launch that
+// ends in the last-arriving workgroup of each (b, g), then S5 + S6.
+// counters: B*Hkv arrival counters (zero before and after every call).
+struct CompositeBuffers {
+  uint32_t* status;
+  uint32_t* counters;
+  float* scores;
+  uint32_t* q_codes;
+  int32_t* kept;
+  int32_t* kept_count;
+  uint16_t* dist;
+  int* chist;
+};
+hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
+                                   const float* R, const float* W, const uint32_t* codes,
+                                   const float* meta, int32_t keep_num, int32_t keep_den,
+                                   int32_t keep_abs, int32_t p_max, int32_t top_k,
+                                   int32_t* sel_idx, int32_t* sel_count,
+                                   const CompositeBuffers& buf, hipStream_t stream);
+
 
 // Control block: status word at byte 0; bytes 64..255 and kCountersPerGroup
 // words per (b, g) from byte 256 are reserved for cross-workgroup scheduling.

@@ -81,8 +81,8 @@ __device__ __forceinline__ int kept_pages(const int32_t* kept_count, int bg, int
 __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
     const uint32_t* __restrict__ q_codes, const uint32_t* __restrict__ codes,
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
-    const int32_t* __restrict__ kept_count, int p_max, int nchk, int Hq, int Hkv, int Lcap,
-    uint16_t* __restrict__ dist, int* __restrict__ chist) {
+    const int32_t* __restrict__ kept_count, int p_max, int Hq, int Hkv, int Lcap,
+    uint16_t* __restrict__ dist, int* __restrict__ hist) {
   __shared__ HamDistSmem sm;
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
@@ -90,24 +90,23 @@ __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
   const int P = kept_pages(kept_count, bg, L, p_max);
   if ((int)blockIdx.x >= ham_chunks(P)) return;
   ham_dist_chunk<kHamDistThreads, false>(b, bg % Hkv, Hq, Hkv, Lcap, L, P, blockIdx.x, p_max,
-                                         nchk, q_codes, codes, kept, dist, chist, sm);
+                                         q_codes, codes, kept, dist, hist, sm);
 }
 
 // Exact top-k of one (b, g) from its distances and chunk histograms.
 __global__ __launch_bounds__(kHamSelThreads) void k_ham_select(
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
-    const int32_t* __restrict__ kept_count, int p_max, int nchk, int top_k, int Hq, int Hkv,
-    int Lcap, const uint16_t* __restrict__ dist, const int* __restrict__ chist,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
-    uint32_t* __restrict__ status) {
+    const int32_t* __restrict__ kept_count, int p_max, int top_k, int Hq, int Hkv, int Lcap,
+    const uint16_t* __restrict__ dist, int* __restrict__ hist, int32_t* __restrict__ sel_idx,
+    int32_t* __restrict__ sel_count, uint32_t* __restrict__ status) {
   __shared__ HamSmem sm;
   const int bg = blockIdx.x;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
   const int L = checked_len(seq_len, b, Lcap, g == 0 ? status : nullptr);
   const int P = kept_pages(kept_count, bg, L, p_max);
-  ham_select<kHamSelThreads, false>(b, g, Hq, Hkv, P, top_k, p_max, nchk, kept, false, dist,
-                                    chist, sel_idx, sel_count, sm);
+  ham_select<kHamSelThreads, false>(b, g, Hq, Hkv, P, top_k, p_max, kept, false, dist, hist,
+                                    sel_idx, sel_count, sm);
 }
 
 }  // namespace
@@ -140,13 +139,13 @@ hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, cons
   const int BG = s.batch * s.n_kv_heads;
   const int nchk = ham_chunks(p_max);
   hipLaunchKernelGGL(k_ham_dist, dim3(nchk, BG), dim3(kHamDistThreads), 0, stream, q_codes,
-                     codes, seq_len, kept, kept_count, p_max, nchk, s.n_q_heads, s.n_kv_heads,
+                     codes, seq_len, kept, kept_count, p_max, s.n_q_heads, s.n_kv_heads,
                      s.max_ctx, dist, chist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_ham_select, dim3(BG), dim3(kHamSelThreads), 0, stream, seq_len, kept,
-                     kept_count, p_max, nchk, top_k, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist,
-                     chist, sel_idx, sel_count, status);
+                     kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, chist,
+                     sel_idx, sel_count, status);
   return hipGetLastError();
 }
 

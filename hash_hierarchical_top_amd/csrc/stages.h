@@ -38,13 +38,15 @@ __device__ __forceinline__ void spin_until_geq(const uint32_t* flag, uint32_t ta
 }
 
 // ============================================================== S2: query
-// Thread t < 512 owns columns 4*(t%64) .. +3 of [R | W] (256 columns) over the
-// 16 input dims 16*((t/64)%8) .. +15: it issues its 16 float4 loads at once,
-// keeps them in registers and forms partial dot products for 4 query heads at
-// a time; the 8 partials of each output are summed in LDS in fixed order.
-// Outputs q' = q R (columns < 128) and the sign bits of q W (packed by ballot).
-// Every thread of the workgroup must call (it contains barriers); threads
-// >= 512 only take part in the barriers.
+// Columns 0..127 of [R | W] give q' = q R, columns 128..255 give the sign
+// bits of q W.  Every output (head h, column c) is computed the same way:
+// 8 partial sums over the input dims 16 k .. 16 k + 15 (sequential FMAs),
+// then the partials added in LDS in order k = 0..7.  NT threads share the
+// (column, k) work items, CPT = 8 NCOL / NT adjacent columns each, so a thread
+// holds 16 CPT matrix values in registers and the result does not depend on
+// NT or on NCOL (256: rotation and codes; 128: rotation only).
+// rot(h, col, v) receives q'; code(h, word, bits) receives 32 code bits.
+// Every thread of the workgroup must call (barriers).
 constexpr int kQeThreads = 512;
 
 struct QencSmem {
@@ -52,68 +54,96 @@ struct QencSmem {
   float red[8][4][2 * kD];
 };
 
-template <bool COH>
-__device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
-                           const float* __restrict__ R, const float* __restrict__ W,
-                           float* q_rot, uint32_t* q_codes, QencSmem& sm) {
+template <int NCOL, int NT, typename Rot, typename Code>
+__device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
+                          const float* __restrict__ R, const float* __restrict__ W,
+                          QencSmem& sm, Rot rot, Code code) {
+  static_assert(NCOL == kD || NCOL == 2 * kD, "rotation, or rotation and codes");
+  constexpr int CPT = 8 * NCOL / NT;  // columns per thread
+  static_assert(CPT == 1 || CPT == 2 || CPT == 4, "8 NCOL / NT columns per thread");
+  constexpr int kGroupsC = NCOL / CPT;
+  constexpr int kOut = 4 * NCOL;  // outputs per 4-head chunk
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
-  const bool act = tid < kQeThreads;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
-  if (act)
-    for (int i = tid; i < G * kD; i += kQeThreads) sm.sq[i / kD][i % kD] = q[qbase + i];
-  const int cg = tid & 63;
-  const int dg = (tid >> 6) & 7;
-  const int c0 = 4 * cg;  // column in [0, 256)
+  const int cg = tid % kGroupsC;
+  const int dg = tid / kGroupsC;  // 0..7
+  const int c0 = CPT * cg;        // first column in [0, NCOL)
   const float* M = (c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kD + (c0 - kD));
-  floatx4 m[16];
+  float m[16][CPT];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    m[j] = act ? *(const floatx4*)(M + (size_t)(16 * dg + j) * kD) : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 16; ++j) {
+    const float* row = M + (size_t)(16 * dg + j) * kD;
+    if constexpr (CPT == 4) {
+      const floatx4 v = *(const floatx4*)row;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[j][k] = v[k];
+    } else if constexpr (CPT == 2) {
+      const float2 v = *(const float2*)row;
+      m[j][0] = v.x;
+      m[j][1] = v.y;
+    } else {
+      m[j][0] = *row;
+    }
+  }
+  for (int i = tid; i < G * kD; i += NT) sm.sq[i / kD][i % kD] = q[qbase + i];
   __syncthreads();
   for (int hc = 0; hc < G; hc += 4) {
-    if (act) {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (hc + hh < G) {
+    for (int hh = 0; hh < 4; ++hh) {
+      float acc[CPT];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float x = sm.sq[hc + hh][16 * dg + j];
+      for (int k = 0; k < CPT; ++k) acc[k] = 0.f;
+      if (hc + hh < G) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[k] = fmaf(x, m[j][k], acc[k]);
-          }
+        for (int j = 0; j < 16; ++j) {
+          const float x = sm.sq[hc + hh][16 * dg + j];
+#pragma unroll
+          for (int k = 0; k < CPT; ++k) acc[k] = fmaf(x, m[j][k], acc[k]);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sm.red[dg][hh][c0 + k] = acc[k];
       }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) sm.red[dg][hh][c0 + k] = acc[k];
     }
     __syncthreads();
-    if (act) {
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int o = tid + kQeThreads * pass;  // (head hh, column col) of this chunk
-        const int hh = o >> 8;
-        const int col = o & 255;
-        float v = 0.f;
+    for (int pass = 0; pass < (kOut + NT - 1) / NT; ++pass) {
+      const int o = tid + NT * pass;  // (head hh, column col) of this chunk
+      if (o >= kOut) break;           // wave-uniform: kOut is a multiple of 64
+      const int hh = o / NCOL;
+      const int col = o % NCOL;
+      float v = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v += sm.red[k][hh][col];
-        const int h = hc + hh;
-        if (col < kD) {
-          if (h < G) Mem<COH>::st(q_rot + qbase + (size_t)h * kD + col, v);
-        } else {
-          const uint64_t bits = __ballot(v >= 0.0f);
-          if ((tid & 63) == 0 && h < G) {
-            const int word = (col - kD) >> 5;  // col is the wave's first column here
-            uint32_t* dst = q_codes + ((size_t)b * Hq + (size_t)g * G + h) * kNW + word;
-            Mem<COH>::st(dst, (uint32_t)bits);
-            Mem<COH>::st(dst + 1, (uint32_t)(bits >> 32));
-          }
+      for (int k = 0; k < 8; ++k) v += sm.red[k][hh][col];
+      const int h = hc + hh;
+      if (col < kD) {
+        if (h < G) rot(h, col, v);
+      } else {
+        const uint64_t bits = __ballot(v >= 0.0f);
+        if ((tid & 63) == 0 && h < G) {
+          const int word = (col - kD) >> 5;  // col is the wave's first column here
+          code(h, word, (uint32_t)bits);
+          code(h, word + 1, (uint32_t)(bits >> 32));
         }
       }
     }
     __syncthreads();
   }
+}
+
+// q' and the codes of one (b, g) to global memory.
+template <bool COH>
+__device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
+                           const float* __restrict__ R, const float* __restrict__ W,
+                           float* q_rot, uint32_t* q_codes, QencSmem& sm) {
+  const int G = Hq / Hkv;
+  const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
+  qenc_core<2 * kD, kQeThreads>(
+      b, g, Hq, Hkv, q, R, W, sm,
+      [&](int h, int col, float v) { Mem<COH>::st(q_rot + qbase + (size_t)h * kD + col, v); },
+      [&](int h, int word, uint32_t bits) {
+        Mem<COH>::st(q_codes + ((size_t)b * Hq + (size_t)g * G + h) * kNW + word, bits);
+      });
 }
 
 // ============================================================== S3: bound
@@ -132,19 +162,21 @@ __device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restric
 // must be active (cross-lane DPP exchanges).
 constexpr int kScorePagesPerWave = 16;
 
-template <bool COH, int NB = 1>
-__device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, int pb,
-                            const float* q_rot, const float* __restrict__ meta, float* scores,
-                            const uint32_t* ready, uint32_t* status) {
-  // NB consecutive 16-page batches pb, pb + 16, ...; every load of every batch
-  // is issued before any of them is used.
-  const int G = Hq / Hkv;
-  const int bg = b * Hkv + g;
+// Metadata of NB consecutive 16-page batches pb, pb + 16, ... of one (b, g),
+// loaded by one wave (lane layout above).  Pages past Np are clamped to the
+// last page; their results are never stored.
+template <int NB>
+struct PageLoads {
+  floatx4 m[NB][4][4];
+};
+
+template <int NB>
+__device__ __forceinline__ void score_load(int bg, int NpCap, int Np, int pb,
+                                           const float* __restrict__ meta, PageLoads<NB>& pl) {
   const int l = threadIdx.x & 63;
   const int r = l >> 4;
   const int sub = l & 15;
   const float* mbase = meta + (size_t)bg * NpCap * kD * 2 + 4 * sub;
-  floatx4 m[NB][4][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -152,25 +184,39 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
       const int p = min(pb + kScorePagesPerWave * nb + 4 * j + r, Np - 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        m[nb][j][k] =
+        pl.m[nb][j][k] =
             __builtin_nontemporal_load((const floatx4*)(mbase + (size_t)p * kD * 2 + 64 * k));
     }
-  if (ready != nullptr && l == 0) spin_until_geq(ready, 1u, status);
-  float A[4][2], B[4][2];
+}
+
+// A/B of this lane's dims 2 sub + 32 k (+1), k = 0..3, summed over the G
+// heads in order: rot_of(h, d) returns q'_hd.
+template <typename RotOf>
+__device__ __forceinline__ void score_ab(int G, RotOf rot_of, float A[4][2], float B[4][2]) {
+  const int sub = threadIdx.x & 15;
 #pragma unroll
   for (int k = 0; k < 4; ++k) A[k][0] = A[k][1] = B[k][0] = B[k][1] = 0.f;
-  const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD + 2 * sub;
   for (int h = 0; h < G; ++h) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float vx = Mem<COH>::ld(qr + (size_t)h * kD + 32 * k);
-      const float vy = Mem<COH>::ld(qr + (size_t)h * kD + 32 * k + 1);
+      const float vx = rot_of(h, 2 * sub + 32 * k);
+      const float vy = rot_of(h, 2 * sub + 32 * k + 1);
       A[k][0] += fmaxf(vx, 0.f);
       B[k][0] += fminf(vx, 0.f);
       A[k][1] += fmaxf(vy, 0.f);
       B[k][1] += fminf(vy, 0.f);
     }
   }
+}
+
+// Bounds of the loaded pages; each page's bound is stored by one lane, and
+// emit(p, v) sees it too.
+template <bool COH, int NB, typename Emit>
+__device__ __forceinline__ void score_finish(int bg, int NpCap, int Np, int pb,
+                                             const PageLoads<NB>& pl, const float A[4][2],
+                                             const float B[4][2], float* scores, Emit emit) {
+  const int l = threadIdx.x & 63;
+  const int r = l >> 4;
   const bool b3 = l & 8, b2 = l & 4;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -180,8 +226,8 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
       float x = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k)  // m = {mn[d0], mx[d0], mn[d1], mx[d1]}
-        x += A[k][0] * m[nb][j][k][1] + B[k][0] * m[nb][j][k][0] + A[k][1] * m[nb][j][k][3] +
-             B[k][1] * m[nb][j][k][2];
+        x += A[k][0] * pl.m[nb][j][k][1] + B[k][0] * pl.m[nb][j][k][0] +
+             A[k][1] * pl.m[nb][j][k][3] + B[k][1] * pl.m[nb][j][k][2];
       v[j] = x;
     }
     // partner lanes: 15 - sub (other 8-lane half), then 7 - (sub % 8) (other
@@ -200,8 +246,28 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
     v[0] += dpp_f<dpp::kQuadXor2>(v[0]);
     v[0] += dpp_f<dpp::kQuadXor1>(v[0]);
     const int p = pb + kScorePagesPerWave * nb + 4 * ((b3 ? 2 : 0) + (b2 ? 1 : 0)) + r;
-    if ((l & 3) == 0 && p < Np) Mem<COH>::st(scores + (size_t)bg * NpCap + p, v[0]);
+    if ((l & 3) == 0 && p < Np) {
+      Mem<COH>::st(scores + (size_t)bg * NpCap + p, v[0]);
+      emit(p, v[0]);
+    }
   }
+}
+
+// One wave: load, read q' from q_rot (waiting for `ready` first if given),
+// finish.
+template <bool COH, int NB = 1>
+__device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, int pb,
+                            const float* q_rot, const float* __restrict__ meta, float* scores,
+                            const uint32_t* ready, uint32_t* status) {
+  const int G = Hq / Hkv;
+  const int bg = b * Hkv + g;
+  PageLoads<NB> pl;
+  score_load<NB>(bg, NpCap, Np, pb, meta, pl);
+  if (ready != nullptr && (threadIdx.x & 63) == 0) spin_until_geq(ready, 1u, status);
+  float A[4][2], B[4][2];
+  const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD;
+  score_ab(G, [&](int h, int d) { return Mem<COH>::ld(qr + (size_t)h * kD + d); }, A, B);
+  score_finish<COH, NB>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
 }
 
 // ============================================================== S4: prune
@@ -242,13 +308,14 @@ __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den
 // position order: candidate c = (kept slot c/16, row c%16).  Two stages:
 //   distances (many workgroups): chunk k holds the candidates of kept slots
 //     [64k, 64k + 64); each workgroup computes H for its chunk, writes it
-//     (0xFFFF for a row past the sequence end) and its chunk's histogram
-//     over H = 0 .. 128 G.  Spreading this over many CUs matters: per
-//     candidate it costs a 16-byte gather and ~50 vector ops;
-//   selection (one workgroup per (b, g)): sums the chunk histograms, finds
-//     the smallest H value T whose cumulative count reaches top_k and how
-//     many candidates with H == T are taken, then compacts in candidate
-//     order.
+//     (0xFFFF for a row past the sequence end) and adds its chunk's
+//     histogram over H = 0 .. 128 G into the (b, g)'s histogram with integer
+//     atomics (order-free, so exact).  Spreading this over many CUs matters:
+//     per candidate it costs a 16-byte gather and ~50 vector ops;
+//   selection (one workgroup per (b, g)): reads the histogram (and zeroes it
+//     for the next call), finds the smallest H value T whose cumulative count
+//     reaches top_k and how many candidates with H == T are taken, then
+//     compacts in candidate order.
 constexpr int kHamBins = 128 * kMaxG + 1;  // 2049
 constexpr int kHistCopies = 4;
 constexpr int kHamChunk = kHamChunkPages * kPS;  // 1024 candidates
@@ -271,13 +338,13 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 }
 
 // Distances of chunk k of (b, g): candidates c in [1024k, 1024k + 1024) with
-// c < 16 P.  dist [B][Hkv][p_max*16] u16; chist [B][Hkv][nchk][128 G + 1].
-// All threads call; NT divides 1024.
+// c < 16 P.  dist [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts
+// added atomically).  All threads call; NT divides 1024.
 template <int NT, bool COH>
 __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, int P, int k,
-                               int p_max, int nchk, const uint32_t* q_codes,
+                               int p_max, const uint32_t* q_codes,
                                const uint32_t* __restrict__ codes, const int32_t* kept,
-                               uint16_t* dist, int* chist, HamDistSmem& sm) {
+                               uint16_t* dist, int* hist, HamDistSmem& sm) {
   constexpr int kItems = kHamChunk / NT;
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
@@ -325,12 +392,12 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, i
     if (c < ncl) Mem<COH>::st(dc + c, (uint16_t)(ok[j] ? h[j] : 0xFFFFu));
   }
   __syncthreads();
-  int* ch = chist + ((size_t)bg * nchk + k) * nbins;
+  int* hb = hist + (size_t)bg * nbins;
   for (int i = tid; i < nbins; i += NT) {
     int c = 0;
 #pragma unroll
     for (int r = 0; r < kHistCopies; ++r) c += sm.hist[r][i];
-    Mem<COH>::st(ch + i, c);
+    if (c != 0) atomicAdd(hb + i, c);  // device-scope: chunks run on every XCD
   }
 }
 
@@ -346,20 +413,18 @@ struct HamSmem {
   TopScratch top;
 };
 
-// Selection of (b, g) from the distances and chunk histograms of its
-// ham_chunks(P) chunks.  If skept_ready, sm.skept already holds the kept
-// pages; otherwise they are read from kept.  All threads call.
+// Selection of (b, g) from the distances and histogram its distance chunks
+// wrote; leaves the histogram zero.  If skept_ready, sm.skept already holds
+// the kept pages; otherwise they are read from kept.  All threads call.
 template <int NT, bool COH>
-__device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int p_max, int nchk,
+__device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int p_max,
                            const int32_t* kept, bool skept_ready, const uint16_t* dist,
-                           const int* chist, int32_t* sel_idx, int32_t* sel_count,
-                           HamSmem& sm) {
+                           int* hist, int32_t* sel_idx, int32_t* sel_count, HamSmem& sm) {
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
   const int ncand = P * kPS;
   const int nbins = 128 * G + 1;
-  const int nch = ham_chunks(P);
 
   // gather: kept pages, distances (8 per 16-byte load), summed histograms
   if (!skept_ready)
@@ -371,12 +436,10 @@ __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int 
     for (int i = tid; i < nv8; i += NT)
       reinterpret_cast<u32x4*>(sm.hval)[i] = ld_u32x4<COH>(d32 + 4 * i);
   }
-  const int* chb = chist + (size_t)bg * nchk * nbins;
+  int* hb = hist + (size_t)bg * nbins;
   for (int i = tid; i < nbins; i += NT) {
-    int c = 0;
-#pragma unroll 8
-    for (int k = 0; k < nch; ++k) c += Mem<COH>::ld(chb + (size_t)k * nbins + i);
-    sm.hist[i] = c;
+    sm.hist[i] = Mem<COH>::ld(hb + i);
+    Mem<COH>::st(hb + i, 0);
   }
   __syncthreads();
 
@@ -605,11 +668,13 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   }
 }
 
-// Merge the ns chunk partials of one (b, g) into o (1024 threads):
+// Merge the ns chunk partials of one (b, g) into o (kCombThreads threads):
 //   M_h = max_s m_sh, f_sh = e^(m_sh - M_h), L_h = sum_s f_sh l_sh,
 //   o_h = sum_s f_sh o~_sh / L_h  (o = 0 when nothing was selected).
-// Thread (h, dim quad, s-group) sums chunks s = sgrp, sgrp + NSG, ...; the
-// s-groups are then added in order in LDS.
+// Thread (h, dim quad, s-group) sums chunks s = sgrp, sgrp + NSG, ... in
+// ascending order; the s-groups are then added in order in LDS.  The first
+// 16 of each thread's partials are loaded together with every (m, l) before
+// the weights are known, so up to 16 NSG chunks cost one round trip.
 constexpr int kCombThreads = 512;
 constexpr int kCombMaxChunks = kMaxCand / kCh;  // 512
 
@@ -619,11 +684,22 @@ struct CombSmem {
   floatx4 red[kCombThreads];
 };
 
+template <bool COH>
+__device__ __forceinline__ floatx4 ld_f32x4(const float* p) {
+  if constexpr (COH) {
+    return floatx4{Mem<true>::ld(p), Mem<true>::ld(p + 1), Mem<true>::ld(p + 2),
+                   Mem<true>::ld(p + 3)};
+  } else {
+    return *(const floatx4*)p;
+  }
+}
+
 // kCombThreads threads (every caller uses this count, so all sum in the same
 // order).
 template <bool COH>
 __device__ void attn_combine(int b, int g, int Hq, int Hkv, int ns, int n_split,
                              const float* part, float* __restrict__ out, CombSmem& sm) {
+  constexpr int kB = 16;  // partials per thread per round trip
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
@@ -631,51 +707,62 @@ __device__ void attn_combine(int b, int g, int Hq, int Hkv, int ns, int n_split,
   const int l = tid & 63;
   const size_t sstride = (size_t)kMaxG * kPartStride;
   const float* pb = part + (size_t)bg * n_split * sstride;
-  // chunk weights: one wave per head
-  for (int h = w; h < G; h += kCombThreads / kWave) {
-    float M = -__builtin_huge_valf();
-    for (int s = l; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(pb + s * sstride + h * kPartStride + kD));
-    M = wave_max(M);
-    float ls = 0.f;
-    for (int s = l; s < ns; s += kWave) {
-      const float* ps = pb + s * sstride + h * kPartStride;
-      const float ms = Mem<COH>::ld(ps + kD);
-      const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
-      sm.f[h][s] = f;
-      ls = fmaf(f, Mem<COH>::ld(ps + kD + 1), ls);
-    }
-    ls = wave_sum(ls);
-    if (l == 0) sm.lsum[h] = ls;
-  }
-  __syncthreads();
-  const int pairs = G * (kD / 4);                       // (head, dim quad)
-  const int nsg = max(1, kCombThreads / pairs);         // chunk groups
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int pairs = G * (kD / 4);                // (head, dim quad)
+  const int nsg = max(1, kCombThreads / pairs);  // chunk groups
   const int pair = tid % pairs;
   const int sgrp = tid / pairs;
   const int h = pair / (kD / 4);
   const int d4 = pair % (kD / 4);
-  if (sgrp < nsg && ns > 0) {
-    // chunks s = sgrp, sgrp + nsg, ... in ascending order, eight loads in
-    // flight (indices clamped; a clamped slot gets weight 0)
-    constexpr int kB = 8;
+  const bool worker = sgrp < nsg && ns > 0;
+  floatx4 v[kB];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int sc = min(s0 + j * nsg, ns - 1);  // clamped; weight 0 past ns
+      v[j] = ld_f32x4<COH>(pb + sc * sstride + h * kPartStride + 4 * d4);
+    }
+  };
+  if (worker) load_batch(sgrp);
+  // chunk weights: one wave per head (chunks s = l, l + 64, ...)
+  for (int hh = w; hh < G; hh += kCombThreads / kWave) {
+    const float* ph = pb + hh * kPartStride + kD;
+    if (ns <= kWave) {
+      const int sc = min(l, max(ns - 1, 0));
+      const float ms = l < ns ? Mem<COH>::ld(ph + sc * sstride) : -__builtin_huge_valf();
+      const float ls_ = l < ns ? Mem<COH>::ld(ph + sc * sstride + 1) : 0.f;
+      const float M = wave_max(ms);
+      const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
+      if (l < ns) sm.f[hh][l] = f;
+      const float ls = wave_sum(fmaf(f, ls_, 0.f));
+      if (l == 0) sm.lsum[hh] = ls;
+    } else {
+      float M = -__builtin_huge_valf();
+      for (int s = l; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(ph + s * sstride));
+      M = wave_max(M);
+      float ls = 0.f;
+      for (int s = l; s < ns; s += kWave) {
+        const float ms = Mem<COH>::ld(ph + s * sstride);
+        const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
+        sm.f[hh][s] = f;
+        ls = fmaf(f, Mem<COH>::ld(ph + s * sstride + 1), ls);
+      }
+      ls = wave_sum(ls);
+      if (l == 0) sm.lsum[hh] = ls;
+    }
+  }
+  __syncthreads();
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (worker) {
 #pragma unroll 1
     for (int s0 = sgrp; s0 < ns; s0 += kB * nsg) {
-      floatx4 v[kB];
-      float f[kB];
+      if (s0 != sgrp) load_batch(s0);
 #pragma unroll
       for (int j = 0; j < kB; ++j) {
         const int s = s0 + j * nsg;
-        const int sc = min(s, ns - 1);
-        const float* po = pb + sc * sstride + h * kPartStride + 4 * d4;
+        const float f = s < ns ? sm.f[h][min(s, ns - 1)] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[j][k] = Mem<COH>::ld(po + k);
-        f[j] = s < ns ? sm.f[h][sc] : 0.f;
+        for (int k = 0; k < 4; ++k) acc[k] = fmaf(f, v[j][k], acc[k]);
       }
-#pragma unroll
-      for (int j = 0; j < kB; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = fmaf(f[j], v[j][k], acc[k]);
     }
   }
   sm.red[tid] = acc;

@@ -43,16 +43,17 @@
  *   - Results are deterministic: repeated calls on the same inputs give
  *     bit-identical outputs.
  *   - Workspace: device memory of at least the size the matching
- *     *_workspace_size() function returns.  It starts with a control block
- *     (the device status word at offset 0; bytes 64..255 and eight words per
- *     (b, g) from offset 256 are reserved for cross-workgroup scheduling)
- *     that must be zero before the workspace is first used -- allocate it
- *     zero-filled.  Every call leaves the reserved words zero (after an
+ *     *_workspace_size() function returns, zero-filled before its first use.
+ *     It starts with a control block: the device status word at offset 0;
+ *     bytes 64..255, eight words per (b, g) from offset 256 and then one
+ *     H histogram per (b, g) (the fine top-k's) are reserved and zero
+ *     between calls.  Every call leaves them zero again (after an
  *     HHR_DEV_TIMEOUT, zero the workspace before reusing it); the status word
  *     keeps its error bits until hhr_read_device_status clears it.  The
- *     control block sits at the same offsets in every layout, so one
- *     workspace may serve every entry point.  Calls that share a workspace
- *     must not overlap in time (order them on one stream).
+ *     control block sits at the same offsets in every HHR layout and every
+ *     other region follows it, so one workspace may serve every HHR entry
+ *     point; the HISA entry points use a workspace of their own.  Calls that
+ *     share a workspace must not overlap in time (order them on one stream).
  */
 #ifndef HHR_H_
 #define HHR_H_
@@ -193,8 +194,9 @@ hhr_status hhr_top_pages(const hhr_shape* shape, const float* scores, const int3
  *   dist       [B][Hkv][p_max*ps] uint16, out, or NULL: H of candidate
  *              i = (kept slot i/ps, row i%ps); 0xFFFF for rows >= seq_len
  *   workspace  >= hhr_workspace_size(...) bytes for the keep parameters that
- *              gave p_max (scratch for per-chunk H histograms, and for the
- *              distances when dist is NULL); HHR_ERR_WORKSPACE if smaller */
+ *              gave p_max (an H histogram per (b, g), zero between calls, and
+ *              scratch for the distances when dist is NULL);
+ *              HHR_ERR_WORKSPACE if smaller */
 hhr_status hhr_hamming_topk(const hhr_shape* shape, const uint32_t* q_codes,
                             const uint32_t* codes, const int32_t* seq_len, const int32_t* kept,
                             const int32_t* kept_count, int32_t p_max, int32_t top_k,
