@@ -416,7 +416,8 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
                               const float* page_meta, int32_t keep_num, int32_t keep_den,
                               int32_t keep_abs, int32_t top_k, int32_t* sel_idx,
                               int32_t* sel_count, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, hhr::Workspace* layout) {
+                              hipStream_t stream, bool finish, hhr::Workspace* layout,
+                              hhr::CompositeBuffers* bufs) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_keep(keep_num, keep_den, keep_abs));
   HHR_TRY(check_top_k(top_k));
@@ -447,9 +448,10 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
   buf.chist = reinterpret_cast<int*>(base + ws.ham_hist);
   HHR_LAUNCH(hhr::launch_select_composite(*shape, q, seq_len, R, W, codes, page_meta, keep_num,
                                           keep_den, keep_abs, ws.p_max, top_k, sel_idx,
-                                          sel_count, buf, stream),
+                                          sel_count, buf, finish, stream),
              "select launch");
   *layout = ws;
+  *bufs = buf;
   return HHR_OK;
 }
 
@@ -460,9 +462,10 @@ hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,
                       void* stream) {
   hhr::Workspace ws;
+  hhr::CompositeBuffers buf;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
-                      as_stream(stream), &ws));
+                      as_stream(stream), true, &ws, &buf));
   return ok();
 }
 
@@ -478,14 +481,16 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
   HHR_TRY(check_ptr(out, "out"));
   if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
   hhr::Workspace ws;
+  hhr::CompositeBuffers buf;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
-                      as_stream(stream), &ws));
+                      as_stream(stream), false, &ws, &buf));
   char* base = static_cast<char*>(workspace);
-  HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
-                                       scale, out, reinterpret_cast<float*>(base + ws.attn_part),
-                                       ws.n_split, status_of(workspace), as_stream(stream)),
-             "sparse_decode launch");
+  HHR_LAUNCH(hhr::launch_attend_picked(*shape, q, k_cache, v_cache, seq_len, ws.p_max, top_k,
+                                       scale, sel_idx, sel_count, out,
+                                       reinterpret_cast<float*>(base + ws.attn_part), ws.n_split,
+                                       buf, as_stream(stream)),
+             "attend launch");
   return ok();
 }
 

@@ -1,5 +1,6 @@
-// The composite selection (hhr_select, and the selection part of hhr_decode):
-// S2 + S3 + S4 in one launch, then the fine top-k kernels.
+// The composite paths.  hhr_select: k_score_topp (S2 + S3 + S4), k_ham_dist,
+// k_ham_select.  hhr_decode: k_score_topp, k_ham_dist, k_attn_pick (S6 + S7:
+// every attention workgroup finds its own 64 selected keys), k_attn_merge.
 //
 // k_score_topp ends the page stage with the workgroup that finishes last:
 // every workgroup writes its bounds with agent-scope stores, waits for them
@@ -116,6 +117,50 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
                                       sm.sel.top, [&](int pos, int c) { out[pos] = c; });
 }
 
+// S6 + S7 for hhr_decode.  grid (n_split, B*Hkv), 256 threads: workgroup j
+// picks the keys of output ranks [64 j, 64 j + 64) straight from the
+// distances and histogram (pick_chunk), writes that slice of sel_idx (and
+// workgroup 0 the count), and attends over them exactly as k_attn would.
+template <bool KF32>
+__global__ __launch_bounds__(256) void k_attn_pick(
+    const float* __restrict__ q, const void* __restrict__ kcache, const void* __restrict__ vcache,
+    const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
+    const int32_t* __restrict__ kept_count, const uint16_t* __restrict__ dist,
+    const int* __restrict__ hist, int p_max, int Hq, int Hkv, int Lcap, int top_k, int n_split,
+    float scale, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
+    float* __restrict__ part, uint32_t* __restrict__ status) {
+  __shared__ AttnSmem<KF32> sm;
+  __shared__ PickSmem ps;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv;
+  const int g = bg % Hkv;
+  const int tid = threadIdx.x;
+  const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
+  const int P = L > 0 ? max(0, min(kept_count[bg], p_max)) : 0;
+  const int k0 = blockIdx.x * kCh;
+  const int count = pick_chunk<256>(bg, P, p_max, 128 * (Hq / Hkv) + 1, top_k, k0, kept, dist,
+                                    hist, sm.sidx, ps);
+  if (tid < kCh && k0 + tid < top_k) sel_idx[(size_t)bg * top_k + k0 + tid] = sm.sidx[tid];
+  if (blockIdx.x == 0 && tid == 0) sel_count[bg] = count;
+  if (k0 >= count) return;  // block-uniform
+  attn_chunk<KF32, false>(b, g, Hq, Hkv, Lcap, top_k, k0, min(kCh, count - k0), scale, q, kcache,
+                          vcache, nullptr,
+                          part + ((size_t)bg * n_split + blockIdx.x) * kMaxG * kPartStride, status,
+                          sm);
+}
+
+// The chunk merge of one (b, g), then the (b, g)'s H histogram back to zero.
+__global__ __launch_bounds__(kCombThreads) void k_attn_merge(
+    const float* __restrict__ part, const int32_t* __restrict__ sel_count,
+    float* __restrict__ out, int* __restrict__ hist, int Hq, int Hkv, int top_k, int n_split) {
+  __shared__ CombSmem sm;
+  const int bg = blockIdx.x;
+  const int cnt = max(0, min(sel_count[bg], top_k));
+  attn_combine<false>(bg / Hkv, bg % Hkv, Hq, Hkv, (cnt + kCh - 1) / kCh, n_split, part, out, sm);
+  const int nbins = 128 * (Hq / Hkv) + 1;
+  for (int i = threadIdx.x; i < nbins; i += kCombThreads) hist[(size_t)bg * nbins + i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
@@ -123,7 +168,8 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                    const float* meta, int32_t keep_num, int32_t keep_den,
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
-                                   const CompositeBuffers& buf, hipStream_t stream) {
+                                   const CompositeBuffers& buf, bool finish,
+                                   hipStream_t stream) {
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   hipLaunchKernelGGL(k_score_topp, dim3((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG),
@@ -132,8 +178,36 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                      buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
-                             top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status, stream);
+  if (finish)
+    return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
+                               top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status,
+                               stream);
+  return launch_ham_dist(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
+                         buf.dist, buf.chist, stream);
+}
+
+hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_len, int32_t p_max,
+                                int32_t top_k, float scale, int32_t* sel_idx,
+                                int32_t* sel_count, float* out, float* part, int32_t n_split,
+                                const CompositeBuffers& buf, hipStream_t stream) {
+  const int BG = s.batch * s.n_kv_heads;
+  dim3 grid(n_split, BG);
+  if (s.kv_dtype == HHR_F32)
+    hipLaunchKernelGGL(k_attn_pick<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
+                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, p_max,
+                       s.n_q_heads, s.n_kv_heads, s.max_ctx, top_k, n_split, scale, sel_idx,
+                       sel_count, part, buf.status);
+  else
+    hipLaunchKernelGGL(k_attn_pick<false>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
+                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, p_max,
+                       s.n_q_heads, s.n_kv_heads, s.max_ctx, top_k, n_split, scale, sel_idx,
+                       sel_count, part, buf.status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3(BG), dim3(kCombThreads), 0, stream, part, sel_count, out,
+                     buf.chist, s.n_q_heads, s.n_kv_heads, top_k, n_split);
+  return hipGetLastError();
 }
 
 }  // namespace hhr

@@ -59,6 +59,10 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
                             int32_t keep_num, int32_t keep_den, int32_t keep_abs, int32_t p_max,
                             int32_t* kept, int32_t* kept_count, uint32_t* status,
                             hipStream_t stream);
+hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
+                           const int32_t* seq_len, const int32_t* kept,
+                           const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
+                           hipStream_t stream);
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                                const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
@@ -70,8 +74,9 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
                                 float* part, int32_t n_split, uint32_t* status,
                                 hipStream_t stream);
 
-// Composite selection (hhr_select, hhr_decode): S2..S4 in one launch that
-// ends in the last-arriving workgroup of each (b, g), then S5 + S6.
+// Composite paths (hhr_select, hhr_decode): S2..S4 in one launch that ends in
+// the last-arriving workgroup of each (b, g), then S5, then S6 (or, for
+// hhr_decode, S6 + S7 with every attention workgroup picking its own keys).
 // counters: B*Hkv arrival counters (zero before and after every call).
 struct CompositeBuffers {
   uint32_t* status;
@@ -88,7 +93,15 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                    const float* meta, int32_t keep_num, int32_t keep_den,
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
-                                   const CompositeBuffers& buf, hipStream_t stream);
+                                   const CompositeBuffers& buf, bool finish,
+                                   hipStream_t stream);
+// S6 + S7 for hhr_decode after launch_select_composite(..., finish = false):
+// every attention workgroup picks its own chunk of the selection.
+hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_len, int32_t p_max,
+                                int32_t top_k, float scale, int32_t* sel_idx,
+                                int32_t* sel_count, float* out, float* part, int32_t n_split,
+                                const CompositeBuffers& buf, hipStream_t stream);
 
 
 // Control block: status word at byte 0; bytes 64..255 and kCountersPerGroup

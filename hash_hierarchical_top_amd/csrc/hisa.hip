@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
     sbuf[c] = sc[min(c, max(Nb - 1, 0))];
   }
   __syncthreads();
-  const int cnt = top_largest_lds<kHisaThreads>(
+  const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
       sbuf, Nb, [](int) { return true; }, keep_blocks, sh,
       [&](int pos, int c) { out[pos] = c; });
   for (int i = cnt + tid; i < keep_blocks; i += kHisaThreads) out[i] = -1;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
     return blk >= 0 && blk * block + c % block < L;
   };
   int32_t* out = sel_idx + (size_t)b * top_k;
-  const int cnt = top_largest_lds<kHisaThreads>(
+  const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
       sbuf, ncand, present, top_k, sh,
       [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; });
   for (int i = cnt + tid; i < top_k; i += kHisaThreads) out[i] = -1;

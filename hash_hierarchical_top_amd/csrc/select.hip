@@ -131,21 +131,27 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
   return hipGetLastError();
 }
 
+hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
+                           const int32_t* seq_len, const int32_t* kept,
+                           const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(k_ham_dist, dim3(ham_chunks(p_max), s.batch * s.n_kv_heads),
+                     dim3(kHamDistThreads), 0, stream, q_codes, codes, seq_len, kept, kept_count,
+                     p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, hist);
+  return hipGetLastError();
+}
+
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                                const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
-                               int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* chist,
+                               int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* hist,
                                uint32_t* status, hipStream_t stream) {
-  const int BG = s.batch * s.n_kv_heads;
-  const int nchk = ham_chunks(p_max);
-  hipLaunchKernelGGL(k_ham_dist, dim3(nchk, BG), dim3(kHamDistThreads), 0, stream, q_codes,
-                     codes, seq_len, kept, kept_count, p_max, s.n_q_heads, s.n_kv_heads,
-                     s.max_ctx, dist, chist);
-  hipError_t e = hipGetLastError();
+  hipError_t e =
+      launch_ham_dist(s, q_codes, codes, seq_len, kept, kept_count, p_max, dist, hist, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_ham_select, dim3(BG), dim3(kHamSelThreads), 0, stream, seq_len, kept,
-                     kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, chist,
-                     sel_idx, sel_count, status);
+  hipLaunchKernelGGL(k_ham_select, dim3(s.batch * s.n_kv_heads), dim3(kHamSelThreads), 0, stream,
+                     seq_len, kept, kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads,
+                     s.max_ctx, dist, hist, sel_idx, sel_count, status);
   return hipGetLastError();
 }
 

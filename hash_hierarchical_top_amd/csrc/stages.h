@@ -294,7 +294,8 @@ __device__ int top_pages_core(const float* sc, int Np, int P, float* sbuf, TopSc
     }
   }
   __syncthreads();
-  return top_largest_lds<NT>(sbuf, Np, [](int) { return true; }, P, sh, emit);
+  return top_largest_lds<NT, kMaxCtx / kPS / (4 * NT)>(sbuf, Np, [](int) { return true; }, P,
+                                                         sh, emit);
 }
 
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
@@ -516,11 +517,171 @@ __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int 
   if (tid == 0) Mem<COH>::st(sel_count + bg, count);
 }
 
+// The 64 selected positions of output chunk [k0, k0 + 64) of (b, g), found
+// without the compacted list: the cut (T, need) from the H histogram, then
+// every thread counts the taken candidates of its run of distances, one
+// block scan gives each run its first output position, and only the runs
+// that reach into the chunk walk their candidates again to place them.  The
+// result is sidx[i] = the position of output rank k0 + i (-1 past the
+// selection); returns the selection size min(top_k, #valid).  Reads dist,
+// hist and kept written by earlier launches.  All NT threads call.
+constexpr int kPickBatch = 8;  // 8-distance words per thread per round trip
+
+struct PickSmem {
+  int scan[17];
+  uint32_t uscan[17];
+  int s_T, s_need;
+  u32x4 words[kPickBatch][256];  // this thread's current batch of words
+  int run_gb[256], run_eb[256];  // > and == T candidates before each run
+};
+
+template <int NT>
+__device__ __forceinline__ int pick_chunk(int bg, int P, int p_max, int nbins, int top_k, int k0,
+                          const int32_t* kept, const uint16_t* dist, const int* hist, int* sidx,
+                          PickSmem& ps) {
+  static_assert(NT == 256, "PickSmem::words holds one batch per thread of 256");
+  constexpr int kMaxPer = (kHamBins + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  const int ncand = P * kPS;
+  // the cut: smallest T with #(H <= T) >= top_k, and how many H == T are taken
+  const int* hb = hist + (size_t)bg * nbins;
+  const int per = (nbins + NT - 1) / NT;
+  const int b0 = tid * per;
+  int cnt_bin[kMaxPer];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    cnt_bin[i] = (i < per && b0 + i < nbins) ? hb[min(b0 + i, nbins - 1)] : 0;
+    local += cnt_bin[i];
+  }
+  int total;
+  const int ex = block_exclusive_scan<NT, int>(local, ps.scan, &total);
+  if (tid == 0) {
+    ps.s_T = nbins;  // every valid H is < nbins: take all valid candidates
+    ps.s_need = 0;
+  }
+  if (tid < kAttnChunk) sidx[tid] = -1;
+  __syncthreads();
+  if (total > top_k) {
+    int run = ex;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (run < top_k && run + cnt_bin[i] >= top_k && cnt_bin[i] > 0) {
+        ps.s_T = b0 + i;
+        ps.s_need = top_k - run;
+      }
+      run += cnt_bin[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t Th = (uint32_t)ps.s_T;
+  const int need = ps.s_need;
+  const int count = min(top_k, total);
+
+  // output ranks over contiguous runs of 8-distance words, staged through LDS
+  // (ps.words) so that both passes are small rolled loops
+  const int nv8 = (ncand + 8 * NT - 1) / (8 * NT);
+  const int c0 = 8 * nv8 * tid;
+  const uint32_t* d32 = reinterpret_cast<const uint32_t*>(dist + (size_t)bg * p_max * kPS);
+  auto cls_of = [&](const u32x4& hw, int e, int c) -> int {
+    const uint32_t word = hw[e >> 1];
+    uint32_t h = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+    if (c >= ncand) h = 0xFFFFu;
+    return h < Th ? 1 : (h == Th ? 2 : 0);
+  };
+  int gt = 0, eq = 0;
+#pragma unroll 1
+  for (int j0 = 0; j0 < nv8; j0 += kPickBatch) {
+    const int nb = min(kPickBatch, nv8 - j0);
+    u32x4 hw[kPickBatch];
+#pragma unroll
+    for (int j = 0; j < kPickBatch; ++j) {
+      const int c = min(c0 + 8 * (j0 + j), max(ncand - 8, 0));  // in bounds; masked below
+      hw[j] = *(const u32x4*)(d32 + c / 2);
+    }
+#pragma unroll
+    for (int j = 0; j < kPickBatch; ++j) ps.words[j][tid] = hw[j];
+#pragma unroll 1
+    for (int j = 0; j < nb; ++j) {
+      const u32x4 w8 = ps.words[j][tid];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = cls_of(w8, e, c0 + 8 * (j0 + j) + e);
+        gt += k == 1;
+        eq += k == 2;
+      }
+    }
+  }
+  uint32_t tot;
+  const uint32_t pre =
+      block_exclusive_scan<NT, uint32_t>((uint32_t)gt | ((uint32_t)eq << 16), ps.uscan, &tot);
+  // taken candidates before each run: gt before + min(eq before, need)
+  ps.run_gb[tid] = (int)(pre & 0xFFFFu);
+  ps.run_eb[tid] = (int)(pre >> 16);
+  __syncthreads();
+  // wave 0 places the window: the runs whose taken ranks reach into
+  // [k0, k0 + 64), walked 64 candidates at a time with wave scans for the
+  // tie rank and the output position
+  if (tid < kWave) {
+    const int l = tid;
+    auto taken_before = [&](int t) { return ps.run_gb[t] + min(ps.run_eb[t], need); };
+    int lo = NT, hi = -1;
+    for (int t = l; t < NT; t += kWave) {
+      const int f = taken_before(t);
+      const int z = t + 1 < NT ? taken_before(t + 1) : count;
+      if (f < k0 + kAttnChunk && z > k0) {
+        lo = min(lo, t);
+        hi = max(hi, t);
+      }
+    }
+    lo = (int)wave_min_u((uint32_t)lo);
+    hi = (int)wave_max_u((uint32_t)(hi + 1)) - 1;
+    if (hi >= lo) {
+      const int c_lo = 8 * nv8 * lo;
+      const int c_hi = min(8 * nv8 * (hi + 1), ncand);
+      int g_run = ps.run_gb[lo], e_run = ps.run_eb[lo];
+      const uint16_t* db = dist + (size_t)bg * p_max * kPS;
+      const int32_t* kb = kept + (size_t)bg * p_max;
+      constexpr int kPer = 8;  // candidates per lane per round trip
+#pragma unroll 1
+      for (int cb = c_lo; cb < c_hi; cb += kPer * kWave) {
+        uint32_t hv[kPer];
+        int pg[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int cc = min(cb + u * kWave + l, c_hi - 1);
+          hv[u] = db[cc];
+          pg[u] = kb[cc >> 4];
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int cc = cb + u * kWave + l;
+          const uint32_t h = cc < c_hi ? hv[u] : 0xFFFFu;
+          const int gtf = h < Th ? 1 : 0;
+          const int eqf = h == Th ? 1 : 0;
+          const int eq_incl = wave_inclusive_scan(eqf);
+          const int eq_before = e_run + eq_incl - eqf;
+          const int tk = (gtf || (eqf && eq_before < need)) ? 1 : 0;
+          const int tk_incl = wave_inclusive_scan(tk);
+          const int pos = g_run + min(e_run, need) + tk_incl - tk;
+          if (tk && pos >= k0 && pos < k0 + kAttnChunk) sidx[pos - k0] = pg[u] * kPS + (cc & 15);
+          g_run += __builtin_amdgcn_readlane(wave_inclusive_scan(gtf), kWave - 1);
+          e_run += __builtin_amdgcn_readlane(eq_incl, kWave - 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return count;
+}
+
 // ============================================================== S7: attend
 // One 256-thread group takes a chunk of up to 64 selected keys of one (b, g)
-// for all G query heads.  It gathers the chunk's K and V rows with every load
-// in flight at once (row indices clamped, data masked), stages K in LDS for
-// the logits, then reuses the buffer for V; writes the unnormalised partial
+// for all G query heads (their positions from sel_idx, or, with sel_idx
+// NULL, already in sm.sidx: 64 entries, -1 past nk).  It gathers the chunk's
+// K and V rows with every load in flight at once (row indices clamped, data
+// masked), stages K in LDS for the logits, then reuses the buffer for V;
+// writes the unnormalised partial
 // (o~, m, l): o~_h = sum_i e^(x_hi - m_h) V_i, m_h = max_i x_hi,
 // l_h = sum_i e^(x_hi - m_h), x_hi = q_h . K_i * scale.
 // All threads of the workgroup must call (barriers); each 256-thread group
@@ -556,7 +717,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   const int w = tq >> 6;
   const int l = tq & 63;
 
-  if (tq < kCh) {
+  if (sel_idx != nullptr && tq < kCh) {  // else the caller filled sm.sidx (valid or -1)
     int idx = -1;
     if (tq < nk) {
       idx = Mem<COH>::ld(sel_idx + (size_t)bg * top_k + k0 + tq);

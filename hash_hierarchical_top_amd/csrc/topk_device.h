@@ -167,14 +167,22 @@ __device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& g
 // The min(P, #present) largest present scores of sbuf[0..n), ties to the
 // lower index; emit(pos, c) for each taken candidate c, pos = its rank in
 // ascending c.  present(c) tells whether candidate c < n exists.  Thread tid
-// owns candidates [4*nv4*tid, 4*nv4*(tid+1)) with nv4 = ceil(n / (4*NT)),
-// read from LDS as float4 in rolled loops; sbuf must hold 4*NT*nv4 floats,
-// 16-byte aligned (slots past n are read but never used).  Scores must be
-// finite (-0 counts as +0).  Returns the number taken.  All threads call.
-template <int NT, typename Present, typename Emit>
+// owns candidates [4*nv4*tid, 4*nv4*(tid+1)) with nv4 = ceil(n / (4*NT)) <=
+// MAXV4; sbuf must hold 4*NT*MAXV4 floats, 16-byte aligned (slots past n are
+// read but never used).  Scores must be finite (-0 counts as +0).  Returns
+// the number taken.  All threads call.
+//
+// Every pass over the data is vector-throughput bound on one CU, so each
+// slot's bin is computed once and kept in registers (16 bits per slot):
+// the cut is then decided from the bins, and only members of the threshold
+// bin compare values.
+template <int NT, int MAXV4, typename Present, typename Emit>
 __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P, TopScratch& sh,
                                Emit emit) {
   constexpr int NWAVES = NT / kWave;
+  constexpr int MAXV = 4 * MAXV4;
+  static_assert(MAXV <= 32, "2 class bits per slot in 64 bits");
+  constexpr uint32_t kAbsent = 0xFFFFu;  // bin code of an absent slot
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = tid % kWave;
@@ -186,15 +194,17 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
 
   float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
   int cnt = 0;
-#pragma unroll 1
-  for (int j = 0; j < nv4; ++j) {
-    const float4 t = run4[j];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (is_present(c0 + 4 * j + e)) {
-        mn = fminf(mn, val(t, e));
-        mx = fmaxf(mx, val(t, e));
-        ++cnt;
+  for (int j = 0; j < MAXV4; ++j) {
+    if (j < nv4) {
+      const float4 t = run4[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (is_present(c0 + 4 * j + e)) {
+          mn = fminf(mn, val(t, e));
+          mx = fmaxf(mx, val(t, e));
+          ++cnt;
+        }
       }
     }
   }
@@ -211,7 +221,7 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
   __syncthreads();
   float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
   int n_valid = 0;
-#pragma unroll 1
+#pragma unroll
   for (int k = 0; k < NWAVES; ++k) {
     vmin = fminf(vmin, sh.w_min[k]);
     vmax = fmaxf(vmax, sh.w_max[k]);
@@ -220,24 +230,40 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
   const int Pe = min(P, n_valid);
   if (Pe <= 0) return 0;
 
-  // cut-off: mode 0 = every present candidate, 1 = bin >= bstar, 2 = keys
-  int mode = 0, bstar = 0, need_eq = 0;
-  uint32_t T = 0u;
+  // bins: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)) is monotone in v
   const float range = vmax - vmin;
   const float inv = range > 0.f ? (float)kLinBins / range : 0.f;
-  auto bin_of = [&](float x) {
-    const float f = (x - vmin) * inv;
-    const int bb = f < (float)kLinBins ? (int)f : kLinBins - 1;
-    return min(max(bb, 0), kLinBins - 1);
-  };
-  if (Pe < n_valid) {
-#pragma unroll 1
-    for (int j = 0; j < nv4; ++j) {
+  uint32_t bins[MAXV / 2];  // two 16-bit bin codes per word
+  const bool all = Pe >= n_valid;
+#pragma unroll
+  for (int j = 0; j < MAXV4; ++j) {
+    uint32_t b4[4];
+    if (j < nv4) {
       const float4 t = run4[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (is_present(c0 + 4 * j + e)) atomicAdd(&sh.hist[bin_of(val(t, e))], 1);
+      for (int e = 0; e < 4; ++e) {
+        uint32_t bb = kAbsent;
+        if (is_present(c0 + 4 * j + e)) {
+          const float f = (val(t, e) - vmin) * inv;
+          bb = (uint32_t)min(max(f < (float)kLinBins ? (int)f : kLinBins - 1, 0), kLinBins - 1);
+          if (!all) atomicAdd(&sh.hist[bb], 1);
+        }
+        b4[e] = bb;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b4[e] = kAbsent;
     }
+    bins[2 * j] = b4[0] | (b4[1] << 16);
+    bins[2 * j + 1] = b4[2] | (b4[3] << 16);
+  }
+  auto bin_at = [&](int i) { return (bins[i >> 1] >> (16 * (i & 1))) & 0xFFFFu; };
+
+  // cut-off: mode 0 = every present slot, 1 = bin >= bstar, 2 = bin > bstar or
+  // (bin == bstar and key >= T, ties by need_eq)
+  int mode = 0, need_eq = 0;
+  uint32_t bstar = 0, T = 0u;
+  if (!all) {
     __syncthreads();
     {
       constexpr int PER = kLinBins / NT > 0 ? kLinBins / NT : 1;
@@ -263,21 +289,16 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
       }
     }
     __syncthreads();
-    bstar = sh.bstar;
+    bstar = (uint32_t)sh.bstar;
     const int need = Pe - sh.above;  // 1 <= need <= hist[b*]
     const int cstar = sh.hist[bstar];
     if (need == cstar) {
       mode = 1;
     } else if (cstar <= kLinListMax) {
       mode = 2;
-#pragma unroll 1
-      for (int j = 0; j < nv4; ++j) {
-        const float4 t = run4[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (is_present(c0 + 4 * j + e) && bin_of(val(t, e)) == bstar)
-            sh.list_v[atomicAdd(&sh.list_n, 1)] = val(t, e);
-      }
+      for (int i = 0; i < MAXV; ++i)
+        if (bin_at(i) == bstar) sh.list_v[atomicAdd(&sh.list_n, 1)] = sbuf[c0 + i];
       __syncthreads();
       // T = the value with (#greater in b*) < need <= (#greater) + (#equal)
       for (int j = tid; j < cstar; j += NT) {
@@ -298,7 +319,7 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
       T = sh.T;
       need_eq = sh.need_eq;
     } else {
-      mode = 2;
+      mode = 3;  // radix over the keys of the whole set
       radix_cutoff<NT>(
           [&](int i) -> uint32_t {
             const int c = c0 + i;
@@ -309,34 +330,35 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
       need_eq = sh.need_eq;
     }
   }
-  auto cls_of = [&](float x, int c) -> int {
-    const uint32_t k = orderable_key(x);
-    const int by_key = k > T ? 1 : (k == T ? 2 : 0);
-    const int by_bin = bin_of(x) >= bstar ? 1 : 0;
-    const int cls = mode == 0 ? 1 : (mode == 1 ? by_bin : by_key);
-    return is_present(c) ? cls : 0;
-  };
+  // classify each slot once (2 bits: 1 = inside the cut, 2 = on it)
+  uint64_t cls = 0;
   int gt = 0, eq = 0;
-#pragma unroll 1
-  for (int j = 0; j < nv4; ++j) {
-    const float4 t = run4[j];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = cls_of(val(t, e), c0 + 4 * j + e);
-      gt += k == 1;
-      eq += k == 2;
+  for (int i = 0; i < MAXV; ++i) {
+    const uint32_t bb = bin_at(i);
+    int k = 0;
+    if (bb != kAbsent) {
+      if (mode == 0) {
+        k = 1;
+      } else if (mode == 1) {
+        k = bb >= bstar ? 1 : 0;
+      } else if (mode == 2 && bb != bstar) {
+        k = bb > bstar ? 1 : 0;
+      } else {  // key comparison: mode 3, or a member of the threshold bin
+        const uint32_t key = orderable_key(sbuf[c0 + i]);
+        k = key > T ? 1 : (key == T ? 2 : 0);
+      }
     }
+    cls |= (uint64_t)k << (2 * i);
+    gt += k == 1;
+    eq += k == 2;
   }
   int gb, eb;
   run_offsets<NT>(gt, eq, sh, gb, eb);
 #pragma unroll 1
-  for (int j = 0; j < nv4; ++j) {
-    const float4 t = run4[j];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = c0 + 4 * j + e;
-      emit_ordered(cls_of(val(t, e), c), c, need_eq, gb, eb, emit);
-    }
+  for (int i = 0; i < 4 * nv4; ++i) {
+    const int k = (int)(cls >> (2 * i)) & 3;
+    if (k != 0) emit_ordered(k, c0 + i, need_eq, gb, eb, emit);
   }
   return Pe;
 }
