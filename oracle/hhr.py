@@ -111,13 +111,42 @@ def page_minmax(X, page_size: int) -> np.ndarray:
     return meta
 
 
-def encode_keys(K, R, W, page_size: int) -> Dict[str, np.ndarray]:
+def bf16_round(v, up: bool) -> np.ndarray:
+    """Each value rounded to bfloat16 toward +inf (up) or -inf (down).
+
+    bfloat16 keeps 8 significant bits, so in the binade [2^e, 2^(e+1)) its grid
+    spacing is 2^(e-7) (2^-133 below the normal range).  Dividing by a power of
+    two, floor / ceil and multiplying back are exact in fp64.
+    """
+    v = _f64(v)
+    _, e = np.frexp(np.abs(v))  # |v| = m 2^e with m in [0.5, 1): binade 2^(e-1)
+    ulp = np.exp2(np.maximum(e - 1, -126) - 7.0)
+    q = v / ulp
+    return (np.ceil(q) if up else np.floor(q)) * ulp
+
+
+def bf16_outward(meta) -> np.ndarray:
+    """Compressed page metadata: every min rounded down and every max rounded up
+    to bfloat16, so the page bound built from it still bounds every key
+    (looser by at most one bfloat16 step per dimension)."""
+    meta = _f64(meta)
+    out = np.empty_like(meta)
+    out[..., 0] = bf16_round(meta[..., 0], up=False)
+    out[..., 1] = bf16_round(meta[..., 1], up=True)
+    return out
+
+
+def encode_keys(K, R, W, page_size: int, meta_dtype: str = "f32") -> Dict[str, np.ndarray]:
     """What appending keys K [L][d] (valid rows only) to the cache produces.
 
-    Returns X = K R (fp64), codes = pack(sign(K W)), meta = page min/max of X.
+    Returns X = K R (fp64), codes = pack(sign(K W)), meta = page min/max of X
+    (outward-rounded to bfloat16 when meta_dtype is "bf16").
     """
     X = rotate(K, R)
-    return dict(X=X, codes=hash_codes(K, W), meta=page_minmax(X, page_size))
+    meta = page_minmax(X, page_size)
+    if meta_dtype == "bf16":
+        meta = bf16_outward(meta)
+    return dict(X=X, codes=hash_codes(K, W), meta=meta)
 
 
 def encode_query(q_group, R, W) -> Dict[str, np.ndarray]:

@@ -308,3 +308,63 @@ def test_pipeline_degenerate_lengths():
     assert res["n_keep"] == 1 and res["sel"].tolist() == [0]
     res0 = O.select(inp["q"][0], inp["K"][0, 0, :0], inp["R"][0], inp["W"][0], 16, 1, 4, 0, 8)
     assert res0["n_keep"] == 0 and res0["sel"].size == 0
+
+
+# --------------------------------------------------------------------------- #
+# bfloat16 page metadata (outward rounding)
+# --------------------------------------------------------------------------- #
+def _bf16_neighbours(v):
+    """bfloat16 values around v from torch's round-to-nearest-even conversion
+    (an independent library routine): the nearest one and the next grid points
+    on both sides, as float64."""
+    import torch
+
+    near = torch.tensor(v, dtype=torch.float64).to(torch.bfloat16)
+    bits = near.view(torch.int16).to(torch.int32) & 0xFFFF
+    out = []
+    for dbits in (-1, 0, 1):
+        b = bits + dbits * torch.where(near >= 0, 1, -1)
+        b = b & 0xFFFF
+        out.append(torch.tensor(b.numpy().astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+                   .to(torch.float64).numpy())
+    return np.stack(out)
+
+
+def test_bf16_round_is_the_nearest_grid_point_in_each_direction():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 7, 4000),
+                        [0.0, 1.0, -1.0, 2.0 ** -130, -3.0 * 2.0 ** -133, 1.0 + 2.0 ** -8]])
+    down, up = O.bf16_round(v, up=False), O.bf16_round(v, up=True)
+    # representable in bfloat16: the float32 bit pattern has zero low half
+    for r in (down, up):
+        f = r.astype(np.float32)
+        assert np.all(f.astype(np.float64) == r)
+        assert np.all((f.view(np.uint32) & 0xFFFF) == 0)
+    assert np.all(down <= v) and np.all(up >= v)
+    # no bfloat16 value lies strictly between: check against torch's grid
+    nb = _bf16_neighbours(v)  # [3][n]
+    below = np.where(nb <= v, nb, -np.inf).max(axis=0)
+    above = np.where(nb >= v, nb, np.inf).min(axis=0)
+    assert np.all(down == below) and np.all(up == above)
+    exact = v == down
+    assert np.all(up[exact] == v[exact])
+
+
+def test_bf16_outward_metadata_keeps_the_bound_valid():
+    rng = np.random.default_rng(6)
+    d, G = 32, 3
+    Q = rng.standard_normal((G, d))
+    K = rng.standard_normal((50, d)) * np.array([8.0 if i < 2 else 1.0 for i in range(d)])
+    R = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    W = rng.standard_normal((d, d))
+    enc32 = O.encode_keys(K, R, W, 16)
+    enc16 = O.encode_keys(K, R, W, 16, meta_dtype="bf16")
+    assert np.all(enc16["meta"][..., 0] <= enc32["meta"][..., 0])
+    assert np.all(enc16["meta"][..., 1] >= enc32["meta"][..., 1])
+    qr = O.rotate(Q, R)
+    s16 = O.page_scores(qr, enc16["meta"])
+    s32 = O.page_scores(qr, enc32["meta"])
+    assert np.all(s16 >= s32 - 1e-9 * np.abs(s32))
+    true = (K @ Q.T).sum(axis=1)
+    for p in range(s16.size):
+        assert s16[p] >= true[p * 16:(p + 1) * 16].max() - 1e-9
