@@ -12,13 +12,16 @@ To keep the 256 MB Infinity Cache from serving repeated steps, the step
 rotates through --layers independent copies of every per-layer buffer
 (K, V, codes, page metadata, R, W), about 4.8 GB at 8 layers.
 
-Prints one JSON line.  `roofline` is for the page-bound scorer, the kernel
-that moves most of the step's bytes; its average launch duration is measured
-with one pair of HIP events on its stream around a pass of back-to-back
-launches over the same rotating layers; `traffic` is its counter-measured HBM
-bytes per launch from the committed profile, while the scorer's sources are
-unchanged since.  `cpu_baseline` times the CPU oracle (numpy, 1 thread)
-on whole decode steps of the same workload for a bounded number of seconds.
+Prints one JSON line.  `roofline` is for k_score_topp (query rotation, page
+bounds and top-P in one launch), the step's longest kernel and the one that
+moves most of its bytes; its average launch duration is measured with one pair
+of HIP events on its stream around a pass of back-to-back hhr_select_pages
+calls (which launch it alone) over the same rotating layers; `traffic` is its
+counter-measured HBM bytes per launch from the committed profile, while the
+kernel's sources are unchanged since.  `--meta bf16` runs the same step on
+bfloat16 page metadata rounded outward (half the metadata bytes).
+`cpu_baseline` times the CPU oracle (numpy, 1 thread) on whole decode steps
+of the same workload for a bounded number of seconds.
 """
 from __future__ import annotations
 
@@ -40,8 +43,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # Measured HBM traffic of the page-bound scorer comes from a committed counter
 # profile; it is reported only while the kernel sources that build that kernel
 # (the files below) are unchanged since the counters were taken.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "page_scores_llama8b_128k_hbm_traffic.md")
-SCORER_SOURCES = ["hash_hierarchical_top_amd/csrc/select.hip",
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_topp_llama8b_128k_hbm_traffic.md")
+SCORER_SOURCES = ["hash_hierarchical_top_amd/csrc/compose.hip",
                   "hash_hierarchical_top_amd/csrc/stages.h",
                   "hash_hierarchical_top_amd/csrc/topk_device.h",
                   "hash_hierarchical_top_amd/csrc/hhr_device.h",
@@ -59,18 +62,21 @@ def scorer_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """Calibrated HBM bytes per k_page_scores launch from the counter profile, or None if
-    there is none for this workload or the scorer's sources changed since."""
+def measured_traffic(workload: str, meta_dtype: str):
+    """Calibrated HBM bytes per k_score_topp launch from the counter profile, or None if
+    there is none for this workload and metadata format or the kernel's sources changed
+    since."""
     try:
         with open(TRAFFIC_PROFILE) as f:
             text = f.read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != scorer_source_digest():
-        return None
-    return int(rec["traffic_bytes_per_launch"])
+    for r in rec if isinstance(rec, list) else [rec]:
+        if (r.get("workload") == workload and r.get("meta_dtype", "f32") == meta_dtype
+                and r.get("source_sha256") == scorer_source_digest()):
+            return int(r["traffic_bytes_per_launch"])
+    return None
 
 
 def parse():
@@ -86,6 +92,8 @@ def parse():
     ap.add_argument("--path", choices=("decode", "staged"), default="decode",
                     help="decode: one hhr_decode call per step; staged: hhr_select then "
                          "hhr_sparse_decode")
+    ap.add_argument("--meta", choices=("f32", "bf16"), default="f32",
+                    help="page metadata format: f32 min/max, or bfloat16 rounded outward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -115,7 +123,9 @@ def main():
     inp = synth.make_workload_inputs(args.workload)
     t_gen = time.time() - t_gen
     seq_np = inp["seq_len"]
-    shape = hhr.make_shape(B, Hq, Hkv, Lcap, w.kv_dtype)
+    shape = hhr.make_shape(B, Hq, Hkv, Lcap, w.kv_dtype, meta_dtype=args.meta)
+    meta_dt = torch.float32 if args.meta == "f32" else torch.int32
+    meta_page_bytes = 1024 if args.meta == "f32" else 512
     NpCap = Lcap // 16
     scale = 1.0 / math.sqrt(128.0)
 
@@ -134,7 +144,7 @@ def main():
         lay = dict(K=K0 if i == 0 else K0.clone(), V=V0 if i == 0 else V0.clone(),
                    R=R0 if i == 0 else R0.clone(), W=W0 if i == 0 else W0.clone(),
                    codes=torch.zeros((B, Hkv, Lcap, 4), dtype=torch.int32, device=dev),
-                   meta=torch.zeros((B, Hkv, NpCap, 128, 2), dtype=torch.float32, device=dev))
+                   meta=torch.zeros(hhr.meta_shape(shape), dtype=meta_dt, device=dev))
         layers.append(lay)
     ws_bytes = hhr.hhr_workspace_size(shape, *keep, top_k)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
@@ -157,7 +167,7 @@ def main():
     n_keys = int(seq_np.sum()) * Hkv
     kv_bytes = 2 if w.kv_dtype == "bf16" else 4
     enc_bytes = n_keys * (128 * kv_bytes + 16) + sum(
-        -(-int(L) // 16) for L in seq_np) * Hkv * 1024 + Hkv * 2 * 128 * 128 * 4
+        -(-int(L) // 16) for L in seq_np) * Hkv * meta_page_bytes + Hkv * 2 * 128 * 128 * 4
     enc_flops = 2.0 * n_keys * 128 * 256
     passes = 2 if w.kv_dtype == "bf16" else 3
     enc = {"ms": round(enc_ms, 4), "hbm_gbs": round(enc_bytes / enc_ms / 1e6, 1),
@@ -226,36 +236,66 @@ def main():
     Np = np.array([-(-int(L) // 16) for L in seq_np])
     P = np.array([hhr.hhr_keep_count(int(n), *keep) for n in Np])
     cand = int(P.sum()) * 16 * Hkv
-    meta_bytes = int(Np.sum()) * Hkv * 1024
+    meta_bytes = int(Np.sum()) * Hkv * meta_page_bytes
     sel_rows = int(cnt.sum().item())
     step_bytes = (meta_bytes + cand * 16 + sel_rows * 2 * 128 * kv_bytes
                   + Hkv * 2 * 128 * 128 * 4 + B * Hq * 128 * 4 * 2)
     step_gbs = step_bytes / (ms_per_step * 1e6)
 
-    # ---- dominant kernel: page-bound scorer, per-launch HIP events on its stream
+    # ---- dominant kernel: k_score_topp (query rotation, page bounds, top-P), which
+    # hhr_select_pages launches alone; back to back on its stream between one pair of
+    # HIP events, rotating layers as the step does
+    nk = min(args.steps, 400)
+    p_max = hhr.hhr_keep_count(NpCap, *keep)
+    kept_b = torch.zeros((B, Hkv, p_max), dtype=torch.int32, device=dev)
+    kc_b = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    ws_p = torch.zeros(hhr.hhr_workspace_size(shape, *keep, 1), dtype=torch.uint8, device=dev)
+
+    def select_pages(i):
+        lay = layers[i % args.layers]
+        hhr.hhr_select_pages(shape, q, seq, lay["R"], lay["W"], lay["meta"], *keep, kept_b, kc_b,
+                             None, ws_p)
+
+    def time_launches(fn):
+        for i in range(args.layers):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(nk):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nk
+
+    k_ms = time_launches(select_pages)
+    assert hhr.hhr_read_device_status(ws_p) == 0
+    n_pages_all = int(Np.sum()) * Hkv
+    # metadata, queries, R and W once per KV head, the bounds written and read back by the
+    # last workgroup, kept pages and query codes written
+    k_bytes = (meta_bytes + B * Hq * 128 * 4 + Hkv * 128 * 256 * 4 + n_pages_all * 8
+               + int(P.sum()) * Hkv * 4 + B * Hq * 16)
+    roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload, args.meta),
+                "kernel": "k_score_topp", "bytes_per_launch": k_bytes,
+                "avg_launch_us": round(k_ms * 1e3, 3)}
+
+    # the bound computation alone (staged k_page_scores, S3 only), for context
     q_rot = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)
     q_codes = torch.zeros((B, Hq, 4), dtype=torch.int32, device=dev)
     scores = torch.zeros((B, Hkv, NpCap), dtype=torch.float32, device=dev)
     hhr.hhr_encode_queries(shape, q, R0, W0, q_rot, q_codes)
-    nk = min(args.steps, 400)
-    for i in range(args.layers):
-        hhr.hhr_page_scores(shape, q_rot, seq, layers[i]["meta"], scores, ws)
-    torch.cuda.synchronize()
-    ke0 = torch.cuda.Event(enable_timing=True)
-    ke1 = torch.cuda.Event(enable_timing=True)
-    ke0.record(stream)
-    for i in range(nk):  # back to back on the scorer's stream, rotating layers
-        hhr.hhr_page_scores(shape, q_rot, seq, layers[i % args.layers]["meta"], scores, ws)
-    ke1.record(stream)
-    torch.cuda.synchronize()
-    k_ms = ke0.elapsed_time(ke1) / nk
-    k_bytes = meta_bytes + B * Hq * 128 * 4 + int(Np.sum()) * Hkv * 4
-    roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.workload),
-                "kernel": "k_page_scores", "bytes_per_launch": k_bytes,
-                "avg_launch_us": round(k_ms * 1e3, 3)}
+    s_ms = time_launches(lambda i: hhr.hhr_page_scores(shape, q_rot, seq,
+                                                       layers[i % args.layers]["meta"], scores,
+                                                       ws))
+    s_bytes = meta_bytes + B * Hq * 128 * 4 + n_pages_all * 4
+    scorer_only = {"kernel": "k_page_scores", "bytes_per_launch": s_bytes,
+                   "avg_launch_us": round(s_ms * 1e3, 3),
+                   "achieved_gbs": round(s_bytes / (s_ms * 1e6), 1),
+                   "frac": round(s_bytes / (s_ms * 1e6) / HBM_PEAK_GBS, 4)}
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -290,11 +330,13 @@ def main():
         "config": {"workload": args.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "ctx": int(seq_np.max()), "page_size": 16, "code_bits": 128,
                    "keep": f"{keep[0]}/{keep[1]}" if keep[2] == 0 else keep[2], "top_k": top_k,
+                   "meta_dtype": args.meta,
                    "layers_rotated": args.layers, "hip_graph": bool(graph is not None),
                    "entry": "hhr_decode" if args.path == "decode"
                    else "hhr_select+hhr_sparse_decode"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "page_scores_only": scorer_only,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),

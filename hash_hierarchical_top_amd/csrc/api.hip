@@ -71,6 +71,8 @@ hhr_status check_shape(const hhr_shape* s) {
     return fail(HHR_ERR_UNSUPPORTED, "max_ctx must be <= %d", hhr::kMaxCtx);
   if (s->kv_dtype != HHR_F32 && s->kv_dtype != HHR_BF16)
     return fail(HHR_ERR_INVALID_ARG, "kv_dtype must be HHR_F32 or HHR_BF16");
+  if (s->meta_dtype != HHR_F32 && s->meta_dtype != HHR_BF16)
+    return fail(HHR_ERR_INVALID_ARG, "meta_dtype must be HHR_F32 or HHR_BF16");
   if ((long long)s->batch * s->n_kv_heads > 65535 || (long long)s->batch * s->n_q_heads > 1 << 30)
     return fail(HHR_ERR_UNSUPPORTED, "batch * n_kv_heads must be <= 65535");
   return HHR_OK;
@@ -255,7 +257,7 @@ const char* hhr_status_string(int32_t status) {
 
 const char* hhr_last_error(void) { return g_err; }
 
-int32_t hhr_abi_version(void) { return 1; }
+int32_t hhr_abi_version(void) { return 2; }
 
 int32_t hhr_keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den,
                        int32_t keep_pages_abs) {
@@ -287,7 +289,7 @@ hhr_status hhr_read_device_status(void* workspace, void* stream, uint32_t* flags
 
 hhr_status hhr_append_keys(const hhr_shape* shape, const void* k_cache, const int32_t* start,
                            const int32_t* n_new, int32_t max_new, const float* R,
-                           const float* W, uint32_t* codes, float* page_meta,
+                           const float* W, uint32_t* codes, void* page_meta,
                            uint32_t* status_word, void* stream) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_ptr(k_cache, "k_cache"));
@@ -320,7 +322,7 @@ hhr_status hhr_encode_queries(const hhr_shape* shape, const float* q, const floa
 }
 
 hhr_status hhr_page_scores(const hhr_shape* shape, const float* q_rot, const int32_t* seq_len,
-                           const float* page_meta, float* scores, uint32_t* status_word,
+                           const void* page_meta, float* scores, uint32_t* status_word,
                            void* stream) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_ptr(q_rot, "q_rot"));
@@ -411,9 +413,60 @@ hhr_status hhr_sparse_decode(const hhr_shape* shape, const float* q, const void*
   return ok();
 }
 
+// Workspace layout for these parameters and the composite kernels' buffers in it.
+static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, int32_t keep_den,
+                                    int32_t keep_abs, int32_t top_k, void* workspace,
+                                    size_t workspace_bytes, hhr::Workspace* ws,
+                                    hhr::CompositeBuffers* buf) {
+  hhr::make_workspace(shape, keep_num, keep_den, keep_abs, top_k, ws);
+  HHR_TRY(check_p_max(ws->p_max));
+  if (workspace_bytes < ws->total)
+    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                ws->total);
+  char* base = static_cast<char*>(workspace);
+  buf->status = status_of(workspace);
+  buf->counters = reinterpret_cast<uint32_t*>(base + ws->counters);
+  buf->scores = reinterpret_cast<float*>(base + ws->scores);
+  buf->q_codes = reinterpret_cast<uint32_t*>(base + ws->q_codes);
+  buf->kept = reinterpret_cast<int32_t*>(base + ws->kept);
+  buf->kept_count = reinterpret_cast<int32_t*>(base + ws->kept_count);
+  buf->dist = reinterpret_cast<uint16_t*>(base + ws->ham_dist);
+  buf->chist = reinterpret_cast<int*>(base + ws->ham_hist);
+  return HHR_OK;
+}
+
+hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                            const float* R, const float* W, const void* page_meta,
+                            int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                            int32_t* kept, int32_t* kept_count, uint32_t* q_codes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_keep(keep_num, keep_den, keep_pages_abs));
+  HHR_TRY(check_ptr(q, "q"));
+  HHR_TRY(check_ptr(seq_len, "seq_len"));
+  HHR_TRY(check_ptr(R, "R"));
+  HHR_TRY(check_ptr(W, "W"));
+  HHR_TRY(check_ptr(page_meta, "page_meta"));
+  HHR_TRY(check_ptr(kept, "kept"));
+  HHR_TRY(check_ptr(kept_count, "kept_count"));
+  HHR_TRY(check_opt_ptr(q_codes, "q_codes"));
+  HHR_TRY(check_ptr(workspace, "workspace"));
+  hhr::Workspace ws;
+  hhr::CompositeBuffers buf;
+  HHR_TRY(composite_buffers(*shape, keep_num, keep_den, keep_pages_abs, 1, workspace,
+                            workspace_bytes, &ws, &buf));
+  buf.kept = kept;
+  buf.kept_count = kept_count;
+  if (q_codes) buf.q_codes = q_codes;
+  HHR_LAUNCH(hhr::launch_score_topp(*shape, q, seq_len, R, W, page_meta, keep_num, keep_den,
+                                    keep_pages_abs, ws.p_max, buf, as_stream(stream)),
+             "select_pages launch");
+  return ok();
+}
+
 static hhr_status select_impl(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                               const float* R, const float* W, const uint32_t* codes,
-                              const float* page_meta, int32_t keep_num, int32_t keep_den,
+                              const void* page_meta, int32_t keep_num, int32_t keep_den,
                               int32_t keep_abs, int32_t top_k, int32_t* sel_idx,
                               int32_t* sel_count, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, bool finish, hhr::Workspace* layout,
@@ -431,21 +484,9 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
   HHR_TRY(check_ptr(sel_count, "sel_count"));
   HHR_TRY(check_ptr(workspace, "workspace"));
   hhr::Workspace ws;
-  hhr::make_workspace(*shape, keep_num, keep_den, keep_abs, top_k, &ws);
-  HHR_TRY(check_p_max(ws.p_max));
-  if (workspace_bytes < ws.total)
-    return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                ws.total);
-  char* base = static_cast<char*>(workspace);
   hhr::CompositeBuffers buf;
-  buf.status = status_of(workspace);
-  buf.counters = reinterpret_cast<uint32_t*>(base + ws.counters);
-  buf.scores = reinterpret_cast<float*>(base + ws.scores);
-  buf.q_codes = reinterpret_cast<uint32_t*>(base + ws.q_codes);
-  buf.kept = reinterpret_cast<int32_t*>(base + ws.kept);
-  buf.kept_count = reinterpret_cast<int32_t*>(base + ws.kept_count);
-  buf.dist = reinterpret_cast<uint16_t*>(base + ws.ham_dist);
-  buf.chist = reinterpret_cast<int*>(base + ws.ham_hist);
+  HHR_TRY(composite_buffers(*shape, keep_num, keep_den, keep_abs, top_k, workspace,
+                            workspace_bytes, &ws, &buf));
   HHR_LAUNCH(hhr::launch_select_composite(*shape, q, seq_len, R, W, codes, page_meta, keep_num,
                                           keep_den, keep_abs, ws.p_max, top_k, sel_idx,
                                           sel_count, buf, finish, stream),
@@ -457,7 +498,7 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
 
 hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
-                      const float* page_meta, int32_t keep_num, int32_t keep_den,
+                      const void* page_meta, int32_t keep_num, int32_t keep_den,
                       int32_t keep_pages_abs, int32_t top_k, int32_t* sel_idx,
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,
                       void* stream) {
@@ -471,7 +512,7 @@ hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq
 
 hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
-                      const float* page_meta, const void* k_cache, const void* v_cache,
+                      const void* page_meta, const void* k_cache, const void* v_cache,
                       int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
                       float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
                       void* workspace, size_t workspace_bytes, void* stream) {

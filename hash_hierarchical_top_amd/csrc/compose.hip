@@ -68,9 +68,10 @@ struct ScoreTopSmem {
 // pages.  Each workgroup rotates its group's queries itself (64 KiB of R from
 // L2, issued after its metadata loads so both are in flight together);
 // workgroup 0 of each (b, g) also writes the query codes.
+template <bool MBF>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
-    const float* __restrict__ R, const float* __restrict__ W, const float* __restrict__ meta,
+    const float* __restrict__ R, const float* __restrict__ W, const void* __restrict__ meta,
     int keep_num, int keep_den, int keep_abs, int p_max, int Hq, int Hkv, int Lcap,
     float* __restrict__ scores, uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   const bool wave_has = pb < Np;                                    // wave-uniform
   const bool wg_has = (int)blockIdx.x * kScorePagesPerWg < Np;      // block-uniform
   PageLoads<1> pl;
-  if (wave_has) score_load<1>(bg, NpCap, Np, pb, meta, pl);
+  if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
   if (blockIdx.x == 0) {
     const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
@@ -102,9 +103,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
                                  [](int, int, uint32_t) {});
   }
   if (wave_has) {
-    float A[4][2], B[4][2];
-    score_ab(G, [&](int h, int d) { return sm.rot.qrot[h][d]; }, A, B);
-    score_finish<true, 1>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
+    float A[8], B[8];
+    score_ab<MBF>(G, [&](int h, int d) { return sm.rot.qrot[h][d]; }, A, B);
+    score_finish<MBF, true, 1>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
   }
   if (!arrive_last(&counters[bg], gridDim.x, &s_last)) return;
 
@@ -163,20 +164,35 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_merge(
 
 }  // namespace
 
+hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
+                             const float* R, const float* W, const void* meta, int32_t keep_num,
+                             int32_t keep_den, int32_t keep_abs, int32_t p_max,
+                             const CompositeBuffers& buf, hipStream_t stream) {
+  const int BG = s.batch * s.n_kv_heads;
+  const int NpCap = s.max_ctx / kPS;
+  const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
+  if (s.meta_dtype == HHR_BF16)
+    hipLaunchKernelGGL(k_score_topp<true>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R, W,
+                       meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
+                       s.max_ctx, buf.scores, buf.q_codes, buf.kept, buf.kept_count,
+                       buf.counters, buf.status);
+  else
+    hipLaunchKernelGGL(k_score_topp<false>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R,
+                       W, meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
+                       s.max_ctx, buf.scores, buf.q_codes, buf.kept, buf.kept_count,
+                       buf.counters, buf.status);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
                                    const float* R, const float* W, const uint32_t* codes,
-                                   const float* meta, int32_t keep_num, int32_t keep_den,
+                                   const void* meta, int32_t keep_num, int32_t keep_den,
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,
                                    hipStream_t stream) {
-  const int BG = s.batch * s.n_kv_heads;
-  const int NpCap = s.max_ctx / kPS;
-  hipLaunchKernelGGL(k_score_topp, dim3((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG),
-                     dim3(kScoreThreads), 0, stream, q, seq_len, R, W, meta, keep_num, keep_den,
-                     keep_abs, p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, buf.scores,
-                     buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_score_topp(s, q, seq_len, R, W, meta, keep_num, keep_den, keep_abs,
+                                   p_max, buf, stream);
   if (e != hipSuccess) return e;
   if (finish)
     return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,

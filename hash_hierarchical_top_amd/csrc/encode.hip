@@ -27,8 +27,8 @@ template <bool KF32>
 __global__ __launch_bounds__(256) void k_append_encode(
     const void* __restrict__ kcache, const int32_t* __restrict__ start,
     const int32_t* __restrict__ n_new, const float* __restrict__ R, const float* __restrict__ W,
-    uint32_t* __restrict__ codes, float* __restrict__ meta, uint32_t* __restrict__ status,
-    int Hkv, int Lcap, int tiles_per_wg) {
+    uint32_t* __restrict__ codes, void* __restrict__ meta, int meta_bf16,
+    uint32_t* __restrict__ status, int Hkv, int Lcap, int tiles_per_wg) {
   __shared__ __attribute__((aligned(16))) uint16_t a_hi[kTileRows * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t a_lo[KF32 ? kTileRows * kLdsStride : 8];
 
@@ -169,9 +169,11 @@ __global__ __launch_bounds__(256) void k_append_encode(
           mn = fminf(mn, __shfl_xor(mn, 32));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
           if (lgrp == 0) {
-            const int col = col0 + 16 * nt + lrow;
-            float2* dst = (float2*)(meta + (((size_t)bg * NpCap + page) * kD + col) * 2);
-            *dst = make_float2(mn, mx);
+            const size_t at = ((size_t)bg * NpCap + page) * kD + col0 + 16 * nt + lrow;
+            if (meta_bf16)  // {min down, max up} as bf16 in one word
+              ((uint32_t*)meta)[at] = f32_to_bf16_down(mn) | (f32_to_bf16_up(mx) << 16);
+            else
+              ((float2*)meta)[at] = make_float2(mn, mx);
           }
         }
       } else {
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(kQeThreads) void k_encode_queries(
 
 hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int32_t* start,
                               const int32_t* n_new, int32_t max_new, const float* R,
-                              const float* W, uint32_t* codes, float* meta, uint32_t* status,
+                              const float* W, uint32_t* codes, void* meta, uint32_t* status,
                               hipStream_t stream) {
   if (max_new <= 0) return hipSuccess;
   const int touched_pages = (max_new + kPS - 1) / kPS + 1;
@@ -229,10 +231,12 @@ hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int
   dim3 grid((max_tiles + tpw - 1) / tpw, bgs);
   if (s.kv_dtype == HHR_F32)
     hipLaunchKernelGGL(k_append_encode<true>, grid, dim3(256), 0, stream, k_cache, start, n_new,
-                       R, W, codes, meta, status, s.n_kv_heads, s.max_ctx, tpw);
+                       R, W, codes, meta, s.meta_dtype == HHR_BF16, status, s.n_kv_heads,
+                       s.max_ctx, tpw);
   else
     hipLaunchKernelGGL(k_append_encode<false>, grid, dim3(256), 0, stream, k_cache, start, n_new,
-                       R, W, codes, meta, status, s.n_kv_heads, s.max_ctx, tpw);
+                       R, W, codes, meta, s.meta_dtype == HHR_BF16, status, s.n_kv_heads,
+                       s.max_ctx, tpw);
   return hipGetLastError();
 }
 

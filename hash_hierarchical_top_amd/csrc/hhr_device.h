@@ -34,6 +34,21 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Directed rounding f32 -> bf16 bits.  A bf16 value is the upper half of an
+// f32 pattern, so dropping the lower half rounds the magnitude down (toward
+// zero).  Rounding toward -inf is that for x >= 0 and one step up in magnitude
+// for negative x with a nonzero lower half; toward +inf the other way round.
+// Past the largest finite bf16 the step lands on the infinity of that sign;
+// infinities stay as they are.  Inputs are never NaN here.
+__device__ __forceinline__ uint32_t f32_to_bf16_down(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u >> 16) + ((u >> 31) & ((u & 0xFFFFu) != 0u));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u >> 16) + ((~u >> 31) & ((u & 0xFFFFu) != 0u));
+}
+
 // Monotone map f32 -> u32 (larger float -> larger key); -0 is folded onto +0.
 __device__ __forceinline__ uint32_t orderable_key(float x) {
   uint32_t u = __float_as_uint(x + 0.0f);

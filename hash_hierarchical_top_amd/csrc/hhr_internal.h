@@ -47,13 +47,13 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
 // ---- launchers (all asynchronous on `stream`) ----
 hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int32_t* start,
                               const int32_t* n_new, int32_t max_new, const float* R,
-                              const float* W, uint32_t* codes, float* meta, uint32_t* status,
+                              const float* W, uint32_t* codes, void* meta, uint32_t* status,
                               hipStream_t stream);
 hipError_t launch_encode_queries(const hhr_shape& s, const float* q, const float* R,
                                  const float* W, float* q_rot, uint32_t* q_codes,
                                  hipStream_t stream);
 hipError_t launch_page_scores(const hhr_shape& s, const float* q_rot, const int32_t* seq_len,
-                              const float* meta, float* scores, uint32_t* status,
+                              const void* meta, float* scores, uint32_t* status,
                               hipStream_t stream);
 hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32_t* seq_len,
                             int32_t keep_num, int32_t keep_den, int32_t keep_abs, int32_t p_max,
@@ -88,9 +88,14 @@ struct CompositeBuffers {
   uint16_t* dist;
   int* chist;
 };
+// k_score_topp alone (S2..S4): kept pages, counts and query codes into buf.
+hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
+                             const float* R, const float* W, const void* meta, int32_t keep_num,
+                             int32_t keep_den, int32_t keep_abs, int32_t p_max,
+                             const CompositeBuffers& buf, hipStream_t stream);
 hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
                                    const float* R, const float* W, const uint32_t* codes,
-                                   const float* meta, int32_t keep_num, int32_t keep_den,
+                                   const void* meta, int32_t keep_num, int32_t keep_den,
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,

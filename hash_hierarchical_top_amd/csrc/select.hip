@@ -29,9 +29,10 @@ __device__ __forceinline__ int checked_len(const int32_t* seq_len, int b, int Lc
 constexpr int kScoreWaves = 4;
 constexpr int kScorePagesPerWg = kScoreWaves * kScorePagesPerWave;  // 64
 
+template <bool MBF>
 __global__ __launch_bounds__(256) void k_page_scores(const float* __restrict__ q_rot,
                                                      const int32_t* __restrict__ seq_len,
-                                                     const float* __restrict__ meta,
+                                                     const void* __restrict__ meta,
                                                      float* __restrict__ scores,
                                                      uint32_t* __restrict__ status, int Hq,
                                                      int Hkv, int Lcap) {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void k_page_scores(const float* __restrict__ q
   const int Np = (L + kPS - 1) / kPS;
   const int pb = blockIdx.x * kScorePagesPerWg + (threadIdx.x >> 6) * kScorePagesPerWave;
   if (pb >= Np) return;
-  score_batch<false>(b, g, Hq, Hkv, Lcap / kPS, Np, pb, q_rot, meta, scores, nullptr, status);
+  score_batch<MBF, false>(b, g, Hq, Hkv, Lcap / kPS, Np, pb, q_rot, meta, scores);
 }
 
 // ------------------------------------------------------------------ S4
@@ -112,12 +113,16 @@ __global__ __launch_bounds__(kHamSelThreads) void k_ham_select(
 }  // namespace
 
 hipError_t launch_page_scores(const hhr_shape& s, const float* q_rot, const int32_t* seq_len,
-                              const float* meta, float* scores, uint32_t* status,
+                              const void* meta, float* scores, uint32_t* status,
                               hipStream_t stream) {
   const int NpCap = s.max_ctx / kPS;
   dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, s.batch * s.n_kv_heads);
-  hipLaunchKernelGGL(k_page_scores, grid, dim3(256), 0, stream, q_rot, seq_len, meta, scores,
-                     status, s.n_q_heads, s.n_kv_heads, s.max_ctx);
+  if (s.meta_dtype == HHR_BF16)
+    hipLaunchKernelGGL(k_page_scores<true>, grid, dim3(256), 0, stream, q_rot, seq_len, meta,
+                       scores, status, s.n_q_heads, s.n_kv_heads, s.max_ctx);
+  else
+    hipLaunchKernelGGL(k_page_scores<false>, grid, dim3(256), 0, stream, q_rot, seq_len, meta,
+                       scores, status, s.n_q_heads, s.n_kv_heads, s.max_ctx);
   return hipGetLastError();
 }
 

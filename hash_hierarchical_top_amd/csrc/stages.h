@@ -15,28 +15,6 @@
 
 namespace hhr {
 
-constexpr uint32_t kSpinLimit = 1u << 18;  // polls (each up to ~1000 cycles apart): well under a second
-
-// One lane waits until *flag >= target (agent-scope polls).  On timeout it sets
-// HHR_DEV_TIMEOUT and returns, and once that bit is set every other wait gives
-// up at its next check, so a kernel always terminates promptly.
-__device__ __forceinline__ void spin_until_geq(const uint32_t* flag, uint32_t target,
-                                               uint32_t* status) {
-  // exponential back-off up to ~1000 cycles keeps hundreds of waiting
-  // workgroups from hammering the few cache lines that hold the counters
-  uint32_t n = 0, nap = 1;
-  while (ld_agent_u32(flag) < target) {
-    ++n;
-    if ((n & 63u) == 0u && status && (ld_agent_u32(status) & HHR_DEV_TIMEOUT)) return;
-    if (n >= kSpinLimit) {
-      if (status) atomicOr(status, HHR_DEV_TIMEOUT);
-      return;
-    }
-    for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(1);
-    if (nap < 16u) nap <<= 1;
-  }
-}
-
 // ============================================================== S2: query
 // Columns 0..127 of [R | W] give q' = q R, columns 128..255 give the sign
 // bits of q W.  Every output (head h, column c) is computed the same way:
@@ -154,67 +132,76 @@ __device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restric
 //
 // One wave scores pages pb .. pb+15 (those < Np).  Lane (row r = l/16,
 // sub = l%16) handles pages pb + 4j + r (j = 0..3) and, in each, the 16-byte
-// pieces k = 0..3 at byte 256k + 16 sub (dims 2(sub + 16k) and +1), so every
-// load instruction reads four whole 256-byte runs.  All 16 loads are issued
-// first (addresses clamped, not branched on); if `ready` is given, lane 0 then
-// waits for the query encoding; a 4-value reduce-scatter over the 16 lanes of
-// a row leaves page pb + 4j + r in lanes with j = 2 b3 + b2.  The whole wave
-// must be active (cross-lane DPP exchanges).
+// pieces k at byte 256k + 16 sub of the page's metadata, so every load
+// instruction reads four whole 256-byte runs.  f32 metadata (1 KiB a page):
+// k = 0..3, each piece {mn, mx} of dims 2(sub + 16k) and +1.  bf16 metadata
+// (512 B a page): k = 0..1, each piece one {mn | mx << 16} word for dims
+// 4(sub + 16k) + 0..3.  Either way a lane owns 8 dims (slots 0..7, dim_of).
+// All loads are issued first (addresses clamped, not branched on); a 4-value
+// reduce-scatter over the 16 lanes of a row then leaves page pb + 4j + r in
+// lanes with j = 2 b3 + b2.  The whole wave must be active (cross-lane DPP
+// exchanges).
 constexpr int kScorePagesPerWave = 16;
 
+// Dimension of this lane's slot (0..7) for the metadata format MBF.
+template <bool MBF>
+__device__ __forceinline__ int score_dim(int sub, int slot) {
+  return MBF ? 4 * sub + 64 * (slot >> 2) + (slot & 3) : 2 * sub + 32 * (slot >> 1) + (slot & 1);
+}
+
 // Metadata of NB consecutive 16-page batches pb, pb + 16, ... of one (b, g),
-// loaded by one wave (lane layout above).  Pages past Np are clamped to the
-// last page; their results are never stored.
+// loaded by one wave (lane layout above; bf16 words are kept as raw bits in
+// pieces 0..1).  Pages past Np are clamped to the last page; their results
+// are never stored.
 template <int NB>
 struct PageLoads {
   floatx4 m[NB][4][4];
 };
 
-template <int NB>
+template <bool MBF, int NB>
 __device__ __forceinline__ void score_load(int bg, int NpCap, int Np, int pb,
-                                           const float* __restrict__ meta, PageLoads<NB>& pl) {
+                                           const void* __restrict__ meta, PageLoads<NB>& pl) {
+  constexpr int kPageFloats = MBF ? kD : 2 * kD;  // 4-byte words per page
+  constexpr int kPieces = MBF ? 2 : 4;
   const int l = threadIdx.x & 63;
   const int r = l >> 4;
   const int sub = l & 15;
-  const float* mbase = meta + (size_t)bg * NpCap * kD * 2 + 4 * sub;
+  const float* mbase = (const float*)meta + (size_t)bg * NpCap * kPageFloats + 4 * sub;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = min(pb + kScorePagesPerWave * nb + 4 * j + r, Np - 1);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        pl.m[nb][j][k] =
-            __builtin_nontemporal_load((const floatx4*)(mbase + (size_t)p * kD * 2 + 64 * k));
+      for (int k = 0; k < kPieces; ++k)
+        pl.m[nb][j][k] = __builtin_nontemporal_load(
+            (const floatx4*)(mbase + (size_t)p * kPageFloats + 64 * k));
     }
 }
 
-// A/B of this lane's dims 2 sub + 32 k (+1), k = 0..3, summed over the G
-// heads in order: rot_of(h, d) returns q'_hd.
-template <typename RotOf>
-__device__ __forceinline__ void score_ab(int G, RotOf rot_of, float A[4][2], float B[4][2]) {
+// A/B of this lane's 8 dims (slot order of score_dim), summed over the G heads
+// in order: rot_of(h, d) returns q'_hd.
+template <bool MBF, typename RotOf>
+__device__ __forceinline__ void score_ab(int G, RotOf rot_of, float A[8], float B[8]) {
   const int sub = threadIdx.x & 15;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) A[k][0] = A[k][1] = B[k][0] = B[k][1] = 0.f;
+  for (int i = 0; i < 8; ++i) A[i] = B[i] = 0.f;
   for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float vx = rot_of(h, 2 * sub + 32 * k);
-      const float vy = rot_of(h, 2 * sub + 32 * k + 1);
-      A[k][0] += fmaxf(vx, 0.f);
-      B[k][0] += fminf(vx, 0.f);
-      A[k][1] += fmaxf(vy, 0.f);
-      B[k][1] += fminf(vy, 0.f);
+    for (int i = 0; i < 8; ++i) {
+      const float v = rot_of(h, score_dim<MBF>(sub, i));
+      A[i] += fmaxf(v, 0.f);
+      B[i] += fminf(v, 0.f);
     }
   }
 }
 
 // Bounds of the loaded pages; each page's bound is stored by one lane, and
 // emit(p, v) sees it too.
-template <bool COH, int NB, typename Emit>
+template <bool MBF, bool COH, int NB, typename Emit>
 __device__ __forceinline__ void score_finish(int bg, int NpCap, int Np, int pb,
-                                             const PageLoads<NB>& pl, const float A[4][2],
-                                             const float B[4][2], float* scores, Emit emit) {
+                                             const PageLoads<NB>& pl, const float A[8],
+                                             const float B[8], float* scores, Emit emit) {
   const int l = threadIdx.x & 63;
   const int r = l >> 4;
   const bool b3 = l & 8, b2 = l & 4;
@@ -224,10 +211,21 @@ __device__ __forceinline__ void score_finish(int bg, int NpCap, int Np, int pb,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float x = 0.f;
+      if constexpr (MBF) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)  // m = {mn[d0], mx[d0], mn[d1], mx[d1]}
-        x += A[k][0] * pl.m[nb][j][k][1] + B[k][0] * pl.m[nb][j][k][0] +
-             A[k][1] * pl.m[nb][j][k][3] + B[k][1] * pl.m[nb][j][k][2];
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w = __float_as_uint(pl.m[nb][j][k][i]);
+            x += A[4 * k + i] * __uint_as_float(w & 0xFFFF0000u) +
+                 B[4 * k + i] * __uint_as_float(w << 16);
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)  // m = {mn[d0], mx[d0], mn[d1], mx[d1]}
+          x += A[2 * k] * pl.m[nb][j][k][1] + B[2 * k] * pl.m[nb][j][k][0] +
+               A[2 * k + 1] * pl.m[nb][j][k][3] + B[2 * k + 1] * pl.m[nb][j][k][2];
+      }
       v[j] = x;
     }
     // partner lanes: 15 - sub (other 8-lane half), then 7 - (sub % 8) (other
@@ -253,21 +251,18 @@ __device__ __forceinline__ void score_finish(int bg, int NpCap, int Np, int pb,
   }
 }
 
-// One wave: load, read q' from q_rot (waiting for `ready` first if given),
-// finish.
-template <bool COH, int NB = 1>
+// One wave: load, read q' from q_rot, finish.
+template <bool MBF, bool COH, int NB = 1>
 __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, int pb,
-                            const float* q_rot, const float* __restrict__ meta, float* scores,
-                            const uint32_t* ready, uint32_t* status) {
+                            const float* q_rot, const void* __restrict__ meta, float* scores) {
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   PageLoads<NB> pl;
-  score_load<NB>(bg, NpCap, Np, pb, meta, pl);
-  if (ready != nullptr && (threadIdx.x & 63) == 0) spin_until_geq(ready, 1u, status);
-  float A[4][2], B[4][2];
+  score_load<MBF, NB>(bg, NpCap, Np, pb, meta, pl);
+  float A[8], B[8];
   const float* qr = q_rot + ((size_t)b * Hq + (size_t)g * G) * kD;
-  score_ab(G, [&](int h, int d) { return Mem<COH>::ld(qr + (size_t)h * kD + d); }, A, B);
-  score_finish<COH, NB>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
+  score_ab<MBF>(G, [&](int h, int d) { return Mem<COH>::ld(qr + (size_t)h * kD + d); }, A, B);
+  score_finish<MBF, COH, NB>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
 }
 
 // ============================================================== S4: prune

@@ -22,6 +22,7 @@ HHR_ERR_WORKSPACE = -3
 HHR_ERR_HIP = -4
 HHR_F32 = 0
 HHR_BF16 = 1
+ABI_VERSION = 2  # the include/hhr.h declarations this binding mirrors
 HHR_DEV_BAD_SEQ_LEN = 0x1
 HHR_DEV_BAD_INDEX = 0x2
 
@@ -34,7 +35,7 @@ c_f32 = ctypes.c_float
 class hhr_shape(ctypes.Structure):
     _fields_ = [("batch", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32),
                 ("head_dim", c_i32), ("code_bits", c_i32), ("page_size", c_i32),
-                ("max_ctx", c_i32), ("kv_dtype", c_i32)]
+                ("max_ctx", c_i32), ("kv_dtype", c_i32), ("meta_dtype", c_i32)]
 
 
 class hhr_hisa_shape(ctypes.Structure):
@@ -66,6 +67,8 @@ _SIGS = {
                                  c_vp, c_vp, c_size, c_vp]),
     "hhr_sparse_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_vp, c_vp,
                                   c_size, c_vp]),
+    "hhr_select_pages": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp,
+                                 c_vp, c_vp, c_vp, c_size, c_vp]),
     "hhr_select": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                            c_vp, c_vp, c_vp, c_size, c_vp]),
     "hhr_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
@@ -96,6 +99,10 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.hhr_abi_version() != ABI_VERSION:
+            raise HHRError(HHR_ERR_INVALID_ARG, "load",
+                           f"{LIB_PATH} has ABI version {lib.hhr_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}; rebuild it")
         _LIB = lib
     return _LIB
 
@@ -132,9 +139,17 @@ def _call(name: str, *args) -> None:
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, max_ctx, kv_dtype, head_dim=128, code_bits=128,
-               page_size=16) -> hhr_shape:
-    dt = {"f32": HHR_F32, "bf16": HHR_BF16}.get(kv_dtype, kv_dtype)
-    return hhr_shape(batch, n_q_heads, n_kv_heads, head_dim, code_bits, page_size, max_ctx, dt)
+               page_size=16, meta_dtype="f32") -> hhr_shape:
+    dt = {"f32": HHR_F32, "bf16": HHR_BF16}
+    return hhr_shape(batch, n_q_heads, n_kv_heads, head_dim, code_bits, page_size, max_ctx,
+                     dt.get(kv_dtype, kv_dtype), dt.get(meta_dtype, meta_dtype))
+
+
+def meta_shape(shape: hhr_shape) -> tuple:
+    """Shape of the page-metadata tensor for `shape` (f32 elements for HHR_F32,
+    int32 words for HHR_BF16: one {min, max} bfloat16 pair each)."""
+    base = (shape.batch, shape.n_kv_heads, shape.max_ctx // shape.page_size, shape.head_dim)
+    return base + (2,) if shape.meta_dtype == HHR_F32 else base
 
 
 def make_hisa_shape(batch, n_index_heads, block, max_ctx, head_dim=128) -> hhr_hisa_shape:
@@ -201,6 +216,15 @@ def hhr_sparse_decode(shape, q, k_cache, v_cache, sel_idx, sel_count, top_k, sca
     _call("hhr_sparse_decode", ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
           _ptr(sel_idx), _ptr(sel_count), int(top_k), float(scale), _ptr(out), _ptr(workspace),
           wb, _stream(stream))
+
+
+def hhr_select_pages(shape, q, seq_len, R, W, page_meta, keep_num, keep_den, keep_pages_abs,
+                     kept, kept_count, q_codes, workspace, workspace_bytes=None,
+                     stream=None) -> None:
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _call("hhr_select_pages", ctypes.byref(shape), _ptr(q), _ptr(seq_len), _ptr(R), _ptr(W),
+          _ptr(page_meta), keep_num, keep_den, keep_pages_abs, _ptr(kept), _ptr(kept_count),
+          _ptr(q_codes), _ptr(workspace), wb, _stream(stream))
 
 
 def hhr_select(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den, keep_pages_abs,

@@ -95,8 +95,20 @@ typedef struct {
   int32_t code_bits;
   int32_t page_size;
   int32_t max_ctx;
-  int32_t kv_dtype; /* hhr_dtype of the K and V caches */
+  int32_t kv_dtype;   /* hhr_dtype of the K and V caches */
+  int32_t meta_dtype; /* hhr_dtype of the page metadata (the page_meta layout below) */
 } hhr_shape;
+
+/* Page metadata layout, by meta_dtype (d = head_dim, NpCap = max_ctx / page_size):
+ *   HHR_F32  : [B][Hkv][NpCap][d][2] f32, {min, max} of each rotated key dimension
+ *              over the page's valid rows;
+ *   HHR_BF16 : [B][Hkv][NpCap][d] uint32, the same {min, max} as bfloat16 bit patterns
+ *              (min in bits 0..15, max in bits 16..31), the min rounded toward -inf and
+ *              the max toward +inf from the f32 values, so the page bound computed from
+ *              them is never below the one from f32 metadata (it is looser by at most one
+ *              bfloat16 step per dimension) and the metadata is half the bytes.  The
+ *              storage precision of the GKR bounds [HHR abstract, GKR] is not fixed
+ *              by the method; this is a compressed form of them. */
 
 /* Text for a status code (static storage). */
 const char* hhr_status_string(int32_t status);
@@ -134,7 +146,7 @@ hhr_status hhr_read_device_status(void* workspace, void* stream, uint32_t* flags
  *   codes     [B][Hkv][Lcap][nw] uint32   out: bit j of a key's code is
  *             [ (k W)_j >= 0 ], stored in word j/32 at bit j%32; written for
  *             the new rows only
- *   page_meta [B][Hkv][NpCap][d][2] f32   out: {min, max} over the valid rows
+ *   page_meta page metadata, meta_dtype layout   out: {min, max} over the valid rows
  *             (rows < start+n_new) of each touched page of X = k R
  * Rows of a touched page below start are read from k_cache (already present).
  * The products run on MFMA with bf16 hi/lo splits of R, W (and of f32 keys),
@@ -143,7 +155,7 @@ hhr_status hhr_read_device_status(void* workspace, void* stream, uint32_t* flags
  * in `status_word` (may be NULL: then such sequences are skipped silently). */
 hhr_status hhr_append_keys(const hhr_shape* shape, const void* k_cache, const int32_t* start,
                            const int32_t* n_new, int32_t max_new, const float* R,
-                           const float* W, uint32_t* codes, float* page_meta,
+                           const float* W, uint32_t* codes, void* page_meta,
                            uint32_t* status_word, void* stream);
 
 /* ------------------------------------------------------------ S2: query  */
@@ -162,11 +174,11 @@ hhr_status hhr_encode_queries(const hhr_shape* shape, const float* q, const floa
  *                                    [HHR abstract: page-level logit bounds]
  *   q_rot     [B][Hq][d] f32       from hhr_encode_queries
  *   seq_len   [B] int32
- *   page_meta [B][Hkv][NpCap][d][2] f32
+ *   page_meta page metadata in the meta_dtype layout
  *   scores    [B][Hkv][NpCap] f32  out
  *   status_word: device uint32 or NULL (HHR_DEV_BAD_SEQ_LEN) */
 hhr_status hhr_page_scores(const hhr_shape* shape, const float* q_rot, const int32_t* seq_len,
-                           const float* page_meta, float* scores, uint32_t* status_word,
+                           const void* page_meta, float* scores, uint32_t* status_word,
                            void* stream);
 
 /* ------------------------------------------------------------ S4: prune  */
@@ -217,12 +229,29 @@ hhr_status hhr_sparse_decode(const hhr_shape* shape, const float* q, const void*
                              const int32_t* sel_count, int32_t top_k, float scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------- S2..S4: page selection */
+/* hhr_select_pages: the coarse stage alone from raw queries, in one launch:
+ * rotate the group's queries (S2), bound every page (S3), keep the top P
+ * (S4).                                      [HHR abstract: GKR, pruning]
+ *   q, seq_len, R, W, page_meta  as for hhr_select
+ *   kept, kept_count  out, exactly as hhr_top_pages writes them from the
+ *              bounds that hhr_page_scores computes (bit-identical bounds)
+ *   q_codes    [B][Hq][nw] uint32 out (as hhr_encode_queries writes them), or
+ *              NULL (then kept in the workspace only)
+ *   workspace  >= hhr_workspace_size(shape, keep_num, keep_den,
+ *              keep_pages_abs, 1) bytes; the bounds stay in it */
+hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                            const float* R, const float* W, const void* page_meta,
+                            int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                            int32_t* kept, int32_t* kept_count, uint32_t* q_codes,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------- S2..S6 and S2..S7 */
 /* hhr_select: S2..S6 in one stream-ordered call; intermediates live in the
  * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk. */
 hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
-                      const float* page_meta, int32_t keep_num, int32_t keep_den,
+                      const void* page_meta, int32_t keep_num, int32_t keep_den,
                       int32_t keep_pages_abs, int32_t top_k, int32_t* sel_idx,
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,
                       void* stream);
@@ -232,7 +261,7 @@ hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq
  * sel_idx / sel_count receive the selection; out receives o. */
 hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
-                      const float* page_meta, const void* k_cache, const void* v_cache,
+                      const void* page_meta, const void* k_cache, const void* v_cache,
                       int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
                       float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);

@@ -215,13 +215,14 @@ def topk_smallest(H, positions, k: int) -> np.ndarray:
 
 
 def select(q_group, K_valid, R, W, page_size: int, keep_num: int, keep_den: int,
-           keep_abs: int, top_k: int) -> Dict[str, np.ndarray]:
+           keep_abs: int, top_k: int, meta_dtype: str = "f32") -> Dict[str, np.ndarray]:
     """The whole selection for one (sequence, KV head), from raw inputs.
 
-    q_group [G][d] queries of the group, K_valid [L][d] the sequence's keys.
+    q_group [G][d] queries of the group, K_valid [L][d] the sequence's keys;
+    meta_dtype "bf16" stores the page metadata outward-rounded (bf16_outward).
     """
     L = K_valid.shape[0]
-    enc = encode_keys(K_valid, R, W, page_size)
+    enc = encode_keys(K_valid, R, W, page_size, meta_dtype)
     qe = encode_query(q_group, R, W)
     s = page_scores(qe["qrot"], enc["meta"])
     P = keep_count(n_pages(L, page_size), keep_num, keep_den, keep_abs)

@@ -56,7 +56,7 @@ class Pipeline:
     """Buffers and stage-by-stage calls of the HIP path for one workload."""
 
     def __init__(self, H, inp, kv_dtype, n_q_heads, n_kv_heads, max_ctx, keep_num, keep_den,
-                 keep_abs, top_k, with_v=True):
+                 keep_abs, top_k, with_v=True, meta_dtype="f32"):
         self.H = H
         self.inp = inp
         self.kv_dtype = kv_dtype
@@ -65,7 +65,9 @@ class Pipeline:
         self.G = n_q_heads // n_kv_heads
         self.keep = (keep_num, keep_den, keep_abs)
         self.top_k = top_k
-        self.shape = H.make_shape(B, n_q_heads, n_kv_heads, max_ctx, kv_dtype)
+        self.meta_dtype = meta_dtype
+        self.shape = H.make_shape(B, n_q_heads, n_kv_heads, max_ctx, kv_dtype,
+                                  meta_dtype=meta_dtype)
         self.d = upload_hhr(inp if with_v else {k: v for k, v in inp.items() if k != "V"},
                             kv_dtype)
         NpCap = max_ctx // 16
@@ -74,7 +76,8 @@ class Pipeline:
         i32 = dict(dtype=torch.int32, device=dev())
         f32 = dict(dtype=torch.float32, device=dev())
         self.codes = torch.zeros((B, n_kv_heads, max_ctx, 4), **i32)
-        self.meta = torch.zeros((B, n_kv_heads, NpCap, 128, 2), **f32)
+        self.meta = torch.zeros(H.meta_shape(self.shape),
+                                **(f32 if meta_dtype == "f32" else i32))
         self.q_rot = torch.zeros((B, n_q_heads, 128), **f32)
         self.q_codes = torch.zeros((B, n_q_heads, 4), **i32)
         self.scores = torch.full((B, n_kv_heads, NpCap), float("nan"), **f32)
@@ -122,10 +125,34 @@ class Pipeline:
                           self.codes, self.meta, self.d["K"], self.d["V"], *self.keep, self.top_k,
                           self.scale, sel, sel_count, out, self.ws)
 
+    def select_pages(self):
+        """hhr_select_pages into fresh buffers (and a workspace of its own)."""
+        kept = torch.full_like(self.kept, 12345)
+        kc = torch.full_like(self.kept_count, -3)
+        qc = torch.zeros_like(self.q_codes)
+        ws = torch.zeros(self.H.hhr_workspace_size(self.shape, *self.keep, 1), dtype=torch.uint8,
+                         device=dev())
+        self.H.hhr_select_pages(self.shape, self.d["q"], self.d["seq_len"], self.d["R"],
+                                self.d["W"], self.meta, *self.keep, kept, kc, qc, ws)
+        torch.cuda.synchronize()
+        assert self.H.hhr_read_device_status(ws) == 0
+        return kept, kc, qc
+
     def status(self):
         return self.H.hhr_read_device_status(self.ws)
 
     # ---- host views
+    def meta_host(self, b, g, Np=None):
+        """Page metadata of (b, g) as float64 [Np][128][2] ({min, max}), decoding the
+        bfloat16 words of the compressed format."""
+        m = self.meta[b, g] if Np is None else self.meta[b, g, :Np]
+        if self.meta_dtype == "f32":
+            return m.cpu().numpy().astype(np.float64)
+        w = m.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+        lo = ((w & 0xFFFF) << 16).astype(np.uint32).view(np.float32)
+        hi = (w & 0xFFFF0000).astype(np.uint32).view(np.float32)
+        return np.stack([lo, hi], axis=-1).astype(np.float64)
+
     def K_valid(self, b, g):
         L = int(self.inp["seq_len"][b])
         return synth.kv_values(self.inp["K"][b, g, :L], self.kv_dtype).astype(np.float64)

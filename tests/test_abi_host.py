@@ -56,7 +56,7 @@ def test_status_strings_and_version(H):
     lib = H.load()
     assert lib.hhr_status_string(0) == b"HHR_OK"
     assert lib.hhr_status_string(-3) == b"HHR_ERR_WORKSPACE"
-    assert lib.hhr_abi_version() >= 1
+    assert lib.hhr_abi_version() == H.ABI_VERSION
 
 
 @pytest.mark.parametrize("n", [0, 1, 2, 3, 10, 255, 256, 513, 2048, 2049, 8192, 16384])
@@ -102,6 +102,7 @@ def test_shape_errors(H):
         (dict(good, max_ctx=1 << 20), H.HHR_ERR_UNSUPPORTED),
         (dict(good, n_q_heads=64, n_kv_heads=2), H.HHR_ERR_UNSUPPORTED),
         (dict(good, kv_dtype=7), H.HHR_ERR_INVALID_ARG),
+        (dict(good, meta_dtype=2), H.HHR_ERR_INVALID_ARG),
     ]
     for kw, want in cases:
         s = H.make_shape(**kw)
@@ -167,6 +168,28 @@ def test_workspace_errors(H):
     for dist in (None, FAKE):
         assert _status(H.hhr_hamming_topk, s, FAKE, FAKE, FAKE, FAKE, FAKE, p_max, 128, FAKE,
                        FAKE, dist, FAKE, workspace_bytes=4096, stream=0) == H.HHR_ERR_WORKSPACE
+
+
+def test_select_pages_errors(H):
+    s = H.make_shape(1, 8, 2, 1024, "bf16", meta_dtype="bf16")
+    need = H.hhr_workspace_size(s, 1, 4, 0, 1)
+    assert need > 0
+    args = (s, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert _status(H.hhr_select_pages, *args, 1, 4, 0, FAKE, FAKE, None, FAKE,
+                   workspace_bytes=need - 1, stream=0) == H.HHR_ERR_WORKSPACE
+    assert _status(H.hhr_select_pages, *args, 1, 4, 0, None, FAKE, None, FAKE,
+                   workspace_bytes=need, stream=0) == H.HHR_ERR_INVALID_ARG
+    assert _status(H.hhr_select_pages, *args, 1, 4, 0, FAKE, FAKE, FAKE + 8, FAKE,
+                   workspace_bytes=need, stream=0) == H.HHR_ERR_INVALID_ARG
+    assert _status(H.hhr_select_pages, *args, 3, 2, 0, FAKE, FAKE, None, FAKE,
+                   workspace_bytes=need, stream=0) == H.HHR_ERR_INVALID_ARG
+
+
+def test_metadata_layouts(H):
+    s = H.make_shape(2, 8, 2, 1024, "bf16")
+    assert H.meta_shape(s) == (2, 2, 64, 128, 2)
+    s = H.make_shape(2, 8, 2, 1024, "bf16", meta_dtype="bf16")
+    assert H.meta_shape(s) == (2, 2, 64, 128)
 
 
 def test_hisa_errors(H):

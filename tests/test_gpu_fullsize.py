@@ -138,6 +138,13 @@ def test_attention_conditioned(full):
         assert np.abs(h["out"][b, g * p.G:(g + 1) * p.G] - want).max() <= atol
 
 
+def test_select_pages_equals_stages(full):
+    name, w, p, h, pairs = full
+    kept, kc, qc = p.select_pages()
+    assert torch.equal(kept, p.kept) and torch.equal(kc, p.kept_count)
+    assert torch.equal(qc, p.q_codes)
+
+
 def test_decode_and_graph_replays_equal_stages(full):
     """The bench launch configuration: hhr_decode captured in a HIP graph and replayed."""
     name, w, p, h, pairs = full

@@ -192,6 +192,14 @@ def test_decode_composite_equals_stages(run, gpu_lib):
     assert p.status() == 0
 
 
+def test_select_pages_equals_stages(run):
+    """The one-launch coarse stage writes what encode + page_scores + top_pages write."""
+    case, p = run
+    kept, kc, qc = p.select_pages()
+    assert torch.equal(kept, p.kept) and torch.equal(kc, p.kept_count)
+    assert torch.equal(qc, p.q_codes)
+
+
 def test_chunked_append_equals_one_shot(gpu_lib):
     case = CASES[1]
     p = _pipeline(gpu_lib, case, with_v=False)
