@@ -208,9 +208,12 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.ham_hist = take(ham_hist_bytes(s));
   const HamScratch hs = ham_scratch(s, w.p_max);
   w.ham_dist = take(hs.end - hs.dist);
+  w.ham_cum = take(BHkv * (size_t)ham_cum_blocks(w.p_max) * (128 * (s.n_q_heads / s.n_kv_heads) + 1) *
+                   sizeof(uint16_t));
   w.q_rot = take(BHq * kD * sizeof(float));
   w.q_codes = take(BHq * kNW * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
+  w.wave_range = take(BHkv * (NpCap / 16) * sizeof(float2));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
   w.attn_part = take(attn_part_bytes(s, w.n_split));
@@ -427,11 +430,13 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->status = status_of(workspace);
   buf->counters = reinterpret_cast<uint32_t*>(base + ws->counters);
   buf->scores = reinterpret_cast<float*>(base + ws->scores);
+  buf->wave_range = reinterpret_cast<float2*>(base + ws->wave_range);
   buf->q_codes = reinterpret_cast<uint32_t*>(base + ws->q_codes);
   buf->kept = reinterpret_cast<int32_t*>(base + ws->kept);
   buf->kept_count = reinterpret_cast<int32_t*>(base + ws->kept_count);
   buf->dist = reinterpret_cast<uint16_t*>(base + ws->ham_dist);
   buf->chist = reinterpret_cast<int*>(base + ws->ham_hist);
+  buf->cum = reinterpret_cast<uint16_t*>(base + ws->ham_cum);
   return HHR_OK;
 }
 

@@ -3,12 +3,15 @@
 // every attention workgroup finds its own 64 selected keys), k_attn_merge.
 //
 // k_score_topp ends the page stage with the workgroup that finishes last:
-// every workgroup writes its bounds with agent-scope stores, waits for them
-// (s_waitcnt), and bumps a per-(b, g) counter with an agent-scope atomic; the
-// workgroup that brings the counter to the grid size resets it and runs top-P
-// on everyone's bounds (read with agent-scope loads).  Nobody waits for
-// anybody, so there is no scheduling hazard.  Each workgroup rotates its
-// group's queries itself, so no separate query-encoding launch precedes it.
+// every workgroup writes its bounds, and each wave the smallest and largest of
+// its 16, with agent-scope stores, waits for them (s_waitcnt), and bumps a
+// per-(b, g) counter with an agent-scope atomic; the workgroup that brings the
+// counter to the grid size resets it and runs top-P on everyone's bounds
+// (read with agent-scope loads), binning them over the range the waves
+// published, so it needs no pass of its own to find it.  (One atomic max per
+// wave on a shared word instead costs ~25 us at 128K: they serialise.)  Nobody waits for anybody, so there
+// is no scheduling hazard.  Each workgroup rotates its group's queries itself,
+// so no separate query-encoding launch precedes it.
 // (Measured: such a hand-off costs about as much as a kernel boundary, ~2 us;
 // the gain here is the query encoding off the critical path.)
 //
@@ -73,7 +76,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
     const float* __restrict__ R, const float* __restrict__ W, const void* __restrict__ meta,
     int keep_num, int keep_den, int keep_abs, int p_max, int Hq, int Hkv, int Lcap,
-    float* __restrict__ scores, uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
+    float* __restrict__ scores, float2* __restrict__ wave_range,
+    uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
     uint32_t* __restrict__ status) {
   __shared__ ScoreTopSmem sm;
@@ -102,32 +106,55 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
                                  [](int, int, uint32_t) {});
   }
+  uint32_t* ctl = counters + (size_t)bg * kCountersPerGroup;
+  float2* wr = wave_range + (size_t)bg * (NpCap / kScorePagesPerWave);
   if (wave_has) {
     float A[8], B[8];
     score_ab<MBF>(G, [&](int h, int d) { return sm.rot.qrot[h][d]; }, A, B);
-    score_finish<MBF, true, 1>(bg, NpCap, Np, pb, pl, A, B, scores, [](int, float) {});
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    score_finish<MBF, true, 1>(bg, NpCap, Np, pb, pl, A, B, scores, [&](int, float v) {
+      lo = v;
+      hi = v;
+    });
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if ((tid & 63) == 0) {
+      float* dst = reinterpret_cast<float*>(wr + pb / kScorePagesPerWave);
+      Mem<true>::st(dst, lo);
+      Mem<true>::st(dst + 1, hi);
+    }
   }
-  if (!arrive_last(&counters[bg], gridDim.x, &s_last)) return;
+  if (!arrive_last(ctl, gridDim.x, &s_last)) return;
 
   const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
   int32_t* out = kept + (size_t)bg * p_max;
   for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
   if (tid == 0) kept_count[bg] = P;
   if (P == 0) return;
-  top_pages_core<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, sm.sel.sbuf,
-                                      sm.sel.top, [&](int pos, int c) { out[pos] = c; });
+  // the range of all bounds from the waves' published {lo, hi}, one per thread
+  static_assert(kMaxCtx / kPS / kScorePagesPerWave <= kScoreThreads, "one wave range per thread");
+  const int n_waves = (Np + kScorePagesPerWave - 1) / kScorePagesPerWave;
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  if (tid < n_waves) {
+    const float* src = reinterpret_cast<const float*>(wr + tid);
+    lo = Mem<true>::ld(src);
+    hi = Mem<true>::ld(src + 1);
+  }
+  top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi, sm.sel.sbuf,
+                                        sm.sel.top, [&](int pos, int c) { out[pos] = c; });
 }
 
 // S6 + S7 for hhr_decode.  grid (n_split, B*Hkv), 256 threads: workgroup j
 // picks the keys of output ranks [64 j, 64 j + 64) straight from the
-// distances and histogram (pick_chunk), writes that slice of sel_idx (and
+// distances and histograms (pick_window), writes that slice of sel_idx (and
 // workgroup 0 the count), and attends over them exactly as k_attn would.
 template <bool KF32>
 __global__ __launch_bounds__(256) void k_attn_pick(
     const float* __restrict__ q, const void* __restrict__ kcache, const void* __restrict__ vcache,
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, const uint16_t* __restrict__ dist,
-    const int* __restrict__ hist, int p_max, int Hq, int Hkv, int Lcap, int top_k, int n_split,
+    const int* __restrict__ hist, const uint16_t* __restrict__ cum, int p_max, int Hq, int Hkv,
+    int Lcap, int top_k, int n_split,
     float scale, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
     float* __restrict__ part, uint32_t* __restrict__ status) {
   __shared__ AttnSmem<KF32> sm;
@@ -139,8 +166,8 @@ __global__ __launch_bounds__(256) void k_attn_pick(
   const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
   const int P = L > 0 ? max(0, min(kept_count[bg], p_max)) : 0;
   const int k0 = blockIdx.x * kCh;
-  const int count = pick_chunk<256>(bg, P, p_max, 128 * (Hq / Hkv) + 1, top_k, k0, kept, dist,
-                                    hist, sm.sidx, ps);
+  const int count = pick_window<256>(bg, P, p_max, 128 * (Hq / Hkv) + 1, top_k, k0, kept, dist,
+                                     hist, cum, sm.sidx, ps);
   if (tid < kCh && k0 + tid < top_k) sel_idx[(size_t)bg * top_k + k0 + tid] = sm.sidx[tid];
   if (blockIdx.x == 0 && tid == 0) sel_count[bg] = count;
   if (k0 >= count) return;  // block-uniform
@@ -174,13 +201,13 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
   if (s.meta_dtype == HHR_BF16)
     hipLaunchKernelGGL(k_score_topp<true>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R, W,
                        meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
-                       s.max_ctx, buf.scores, buf.q_codes, buf.kept, buf.kept_count,
-                       buf.counters, buf.status);
+                       s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept,
+                       buf.kept_count, buf.counters, buf.status);
   else
     hipLaunchKernelGGL(k_score_topp<false>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R,
                        W, meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
-                       s.max_ctx, buf.scores, buf.q_codes, buf.kept, buf.kept_count,
-                       buf.counters, buf.status);
+                       s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept,
+                       buf.kept_count, buf.counters, buf.status);
   return hipGetLastError();
 }
 
@@ -199,7 +226,7 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status,
                                stream);
   return launch_ham_dist(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
-                         buf.dist, buf.chist, stream);
+                         buf.dist, buf.chist, buf.cum, stream);
 }
 
 hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* k_cache,
@@ -211,12 +238,12 @@ hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* 
   dim3 grid(n_split, BG);
   if (s.kv_dtype == HHR_F32)
     hipLaunchKernelGGL(k_attn_pick<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
-                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, p_max,
+                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, buf.cum, p_max,
                        s.n_q_heads, s.n_kv_heads, s.max_ctx, top_k, n_split, scale, sel_idx,
                        sel_count, part, buf.status);
   else
     hipLaunchKernelGGL(k_attn_pick<false>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
-                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, p_max,
+                       seq_len, buf.kept, buf.kept_count, buf.dist, buf.chist, buf.cum, p_max,
                        s.n_q_heads, s.n_kv_heads, s.max_ctx, top_k, n_split, scale, sel_idx,
                        sel_count, part, buf.status);
   hipError_t e = hipGetLastError();

@@ -12,5 +12,8 @@ constexpr int kMaxG = 16;  // query heads per KV head
 // Fine top-k distance chunks: 64 kept pages (1024 candidates) per workgroup.
 constexpr int kHamChunkPages = 64;
 constexpr int ham_chunks(int pages) { return (pages + kHamChunkPages - 1) / kHamChunkPages; }
+// Candidates per cumulative H histogram block, and blocks per (b, g).
+constexpr int kCumBlock = 256;
+constexpr int ham_cum_blocks(int p_max) { return (p_max * kPS + kCumBlock - 1) / kCumBlock; }
 
 }  // namespace hhr

@@ -20,8 +20,8 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Byte offsets of the decode workspace regions.  Region 0 (the control block)
 // holds the device status word at offset 0.
 struct Workspace {
-  size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, q_rot = 0, q_codes = 0, scores = 0,
-         kept = 0, kept_count = 0, attn_part = 0, total = 0;
+  size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, ham_cum = 0, q_rot = 0, q_codes = 0,
+         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, total = 0;
   int32_t p_max = 0, n_split = 0;
 };
 
@@ -62,7 +62,7 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
 hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                            const int32_t* seq_len, const int32_t* kept,
                            const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
-                           hipStream_t stream);
+                           uint16_t* cum, hipStream_t stream);
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                                const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
@@ -77,16 +77,20 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
 // Composite paths (hhr_select, hhr_decode): S2..S4 in one launch that ends in
 // the last-arriving workgroup of each (b, g), then S5, then S6 (or, for
 // hhr_decode, S6 + S7 with every attention workgroup picking its own keys).
-// counters: B*Hkv arrival counters (zero before and after every call).
+// counters: kCountersPerGroup words per (b, g) (zero before and after every
+// call), the first of which counts k_score_topp's arrivals.  wave_range:
+// {smallest, largest} bound of each 16-page wave, [B*Hkv][NpCap/16].
 struct CompositeBuffers {
   uint32_t* status;
   uint32_t* counters;
   float* scores;
+  float2* wave_range;
   uint32_t* q_codes;
   int32_t* kept;
   int32_t* kept_count;
   uint16_t* dist;
   int* chist;
+  uint16_t* cum;  // per-block cumulative H histograms (hhr_decode's pick)
 };
 // k_score_topp alone (S2..S4): kept pages, counts and query codes into buf.
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
     const uint32_t* __restrict__ q_codes, const uint32_t* __restrict__ codes,
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, int p_max, int Hq, int Hkv, int Lcap,
-    uint16_t* __restrict__ dist, int* __restrict__ hist) {
+    uint16_t* __restrict__ dist, int* __restrict__ hist, uint16_t* __restrict__ cum) {
   __shared__ HamDistSmem sm;
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
   const int P = kept_pages(kept_count, bg, L, p_max);
   if ((int)blockIdx.x >= ham_chunks(P)) return;
   ham_dist_chunk<kHamDistThreads, false>(b, bg % Hkv, Hq, Hkv, Lcap, L, P, blockIdx.x, p_max,
-                                         q_codes, codes, kept, dist, hist, sm);
+                                         q_codes, codes, kept, dist, hist, cum, sm);
 }
 
 // Exact top-k of one (b, g) from its distances and chunk histograms.
@@ -139,10 +139,10 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
 hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
                            const int32_t* seq_len, const int32_t* kept,
                            const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
-                           hipStream_t stream) {
+                           uint16_t* cum, hipStream_t stream) {
   hipLaunchKernelGGL(k_ham_dist, dim3(ham_chunks(p_max), s.batch * s.n_kv_heads),
                      dim3(kHamDistThreads), 0, stream, q_codes, codes, seq_len, kept, kept_count,
-                     p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, hist);
+                     p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, hist, cum);
   return hipGetLastError();
 }
 
@@ -152,7 +152,8 @@ hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, cons
                                int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* hist,
                                uint32_t* status, hipStream_t stream) {
   hipError_t e =
-      launch_ham_dist(s, q_codes, codes, seq_len, kept, kept_count, p_max, dist, hist, stream);
+      launch_ham_dist(s, q_codes, codes, seq_len, kept, kept_count, p_max, dist, hist, nullptr,
+                      stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_ham_select, dim3(s.batch * s.n_kv_heads), dim3(kHamSelThreads), 0, stream,
                      seq_len, kept, kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads,

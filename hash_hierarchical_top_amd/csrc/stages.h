@@ -293,6 +293,44 @@ __device__ int top_pages_core(const float* sc, int Np, int P, float* sbuf, TopSc
                                                          sh, emit);
 }
 
+// top_pages_core with the range of the scores given in pieces: every thread
+// passes a (lo, hi) that bounds some of the scores (+inf, -inf for none), and
+// together they bound all of them.  The range is reduced in the barrier that
+// the staging needs anyway, so there is no pass over the scores to find it.
+template <int NT, bool COH, typename Emit>
+__device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
+                                TopScratch& sh, Emit emit) {
+  constexpr int kB = 8;
+  const int tid = threadIdx.x;
+  const int last = max(Np - 1, 0);
+#pragma unroll 1
+  for (int c0 = 0; c0 < Np; c0 += kB * NT) {
+    float x[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) x[j] = Mem<COH>::ld(sc + min(c0 + j * NT + tid, last));
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int c = c0 + j * NT + tid;
+      if (c < Np) sbuf[c] = x[j];
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if ((tid & (kWave - 1)) == 0) {
+    sh.w_min[tid / kWave] = lo;
+    sh.w_max[tid / kWave] = hi;
+  }
+  __syncthreads();
+  float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
+#pragma unroll
+  for (int k = 0; k < NT / kWave; ++k) {
+    vmin = fminf(vmin, sh.w_min[k]);
+    vmax = fmaxf(vmax, sh.w_max[k]);
+  }
+  return top_largest_ranged<NT, kMaxCtx / kPS / (4 * NT)>(sbuf, Np, [](int) { return true; }, P,
+                                                            vmin, vmax, Np, sh, emit);
+}
+
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
   if (Np <= 0) return 0;
   if (keep_abs > 0) return min(Np, keep_abs);
@@ -312,6 +350,10 @@ __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den
 //     for the next call), finds the smallest H value T whose cumulative count
 //     reaches top_k and how many candidates with H == T are taken, then
 //     compacts in candidate order.
+// For hhr_decode the distance stage also writes, per block of 256 candidates,
+// the cumulative histogram cum[blk][i] = #(H <= i) over the block's valid
+// candidates (u16), so that each attention workgroup can find the blocks that
+// hold its 64 output ranks from two entries per block (pick_window).
 constexpr int kHamBins = 128 * kMaxG + 1;  // 2049
 constexpr int kHistCopies = 4;
 constexpr int kHamChunk = kHamChunkPages * kPS;  // 1024 candidates
@@ -320,6 +362,7 @@ struct HamDistSmem {
   int hist[kHistCopies][kHamBins];
   int skept[kHamChunkPages];
   __attribute__((aligned(16))) uint32_t sq[kMaxG * kNW];
+  uint32_t uscan[17];
 };
 
 // 16-byte load; the coherent form is four agent-scope dword loads.
@@ -335,13 +378,16 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 
 // Distances of chunk k of (b, g): candidates c in [1024k, 1024k + 1024) with
 // c < 16 P.  dist [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts
-// added atomically).  All threads call; NT divides 1024.
+// added atomically); cum (or NULL) [B][Hkv][ham_cum_blocks(p_max)][128 G + 1]
+// u16.  Item j of every thread lies in block 4k + j, whose histogram is LDS
+// copy j.  All threads call.
 template <int NT, bool COH>
 __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, int P, int k,
                                int p_max, const uint32_t* q_codes,
                                const uint32_t* __restrict__ codes, const int32_t* kept,
-                               uint16_t* dist, int* hist, HamDistSmem& sm) {
+                               uint16_t* dist, int* hist, uint16_t* cum, HamDistSmem& sm) {
   constexpr int kItems = kHamChunk / NT;
+  static_assert(NT == kCumBlock && kItems == kHistCopies, "item j = block j = LDS copy j");
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
@@ -379,12 +425,11 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, i
       h[j] += __popc(code[j][0] ^ q[0]) + __popc(code[j][1] ^ q[1]) + __popc(code[j][2] ^ q[2]) +
               __popc(code[j][3] ^ q[3]);
   }
-  int* my_hist = sm.hist[w & (kHistCopies - 1)];
   uint16_t* dc = dist + (size_t)bg * p_max * kPS + (size_t)page0 * kPS;
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int c = j * NT + tid;
-    if (ok[j]) atomicAdd(&my_hist[h[j]], 1);
+    if (ok[j]) atomicAdd(&sm.hist[j][h[j]], 1);
     if (c < ncl) Mem<COH>::st(dc + c, (uint16_t)(ok[j] ? h[j] : 0xFFFFu));
   }
   __syncthreads();
@@ -394,6 +439,27 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, i
 #pragma unroll
     for (int r = 0; r < kHistCopies; ++r) c += sm.hist[r][i];
     if (c != 0) atomicAdd(hb + i, c);  // device-scope: chunks run on every XCD
+  }
+  if (cum == nullptr) return;  // block-uniform
+  // cumulative histograms of the chunk's blocks, two blocks per packed scan
+  // (a block's counts stay <= 256, so 16-bit halves cannot carry)
+  const int per = (nbins + NT - 1) / NT;
+  const int i0 = tid * per;
+  uint16_t* cb0 = cum + ((size_t)bg * ham_cum_blocks(p_max) + (size_t)k * kHistCopies) * nbins;
+#pragma unroll
+  for (int r = 0; r < kHistCopies; r += 2) {
+    if (r * kCumBlock >= ncl) break;  // block-uniform
+    uint32_t local = 0;
+    for (int i = i0; i < min(i0 + per, nbins); ++i)
+      local += (uint32_t)sm.hist[r][i] | ((uint32_t)sm.hist[r + 1][i] << 16);
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan<NT, uint32_t>(local, sm.uscan, &tot);
+    for (int i = i0; i < min(i0 + per, nbins); ++i) {
+      run += (uint32_t)sm.hist[r][i] | ((uint32_t)sm.hist[r + 1][i] << 16);
+      cb0[(size_t)r * nbins + i] = (uint16_t)(run & 0xFFFFu);
+      if ((r + 1) * kCumBlock < ncl) cb0[(size_t)(r + 1) * nbins + i] = (uint16_t)(run >> 16);
+    }
+    __syncthreads();  // sm.uscan is reused by the next scan
   }
 }
 
@@ -513,31 +579,36 @@ __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int 
 }
 
 // The 64 selected positions of output chunk [k0, k0 + 64) of (b, g), found
-// without the compacted list: the cut (T, need) from the H histogram, then
-// every thread counts the taken candidates of its run of distances, one
-// block scan gives each run its first output position, and only the runs
-// that reach into the chunk walk their candidates again to place them.  The
-// result is sidx[i] = the position of output rank k0 + i (-1 past the
-// selection); returns the selection size min(top_k, #valid).  Reads dist,
-// hist and kept written by earlier launches.  All NT threads call.
-constexpr int kPickBatch = 8;  // 8-distance words per thread per round trip
+// without the compacted list.  The cut (T, need) comes from the H histogram:
+// candidate c is taken iff H < T, or H == T and fewer than `need` candidates
+// with H == T precede it.  Two entries of each block's cumulative histogram
+// give its counts below and at T; wave scans over the blocks give every
+// block its first output rank, so only the blocks that reach into the chunk
+// (usually one or two) are read, one packed block scan each, to place their
+// taken candidates.  The result is sidx[i] = the position of output rank
+// k0 + i (-1 past the selection); returns the selection size
+// min(top_k, #valid).  Reads dist, hist, cum and kept written by earlier
+// launches.  All NT threads call.
+constexpr int kPickMaxBlocks = 4;  // blocks read per round trip
 
 struct PickSmem {
   int scan[17];
   uint32_t uscan[17];
-  int s_T, s_need;
-  u32x4 words[kPickBatch][256];  // this thread's current batch of words
-  int run_gb[256], run_eb[256];  // > and == T candidates before each run
+  int s_T, s_need, s_blo, s_bhi;
+  int blk_first[2 * kWave];  // first output rank of each block
+  int blk_eq[2 * kWave];     // candidates with H == T in earlier blocks
 };
 
 template <int NT>
-__device__ __forceinline__ int pick_chunk(int bg, int P, int p_max, int nbins, int top_k, int k0,
-                          const int32_t* kept, const uint16_t* dist, const int* hist, int* sidx,
-                          PickSmem& ps) {
-  static_assert(NT == 256, "PickSmem::words holds one batch per thread of 256");
+__device__ __forceinline__ int pick_window(int bg, int P, int p_max, int nbins, int top_k, int k0,
+                                           const int32_t* kept, const uint16_t* dist,
+                                           const int* hist, const uint16_t* cum, int* sidx,
+                                           PickSmem& ps) {
+  static_assert(NT == kCumBlock, "one candidate of a block per thread");
   constexpr int kMaxPer = (kHamBins + NT - 1) / NT;
   const int tid = threadIdx.x;
   const int ncand = P * kPS;
+  const int nblk = (ncand + kCumBlock - 1) / kCumBlock;  // <= 2 * kWave
   // the cut: smallest T with #(H <= T) >= top_k, and how many H == T are taken
   const int* hb = hist + (size_t)bg * nbins;
   const int per = (nbins + NT - 1) / NT;
@@ -569,101 +640,84 @@ __device__ __forceinline__ int pick_chunk(int bg, int P, int p_max, int nbins, i
     }
   }
   __syncthreads();
-  const uint32_t Th = (uint32_t)ps.s_T;
+  const int Th = ps.s_T;
   const int need = ps.s_need;
   const int count = min(top_k, total);
 
-  // output ranks over contiguous runs of 8-distance words, staged through LDS
-  // (ps.words) so that both passes are small rolled loops
-  const int nv8 = (ncand + 8 * NT - 1) / (8 * NT);
-  const int c0 = 8 * nv8 * tid;
-  const uint32_t* d32 = reinterpret_cast<const uint32_t*>(dist + (size_t)bg * p_max * kPS);
-  auto cls_of = [&](const u32x4& hw, int e, int c) -> int {
-    const uint32_t word = hw[e >> 1];
-    uint32_t h = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-    if (c >= ncand) h = 0xFFFFu;
-    return h < Th ? 1 : (h == Th ? 2 : 0);
-  };
-  int gt = 0, eq = 0;
-#pragma unroll 1
-  for (int j0 = 0; j0 < nv8; j0 += kPickBatch) {
-    const int nb = min(kPickBatch, nv8 - j0);
-    u32x4 hw[kPickBatch];
-#pragma unroll
-    for (int j = 0; j < kPickBatch; ++j) {
-      const int c = min(c0 + 8 * (j0 + j), max(ncand - 8, 0));  // in bounds; masked below
-      hw[j] = *(const u32x4*)(d32 + c / 2);
-    }
-#pragma unroll
-    for (int j = 0; j < kPickBatch; ++j) ps.words[j][tid] = hw[j];
-#pragma unroll 1
-    for (int j = 0; j < nb; ++j) {
-      const u32x4 w8 = ps.words[j][tid];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = cls_of(w8, e, c0 + 8 * (j0 + j) + e);
-        gt += k == 1;
-        eq += k == 2;
-      }
-    }
-  }
-  uint32_t tot;
-  const uint32_t pre =
-      block_exclusive_scan<NT, uint32_t>((uint32_t)gt | ((uint32_t)eq << 16), ps.uscan, &tot);
-  // taken candidates before each run: gt before + min(eq before, need)
-  ps.run_gb[tid] = (int)(pre & 0xFFFFu);
-  ps.run_eb[tid] = (int)(pre >> 16);
-  __syncthreads();
-  // wave 0 places the window: the runs whose taken ranks reach into
-  // [k0, k0 + 64), walked 64 candidates at a time with wave scans for the
-  // tie rank and the output position
+  // wave 0: per block, #(H < T) and #(H == T) from its cumulative histogram,
+  // then its first output rank; the window's blocks are [s_blo, s_bhi]
   if (tid < kWave) {
     const int l = tid;
-    auto taken_before = [&](int t) { return ps.run_gb[t] + min(ps.run_eb[t], need); };
-    int lo = NT, hi = -1;
-    for (int t = l; t < NT; t += kWave) {
-      const int f = taken_before(t);
-      const int z = t + 1 < NT ? taken_before(t + 1) : count;
-      if (f < k0 + kAttnChunk && z > k0) {
-        lo = min(lo, t);
-        hi = max(hi, t);
+    const uint16_t* cb = cum + (size_t)bg * ham_cum_blocks(p_max) * nbins;
+    int lt[2], eq[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int blk = r * kWave + l;
+      lt[r] = eq[r] = 0;
+      if (blk < nblk) {
+        const uint16_t* row = cb + (size_t)blk * nbins;
+        const int below = Th == 0 ? 0 : (int)row[min(Th, nbins) - 1];
+        const int upto = Th >= nbins ? below : (int)row[Th];
+        lt[r] = below;
+        eq[r] = upto - below;
       }
+    }
+    int lt_carry = 0, eq_carry = 0, lo = 2 * kWave, hi = -1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int blk = r * kWave + l;
+      const int lt_in = wave_inclusive_scan(lt[r]);
+      const int eq_in = wave_inclusive_scan(eq[r]);
+      const int lt_before = lt_carry + lt_in - lt[r];
+      const int eq_before = eq_carry + eq_in - eq[r];
+      const int first = lt_before + min(eq_before, need);
+      const int taken = lt[r] + min(max(need - eq_before, 0), eq[r]);
+      ps.blk_first[blk] = first;
+      ps.blk_eq[blk] = eq_before;
+      if (blk < nblk && taken > 0 && first < k0 + kAttnChunk && first + taken > k0) {
+        lo = min(lo, blk);
+        hi = max(hi, blk);
+      }
+      lt_carry += __builtin_amdgcn_readlane(lt_in, kWave - 1);
+      eq_carry += __builtin_amdgcn_readlane(eq_in, kWave - 1);
     }
     lo = (int)wave_min_u((uint32_t)lo);
     hi = (int)wave_max_u((uint32_t)(hi + 1)) - 1;
-    if (hi >= lo) {
-      const int c_lo = 8 * nv8 * lo;
-      const int c_hi = min(8 * nv8 * (hi + 1), ncand);
-      int g_run = ps.run_gb[lo], e_run = ps.run_eb[lo];
-      const uint16_t* db = dist + (size_t)bg * p_max * kPS;
-      const int32_t* kb = kept + (size_t)bg * p_max;
-      constexpr int kPer = 8;  // candidates per lane per round trip
+    if (l == 0) {
+      ps.s_blo = lo;
+      ps.s_bhi = hi;
+    }
+  }
+  __syncthreads();
+  const int blo = ps.s_blo, bhi = ps.s_bhi;
+  const uint16_t* db = dist + (size_t)bg * p_max * kPS;
+  const int32_t* kb = kept + (size_t)bg * p_max;
 #pragma unroll 1
-      for (int cb = c_lo; cb < c_hi; cb += kPer * kWave) {
-        uint32_t hv[kPer];
-        int pg[kPer];
+  for (int bb = blo; bb <= bhi; bb += kPickMaxBlocks) {  // block-uniform
+    uint32_t h[kPickMaxBlocks];
+    int pg[kPickMaxBlocks];
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const int cc = min(cb + u * kWave + l, c_hi - 1);
-          hv[u] = db[cc];
-          pg[u] = kb[cc >> 4];
-        }
+    for (int u = 0; u < kPickMaxBlocks; ++u) {
+      const int c = min((bb + u) * kCumBlock + tid, max(ncand - 1, 0));
+      h[u] = db[c];
+      pg[u] = kb[c >> 4];
+    }
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const int cc = cb + u * kWave + l;
-          const uint32_t h = cc < c_hi ? hv[u] : 0xFFFFu;
-          const int gtf = h < Th ? 1 : 0;
-          const int eqf = h == Th ? 1 : 0;
-          const int eq_incl = wave_inclusive_scan(eqf);
-          const int eq_before = e_run + eq_incl - eqf;
-          const int tk = (gtf || (eqf && eq_before < need)) ? 1 : 0;
-          const int tk_incl = wave_inclusive_scan(tk);
-          const int pos = g_run + min(e_run, need) + tk_incl - tk;
-          if (tk && pos >= k0 && pos < k0 + kAttnChunk) sidx[pos - k0] = pg[u] * kPS + (cc & 15);
-          g_run += __builtin_amdgcn_readlane(wave_inclusive_scan(gtf), kWave - 1);
-          e_run += __builtin_amdgcn_readlane(eq_incl, kWave - 1);
-        }
-      }
+    for (int u = 0; u < kPickMaxBlocks; ++u) {
+      const int blk = bb + u;
+      if (blk > bhi) break;  // block-uniform
+      const int c = blk * kCumBlock + tid;
+      const uint32_t hv = c < ncand ? h[u] : 0xFFFFu;
+      const uint32_t ltf = hv < (uint32_t)Th ? 1u : 0u;
+      const uint32_t eqf = hv == (uint32_t)Th ? 1u : 0u;
+      uint32_t tot;
+      const uint32_t pre = block_exclusive_scan<NT, uint32_t>(ltf | (eqf << 16), ps.uscan, &tot);
+      const int lt_b = (int)(pre & 0xFFFFu), eq_b = (int)(pre >> 16);
+      const int r = max(need - ps.blk_eq[blk], 0);  // ties still to take at the block start
+      const bool tk = ltf || (eqf && eq_b < r);
+      const int pos = ps.blk_first[blk] + lt_b + min(eq_b, r);
+      if (tk && pos >= k0 && pos < k0 + kAttnChunk) sidx[pos - k0] = pg[u] * kPS + (c & 15);
+      __syncthreads();  // ps.uscan is reused by the next scan
     }
   }
   __syncthreads();

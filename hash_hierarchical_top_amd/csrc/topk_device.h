@@ -177,12 +177,13 @@ __device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& g
 // the cut is then decided from the bins, and only members of the threshold
 // bin compare values.
 template <int NT, int MAXV4, typename Present, typename Emit>
+__device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
+                                  float vmax, int n_valid, TopScratch& sh, Emit emit);
+
+template <int NT, int MAXV4, typename Present, typename Emit>
 __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P, TopScratch& sh,
                                Emit emit) {
   constexpr int NWAVES = NT / kWave;
-  constexpr int MAXV = 4 * MAXV4;
-  static_assert(MAXV <= 32, "2 class bits per slot in 64 bits");
-  constexpr uint32_t kAbsent = 0xFFFFu;  // bin code of an absent slot
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = tid % kWave;
@@ -190,7 +191,6 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
   const int c0 = 4 * nv4 * tid;
   const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
   auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
-  auto is_present = [&](int c) { return c < n && present(c); };
 
   float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
   int cnt = 0;
@@ -200,7 +200,8 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
       const float4 t = run4[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (is_present(c0 + 4 * j + e)) {
+        const int c = c0 + 4 * j + e;
+        if (c < n && present(c)) {
           mn = fminf(mn, val(t, e));
           mx = fmaxf(mx, val(t, e));
           ++cnt;
@@ -216,8 +217,6 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
     sh.w_max[w] = mx;
     sh.w_n[w] = cnt;
   }
-  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
-  if (tid == 0) sh.list_n = 0;
   __syncthreads();
   float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
   int n_valid = 0;
@@ -227,8 +226,31 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
     vmax = fmaxf(vmax, sh.w_max[k]);
     n_valid += sh.w_n[k];
   }
+  return top_largest_ranged<NT, MAXV4>(sbuf, n, present, P, vmin, vmax, n_valid, sh, emit);
+}
+
+// The same selection with the range of the present scores given: vmin <=
+// every present score <= vmax, and n_valid = #present.  Each thread reads only
+// its own run of sbuf, so a caller that writes its own run needs no barrier
+// before the call.
+template <int NT, int MAXV4, typename Present, typename Emit>
+__device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
+                                  float vmax, int n_valid, TopScratch& sh, Emit emit) {
+  constexpr int MAXV = 4 * MAXV4;
+  static_assert(MAXV <= 32, "2 class bits per slot in 64 bits");
+  constexpr uint32_t kAbsent = 0xFFFFu;  // bin code of an absent slot
+  const int tid = threadIdx.x;
+  const int nv4 = (n + 4 * NT - 1) / (4 * NT);
+  const int c0 = 4 * nv4 * tid;
+  const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
+  auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
+  auto is_present = [&](int c) { return c < n && present(c); };
+
   const int Pe = min(P, n_valid);
-  if (Pe <= 0) return 0;
+  if (Pe <= 0) return 0;  // block-uniform
+  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
+  if (tid == 0) sh.list_n = 0;
+  __syncthreads();
 
   // bins: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)) is monotone in v
   const float range = vmax - vmin;
