@@ -1,8 +1,8 @@
 // S7 sparse decode: softmax attention over only the selected K/V rows
 // [HHR abstract: hash-based sparse attention], split over 64-key chunks of the
 // selected set with an online-softmax (m, l, o) combine.  k_attn runs one
-// chunk per workgroup (attn_chunk); k_attn_combine merges one (b, g) per
-// workgroup of kCombThreads threads (attn_combine).
+// chunk per workgroup (attn_chunk); k_attn_combine merges one (b, g, query
+// head) per workgroup of kCombThreads threads (attn_combine).
 
 #include "hhr_device.h"
 #include "hhr_internal.h"
@@ -33,9 +33,10 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(
     const float* __restrict__ part, const int32_t* __restrict__ sel_count,
     float* __restrict__ out, int Hq, int Hkv, int top_k, int n_split) {
   __shared__ CombSmem sm;
-  const int bg = blockIdx.x;
+  const int bg = blockIdx.y;
   const int cnt = max(0, min(sel_count[bg], top_k));
-  attn_combine<false>(bg / Hkv, bg % Hkv, Hq, Hkv, (cnt + kCh - 1) / kCh, n_split, part, out, sm);
+  attn_combine<false>(bg / Hkv, bg % Hkv, blockIdx.x, Hq, Hkv, (cnt + kCh - 1) / kCh, n_split,
+                      part, out, sm);
 }
 
 }  // namespace
@@ -56,8 +57,9 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
                        n_split, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(s.batch * s.n_kv_heads), dim3(kCombThreads), 0, stream,
-                     part, sel_count, out, s.n_q_heads, s.n_kv_heads, top_k, n_split);
+  hipLaunchKernelGGL(k_attn_combine, dim3(s.n_q_heads / s.n_kv_heads, s.batch * s.n_kv_heads),
+                     dim3(kCombThreads), 0, stream, part, sel_count, out, s.n_q_heads,
+                     s.n_kv_heads, top_k, n_split);
   return hipGetLastError();
 }
 

@@ -177,16 +177,20 @@ __global__ __launch_bounds__(256) void k_attn_pick(
                           sm);
 }
 
-// The chunk merge of one (b, g), then the (b, g)'s H histogram back to zero.
+// The chunk merge of one (b, g, query head), then a slice of the (b, g)'s H
+// histogram back to zero.  grid (G, B*Hkv).
 __global__ __launch_bounds__(kCombThreads) void k_attn_merge(
     const float* __restrict__ part, const int32_t* __restrict__ sel_count,
     float* __restrict__ out, int* __restrict__ hist, int Hq, int Hkv, int top_k, int n_split) {
   __shared__ CombSmem sm;
-  const int bg = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int h = blockIdx.x;
   const int cnt = max(0, min(sel_count[bg], top_k));
-  attn_combine<false>(bg / Hkv, bg % Hkv, Hq, Hkv, (cnt + kCh - 1) / kCh, n_split, part, out, sm);
+  attn_combine<false>(bg / Hkv, bg % Hkv, h, Hq, Hkv, (cnt + kCh - 1) / kCh, n_split, part, out,
+                      sm);
   const int nbins = 128 * (Hq / Hkv) + 1;
-  for (int i = threadIdx.x; i < nbins; i += kCombThreads) hist[(size_t)bg * nbins + i] = 0;
+  for (int i = h * kCombThreads + threadIdx.x; i < nbins; i += gridDim.x * kCombThreads)
+    hist[(size_t)bg * nbins + i] = 0;
 }
 
 }  // namespace
@@ -248,8 +252,9 @@ hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* 
                        sel_count, part, buf.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(BG), dim3(kCombThreads), 0, stream, part, sel_count, out,
-                     buf.chist, s.n_q_heads, s.n_kv_heads, top_k, n_split);
+  hipLaunchKernelGGL(k_attn_merge, dim3(s.n_q_heads / s.n_kv_heads, BG), dim3(kCombThreads), 0,
+                     stream, part, sel_count, out, buf.chist, s.n_q_heads, s.n_kv_heads, top_k,
+                     n_split);
   return hipGetLastError();
 }
 

@@ -303,6 +303,8 @@ __device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float 
   constexpr int kB = 8;
   const int tid = threadIdx.x;
   const int last = max(Np - 1, 0);
+  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the barrier below
+  if (tid == 0) sh.list_n = 0;
 #pragma unroll 1
   for (int c0 = 0; c0 < Np; c0 += kB * NT) {
     float x[kB];
@@ -328,7 +330,7 @@ __device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float 
     vmax = fmaxf(vmax, sh.w_max[k]);
   }
   return top_largest_ranged<NT, kMaxCtx / kPS / (4 * NT)>(sbuf, Np, [](int) { return true; }, P,
-                                                            vmin, vmax, Np, sh, emit);
+                                                            vmin, vmax, Np, sh, emit, true);
 }
 
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
@@ -878,19 +880,21 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   }
 }
 
-// Merge the ns chunk partials of one (b, g) into o (kCombThreads threads):
-//   M_h = max_s m_sh, f_sh = e^(m_sh - M_h), L_h = sum_s f_sh l_sh,
-//   o_h = sum_s f_sh o~_sh / L_h  (o = 0 when nothing was selected).
-// Thread (h, dim quad, s-group) sums chunks s = sgrp, sgrp + NSG, ... in
-// ascending order; the s-groups are then added in order in LDS.  The first
-// 16 of each thread's partials are loaded together with every (m, l) before
-// the weights are known, so up to 16 NSG chunks cost one round trip.
-constexpr int kCombThreads = 512;
-constexpr int kCombMaxChunks = kMaxCand / kCh;  // 512
+// Merge the ns chunk partials of query head h of one (b, g) into o_h
+// (kCombThreads threads, one workgroup per (b, g, h)):
+//   M = max_s m_s, f_s = e^(m_s - M), L = sum_s f_s l_s,
+//   o_h = sum_s f_s o~_s / L  (o = 0 when nothing was selected).
+// Thread (dim quad, s-group) sums chunks s = sgrp, sgrp + 4, ... in ascending
+// order; the four s-groups are then added in order in LDS.  The first 16 of
+// each thread's partials are loaded together with every (m, l) before the
+// weights are known, so up to 64 chunks cost one round trip.
+constexpr int kCombThreads = 128;
+constexpr int kCombGroups = kCombThreads / (kD / 4);  // 4 chunk groups
+constexpr int kCombMaxChunks = kMaxCand / kCh;        // 512
 
 struct CombSmem {
-  float f[kMaxG][kCombMaxChunks];
-  float lsum[kMaxG];
+  float f[kCombMaxChunks];
+  float lsum;
   floatx4 red[kCombThreads];
 };
 
@@ -907,44 +911,38 @@ __device__ __forceinline__ floatx4 ld_f32x4(const float* p) {
 // kCombThreads threads (every caller uses this count, so all sum in the same
 // order).
 template <bool COH>
-__device__ void attn_combine(int b, int g, int Hq, int Hkv, int ns, int n_split,
+__device__ void attn_combine(int b, int g, int h, int Hq, int Hkv, int ns, int n_split,
                              const float* part, float* __restrict__ out, CombSmem& sm) {
   constexpr int kB = 16;  // partials per thread per round trip
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
   const int l = tid & 63;
   const size_t sstride = (size_t)kMaxG * kPartStride;
-  const float* pb = part + (size_t)bg * n_split * sstride;
-  const int pairs = G * (kD / 4);                // (head, dim quad)
-  const int nsg = max(1, kCombThreads / pairs);  // chunk groups
-  const int pair = tid % pairs;
-  const int sgrp = tid / pairs;
-  const int h = pair / (kD / 4);
-  const int d4 = pair % (kD / 4);
-  const bool worker = sgrp < nsg && ns > 0;
+  const float* pb = part + (size_t)bg * n_split * sstride + (size_t)h * kPartStride;
+  const int d4 = tid % (kD / 4);
+  const int sgrp = tid / (kD / 4);
   floatx4 v[kB];
   auto load_batch = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
-      const int sc = min(s0 + j * nsg, ns - 1);  // clamped; weight 0 past ns
-      v[j] = ld_f32x4<COH>(pb + sc * sstride + h * kPartStride + 4 * d4);
+      const int sc = min(s0 + j * kCombGroups, max(ns - 1, 0));  // clamped; weight 0 past ns
+      v[j] = ld_f32x4<COH>(pb + sc * sstride + 4 * d4);
     }
   };
-  if (worker) load_batch(sgrp);
-  // chunk weights: one wave per head (chunks s = l, l + 64, ...)
-  for (int hh = w; hh < G; hh += kCombThreads / kWave) {
-    const float* ph = pb + hh * kPartStride + kD;
+  if (ns > 0) load_batch(sgrp);
+  // chunk weights: wave 0 (chunks s = l, l + 64, ...)
+  if (tid < kWave) {
+    const float* ph = pb + kD;
     if (ns <= kWave) {
       const int sc = min(l, max(ns - 1, 0));
       const float ms = l < ns ? Mem<COH>::ld(ph + sc * sstride) : -__builtin_huge_valf();
       const float ls_ = l < ns ? Mem<COH>::ld(ph + sc * sstride + 1) : 0.f;
       const float M = wave_max(ms);
       const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
-      if (l < ns) sm.f[hh][l] = f;
+      if (l < ns) sm.f[l] = f;
       const float ls = wave_sum(fmaf(f, ls_, 0.f));
-      if (l == 0) sm.lsum[hh] = ls;
+      if (l == 0) sm.lsum = ls;
     } else {
       float M = -__builtin_huge_valf();
       for (int s = l; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(ph + s * sstride));
@@ -953,45 +951,41 @@ __device__ void attn_combine(int b, int g, int Hq, int Hkv, int ns, int n_split,
       for (int s = l; s < ns; s += kWave) {
         const float ms = Mem<COH>::ld(ph + s * sstride);
         const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
-        sm.f[hh][s] = f;
+        sm.f[s] = f;
         ls = fmaf(f, Mem<COH>::ld(ph + s * sstride + 1), ls);
       }
       ls = wave_sum(ls);
-      if (l == 0) sm.lsum[hh] = ls;
+      if (l == 0) sm.lsum = ls;
     }
   }
   __syncthreads();
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (worker) {
 #pragma unroll 1
-    for (int s0 = sgrp; s0 < ns; s0 += kB * nsg) {
-      if (s0 != sgrp) load_batch(s0);
+  for (int s0 = sgrp; s0 < ns; s0 += kB * kCombGroups) {
+    if (s0 != sgrp) load_batch(s0);
 #pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const int s = s0 + j * nsg;
-        const float f = s < ns ? sm.f[h][min(s, ns - 1)] : 0.f;
+    for (int j = 0; j < kB; ++j) {
+      const int s = s0 + j * kCombGroups;
+      const float f = s < ns ? sm.f[min(s, ns - 1)] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = fmaf(f, v[j][k], acc[k]);
-      }
+      for (int k = 0; k < 4; ++k) acc[k] = fmaf(f, v[j][k], acc[k]);
     }
   }
   sm.red[tid] = acc;
   __syncthreads();
-  // pairs may exceed the thread count (G = 16: 512 pairs, 2 groups): loop
-  for (int pp = tid; pp < pairs; pp += kCombThreads) {
+  if (tid < kD / 4) {
     floatx4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < nsg; ++k) {
-      const floatx4 r = sm.red[k * pairs + pp];
+#pragma unroll
+    for (int k = 0; k < kCombGroups; ++k) {
+      const floatx4 r = sm.red[k * (kD / 4) + tid];
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] += r[j];
     }
-    const int hh = pp / (kD / 4);
-    const int dd = pp % (kD / 4);
-    const float L = sm.lsum[hh];
+    const float L = sm.lsum;
     floatx4 res;
 #pragma unroll
     for (int j = 0; j < 4; ++j) res[j] = (ns > 0 && L > 0.f) ? o[j] / L : 0.f;
-    *(floatx4*)(out + ((size_t)b * Hq + (size_t)g * G + hh) * kD + 4 * dd) = res;
+    *(floatx4*)(out + ((size_t)b * Hq + (size_t)g * G + h) * kD + 4 * tid) = res;
   }
 }
 

@@ -178,7 +178,8 @@ __device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& g
 // bin compare values.
 template <int NT, int MAXV4, typename Present, typename Emit>
 __device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
-                                  float vmax, int n_valid, TopScratch& sh, Emit emit);
+                                  float vmax, int n_valid, TopScratch& sh, Emit emit,
+                                  bool hist_clear = false);
 
 template <int NT, int MAXV4, typename Present, typename Emit>
 __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P, TopScratch& sh,
@@ -232,15 +233,48 @@ __device__ int top_largest_lds(const float* sbuf, int n, Present present, int P,
 // The same selection with the range of the present scores given: vmin <=
 // every present score <= vmax, and n_valid = #present.  Each thread reads only
 // its own run of sbuf, so a caller that writes its own run needs no barrier
-// before the call.
+// before the call.  hist_clear: the caller has already zeroed sh.hist and
+// sh.list_n before a barrier (saving a barrier here).
+template <int NT, int NV4, typename Present, typename Emit>
+__device__ int top_largest_fixed(const float* sbuf, int n, Present present, int P, float vmin,
+                                 float vmax, int n_valid, TopScratch& sh, Emit& emit,
+                                 bool hist_clear);
+
+// Dispatch on the run length nv4 = ceil(n / (4 NT)) (block-uniform), so that
+// every per-slot loop is exactly as long as the live run: these passes are
+// vector-throughput bound, and dead slots cost as much as live ones.
 template <int NT, int MAXV4, typename Present, typename Emit>
 __device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
-                                  float vmax, int n_valid, TopScratch& sh, Emit emit) {
+                                  float vmax, int n_valid, TopScratch& sh, Emit emit,
+                                  bool hist_clear) {
+  static_assert(MAXV4 >= 1 && MAXV4 <= 8, "run length");
+  const int nv4 = max((n + 4 * NT - 1) / (4 * NT), 1);
+#define HHR_TOP_CASE(k)                                                                      \
+  if (MAXV4 >= (k) && nv4 == (k))                                                            \
+    return top_largest_fixed<NT, ((k) <= MAXV4 ? (k) : 1)>(sbuf, n, present, P, vmin, vmax, \
+                                                           n_valid, sh, emit, hist_clear);
+  HHR_TOP_CASE(1)
+  HHR_TOP_CASE(2)
+  HHR_TOP_CASE(3)
+  HHR_TOP_CASE(4)
+  HHR_TOP_CASE(5)
+  HHR_TOP_CASE(6)
+  HHR_TOP_CASE(7)
+  HHR_TOP_CASE(8)
+#undef HHR_TOP_CASE
+  return 0;  // unreachable for n <= 4 NT MAXV4
+}
+
+template <int NT, int NV4, typename Present, typename Emit>
+__device__ int top_largest_fixed(const float* sbuf, int n, Present present, int P, float vmin,
+                                 float vmax, int n_valid, TopScratch& sh, Emit& emit,
+                                 bool hist_clear) {
+  constexpr int MAXV4 = NV4;
   constexpr int MAXV = 4 * MAXV4;
   static_assert(MAXV <= 32, "2 class bits per slot in 64 bits");
   constexpr uint32_t kAbsent = 0xFFFFu;  // bin code of an absent slot
   const int tid = threadIdx.x;
-  const int nv4 = (n + 4 * NT - 1) / (4 * NT);
+  constexpr int nv4 = NV4;
   const int c0 = 4 * nv4 * tid;
   const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
   auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
@@ -248,9 +282,11 @@ __device__ int top_largest_ranged(const float* sbuf, int n, Present present, int
 
   const int Pe = min(P, n_valid);
   if (Pe <= 0) return 0;  // block-uniform
-  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
-  if (tid == 0) sh.list_n = 0;
-  __syncthreads();
+  if (!hist_clear) {
+    for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
+    if (tid == 0) sh.list_n = 0;
+    __syncthreads();
+  }
 
   // bins: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)) is monotone in v
   const float range = vmax - vmin;

@@ -200,6 +200,30 @@ def test_select_pages_equals_stages(run):
     assert torch.equal(qc, p.q_codes)
 
 
+@pytest.mark.parametrize("L,keep", [(150000, (1, 16, 0)), (262144, (1, 8, 0)),
+                                    (262000, (0, 1, 2000))])
+def test_long_context_top_pages(gpu_lib, L, keep):
+    """Contexts past 128K give every top-P thread 3 or 4 float4 runs of bounds: the staged
+    and one-launch top-P both equal the oracle's top-P of the GPU's own bounds."""
+    print(f"\n[gpu long-context top-P] L={L} keep={keep}", flush=True)
+    Lcap = -(-L // 16) * 16
+    inp = synth.make_hhr_inputs(1, 4, 1, [L], Lcap, "bf16", seed=31, make_v=False)
+    p = U.Pipeline(gpu_lib, inp, "bf16", 4, 1, Lcap, *keep, 64, with_v=False)
+    p.append_all()
+    p.encode_queries()
+    p.page_scores()
+    p.top_pages()
+    torch.cuda.synchronize()
+    Np = O.n_pages(L, 16)
+    P = O.keep_count(Np, *keep)
+    s = p.scores[0, 0, :Np].cpu().numpy().astype(np.float64)
+    want = O.top_pages(s, P).tolist()
+    assert int(p.kept_count[0, 0]) == P and p.kept[0, 0, :P].cpu().tolist() == want
+    kept, kc, qc = p.select_pages()
+    assert int(kc[0, 0]) == P and kept[0, 0, :P].cpu().tolist() == want
+    assert torch.equal(qc, p.q_codes)
+
+
 def test_chunked_append_equals_one_shot(gpu_lib):
     case = CASES[1]
     p = _pipeline(gpu_lib, case, with_v=False)
