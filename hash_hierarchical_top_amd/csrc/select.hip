@@ -86,12 +86,9 @@ __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
     uint16_t* __restrict__ dist, int* __restrict__ hist, uint16_t* __restrict__ cum) {
   __shared__ HamDistSmem sm;
   const int bg = blockIdx.y;
-  const int b = bg / Hkv;
-  const int L = checked_len(seq_len, b, Lcap, nullptr);
-  const int P = kept_pages(kept_count, bg, L, p_max);
-  if ((int)blockIdx.x >= ham_chunks(P)) return;
-  ham_dist_chunk<kHamDistThreads, false>(b, bg % Hkv, Hq, Hkv, Lcap, L, P, blockIdx.x, p_max,
-                                         q_codes, codes, kept, dist, hist, cum, sm);
+  ham_dist_chunk<kHamDistThreads, false>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, blockIdx.x, p_max,
+                                         seq_len, kept_count, q_codes, codes, kept, dist, hist,
+                                         cum, sm);
 }
 
 // Exact top-k of one (b, g) from its distances and chunk histograms.

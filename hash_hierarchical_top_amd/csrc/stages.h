@@ -355,7 +355,9 @@ __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den
 // For hhr_decode the distance stage also writes, per block of 256 candidates,
 // the cumulative histogram cum[blk][i] = #(H <= i) over the block's valid
 // candidates (u16), so that each attention workgroup can find the blocks that
-// hold its 64 output ranks from two entries per block (pick_window).
+// hold its 64 output ranks from two entries per block (pick_window).  (Stored
+// bin-major instead, the pick's loads coalesce but the 2-byte stores scatter
+// over a cache line each, which costs more than it saves.)
 constexpr int kHamBins = 128 * kMaxG + 1;  // 2049
 constexpr int kHistCopies = 4;
 constexpr int kHamChunk = kHamChunkPages * kPS;  // 1024 candidates
@@ -364,7 +366,6 @@ struct HamDistSmem {
   int hist[kHistCopies][kHamBins];
   int skept[kHamChunkPages];
   __attribute__((aligned(16))) uint32_t sq[kMaxG * kNW];
-  uint32_t uscan[17];
 };
 
 // 16-byte load; the coherent form is four agent-scope dword loads.
@@ -379,29 +380,42 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 }
 
 // Distances of chunk k of (b, g): candidates c in [1024k, 1024k + 1024) with
-// c < 16 P.  dist [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts
-// added atomically); cum (or NULL) [B][Hkv][ham_cum_blocks(p_max)][128 G + 1]
-// u16.  Item j of every thread lies in block 4k + j, whose histogram is LDS
-// copy j.  All threads call.
+// c < 16 P, P = the (b, g)'s kept count (nothing to do past it).  dist
+// [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts added
+// atomically); cum (or NULL) [B][Hkv][ham_cum_blocks(p_max)][128 G + 1] u16.
+// Item j of every thread lies in block 4k + j, whose histogram is LDS copy j.
+// All threads call.
 template <int NT, bool COH>
-__device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, int P, int k,
-                               int p_max, const uint32_t* q_codes,
-                               const uint32_t* __restrict__ codes, const int32_t* kept,
-                               uint16_t* dist, int* hist, uint16_t* cum, HamDistSmem& sm) {
+__device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, int p_max,
+                               const int32_t* seq_len, const int32_t* kept_count,
+                               const uint32_t* q_codes, const uint32_t* __restrict__ codes,
+                               const int32_t* kept, uint16_t* dist, int* hist, uint16_t* cum,
+                               HamDistSmem& sm) {
   constexpr int kItems = kHamChunk / NT;
   static_assert(NT == kCumBlock && kItems == kHistCopies, "item j = block j = LDS copy j");
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
+  const int l = tid & 63;
   const int nbins = 128 * G + 1;
-  const int Np = (L + kPS - 1) / kPS;
   const int page0 = k * kHamChunkPages;
+  // kept pages and query codes are loaded before the kept count is known
+  // (addresses clamped into the buffers), so they share its round trip
+  int kp = 0;
+  uint32_t qw = 0u;
+  if (tid < kHamChunkPages)
+    kp = Mem<COH>::ld(kept + (size_t)bg * p_max + min(page0 + tid, p_max - 1));
+  if (tid < G * kNW) qw = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * kNW + tid);
+  const int L0 = seq_len[b];
+  const int L = (L0 < 0 || L0 > Lcap) ? 0 : L0;
+  const int P = L > 0 ? max(0, min(kept_count[bg], p_max)) : 0;
+  if (page0 >= P) return;  // block-uniform
+  const int Np = (L + kPS - 1) / kPS;
   const int npg = min(kHamChunkPages, P - page0);
   const int ncl = npg * kPS;  // candidates in this chunk
-  if (tid < npg) sm.skept[tid] = Mem<COH>::ld(kept + (size_t)bg * p_max + page0 + tid);
-  if (tid < G * kNW)
-    sm.sq[tid] = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * kNW + tid);
+  if (tid < npg) sm.skept[tid] = kp;
+  if (tid < G * kNW) sm.sq[tid] = qw;
   for (int i = tid; i < kHistCopies * nbins; i += NT) sm.hist[i / nbins][i % nbins] = 0;
   __syncthreads();
 
@@ -442,26 +456,16 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int L, i
     for (int r = 0; r < kHistCopies; ++r) c += sm.hist[r][i];
     if (c != 0) atomicAdd(hb + i, c);  // device-scope: chunks run on every XCD
   }
-  if (cum == nullptr) return;  // block-uniform
-  // cumulative histograms of the chunk's blocks, two blocks per packed scan
-  // (a block's counts stay <= 256, so 16-bit halves cannot carry)
-  const int per = (nbins + NT - 1) / NT;
-  const int i0 = tid * per;
-  uint16_t* cb0 = cum + ((size_t)bg * ham_cum_blocks(p_max) + (size_t)k * kHistCopies) * nbins;
-#pragma unroll
-  for (int r = 0; r < kHistCopies; r += 2) {
-    if (r * kCumBlock >= ncl) break;  // block-uniform
-    uint32_t local = 0;
-    for (int i = i0; i < min(i0 + per, nbins); ++i)
-      local += (uint32_t)sm.hist[r][i] | ((uint32_t)sm.hist[r + 1][i] << 16);
-    uint32_t tot;
-    uint32_t run = block_exclusive_scan<NT, uint32_t>(local, sm.uscan, &tot);
-    for (int i = i0; i < min(i0 + per, nbins); ++i) {
-      run += (uint32_t)sm.hist[r][i] | ((uint32_t)sm.hist[r + 1][i] << 16);
-      cb0[(size_t)r * nbins + i] = (uint16_t)(run & 0xFFFFu);
-      if ((r + 1) * kCumBlock < ncl) cb0[(size_t)(r + 1) * nbins + i] = (uint16_t)(run >> 16);
-    }
-    __syncthreads();  // sm.uscan is reused by the next scan
+  // cumulative histogram of block 4k + w by wave w, 64 bins per wave scan, so
+  // each store instruction writes 128 contiguous bytes
+  if (cum == nullptr || w * kCumBlock >= ncl) return;  // wave-uniform; no barrier follows
+  uint16_t* row = cum + ((size_t)bg * ham_cum_blocks(p_max) + (size_t)k * kHistCopies + w) * nbins;
+  int carry = 0;
+  for (int i0 = 0; i0 < nbins; i0 += kWave) {
+    const int i = i0 + l;
+    const int incl = wave_inclusive_scan(i < nbins ? sm.hist[w][i] : 0) + carry;
+    if (i < nbins) row[i] = (uint16_t)incl;
+    carry = __builtin_amdgcn_readlane(incl, kWave - 1);
   }
 }
 
