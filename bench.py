@@ -276,12 +276,16 @@ def main():
     # last workgroup, kept pages and query codes written
     k_bytes = (meta_bytes + B * Hq * 128 * 4 + Hkv * 128 * 256 * 4 + n_pages_all * 8
                + int(P.sum()) * Hkv * 4 + B * Hq * 16)
+    # the library runs k_score_topp while the scoring grid is at most two rounds of
+    # one 1024-thread workgroup per CU, else the staged coarse launches
+    one_launch = -(-NpCap // 256) * B * Hkv <= 512
     roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.workload, args.meta),
-                "kernel": "k_score_topp", "bytes_per_launch": k_bytes,
-                "avg_launch_us": round(k_ms * 1e3, 3)}
+                "traffic": measured_traffic(args.workload, args.meta) if one_launch else None,
+                "kernel": "k_score_topp" if one_launch
+                else "hhr_select_pages (k_encode_queries + k_page_scores + k_top_pages)",
+                "bytes_per_launch": k_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}
 
     # the bound computation alone (staged k_page_scores, S3 only), for context
     q_rot = torch.zeros((B, Hq, 128), dtype=torch.float32, device=dev)

@@ -430,6 +430,7 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->status = status_of(workspace);
   buf->counters = reinterpret_cast<uint32_t*>(base + ws->counters);
   buf->scores = reinterpret_cast<float*>(base + ws->scores);
+  buf->q_rot = reinterpret_cast<float*>(base + ws->q_rot);
   buf->wave_range = reinterpret_cast<float2*>(base + ws->wave_range);
   buf->q_codes = reinterpret_cast<uint32_t*>(base + ws->q_codes);
   buf->kept = reinterpret_cast<int32_t*>(base + ws->kept);
@@ -528,15 +529,27 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
   if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
   hhr::Workspace ws;
   hhr::CompositeBuffers buf;
+  // Few attention workgroups: each picks its own keys (no selection launch).
+  // Many: the one-workgroup-per-(b, g) selection, then plain attention, which
+  // costs less than every workgroup repeating the pick.  Same results.
+  hhr::Workspace probe;
+  hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &probe);
+  const bool pick = (long long)shape->batch * shape->n_kv_heads * probe.n_split <=
+                    hhr::kPickInAttentionMaxWgs;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
-                      as_stream(stream), false, &ws, &buf));
-  char* base = static_cast<char*>(workspace);
-  HHR_LAUNCH(hhr::launch_attend_picked(*shape, q, k_cache, v_cache, seq_len, ws.p_max, top_k,
-                                       scale, sel_idx, sel_count, out,
-                                       reinterpret_cast<float*>(base + ws.attn_part), ws.n_split,
-                                       buf, as_stream(stream)),
-             "attend launch");
+                      as_stream(stream), !pick, &ws, &buf));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.attn_part);
+  if (pick)
+    HHR_LAUNCH(hhr::launch_attend_picked(*shape, q, k_cache, v_cache, seq_len, ws.p_max, top_k,
+                                         scale, sel_idx, sel_count, out, part, ws.n_split, buf,
+                                         as_stream(stream)),
+               "attend launch");
+  else
+    HHR_LAUNCH(hhr::launch_sparse_decode(*shape, q, k_cache, v_cache, sel_idx, sel_count, top_k,
+                                         scale, out, part, ws.n_split, buf.status,
+                                         as_stream(stream)),
+               "attend launch");
   return ok();
 }
 

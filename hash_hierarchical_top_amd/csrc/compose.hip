@@ -28,6 +28,9 @@ namespace hhr {
 namespace {
 
 constexpr int kScoreThreads = 1024;
+// k_score_topp runs one 1024-thread workgroup per CU; past two rounds of them
+// the coarse stage runs staged instead (query encode, bounds, top-P).
+constexpr int kScoreToppMaxWgs = 2 * 256;
 constexpr int kScorePagesPerWg = (kScoreThreads / kWave) * kScorePagesPerWave;  // 256
 
 __device__ __forceinline__ int clamped_len(const int32_t* seq_len, int b, int Lcap,
@@ -202,6 +205,17 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
+  if ((long long)grid.x * grid.y > kScoreToppMaxWgs) {
+    // many rounds of one-CU workgroups: the launch boundaries of the staged
+    // stages cost less than the latency each round would leave exposed
+    hipError_t e = launch_encode_queries(s, q, R, W, buf.q_rot, buf.q_codes, stream);
+    if (e == hipSuccess)
+      e = launch_page_scores(s, buf.q_rot, seq_len, meta, buf.scores, buf.status, stream);
+    if (e == hipSuccess)
+      e = launch_top_pages(s, buf.scores, seq_len, keep_num, keep_den, keep_abs, p_max, buf.kept,
+                           buf.kept_count, buf.status, stream);
+    return e;
+  }
   if (s.meta_dtype == HHR_BF16)
     hipLaunchKernelGGL(k_score_topp<true>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R, W,
                        meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,

@@ -33,6 +33,9 @@ struct HamScratch {
 };
 HamScratch ham_scratch(const hhr_shape& s, int32_t p_max);
 constexpr int kCountersPerGroup = 8;  // control words per (b, g) after the first 256 bytes
+// hhr_decode lets every attention workgroup pick its own keys while there are
+// at most this many of them (B * Hkv * top_k / 64), else it selects first.
+constexpr int kPickInAttentionMaxWgs = 1024;
 
 // Workspace of hhr_sparse_decode alone: control block, tickets, partials.
 struct AttnWorkspace {
@@ -84,6 +87,7 @@ struct CompositeBuffers {
   uint32_t* status;
   uint32_t* counters;
   float* scores;
+  float* q_rot;
   float2* wave_range;
   uint32_t* q_codes;
   int32_t* kept;

@@ -4,6 +4,7 @@ end to end (with excused-mismatch accounting), on small seeded cases that span
 several tiles, ragged tails, GQA 1/4/8, an empty-ish sequence and top_k above
 the candidate count.
 """
+import functools
 import math
 
 import numpy as np
@@ -222,6 +223,61 @@ def test_long_context_top_pages(gpu_lib, L, keep):
     kept, kc, qc = p.select_pages()
     assert int(kc[0, 0]) == P and kept[0, 0, :P].cpu().tolist() == want
     assert torch.equal(qc, p.q_codes)
+
+
+@functools.lru_cache(maxsize=1)
+def _wide_inputs(B, Hq, Hkv, Lcap):
+    rng = np.random.Generator(np.random.PCG64(41))
+    lens = rng.integers(1, Lcap + 1, B)
+    lens[0], lens[1] = Lcap, 17
+    return lens, synth.make_hhr_inputs(B, Hq, Hkv, lens.tolist(), Lcap, "bf16", seed=42)
+
+
+@pytest.mark.parametrize("meta_dtype", ["f32", "bf16"])
+def test_wide_batch_decode(gpu_lib, meta_dtype):
+    """33 sequences x 8 KV heads: 528 scoring workgroups and 1056 attention workgroups, past
+    the sizes where hhr_decode encodes the queries in a launch of their own and selects
+    before attending.  hhr_decode and hhr_select_pages equal the stage-by-stage run bit for
+    bit; sampled (b, g) pairs match the conditioned oracle."""
+    print(f"\n[gpu wide batch] meta={meta_dtype}", flush=True)
+    B, Hq, Hkv, Lcap, top_k = 33, 32, 8, 8192, 256
+    lens, inp = _wide_inputs(B, Hq, Hkv, Lcap)
+    p = U.Pipeline(gpu_lib, inp, "bf16", Hq, Hkv, Lcap, 1, 4, 0, top_k, meta_dtype=meta_dtype)
+    p.append_all()
+    p.encode_queries()
+    p.page_scores()
+    p.top_pages()
+    p.hamming_topk()
+    p.sparse_decode()
+    torch.cuda.synchronize()
+    sel = torch.zeros_like(p.sel)
+    sc = torch.zeros_like(p.sel_count)
+    out = torch.zeros_like(p.out)
+    p.decode(sel, sc, out)
+    torch.cuda.synchronize()
+    assert p.status() == 0
+    assert torch.equal(sel, p.sel) and torch.equal(sc, p.sel_count) and torch.equal(out, p.out)
+    kept, kc, qc = p.select_pages()
+    assert torch.equal(kept, p.kept) and torch.equal(kc, p.kept_count)
+    assert torch.equal(qc, p.q_codes)
+    codes, q_codes = U.u32(p.codes), U.u32(p.q_codes)
+    for b, g in [(0, 0), (1, 3), (int(np.argmax(lens[2:])) + 2, 7), (B - 1, 5)]:
+        L = int(lens[b])
+        Np = O.n_pages(L, 16)
+        qr = p.q_rot[b, g * p.G:(g + 1) * p.G].cpu().numpy().astype(np.float64)
+        s = p.scores[b, g, :Np].cpu().numpy().astype(np.float64)
+        meta = p.meta_host(b, g, Np)
+        mag = (np.abs(qr).sum(0)[None, :] * np.abs(meta).max(-1)).sum(-1)
+        assert np.all(np.abs(s - O.page_scores(qr, meta)) <= 1e-5 * mag + 1e-30)
+        P = O.keep_count(Np, 1, 4, 0)
+        assert p.kept[b, g, :P].cpu().tolist() == O.top_pages(s, P).tolist()
+        res = O.select_from_codes(q_codes[b, g * p.G:(g + 1) * p.G], codes[b, g],
+                                  p.kept[b, g, :P].cpu().numpy(), L, 16, top_k)
+        n = len(res["sel"])
+        assert int(p.sel_count[b, g]) == n and p.sel[b, g, :n].cpu().tolist() == res["sel"].tolist()
+        want = O.attend(p.q_group(b, g), p.K_valid(b, g)[res["sel"]], p.V_valid(b, g)[res["sel"]],
+                        p.scale)
+        assert np.abs(p.out[b, g * p.G:(g + 1) * p.G].cpu().numpy() - want).max() <= 2e-3
 
 
 def test_chunked_append_equals_one_shot(gpu_lib):
