@@ -120,7 +120,35 @@ def _rotate_transposed(x, R):
     return np.asarray(x, np.float64) @ np.asarray(R, np.float64).T
 
 
+def _bf16_round_fine(v, up):
+    """one bit too many: a grid of 9 significant bits"""
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(np.abs(v))
+    ulp = np.exp2(np.maximum(e - 1, -126) - 8.0)
+    return (np.ceil(v / ulp) if up else np.floor(v / ulp)) * ulp
+
+
+def _bf16_round_toward_zero(v, up):
+    """directions applied to the magnitude: negative values round the wrong way"""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    ulp = np.exp2(np.maximum(e - 1, -126) - 7.0)
+    return np.sign(v) * (np.ceil(a / ulp) if up else np.floor(a / ulp)) * ulp
+
+
+def _outward_inward(meta):
+    meta = np.asarray(meta, np.float64)
+    out = np.empty_like(meta)
+    out[..., 0] = O.bf16_round(meta[..., 0], up=True)
+    out[..., 1] = O.bf16_round(meta[..., 1], up=False)
+    return out
+
+
 MUTANTS = [
+    ("bf16_round", _bf16_round_fine),
+    ("bf16_round", _bf16_round_toward_zero),
+    ("bf16_outward", _outward_inward),
     ("page_scores", _scores_drop_head),
     ("page_scores", _scores_swapped),
     ("page_scores", _scores_sum_query),
