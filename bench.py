@@ -108,7 +108,7 @@ def main():
 
     import torch
 
-    from hash_hierarchical_top_amd import hhr, synth
+    from hash_hierarchical_top_amd import hhr, quality, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hhr.load()
@@ -308,16 +308,12 @@ def main():
         torch.cuda.synchronize()
 
     # ---- top-k recall against exact q.k top-k (per KV head, as in HHR Figure 4) on 2 heads
-    from oracle import hhr as O
-
     sel_h = sel.cpu().numpy()
     recalls, planted_hits = [], []
     for g in (0, Hkv - 1):
         L = int(seq_np[0])
-        Kg = synth.kv_values(inp["K"][0, g, :L], w.kv_dtype)
-        qg = inp["q"][0, g * G:(g + 1) * G]
-        exact = O.exact_topk(qg, Kg, top_k)
-        recalls.append(O.recall(sel_h[0, g, :int(cnt[0, g])], exact))
+        exact = quality.exact_topk(q[0, g * G:(g + 1) * G], K0[0, g, :L], top_k)
+        recalls.append(quality.overlap(sel_h[0, g, :int(cnt[0, g])], exact.cpu().numpy()))
         planted_hits.append(np.isin(inp["planted"][0, g], sel_h[0, g]).mean())
 
     # ---- CPU baseline: the oracle's decode step (encoded keys prepared beforehand)
@@ -354,6 +350,8 @@ def main():
 
 
 def main_hisa(args, torch, hhr, synth, dev):
+    from hash_hierarchical_top_amd import quality
+
     """HISA decode step: hhr_hisa_select (block scores, top blocks, fp8 token scores,
     token top-k) then hhr_sparse_decode with the attention heads on one KV head."""
     w = synth.HISA_WORKLOADS[args.workload]
@@ -474,14 +472,11 @@ def main_hisa(args, torch, hhr, synth, dev):
                 "bytes_per_launch": k_bytes, "avg_launch_us": round(k_ms * 1e3, 3),
                 "note": "latency-bound: ~1 MB per launch"}
 
-    # ---- selection quality and CPU baseline (oracle select + attention, 1 thread)
-    from oracle import hhr as OH
-    from oracle import hisa as OS
-
+    # ---- selection quality, then the CPU baseline (oracle select + attention, 1 thread)
     sel_h = sel.cpu().numpy()[0, 0, :n_sel]
-    flat = OS.flat_select(inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], L,
-                          w.top_k)
-    iou = OS.iou(sel_h, flat)
+    flat = quality.flat_indexer_topk(inp["q8"], inp["q_scale"], inp["w"], inp["k8"],
+                                     inp["k_scale"], L, w.top_k, dev)
+    iou_flat = quality.iou(sel_h, flat)
     # the same on the planted-block variant: 16 blocks whose keys lean towards the index
     # queries' mean direction, i.e. data with block structure for the coarse stage to find
     pin = synth.make_hisa_workload_inputs(args.workload, planted_blocks=16, make_kv=False)
@@ -492,12 +487,16 @@ def main_hisa(args, torch, hhr, synth, dev):
                         pks, preps, seq, w.keep_blocks, w.top_k, sel.view(1, w.top_k),
                         cnt.view(1), ws_h)
     torch.cuda.synchronize()
-    iou_planted = OS.iou(sel.cpu().numpy()[0, 0, :int(cnt.item())],
-                         OS.flat_select(pin["q8"], pin["q_scale"], pin["w"], pin["k8"],
-                                        pin["k_scale"], L, w.top_k))
+    iou_planted = quality.iou(sel.cpu().numpy()[0, 0, :int(cnt.item())],
+                              quality.flat_indexer_topk(pin["q8"], pin["q_scale"], pin["w"],
+                                                        pin["k8"], pin["k_scale"], L, w.top_k,
+                                                        dev))
     cpu = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
+
+        from oracle import hhr as OH
+        from oracle import hisa as OS
 
         Kf = synth.bf16_bits_to_f32(inp["K"][0, 0])
         Vf = synth.bf16_bits_to_f32(inp["V"][0, 0])
@@ -530,7 +529,7 @@ def main_hisa(args, torch, hhr, synth, dev):
         "cpu_baseline": cpu,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (ms_per_step * 1e6), 1),
-        "iou_vs_flat_indexer": round(float(iou), 4),
+        "iou_vs_flat_indexer": round(float(iou_flat), 4),
         "iou_vs_flat_indexer_planted_blocks": round(float(iou_planted), 4),
         "pool_prefill_ms": round(float(np.median(pool_ms[1:] if len(pool_ms) > 1 else pool_ms)), 4),
         "wall_s_timed": round(wall, 3),
