@@ -89,9 +89,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", type=int, default=1, help="replay the rotation as one HIP graph")
-    ap.add_argument("--path", choices=("decode", "staged"), default="decode",
+    ap.add_argument("--path", choices=("decode", "staged", "append", "append_then_decode"),
+                    default="decode",
                     help="decode: one hhr_decode call per step; staged: hhr_select then "
-                         "hhr_sparse_decode")
+                         "hhr_sparse_decode; append: hhr_decode_append (the step also encodes "
+                         "the sequence's last key, idempotent when replayed); "
+                         "append_then_decode: hhr_append_keys of that key, then hhr_decode")
     ap.add_argument("--meta", choices=("f32", "bf16"), default="f32",
                     help="page metadata format: f32 min/max, or bfloat16 rounded outward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -176,9 +179,20 @@ def main():
            "mfma_util_vs_bf16_peak": round(passes * enc_flops / enc_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
            "bytes": enc_bytes, "flops": enc_flops}
 
+    last = (seq - 1).clamp(min=0)
+    one = (seq > 0).to(torch.int32)
+
     def step(i):
         lay = layers[i % args.layers]
         if args.path == "decode":
+            hhr.hhr_decode(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"],
+                           lay["K"], lay["V"], *keep, top_k, scale, sel, cnt, out, ws)
+        elif args.path == "append":
+            hhr.hhr_decode_append(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"],
+                                  lay["K"], lay["V"], *keep, top_k, scale, sel, cnt, out, ws)
+        elif args.path == "append_then_decode":
+            hhr.hhr_append_keys(shape, lay["K"], last, one, 1, lay["R"], lay["W"], lay["codes"],
+                                lay["meta"], ws)
             hhr.hhr_decode(shape, q, seq, lay["R"], lay["W"], lay["codes"], lay["meta"],
                            lay["K"], lay["V"], *keep, top_k, scale, sel, cnt, out, ws)
         else:
@@ -332,8 +346,9 @@ def main():
                    "keep": f"{keep[0]}/{keep[1]}" if keep[2] == 0 else keep[2], "top_k": top_k,
                    "meta_dtype": args.meta,
                    "layers_rotated": args.layers, "hip_graph": bool(graph is not None),
-                   "entry": "hhr_decode" if args.path == "decode"
-                   else "hhr_select+hhr_sparse_decode"},
+                   "entry": {"decode": "hhr_decode", "staged": "hhr_select+hhr_sparse_decode",
+                             "append": "hhr_decode_append",
+                             "append_then_decode": "hhr_append_keys+hhr_decode"}[args.path]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "page_scores_only": scorer_only,

@@ -260,7 +260,7 @@ const char* hhr_status_string(int32_t status) {
 
 const char* hhr_last_error(void) { return g_err; }
 
-int32_t hhr_abi_version(void) { return 2; }
+int32_t hhr_abi_version(void) { return 3; }
 
 int32_t hhr_keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den,
                        int32_t keep_pages_abs) {
@@ -476,7 +476,8 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
                               int32_t keep_abs, int32_t top_k, int32_t* sel_idx,
                               int32_t* sel_count, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, bool finish, hhr::Workspace* layout,
-                              hhr::CompositeBuffers* bufs) {
+                              hhr::CompositeBuffers* bufs,
+                              const hhr::AppendArgs* app = nullptr) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_keep(keep_num, keep_den, keep_abs));
   HHR_TRY(check_top_k(top_k));
@@ -495,7 +496,7 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
                             workspace_bytes, &ws, &buf));
   HHR_LAUNCH(hhr::launch_select_composite(*shape, q, seq_len, R, W, codes, page_meta, keep_num,
                                           keep_den, keep_abs, ws.p_max, top_k, sel_idx,
-                                          sel_count, buf, finish, stream),
+                                          sel_count, buf, finish, stream, app),
              "select launch");
   *layout = ws;
   *bufs = buf;
@@ -516,17 +517,20 @@ hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq
   return ok();
 }
 
-hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
-                      const float* R, const float* W, const uint32_t* codes,
-                      const void* page_meta, const void* k_cache, const void* v_cache,
-                      int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
-                      float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                              const float* R, const float* W, const uint32_t* codes,
+                              const void* page_meta, const void* k_cache, const void* v_cache,
+                              int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                              int32_t top_k, float scale, int32_t* sel_idx, int32_t* sel_count,
+                              float* out, void* workspace, size_t workspace_bytes, void* stream,
+                              bool append) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_ptr(k_cache, "k_cache"));
   HHR_TRY(check_ptr(v_cache, "v_cache"));
   HHR_TRY(check_ptr(out, "out"));
   if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
+  // The append writes the new rows' codes and page metadata in place.
+  hhr::AppendArgs app{k_cache, const_cast<uint32_t*>(codes), const_cast<void*>(page_meta)};
   hhr::Workspace ws;
   hhr::CompositeBuffers buf;
   // Few attention workgroups: each picks its own keys (no selection launch).
@@ -538,7 +542,7 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
                     hhr::kPickInAttentionMaxWgs;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
-                      as_stream(stream), !pick, &ws, &buf));
+                      as_stream(stream), !pick, &ws, &buf, append ? &app : nullptr));
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.attn_part);
   if (pick)
     HHR_LAUNCH(hhr::launch_attend_picked(*shape, q, k_cache, v_cache, seq_len, ws.p_max, top_k,
@@ -551,6 +555,28 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
                                          as_stream(stream)),
                "attend launch");
   return ok();
+}
+
+hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                      const float* R, const float* W, const uint32_t* codes,
+                      const void* page_meta, const void* k_cache, const void* v_cache,
+                      int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
+                      float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(shape, q, seq_len, R, W, codes, page_meta, k_cache, v_cache, keep_num,
+                     keep_den, keep_pages_abs, top_k, scale, sel_idx, sel_count, out, workspace,
+                     workspace_bytes, stream, false);
+}
+
+hhr_status hhr_decode_append(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                             const float* R, const float* W, uint32_t* codes, void* page_meta,
+                             const void* k_cache, const void* v_cache, int32_t keep_num,
+                             int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
+                             float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(shape, q, seq_len, R, W, codes, page_meta, k_cache, v_cache, keep_num,
+                     keep_den, keep_pages_abs, top_k, scale, sel_idx, sel_count, out, workspace,
+                     workspace_bytes, stream, true);
 }
 
 

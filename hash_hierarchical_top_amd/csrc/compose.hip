@@ -62,6 +62,7 @@ struct ScoreTopSmem {
     struct {
       QencSmem qe;
       float qrot[kMaxG][kD];
+      float xnew[kD];  // the appended key's rotation (APPEND)
     } rot;
     struct {
       __attribute__((aligned(16))) float sbuf[kMaxCtx / kPS];
@@ -70,14 +71,74 @@ struct ScoreTopSmem {
   };
 };
 
+// Folds the appended key's rotation x (LDS, 128 dims) into page pn's metadata
+// held by this wave (score_load's lane layout), or makes it the page's only row
+// when it opens the page, and stores the page back.  f32: {min, max} per dim;
+// bf16: min rounded down, max rounded up, merged as bf16 values (the rounding
+// is monotone, so this equals rounding the merged f32 values).
+template <bool MBF>
+__device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, int pb, bool opens,
+                                                   const float* x, void* meta,
+                                                   PageLoads<1>& pl) {
+  const int l = threadIdx.x & 63;
+  const int r = l >> 4;
+  const int sub = l & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (pb + 4 * j + r != pn) continue;
+    if constexpr (MBF) {
+      uint32_t* dst = (uint32_t*)meta + ((size_t)bg * NpCap + pn) * kD + 4 * sub;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        floatx4 piece = pl.m[0][j][k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = x[4 * sub + 64 * k + i];
+          uint32_t lo = f32_to_bf16_down(v), hi = f32_to_bf16_up(v);
+          if (!opens) {
+            const uint32_t w = __float_as_uint(piece[i]);
+            if (bf16_to_f32(w & 0xFFFFu) < bf16_to_f32(lo)) lo = w & 0xFFFFu;
+            if (bf16_to_f32(w >> 16) > bf16_to_f32(hi)) hi = w >> 16;
+          }
+          piece[i] = __uint_as_float(lo | (hi << 16));
+        }
+        pl.m[0][j][k] = piece;
+        *(floatx4*)(dst + 64 * k) = piece;
+      }
+    } else {
+      float* dst = (float*)meta + ((size_t)bg * NpCap + pn) * kD * 2 + 4 * sub;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        floatx4 piece = pl.m[0][j][k];  // {mn[d0], mx[d0], mn[d1], mx[d1]}
+        const float x0 = x[2 * sub + 32 * k], x1 = x[2 * sub + 32 * k + 1];
+        piece[0] = opens ? x0 : fminf(piece[0], x0);
+        piece[1] = opens ? x0 : fmaxf(piece[1], x0);
+        piece[2] = opens ? x1 : fminf(piece[2], x1);
+        piece[3] = opens ? x1 : fmaxf(piece[3], x1);
+        pl.m[0][j][k] = piece;
+        *(floatx4*)(dst + 64 * k) = piece;
+      }
+    }
+  }
+}
+
 // S2 + S3 + S4.  grid (ceil(NpCap / 256), B*Hkv), 1024 threads: 16 waves x 16
 // pages.  Each workgroup rotates its group's queries itself (64 KiB of R from
 // L2, issued after its metadata loads so both are in flight together);
 // workgroup 0 of each (b, g) also writes the query codes.
-template <bool MBF>
+//
+// APPEND: row L - 1 of every sequence is a key appended since the last encode
+// (its K row is in kcache).  The workgroup that holds the last page encodes
+// it with its queries (rotation and code bits, the same per-column sums),
+// writes its code, and the wave that holds the page folds it into the page's
+// {min, max} (or starts the page with it) in registers before the bound, and
+// stores the page's metadata back.  Nothing else touches that page, so no
+// other workgroup can see it half-updated.
+template <bool MBF, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
-    const float* __restrict__ R, const float* __restrict__ W, const void* __restrict__ meta,
+    const float* __restrict__ R, const float* __restrict__ W, void* __restrict__ meta,
+    const void* __restrict__ kcache, int kv_f32, uint32_t* __restrict__ codes,
     int keep_num, int keep_den, int keep_abs, int p_max, int Hq, int Hkv, int Lcap,
     float* __restrict__ scores, float2* __restrict__ wave_range,
     uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
@@ -99,7 +160,31 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   PageLoads<1> pl;
   if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
-  if (blockIdx.x == 0) {
+  // the workgroup holding the last page, when a key was appended (block-uniform)
+  const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / kScorePagesPerWg;
+  if (owner) {
+    const size_t krow = ((size_t)bg * Lcap + (size_t)(L - 1)) * kD;
+    const void* key = kv_f32 ? (const void*)((const float*)kcache + krow)
+                             : (const void*)((const uint16_t*)kcache + krow);
+    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
+    uint32_t* crow = codes + ((size_t)bg * Lcap + (size_t)(L - 1)) * kNW;
+    auto rot_key = [&](int h, int col, float v) {
+      if (h < G)
+        sm.rot.qrot[h][col] = v;
+      else
+        sm.rot.xnew[col] = v;
+    };
+    auto code_key = [&](int h, int word, uint32_t bits) {
+      if (h == G)
+        crow[word] = bits;
+      else if (blockIdx.x == 0)
+        q_codes[cbase + (size_t)h * kNW + word] = bits;
+    };
+    qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, rot_key, code_key, key,
+                                     kv_f32 != 0);
+    if (wave_has && pb + kScorePagesPerWave > Np - 1)  // wave-uniform: the last page's wave
+      merge_appended_row<MBF>(bg, NpCap, Np - 1, pb, (L - 1) % kPS == 0, sm.rot.xnew, meta, pl);
+  } else if (blockIdx.x == 0) {
     const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
     qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
                       [&](int h, int word, uint32_t bits) {
@@ -201,14 +286,19 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_merge(
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
-                             const CompositeBuffers& buf, hipStream_t stream) {
+                             const CompositeBuffers& buf, hipStream_t stream,
+                             const AppendArgs* app) {
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
   if ((long long)grid.x * grid.y > kScoreToppMaxWgs) {
     // many rounds of one-CU workgroups: the launch boundaries of the staged
     // stages cost less than the latency each round would leave exposed
-    hipError_t e = launch_encode_queries(s, q, R, W, buf.q_rot, buf.q_codes, stream);
+    hipError_t e = hipSuccess;
+    if (app)
+      e = launch_append_last_row(s, app->k_cache, seq_len, R, W, app->codes, app->meta,
+                                 buf.status, stream);
+    if (e == hipSuccess) e = launch_encode_queries(s, q, R, W, buf.q_rot, buf.q_codes, stream);
     if (e == hipSuccess)
       e = launch_page_scores(s, buf.q_rot, seq_len, meta, buf.scores, buf.status, stream);
     if (e == hipSuccess)
@@ -216,16 +306,25 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
                            buf.kept_count, buf.status, stream);
     return e;
   }
-  if (s.meta_dtype == HHR_BF16)
-    hipLaunchKernelGGL(k_score_topp<true>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R, W,
-                       meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
-                       s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept,
-                       buf.kept_count, buf.counters, buf.status);
+  void* m = app ? app->meta : const_cast<void*>(meta);  // written only with APPEND
+  const void* kc = app ? app->k_cache : nullptr;
+  uint32_t* cd = app ? app->codes : nullptr;
+  const int kf32 = s.kv_dtype == HHR_F32;
+#define HHR_SCORE_TOPP(MBF, APP)                                                                 \
+  hipLaunchKernelGGL((k_score_topp<MBF, APP>), grid, dim3(kScoreThreads), 0, stream, q, seq_len, \
+                     R, W, m, kc, kf32, cd, keep_num, keep_den, keep_abs, p_max, s.n_q_heads,    \
+                     s.n_kv_heads, s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept, \
+                     buf.kept_count, buf.counters, buf.status)
+  const bool mbf = s.meta_dtype == HHR_BF16;
+  if (mbf && app)
+    HHR_SCORE_TOPP(true, true);
+  else if (mbf)
+    HHR_SCORE_TOPP(true, false);
+  else if (app)
+    HHR_SCORE_TOPP(false, true);
   else
-    hipLaunchKernelGGL(k_score_topp<false>, grid, dim3(kScoreThreads), 0, stream, q, seq_len, R,
-                       W, meta, keep_num, keep_den, keep_abs, p_max, s.n_q_heads, s.n_kv_heads,
-                       s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept,
-                       buf.kept_count, buf.counters, buf.status);
+    HHR_SCORE_TOPP(false, false);
+#undef HHR_SCORE_TOPP
   return hipGetLastError();
 }
 
@@ -235,9 +334,9 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const AppendArgs* app) {
   hipError_t e = launch_score_topp(s, q, seq_len, R, W, meta, keep_num, keep_den, keep_abs,
-                                   p_max, buf, stream);
+                                   p_max, buf, stream, app);
   if (e != hipSuccess) return e;
   if (finish)
     return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,

@@ -35,8 +35,10 @@ __global__ __launch_bounds__(256) void k_append_encode(
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
-  const int s = start[b];
-  const int n = n_new[b];
+  // n_new NULL: start holds seq_len and the one row seq_len - 1 is new
+  const int s = n_new ? start[b] : start[b] - 1;
+  const int n = n_new ? n_new[b] : (start[b] > 0 ? 1 : 0);
+  if (n_new == nullptr && start[b] == 0) return;
   if (s < 0 || n < 0 || (long long)s + n > Lcap) {
     if (threadIdx.x == 0 && blockIdx.x == 0 && g == 0 && status)
       atomicOr(status, HHR_DEV_BAD_SEQ_LEN);
@@ -238,6 +240,13 @@ hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int
                        R, W, codes, meta, s.meta_dtype == HHR_BF16, status, s.n_kv_heads,
                        s.max_ctx, tpw);
   return hipGetLastError();
+}
+
+hipError_t launch_append_last_row(const hhr_shape& s, const void* k_cache,
+                                  const int32_t* seq_len, const float* R, const float* W,
+                                  uint32_t* codes, void* meta, uint32_t* status,
+                                  hipStream_t stream) {
+  return launch_append_keys(s, k_cache, seq_len, nullptr, 1, R, W, codes, meta, status, stream);
 }
 
 hipError_t launch_encode_queries(const hhr_shape& s, const float* q, const float* R,

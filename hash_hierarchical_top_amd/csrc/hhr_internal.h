@@ -96,18 +96,33 @@ struct CompositeBuffers {
   int* chist;
   uint16_t* cum;  // per-block cumulative H histograms (hhr_decode's pick)
 };
-// k_score_topp alone (S2..S4): kept pages, counts and query codes into buf.
+// A key appended at row seq_len[b] - 1 of every sequence, to be encoded (its
+// code and its page's metadata) by the coarse stage before it bounds the page.
+struct AppendArgs {
+  const void* k_cache;
+  uint32_t* codes;
+  void* meta;
+};
+
+// k_score_topp alone (S2..S4): kept pages, counts and query codes into buf;
+// with app, the appended keys are encoded first.
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
-                             const CompositeBuffers& buf, hipStream_t stream);
+                             const CompositeBuffers& buf, hipStream_t stream,
+                             const AppendArgs* app = nullptr);
+// S1 for the single row seq_len[b] - 1 of every sequence with seq_len[b] >= 1.
+hipError_t launch_append_last_row(const hhr_shape& s, const void* k_cache,
+                                  const int32_t* seq_len, const float* R, const float* W,
+                                  uint32_t* codes, void* meta, uint32_t* status,
+                                  hipStream_t stream);
 hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int32_t* seq_len,
                                    const float* R, const float* W, const uint32_t* codes,
                                    const void* meta, int32_t keep_num, int32_t keep_den,
                                    int32_t keep_abs, int32_t p_max, int32_t top_k,
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const AppendArgs* app = nullptr);
 // S6 + S7 for hhr_decode after launch_select_composite(..., finish = false):
 // every attention workgroup picks its own chunk of the selection.
 hipError_t launch_attend_picked(const hhr_shape& s, const float* q, const void* k_cache,

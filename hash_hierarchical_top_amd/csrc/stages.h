@@ -24,23 +24,26 @@ namespace hhr {
 // holds 16 CPT matrix values in registers and the result does not depend on
 // NT or on NCOL (256: rotation and codes; 128: rotation only).
 // rot(h, col, v) receives q'; code(h, word, bits) receives 32 code bits.
-// Every thread of the workgroup must call (barriers).
+// With extra_row (a KF32/bf16 key row of length 128, or NULL) it is encoded
+// the same way as row h = G after the G queries.  Every thread of the
+// workgroup must call (barriers).
 constexpr int kQeThreads = 512;
+constexpr int kQeChunk = 4;  // rows (query heads, then the extra key) per reduction round
 
 struct QencSmem {
-  float sq[kMaxG][kD];
-  float red[8][4][2 * kD];
+  float sq[kMaxG + 1][kD];
+  float red[8][kQeChunk][2 * kD];
 };
 
 template <int NCOL, int NT, typename Rot, typename Code>
 __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
                           const float* __restrict__ R, const float* __restrict__ W,
-                          QencSmem& sm, Rot rot, Code code) {
+                          QencSmem& sm, Rot rot, Code code, const void* extra_row = nullptr,
+                          bool extra_f32 = false) {
   static_assert(NCOL == kD || NCOL == 2 * kD, "rotation, or rotation and codes");
   constexpr int CPT = 8 * NCOL / NT;  // columns per thread
   static_assert(CPT == 1 || CPT == 2 || CPT == 4, "8 NCOL / NT columns per thread");
   constexpr int kGroupsC = NCOL / CPT;
-  constexpr int kOut = 4 * NCOL;  // outputs per 4-head chunk
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
@@ -65,14 +68,19 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
     }
   }
   for (int i = tid; i < G * kD; i += NT) sm.sq[i / kD][i % kD] = q[qbase + i];
+  const int rows = G + (extra_row != nullptr ? 1 : 0);  // block-uniform
+  if (extra_row != nullptr && tid < kD)
+    sm.sq[G][tid] = extra_f32 ? ((const float*)extra_row)[tid]
+                              : bf16_to_f32(((const uint16_t*)extra_row)[tid]);
   __syncthreads();
-  for (int hc = 0; hc < G; hc += 4) {
+  constexpr int kOut = kQeChunk * NCOL;  // outputs per round
+  for (int hc = 0; hc < rows; hc += kQeChunk) {
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
+    for (int hh = 0; hh < kQeChunk; ++hh) {
       float acc[CPT];
 #pragma unroll
       for (int k = 0; k < CPT; ++k) acc[k] = 0.f;
-      if (hc + hh < G) {
+      if (hc + hh < rows) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float x = sm.sq[hc + hh][16 * dg + j];
@@ -86,7 +94,7 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < (kOut + NT - 1) / NT; ++pass) {
-      const int o = tid + NT * pass;  // (head hh, column col) of this chunk
+      const int o = tid + NT * pass;  // (row hh, column col) of this round
       if (o >= kOut) break;           // wave-uniform: kOut is a multiple of 64
       const int hh = o / NCOL;
       const int col = o % NCOL;
@@ -95,10 +103,10 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
       for (int k = 0; k < 8; ++k) v += sm.red[k][hh][col];
       const int h = hc + hh;
       if (col < kD) {
-        if (h < G) rot(h, col, v);
+        if (h < rows) rot(h, col, v);
       } else {
         const uint64_t bits = __ballot(v >= 0.0f);
-        if ((tid & 63) == 0 && h < G) {
+        if ((tid & 63) == 0 && h < rows) {
           const int word = (col - kD) >> 5;  // col is the wave's first column here
           code(h, word, (uint32_t)bits);
           code(h, word + 1, (uint32_t)(bits >> 32));

@@ -266,6 +266,26 @@ hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq
                       float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* hhr_decode_append: the decode step of a sequence that has just appended one
+ * token (S1 for that token, then S2..S7), in the same launches as hhr_decode.
+ * Row seq_len[b] - 1 of every sequence with seq_len[b] >= 1 is the new key:
+ * the caller has written its K row into k_cache (and its V row into v_cache);
+ * rows [0, seq_len[b] - 1) must have been encoded before (hhr_append_keys or an
+ * earlier step).  The call writes the new row's code into `codes` and folds its
+ * rotated key into its page's metadata in `page_meta` (or starts the page with
+ * it), exactly what hhr_append_keys with start = seq_len - 1, n_new = 1 stores up
+ * to rounding: the new row's rotation and projection are f32 sums (not the
+ * encoder's bf16-split MFMA products), within about 2^-19 of the exact value
+ * relative to sum_d |k_d M_dj|.  Then it selects and attends as hhr_decode over all
+ * seq_len[b] keys.                     [HHR abstract: GKR, LHP; decode step]
+ * Arguments as for hhr_decode; codes and page_meta are read and written. */
+hhr_status hhr_decode_append(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                             const float* R, const float* W, uint32_t* codes, void* page_meta,
+                             const void* k_cache, const void* v_cache, int32_t keep_num,
+                             int32_t keep_den, int32_t keep_pages_abs, int32_t top_k,
+                             float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ================================================================ HISA  */
 /* Shape of a HISA indexer: per query, n_index_heads fp8 index heads of
  * head_dim 128 scored against one fp8 index key per past token; blocks of

@@ -280,6 +280,92 @@ def test_wide_batch_decode(gpu_lib, meta_dtype):
         assert np.abs(p.out[b, g * p.G:(g + 1) * p.G].cpu().numpy() - want).max() <= 2e-3
 
 
+def _check_decode_append(p, lens, meta_dtype, codes0, meta0, sel, sc, out, pairs):
+    """After hhr_decode_append: the new rows' codes and their pages' metadata against the
+    oracle, everything else untouched, and the staged stages on the updated cache equal
+    the fused call's selection and output bit for bit."""
+    codes, codes_before = U.u32(p.codes), U.u32(codes0)
+    for b, g in pairs:
+        L = int(lens[b])
+        if L == 0:
+            continue
+        K = p.K_valid(b, g)
+        U.check_code_bits(K[L - 1:L], p.inp["W"][g], codes[b, g, L - 1:L])
+        assert np.array_equal(np.delete(codes[b, g], L - 1, axis=0),
+                              np.delete(codes_before[b, g], L - 1, axis=0))
+        Np = O.n_pages(L, 16)
+        pn = Np - 1
+        Kp = K[pn * 16:L]
+        R = p.inp["R"][g].astype(np.float64)
+        ex = O.page_minmax(O.rotate(Kp, R), 16)[0]
+        tol = 3e-5 * (np.abs(Kp) @ np.abs(R)).max()
+        got = p.meta_host(b, g, Np)[pn]
+        if meta_dtype == "f32":
+            assert np.abs(got - ex).max() <= tol, (b, g)
+        else:
+            assert np.all(O.bf16_round(ex[:, 0] - tol, up=False) <= got[:, 0])
+            assert np.all(got[:, 0] <= O.bf16_round(ex[:, 0] + tol, up=False))
+            assert np.all(O.bf16_round(ex[:, 1] - tol, up=True) <= got[:, 1])
+            assert np.all(got[:, 1] <= O.bf16_round(ex[:, 1] + tol, up=True))
+        assert torch.equal(p.meta[b, g, :pn], meta0[b, g, :pn]) and \
+            torch.equal(p.meta[b, g, pn + 1:], meta0[b, g, pn + 1:])
+    p.encode_queries()
+    p.page_scores()
+    p.top_pages()
+    p.hamming_topk()
+    p.sparse_decode()
+    torch.cuda.synchronize()
+    assert torch.equal(sel, p.sel) and torch.equal(sc, p.sel_count) and torch.equal(out, p.out)
+
+
+def _decode_append_run(H, p):
+    """Encode every row but each sequence's last, then one fused append + decode step."""
+    lens = p.inp["seq_len"].astype(np.int64)
+    start = torch.zeros(p.B, dtype=torch.int32, device="cuda")
+    n_new = torch.from_numpy(np.maximum(lens - 1, 0).astype(np.int32)).cuda()
+    H.hhr_append_keys(p.shape, p.d["K"], start, n_new, int(max(lens.max() - 1, 0)), p.d["R"],
+                      p.d["W"], p.codes, p.meta, p.ws)
+    torch.cuda.synchronize()
+    codes0, meta0 = p.codes.clone(), p.meta.clone()
+    sel = torch.zeros_like(p.sel)
+    sc = torch.zeros_like(p.sel_count)
+    out = torch.zeros_like(p.out)
+    H.hhr_decode_append(p.shape, p.d["q"], p.d["seq_len"], p.d["R"], p.d["W"], p.codes, p.meta,
+                        p.d["K"], p.d["V"], *p.keep, p.top_k, p.scale, sel, sc, out, p.ws)
+    torch.cuda.synchronize()
+    assert p.status() == 0
+    return lens, codes0, meta0, sel, sc, out
+
+
+@pytest.mark.parametrize("meta_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_decode_append(gpu_lib, case, meta_dtype):
+    """One fused append + decode step per sequence (one-launch coarse stage), including a
+    one-key sequence, a key that opens a page and keys that extend a partial page."""
+    print(f"\n[gpu decode_append] {case['name']} meta={meta_dtype}", flush=True)
+    inp = synth.make_hhr_inputs(case["batch"], case["n_q_heads"], case["n_kv_heads"],
+                                case["seq_lens"], case["max_ctx"], case["kv_dtype"], case["seed"])
+    p = U.Pipeline(gpu_lib, inp, case["kv_dtype"], case["n_q_heads"], case["n_kv_heads"],
+                   case["max_ctx"], case["keep_num"], case["keep_den"], case["keep_abs"],
+                   case["top_k"], meta_dtype=meta_dtype)
+    lens, codes0, meta0, sel, sc, out = _decode_append_run(gpu_lib, p)
+    pairs = [(b, g) for b in range(p.B) for g in range(p.Hkv)]
+    _check_decode_append(p, lens, meta_dtype, codes0, meta0, sel, sc, out, pairs)
+
+
+@pytest.mark.parametrize("meta_dtype", ["f32", "bf16"])
+def test_wide_batch_decode_append(gpu_lib, meta_dtype):
+    """The same on the 33-sequence batch, where the append runs in the encoder launch ahead
+    of the staged coarse stage."""
+    print(f"\n[gpu wide batch decode_append] meta={meta_dtype}", flush=True)
+    B, Hq, Hkv, Lcap, top_k = 33, 32, 8, 8192, 256
+    lens, inp = _wide_inputs(B, Hq, Hkv, Lcap)
+    p = U.Pipeline(gpu_lib, inp, "bf16", Hq, Hkv, Lcap, 1, 4, 0, top_k, meta_dtype=meta_dtype)
+    lens, codes0, meta0, sel, sc, out = _decode_append_run(gpu_lib, p)
+    _check_decode_append(p, lens, meta_dtype, codes0, meta0, sel, sc, out,
+                         [(0, 0), (1, 3), (5, 7), (B - 1, 2)])
+
+
 def test_chunked_append_equals_one_shot(gpu_lib):
     case = CASES[1]
     p = _pipeline(gpu_lib, case, with_v=False)
