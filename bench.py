@@ -118,6 +118,8 @@ def main():
     dev = torch.device("cuda", 0)
     if args.workload in synth.HISA_WORKLOADS:
         return main_hisa(args, torch, hhr, synth, dev)
+    if args.workload in synth.HISA_PREFILL_WORKLOADS:
+        return main_hisa_prefill(args, torch, hhr, synth, dev)
     w = synth.WORKLOADS[args.workload]
     B, Hq, Hkv, Lcap, top_k = w.batch, w.n_q_heads, w.n_kv_heads, w.max_ctx, w.top_k
     keep = (w.keep_num, w.keep_den, w.keep_pages_abs)
@@ -549,6 +551,89 @@ def main_hisa(args, torch, hhr, synth, dev):
         "pool_prefill_ms": round(float(np.median(pool_ms[1:] if len(pool_ms) > 1 else pool_ms)), 4),
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main_hisa_prefill(args, torch, hhr, synth, dev):
+    """HISA prefill indexer: M query rows spread over a 128K prompt against one shared fp8
+    index-key cache (hhr_hisa_prefill_select), plus hierarchical against flat (every block
+    kept) at 16K, the largest context whose flat candidate set fits one token top-k."""
+    base, M = synth.HISA_PREFILL_WORKLOADS[args.workload]
+    w = synth.HISA_WORKLOADS[base]
+    Hi, blk, L = w.n_index_heads, w.block, w.ctx
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    src = synth.make_hisa_workload_inputs(base, make_kv=False)
+    k8, ks = t(src["k8"]), t(src["k_scale"])
+
+    def pool(Lc):
+        shape1 = hhr.make_hisa_shape(1, Hi, blk, Lc)
+        reps = torch.zeros((1, Lc // blk, 128), dtype=torch.float32, device=dev)
+        ws1 = torch.zeros(hhr.hhr_hisa_workspace_size(shape1, 1, 1), dtype=torch.uint8,
+                          device=dev)
+        hhr.hhr_hisa_pool_keys(shape1, k8[None, :Lc].contiguous(), ks[None, :Lc].contiguous(),
+                               torch.zeros(1, dtype=torch.int32, device=dev),
+                               t(np.array([Lc], np.int32)), Lc, reps, ws1[:4].view(torch.int32))
+        return reps
+
+    def timed(Lc, keep, rows, reps):
+        shape = hhr.make_hisa_shape(M, Hi, blk, Lc)
+        ws = torch.zeros(hhr.hhr_hisa_workspace_size(shape, keep, w.top_k), dtype=torch.uint8,
+                         device=dev)
+        sel = torch.zeros((M, w.top_k), dtype=torch.int32, device=dev)
+        cnt = torch.zeros((M,), dtype=torch.int32, device=dev)
+        args_ = (shape, t(rows["q8"]), t(rows["q_scale"]), t(rows["w"]), k8[:Lc].contiguous(),
+                 ks[:Lc].contiguous(), reps, t(rows["q_len"]), keep, w.top_k, sel, cnt, ws)
+        for _ in range(2):
+            hhr.hhr_hisa_prefill_select(*args_)
+        torch.cuda.synchronize()
+        assert hhr.hhr_read_device_status(ws) == 0
+        n = max(3, min(args.steps, 20))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            hhr.hhr_hisa_prefill_select(*args_)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, sel, cnt
+
+    rows = synth.make_hisa_prefill_rows(args.workload)
+    reps = pool(L)
+    ms, sel, cnt = timed(L, w.keep_blocks, rows, reps)
+    # hierarchical against flat at 16K (same rows' queries, positions over 16K)
+    L16 = 16384
+    rows16 = synth.make_hisa_prefill_rows(args.workload, ctx=L16)
+    reps16 = pool(L16)
+    ms_flat, sel_f, cnt_f = timed(L16, L16 // blk, rows16, reps16)
+    ms_hier, sel_h, cnt_h = timed(L16, 16, rows16, reps16)
+    sf, ch, sh = sel_f.cpu().numpy(), cnt_f.cpu().numpy(), sel_h.cpu().numpy()
+    from hash_hierarchical_top_amd import quality
+
+    iou16 = float(np.mean([quality.iou(sh[r, :cnt_h[r].item()], sf[r, :ch[r]])
+                           for r in range(M)]))
+    q_len = rows["q_len"].astype(np.int64)
+    # flops: block scores (f32) over each row's blocks, fp8 token scores over kept tokens
+    nb = -(-q_len // blk)
+    flops = float((nb * Hi * 128 * 2).sum() + (np.minimum(nb, w.keep_blocks) * blk * Hi * 128 * 2)
+                  .sum())
+    line = {
+        "metric": "HISA prefill indexer query rows/s at 128K ctx",
+        "value": round(M / (ms / 1e3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": max(3, min(args.steps, 20)), "warmup": 2, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 index, f32 block scores",
+        "data": "synthetic (seeded; N(0,1) index queries and keys quantised to e4m3)",
+        "config": {"workload": args.workload, "ctx": L, "rows": M, "index_heads": Hi,
+                   "block": blk, "keep_blocks": w.keep_blocks, "top_k": w.top_k,
+                   "row_positions": "evenly spread over the context",
+                   "entry": "hhr_hisa_prefill_select"},
+        "roofline": None,
+        "cpu_baseline": None,
+        "indexer_tflops": round(flops / (ms * 1e9), 2),
+        "flat_vs_hierarchical_16k": {
+            "ctx": L16, "flat_ms": round(ms_flat, 4), "hierarchical_ms": round(ms_hier, 4),
+            "speedup": round(ms_flat / ms_hier, 2), "keep_blocks": 16,
+            "mean_iou_with_flat": round(iou16, 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -260,7 +260,7 @@ const char* hhr_status_string(int32_t status) {
 
 const char* hhr_last_error(void) { return g_err; }
 
-int32_t hhr_abi_version(void) { return 3; }
+int32_t hhr_abi_version(void) { return 4; }
 
 int32_t hhr_keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den,
                        int32_t keep_pages_abs) {
@@ -677,11 +677,12 @@ hhr_status hhr_hisa_token_topk(const hhr_hisa_shape* shape, const uint8_t* q8,
   return ok();
 }
 
-hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const float* q_scale,
-                           const float* w, const uint8_t* k8, const float* k_scale,
-                           const float* reps, const int32_t* seq_len, int32_t keep_blocks,
-                           int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+static hhr_status hisa_select_impl(const hhr_hisa_shape* shape, const uint8_t* q8,
+                                   const float* q_scale, const float* w, const uint8_t* k8,
+                                   const float* k_scale, const float* reps,
+                                   const int32_t* seq_len, int32_t keep_blocks, int32_t top_k,
+                                   int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                   size_t workspace_bytes, void* stream, bool shared) {
   HHR_TRY(check_hisa_shape(shape));
   HHR_TRY(check_hisa_sel(shape, keep_blocks, top_k));
   HHR_TRY(check_ptr(q8, "q8"));
@@ -706,14 +707,35 @@ hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const
   int32_t* kc = reinterpret_cast<int32_t*>(base + ws.kept_count);
   float* ts = reinterpret_cast<float*>(base + ws.token_scores);
   hipStream_t st = as_stream(stream);
-  HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status, st),
+  HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status, st,
+                                           shared),
              "hisa_block_scores launch");
   HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, bs, seq_len, keep_blocks, kept, kc, status, st),
              "hisa_top_blocks launch");
   HHR_LAUNCH(hhr::launch_hisa_token_topk(*shape, q8, q_scale, w, k8, k_scale, seq_len, kept, kc,
-                                         keep_blocks, top_k, sel_idx, sel_count, ts, status, st),
+                                         keep_blocks, top_k, sel_idx, sel_count, ts, status, st,
+                                         shared),
              "hisa_token_topk launch");
   return ok();
+}
+
+hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const float* q_scale,
+                           const float* w, const uint8_t* k8, const float* k_scale,
+                           const float* reps, const int32_t* seq_len, int32_t keep_blocks,
+                           int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return hisa_select_impl(shape, q8, q_scale, w, k8, k_scale, reps, seq_len, keep_blocks, top_k,
+                          sel_idx, sel_count, workspace, workspace_bytes, stream, false);
+}
+
+hhr_status hhr_hisa_prefill_select(const hhr_hisa_shape* shape, const uint8_t* q8,
+                                   const float* q_scale, const float* w, const uint8_t* k8,
+                                   const float* k_scale, const float* reps,
+                                   const int32_t* q_len, int32_t keep_blocks, int32_t top_k,
+                                   int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return hisa_select_impl(shape, q8, q_scale, w, k8, k_scale, reps, q_len, keep_blocks, top_k,
+                          sel_idx, sel_count, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -149,7 +149,7 @@ hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const fl
 hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const float* q_scale, const float* w, const float* reps,
                                     const int32_t* seq_len, float* block_scores,
-                                    uint32_t* status, hipStream_t stream);
+                                    uint32_t* status, hipStream_t stream, bool shared = false);
 hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_scores,
                                   const int32_t* seq_len, int32_t keep_blocks, int32_t* kept,
                                   int32_t* kept_count, uint32_t* status, hipStream_t stream);
@@ -159,6 +159,6 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                                   const int32_t* kept, const int32_t* kept_count,
                                   int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
                                   int32_t* sel_count, float* token_scores, uint32_t* status,
-                                  hipStream_t stream);
+                                  hipStream_t stream, bool shared = false);
 
 }  // namespace hhr

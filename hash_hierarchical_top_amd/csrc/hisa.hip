@@ -74,11 +74,12 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
 
 // H2: 16 blocks per workgroup; thread (bl = tid/16, hg = tid%16) takes heads
 // hg, hg+16, hg+32, hg+48 of block bl, and the 16 threads of a block reduce.
+// shared: every query row b reads the one cache (row 0) of reps, as in prefill.
 __global__ __launch_bounds__(256) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
     const int32_t* __restrict__ seq_len, float* __restrict__ block_scores,
-    uint32_t* __restrict__ status, int Hi, int Lcap, int block) {
+    uint32_t* __restrict__ status, int Hi, int Lcap, int block, int shared) {
   __shared__ float sq[kMaxIndexHeads][kD + 1];
   __shared__ float srep[16][kD];
   const int b = blockIdx.y;
@@ -94,7 +95,8 @@ __global__ __launch_bounds__(256) void k_hisa_block_scores(
   }
   for (int i = tid; i < 16 * kD; i += 256) {
     const int bl = i / kD, d = i % kD;
-    srep[bl][d] = (blk0 + bl < Nb) ? reps[((size_t)b * NbCap + blk0 + bl) * kD + d] : 0.f;
+    srep[bl][d] =
+        (blk0 + bl < Nb) ? reps[((size_t)(shared ? 0 : b) * NbCap + blk0 + bl) * kD + d] : 0.f;
   }
   __syncthreads();
   const int bl = tid >> 4;
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(256) void k_hisa_token_scores(
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
-    float* __restrict__ token_scores, int Hi, int Lcap, int block) {
+    float* __restrict__ token_scores, int Hi, int Lcap, int block, int shared) {
   const int b = blockIdx.y;
   const int slot = blockIdx.x;
   int L = seq_len[b];
@@ -179,8 +181,9 @@ __global__ __launch_bounds__(256) void k_hisa_token_scores(
     for (int ks = 0; ks < 4; ++ks)
       bq[nt][ks] = h < Hi ? *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp) : 0;
   }
-  const uint8_t* kb = k8 + (size_t)b * Lcap * kD;
-  const float* ksb = k_scale + (size_t)b * Lcap;
+  const size_t cb = shared ? 0 : (size_t)b;  // the query row's cache
+  const uint8_t* kb = k8 + cb * Lcap * kD;
+  const float* ksb = k_scale + cb * Lcap;
   float* ts = token_scores + ((size_t)b * keep_blocks + slot) * block;
   const int ntile = block / 16;
   for (int mt = wv; mt < ntile; mt += 4) {
@@ -265,11 +268,11 @@ hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const fl
 hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const float* q_scale, const float* w, const float* reps,
                                     const int32_t* seq_len, float* block_scores,
-                                    uint32_t* status, hipStream_t stream) {
+                                    uint32_t* status, hipStream_t stream, bool shared) {
   const int NbCap = s.max_ctx / s.block;
   hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + 15) / 16, s.batch), dim3(256), 0, stream,
                      q8, q_scale, w, reps, seq_len, block_scores, status, s.n_index_heads,
-                     s.max_ctx, s.block);
+                     s.max_ctx, s.block, shared ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -288,11 +291,11 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                                   const int32_t* kept, const int32_t* kept_count,
                                   int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
                                   int32_t* sel_count, float* token_scores, uint32_t* status,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, bool shared) {
   (void)status;
   hipLaunchKernelGGL(k_hisa_token_scores, dim3(keep_blocks, s.batch), dim3(256), 0, stream, q8,
                      q_scale, w, k8, k_scale, seq_len, kept, kept_count, keep_blocks,
-                     token_scores, s.n_index_heads, s.max_ctx, s.block);
+                     token_scores, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_hisa_topk, dim3(s.batch), dim3(kHisaThreads), 0, stream, token_scores,

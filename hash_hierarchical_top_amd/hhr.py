@@ -22,7 +22,7 @@ HHR_ERR_WORKSPACE = -3
 HHR_ERR_HIP = -4
 HHR_F32 = 0
 HHR_BF16 = 1
-ABI_VERSION = 3  # the include/hhr.h declarations this binding mirrors
+ABI_VERSION = 4  # the include/hhr.h declarations this binding mirrors
 HHR_DEV_BAD_SEQ_LEN = 0x1
 HHR_DEV_BAD_INDEX = 0x2
 
@@ -82,6 +82,8 @@ _SIGS = {
     "hhr_hisa_top_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "hhr_hisa_token_topk": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                     c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "hhr_hisa_prefill_select": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                        c_i32, c_vp, c_vp, c_vp, c_size, c_vp]),
     "hhr_hisa_select": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                 c_vp, c_vp, c_vp, c_size, c_vp]),
 }
@@ -293,3 +295,12 @@ def hhr_hisa_select(shape, q8, q_scale, w, k8, k_scale, reps, seq_len, keep_bloc
     _call("hhr_hisa_select", ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8),
           _ptr(k_scale), _ptr(reps), _ptr(seq_len), int(keep_blocks), int(top_k), _ptr(sel_idx),
           _ptr(sel_count), _ptr(workspace), wb, _stream(stream))
+
+
+def hhr_hisa_prefill_select(shape, q8, q_scale, w, k8, k_scale, reps, q_len, keep_blocks, top_k,
+                            sel_idx, sel_count, workspace, workspace_bytes=None,
+                            stream=None) -> None:
+    wb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _call("hhr_hisa_prefill_select", ctypes.byref(shape), _ptr(q8), _ptr(q_scale), _ptr(w),
+          _ptr(k8), _ptr(k_scale), _ptr(reps), _ptr(q_len), int(keep_blocks), int(top_k),
+          _ptr(sel_idx), _ptr(sel_count), _ptr(workspace), wb, _stream(stream))

@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -224,6 +224,28 @@ HISA_WORKLOADS: Dict[str, HISAWorkload] = {
     # token top-2048, then 16 attention heads on one bf16 KV head
     "hisa_128k": HISAWorkload("hisa_128k", 64, 131072, 128, 64, 2048, 16, 1004),
 }
+
+
+# Prefill chunks for the HISA indexer: `rows` query rows (index-query draws of their own)
+# at positions spread evenly over the context of a decode workload's shared cache, so the
+# mean row sees half the context, as over a whole prefill.
+HISA_PREFILL_WORKLOADS: Dict[str, Tuple[str, int]] = {
+    "hisa_prefill_128k": ("hisa_128k", 512),
+}
+
+
+def make_hisa_prefill_rows(name: str, ctx: int = 0) -> Dict[str, np.ndarray]:
+    """q8 [M][Hi][d], q_scale [M][Hi], w [M][Hi] and q_len [M] (positions + 1 spread over
+    [1, ctx], ctx defaulting to the workload's)."""
+    base, rows = HISA_PREFILL_WORKLOADS[name]
+    w = HISA_WORKLOADS[base]
+    ctx = ctx or w.ctx
+    parts = [make_hisa_inputs(w.n_index_heads, 1, 16, 0, w.seed + 1000 + r, w.head_dim,
+                              block=16, make_kv=False) for r in range(rows)]
+    q_len = ((np.arange(rows, dtype=np.int64) + 1) * ctx // rows).astype(np.int32)
+    return dict(q8=np.stack([x["q8"] for x in parts]),
+                q_scale=np.stack([x["q_scale"] for x in parts]),
+                w=np.stack([x["w"] for x in parts]), q_len=q_len)
 
 
 def quantize_rows_e4m3(x: np.ndarray):

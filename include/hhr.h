@@ -350,6 +350,26 @@ hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const
                            int32_t top_k, int32_t* sel_idx, int32_t* sel_count, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Prefill indexer: H2..H5 for a chunk of query rows against ONE shared index-key
+ * cache, each row over its own causal prefix (the O(L^2) per-layer case the
+ * HISA abstract names).  Row r sees tokens t < q_len[r] (its position + 1): the
+ * coarse filter scores blocks blk < ceil(q_len[r] / block) with the shared
+ * pooled representatives (pooled once over the cache by hhr_hisa_pool_keys, so
+ * a row's last, partly visible block is scored with the whole block's mean),
+ * the token stage scores only tokens t < q_len[r].       [HISA abstract]
+ *   shape.batch = M query rows; max_ctx = the cache capacity
+ *   q8 [M][Hi][d] uint8, q_scale [M][Hi] f32 (> 0), w [M][Hi] f32 (>= 0)
+ *   k8 [Lcap][d] uint8, k_scale [Lcap] f32, reps [Lcap/block][d] f32 (shared)
+ *   q_len [M] int32 in [0, Lcap]
+ *   sel_idx [M][top_k] int32 out (ascending, -1 padded), sel_count [M] int32 out
+ *   workspace >= hhr_hisa_workspace_size(shape, keep_blocks, top_k) (per row) */
+hhr_status hhr_hisa_prefill_select(const hhr_hisa_shape* shape, const uint8_t* q8,
+                                   const float* q_scale, const float* w, const uint8_t* k8,
+                                   const float* k_scale, const float* reps,
+                                   const int32_t* q_len, int32_t keep_blocks, int32_t top_k,
+                                   int32_t* sel_idx, int32_t* sel_count, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

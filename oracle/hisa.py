@@ -94,6 +94,25 @@ def select(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, keep_blocks: i
     return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s, sel=sel)
 
 
+def prefill_select(q8, q_scale, w, k8, k_scale, cache_len: int, q_len: int, block: int,
+                   keep_blocks: int, top_k: int) -> Dict[str, np.ndarray]:
+    """HISA selection for one query row of a prefill chunk [HISA abstract: the
+    indexer's per-layer O(L^2) case].  The index-key cache holds cache_len rows and
+    its block representatives are pooled once over them; the row sees tokens
+    t < q_len (its position + 1): the coarse filter scores the blocks that hold its
+    prefix with those representatives, the token stage only its prefix."""
+    q = dequantize(q8, q_scale)
+    keys = dequantize(np.asarray(k8)[:cache_len], np.asarray(k_scale)[:cache_len])
+    reps = pooled_reps(keys, block)[:(q_len + block - 1) // block]
+    S = indexer_scores(q, w, reps)
+    blocks = top_largest(S, np.arange(reps.shape[0]), keep_blocks)
+    cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    cand = cand[cand < q_len]
+    s = indexer_scores(q, w, keys[cand])
+    sel = top_largest(s, cand, top_k)
+    return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s, sel=sel)
+
+
 def select_in_blocks(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, blocks,
                      top_k: int) -> Dict[str, np.ndarray]:
     """Fine stage alone, on given kept blocks."""

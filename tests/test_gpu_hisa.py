@@ -310,3 +310,77 @@ def test_full_size_hisa_128k(gpu_lib):
     np.testing.assert_array_equal(sel, O.top_largest(ts, cand, r.top_k))
     assert int(r.sel_count[0]) == r.top_k
     assert gpu_lib.hhr_read_device_status(r.ws) == 0
+
+
+# --------------------------------------------------------------------------- #
+# prefill rows: one shared cache, causal prefixes
+# --------------------------------------------------------------------------- #
+def _margin_ok(scores, k):
+    """True when no score sits within the excuse band of the k-th largest (or k >= n)."""
+    s = np.sort(np.asarray(scores, np.float64))[::-1]
+    if k >= s.size:
+        return True
+    return abs(s[k - 1] - s[k]) > SCORE_EXCUSE * max(abs(s[k - 1]), 1e-30)
+
+
+@pytest.mark.parametrize("keep_all", [False, True])
+def test_prefill_select(gpu_lib, keep_all):
+    """Query rows at positions across a 4000-key cache (first token, block edges, the end)
+    against one shared cache: equal, bit for bit, to hhr_hisa_select on per-row copies of
+    the cache and of its shared pooled representatives; equal to the oracle's prefill
+    selection on every row whose block and token cut-offs have no near-tie; with every
+    block kept, equal to the flat indexer on each row's prefix."""
+    H = gpu_lib
+    print(f"\n[gpu hisa prefill] keep_all={keep_all}", flush=True)
+    Hi, blk, Lcap, L, top_k = 16, 64, 4096, 4000, 300
+    keep = Lcap // blk if keep_all else 8
+    rng = np.random.default_rng(61)
+    pos = np.unique(np.concatenate([[0, 62, 63, 64, 127, 128, L - 1],
+                                    rng.integers(0, L, 41)]))
+    q_len = (pos + 1).astype(np.int32)
+    M = q_len.size
+    src = synth.make_hisa_inputs(Hi, L, Lcap, 4, 62, block=blk, make_kv=False)
+    qs = [synth.make_hisa_inputs(Hi, 1, 16, 4, 100 + r, block=16, make_kv=False)
+          for r in range(M)]
+    q8 = np.stack([x["q8"] for x in qs])
+    q_scale = np.stack([x["q_scale"] for x in qs])
+    wt = np.stack([x["w"] for x in qs])
+    dv = U.dev()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dv)
+    k8, ks = t(src["k8"]), t(src["k_scale"])
+    shape1 = H.make_hisa_shape(1, Hi, blk, Lcap)
+    reps = torch.zeros((1, Lcap // blk, 128), dtype=torch.float32, device=dv)
+    ws1 = torch.zeros(H.hhr_hisa_workspace_size(shape1, 1, 1), dtype=torch.uint8, device=dv)
+    zero = torch.zeros(1, dtype=torch.int32, device=dv)
+    H.hhr_hisa_pool_keys(shape1, k8[None], ks[None], zero, t(np.array([L], np.int32)), L, reps,
+                         ws1[:4].view(torch.int32))
+    shape = H.make_hisa_shape(M, Hi, blk, Lcap)
+    ws = torch.zeros(H.hhr_hisa_workspace_size(shape, keep, top_k), dtype=torch.uint8, device=dv)
+    sel = torch.zeros((M, top_k), dtype=torch.int32, device=dv)
+    cnt = torch.zeros((M,), dtype=torch.int32, device=dv)
+    H.hhr_hisa_prefill_select(shape, t(q8), t(q_scale), t(wt), k8, ks, reps, t(q_len), keep,
+                              top_k, sel, cnt, ws)
+    # the same rows on per-row copies of the cache and of the shared representatives
+    ws2 = torch.zeros_like(ws)
+    sel2 = torch.zeros_like(sel)
+    cnt2 = torch.zeros_like(cnt)
+    H.hhr_hisa_select(shape, t(q8), t(q_scale), t(wt), k8[None].expand(M, -1, -1).contiguous(),
+                      ks[None].expand(M, -1).contiguous(), reps.expand(M, -1, -1).contiguous(),
+                      t(q_len), keep, top_k, sel2, cnt2, ws2)
+    torch.cuda.synchronize()
+    assert H.hhr_read_device_status(ws) == 0
+    assert torch.equal(sel, sel2) and torch.equal(cnt, cnt2)
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    checked = 0
+    for r in range(M):
+        res = O.prefill_select(q8[r], q_scale[r], wt[r], src["k8"], src["k_scale"], L,
+                               int(q_len[r]), blk, keep, top_k)
+        assert cnt_h[r] == res["sel"].size and np.all(sel_h[r, cnt_h[r]:] == -1)
+        if _margin_ok(res["block_scores"], keep) and _margin_ok(res["token_scores"], top_k):
+            assert sel_h[r, :cnt_h[r]].tolist() == res["sel"].tolist(), r
+            checked += 1
+        if keep_all and _margin_ok(res["token_scores"], top_k):
+            flat = O.flat_select(q8[r], q_scale[r], wt[r], src["k8"], src["k_scale"],
+                                 int(q_len[r]), top_k)
+            assert sel_h[r, :cnt_h[r]].tolist() == flat.tolist(), r
+    assert checked >= 0.8 * M, (checked, M)

@@ -92,3 +92,39 @@ def test_block_size_one_coarse_equals_fine():
 def test_iou_definition():
     assert O.iou([1, 2, 3], [2, 3, 4]) == pytest.approx(0.5)
     assert O.iou([], []) == 1.0
+
+
+# --------------------------------------------------------------------------- #
+# prefill rows (one shared cache, causal prefixes)
+# --------------------------------------------------------------------------- #
+def _prefill_inputs(seed=31, Hi=8, L=900):
+    rng = np.random.default_rng(seed)
+    q8, qs = synth.quantize_rows_e4m3(rng.standard_normal((Hi, 128)).astype(np.float32))
+    k8, ks = synth.quantize_rows_e4m3(rng.standard_normal((L, 128)).astype(np.float32))
+    return q8, qs, rng.uniform(0, 1, Hi).astype(np.float32), k8, ks
+
+
+def test_prefill_row_at_the_cache_end_is_the_decode_selection():
+    q8, qs, wt, k8, ks = _prefill_inputs()
+    for L in (900, 896, 1):
+        a = O.prefill_select(q8, qs, wt, k8, ks, L, L, 64, 5, 100)
+        b = O.select(q8, qs, wt, k8, ks, L, 64, 5, 100)
+        assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["blocks"], b["blocks"])
+
+
+def test_prefill_row_sees_only_its_prefix():
+    q8, qs, wt, k8, ks = _prefill_inputs()
+    for q_len in (1, 63, 64, 65, 500):
+        r = O.prefill_select(q8, qs, wt, k8, ks, 900, q_len, 64, 4, 300)
+        assert r["sel"].size == min(300, r["cand"].size) and np.all(r["sel"] < q_len)
+        assert r["blocks"].size == min(4, -(-q_len // 64)) and np.all(r["blocks"] * 64 < q_len)
+        # the partly visible last block is scored with the mean over the whole cache block
+        full = O.pooled_reps(O.dequantize(k8[:900], ks[:900]), 64)
+        assert np.array_equal(r["reps"], full[:-(-q_len // 64)])
+
+
+def test_prefill_keep_all_blocks_is_the_flat_indexer_on_the_prefix():
+    q8, qs, wt, k8, ks = _prefill_inputs()
+    for q_len in (1, 100, 640, 900):
+        r = O.prefill_select(q8, qs, wt, k8, ks, 900, q_len, 64, 15, 50)
+        assert np.array_equal(r["sel"], O.flat_select(q8, qs, wt, k8, ks, q_len, 50))

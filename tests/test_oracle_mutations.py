@@ -199,7 +199,30 @@ def _top_largest_high_ties(s, ids, k):
     return np.sort(ids[np.lexsort((-ids, -s))[:k]])
 
 
+def _prefill_reps_of_prefix(q8, q_scale, w, k8, k_scale, cache_len, q_len, block, keep_blocks,
+                            top_k):
+    """the other reading: pool the row's own prefix instead of the shared cache"""
+    return OH.select(q8, q_scale, w, k8, k_scale, q_len, block, keep_blocks, top_k)
+
+
+def _prefill_no_causal_mask(q8, q_scale, w, k8, k_scale, cache_len, q_len, block, keep_blocks,
+                            top_k):
+    """the token stage scans the kept blocks up to the cache end"""
+    q = OH.dequantize(q8, q_scale)
+    keys = OH.dequantize(np.asarray(k8)[:cache_len], np.asarray(k_scale)[:cache_len])
+    reps = OH.pooled_reps(keys, block)[:(q_len + block - 1) // block]
+    S = OH.indexer_scores(q, w, reps)
+    blocks = OH.top_largest(S, np.arange(reps.shape[0]), keep_blocks)
+    cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    cand = cand[cand < cache_len]
+    s = OH.indexer_scores(q, w, keys[cand])
+    return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s,
+                sel=OH.top_largest(s, cand, top_k))
+
+
 HISA_MUTANTS = [
+    ("prefill_select", _prefill_reps_of_prefix),
+    ("prefill_select", _prefill_no_causal_mask),
     ("e4m3fn_decode", _decode_no_subnormal),
     ("e4m3fn_decode", _decode_bias8),
     ("pooled_reps", _reps_sum),
