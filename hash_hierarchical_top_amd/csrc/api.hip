@@ -63,7 +63,8 @@ hhr_status check_shape(const hhr_shape* s) {
   if (s->n_q_heads / s->n_kv_heads > hhr::kMaxG)
     return fail(HHR_ERR_UNSUPPORTED, "query heads per KV head must be <= %d", hhr::kMaxG);
   if (s->head_dim != hhr::kD) return fail(HHR_ERR_UNSUPPORTED, "head_dim must be 128");
-  if (s->code_bits != 128) return fail(HHR_ERR_UNSUPPORTED, "code_bits must be 128");
+  if (s->code_bits != 64 && s->code_bits != 128 && s->code_bits != 256)
+    return fail(HHR_ERR_UNSUPPORTED, "code_bits must be 64, 128 or 256");
   if (s->page_size != hhr::kPS) return fail(HHR_ERR_UNSUPPORTED, "page_size must be 16");
   if (s->max_ctx < hhr::kPS || s->max_ctx % hhr::kPS != 0)
     return fail(HHR_ERR_INVALID_ARG, "max_ctx must be a positive multiple of 16");
@@ -165,7 +166,7 @@ static size_t counters_bytes(const hhr_shape& s) {
 static size_t ham_hist_bytes(const hhr_shape& s) {
   const size_t BG = (size_t)s.batch * s.n_kv_heads;
   const size_t G = (size_t)(s.n_q_heads / s.n_kv_heads);
-  return align_up(BG * (128 * G + 1) * sizeof(int));
+  return align_up(BG * ((size_t)s.code_bits * G + 1) * sizeof(int));
 }
 
 size_t ctrl_bytes(const hhr_shape& s) { return kAlign + counters_bytes(s) + ham_hist_bytes(s); }
@@ -208,10 +209,10 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.ham_hist = take(ham_hist_bytes(s));
   const HamScratch hs = ham_scratch(s, w.p_max);
   w.ham_dist = take(hs.end - hs.dist);
-  w.ham_cum = take(BHkv * (size_t)ham_cum_blocks(w.p_max) * (128 * (s.n_q_heads / s.n_kv_heads) + 1) *
-                   sizeof(uint16_t));
+  w.ham_cum = take(BHkv * (size_t)ham_cum_blocks(w.p_max) *
+                   ((size_t)s.code_bits * (s.n_q_heads / s.n_kv_heads) + 1) * sizeof(uint16_t));
   w.q_rot = take(BHq * kD * sizeof(float));
-  w.q_codes = take(BHq * kNW * sizeof(uint32_t));
+  w.q_codes = take(BHq * (size_t)(s.code_bits / 32) * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
   w.wave_range = take(BHkv * (NpCap / 16) * sizeof(float2));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
@@ -538,8 +539,10 @@ static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int3
   // costs less than every workgroup repeating the pick.  Same results.
   hhr::Workspace probe;
   hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &probe);
-  const bool pick = (long long)shape->batch * shape->n_kv_heads * probe.n_split <=
-                    hhr::kPickInAttentionMaxWgs;
+  // The in-attention pick reads 128-bit-code histograms only.
+  const bool pick = shape->code_bits == 32 * hhr::kNW &&
+                    (long long)shape->batch * shape->n_kv_heads * probe.n_split <=
+                        hhr::kPickInAttentionMaxWgs;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
                       as_stream(stream), !pick, &ws, &buf, append ? &app : nullptr));

@@ -291,9 +291,10 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
-  if ((long long)grid.x * grid.y > kScoreToppMaxWgs) {
+  if ((long long)grid.x * grid.y > kScoreToppMaxWgs || s.code_bits != 32 * kNW) {
     // many rounds of one-CU workgroups: the launch boundaries of the staged
-    // stages cost less than the latency each round would leave exposed
+    // stages cost less than the latency each round would leave exposed.  The
+    // fused kernel encodes 128-bit query codes only; other widths run staged.
     hipError_t e = hipSuccess;
     if (app)
       e = launch_append_last_row(s, app->k_cache, seq_len, R, W, app->codes, app->meta,

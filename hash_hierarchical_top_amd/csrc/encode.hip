@@ -19,12 +19,16 @@ constexpr int kTilePages = 4;                 // pages per tile
 constexpr int kTileRows = kTilePages * kPS;   // 64 key rows per tile
 constexpr int kLdsStride = kD + 8;            // bf16 elements per staged row (bank spread)
 
-// One workgroup = 4 waves; wave w owns output columns [64w, 64w+64) of [R | W]:
-// waves 0-1 produce X (rotated keys), waves 2-3 produce Y (hash projection).
-// The B operand (64 columns x 128 rows, bf16 hi + lo) stays in registers for
-// every tile the workgroup processes; key tiles are staged through LDS.
-template <bool KF32>
-__global__ __launch_bounds__(256) void k_append_encode(
+// One workgroup = 2 + NW/2 waves; wave w owns output columns [64w, 64w+64) of
+// [R | W] (W is [128][32 NW]): waves 0-1 produce X (rotated keys), waves 2..
+// produce Y (hash projection), two code words each.  The B operand (64
+// columns x 128 rows, bf16 hi + lo) stays in registers for every tile the
+// workgroup processes; key tiles are staged through LDS.
+template <int NW>
+constexpr int enc_threads() { return 64 * (2 + NW / 2); }
+
+template <bool KF32, int NW>
+__global__ __launch_bounds__(enc_threads<NW>()) void k_append_encode(
     const void* __restrict__ kcache, const int32_t* __restrict__ start,
     const int32_t* __restrict__ n_new, const float* __restrict__ R, const float* __restrict__ W,
     uint32_t* __restrict__ codes, void* __restrict__ meta, int meta_bf16,
@@ -61,8 +65,10 @@ __global__ __launch_bounds__(256) void k_append_encode(
   const int lgrp = l >> 4;     // lane group: K slots [8*lgrp, 8*lgrp+8)
 
   // B operand: element (k, n) of the wave's 64 columns, k = 32*ks + 8*lgrp + j.
-  const float* M = (w < 2 ? R : W) + (size_t)g * kD * kD;
-  const int col0 = (w & 1) * 64;
+  constexpr int kNT = enc_threads<NW>();
+  const int mstride = w < 2 ? kD : 32 * NW;  // row length of R or W
+  const float* M = w < 2 ? R + (size_t)g * kD * kD : W + (size_t)g * kD * (32 * NW);
+  const int col0 = w < 2 ? 64 * w : 64 * (w - 2);
   bf16x8 bhi[4][4], blo[4][4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -74,8 +80,8 @@ __global__ __launch_bounds__(256) void k_append_encode(
         const int k = 32 * ks + 8 * lgrp + 2 * jj;
         const int col = col0 + 16 * nt + lrow;
         uint32_t h0, l0, h1, l1;
-        split_bf16(M[(size_t)k * kD + col], h0, l0);
-        split_bf16(M[(size_t)(k + 1) * kD + col], h1, l1);
+        split_bf16(M[(size_t)k * mstride + col], h0, l0);
+        split_bf16(M[(size_t)(k + 1) * mstride + col], h1, l1);
         hv[jj] = h0 | (h1 << 16);
         lv[jj] = l0 | (l1 << 16);
       }
@@ -91,32 +97,36 @@ __global__ __launch_bounds__(256) void k_append_encode(
     if constexpr (!KF32) {
       const uint16_t* Kb = (const uint16_t*)kcache + (size_t)bg * Lcap * kD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;  // 16-byte chunk: 64 rows x 16 chunks
-        const int r = c >> 4;
-        const int cc = c & 15;
-        const int grow = row0 + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (grow < e) v = *(const u32x4*)(Kb + (size_t)grow * kD + cc * 8);
-        *(u32x4*)(a_hi + r * kLdsStride + cc * 8) = v;
+      for (int i = 0; i < (kTileRows * 16 + kNT - 1) / kNT; ++i) {
+        const int c = tid + kNT * i;  // 16-byte chunk: 64 rows x 16 chunks
+        if (c < kTileRows * 16) {
+          const int r = c >> 4;
+          const int cc = c & 15;
+          const int grow = row0 + r;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (grow < e) v = *(const u32x4*)(Kb + (size_t)grow * kD + cc * 8);
+          *(u32x4*)(a_hi + r * kLdsStride + cc * 8) = v;
+        }
       }
     } else {
       const float* Kf = (const float*)kcache + (size_t)bg * Lcap * kD;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = tid + 256 * i;  // 16-byte chunk of 4 floats: 64 rows x 32 chunks
-        const int r = c >> 5;
-        const int cc = c & 31;
-        const int grow = row0 + r;
-        floatx4 v = {0.f, 0.f, 0.f, 0.f};
-        if (grow < e) v = *(const floatx4*)(Kf + (size_t)grow * kD + cc * 4);
-        uint32_t h[4], lo[4];
+      for (int i = 0; i < (kTileRows * 32 + kNT - 1) / kNT; ++i) {
+        const int c = tid + kNT * i;  // 16-byte chunk of 4 floats: 64 rows x 32 chunks
+        if (c < kTileRows * 32) {
+          const int r = c >> 5;
+          const int cc = c & 31;
+          const int grow = row0 + r;
+          floatx4 v = {0.f, 0.f, 0.f, 0.f};
+          if (grow < e) v = *(const floatx4*)(Kf + (size_t)grow * kD + cc * 4);
+          uint32_t h[4], lo[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) split_bf16(v[j], h[j], lo[j]);
-        u32x2 hv = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        u32x2 lv = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-        *(u32x2*)(a_hi + r * kLdsStride + cc * 4) = hv;
-        *(u32x2*)(a_lo + r * kLdsStride + cc * 4) = lv;
+          for (int j = 0; j < 4; ++j) split_bf16(v[j], h[j], lo[j]);
+          u32x2 hv = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          u32x2 lv = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+          *(u32x2*)(a_hi + r * kLdsStride + cc * 4) = hv;
+          *(u32x2*)(a_lo + r * kLdsStride + cc * 4) = lv;
+        }
       }
     }
     __syncthreads();
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256) void k_append_encode(
           const int row = prow0 + r;
           if (row >= s && row < e) {
             u32x2 wv = {half[0] | (half[1] << 16), half[2] | (half[3] << 16)};
-            *(u32x2*)(codes + ((size_t)bg * Lcap + row) * kNW + 2 * (w - 2)) = wv;
+            *(u32x2*)(codes + ((size_t)bg * Lcap + row) * NW + 2 * (w - 2)) = wv;
           }
         }
       }
@@ -206,13 +216,14 @@ __global__ __launch_bounds__(256) void k_append_encode(
   }
 }
 
-// S2: one workgroup (512 threads) per (b, KV head) encodes the G queries of the group.
+// S2: one workgroup (kQeThreads) per (b, KV head) encodes the G queries of the group.
+template <int NW>
 __global__ __launch_bounds__(kQeThreads) void k_encode_queries(
     const float* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
     float* __restrict__ q_rot, uint32_t* __restrict__ q_codes, int Hq, int Hkv) {
   __shared__ QencSmem sm;
   const int bg = blockIdx.x;
-  qenc_group<false>(bg / Hkv, bg % Hkv, Hq, Hkv, q, R, W, q_rot, q_codes, sm);
+  qenc_group<false, NW>(bg / Hkv, bg % Hkv, Hq, Hkv, q, R, W, q_rot, q_codes, sm);
 }
 
 }  // namespace
@@ -231,14 +242,18 @@ hipError_t launch_append_keys(const hhr_shape& s, const void* k_cache, const int
   int tpw = (int)(((long long)max_tiles * bgs + target_wgs - 1) / target_wgs);
   if (tpw < 1) tpw = 1;
   dim3 grid((max_tiles + tpw - 1) / tpw, bgs);
-  if (s.kv_dtype == HHR_F32)
-    hipLaunchKernelGGL(k_append_encode<true>, grid, dim3(256), 0, stream, k_cache, start, n_new,
-                       R, W, codes, meta, s.meta_dtype == HHR_BF16, status, s.n_kv_heads,
-                       s.max_ctx, tpw);
-  else
-    hipLaunchKernelGGL(k_append_encode<false>, grid, dim3(256), 0, stream, k_cache, start, n_new,
-                       R, W, codes, meta, s.meta_dtype == HHR_BF16, status, s.n_kv_heads,
-                       s.max_ctx, tpw);
+  const int mbf = s.meta_dtype == HHR_BF16;
+#define HHR_ENC(KF32, NW)                                                                      \
+  hipLaunchKernelGGL((k_append_encode<KF32, NW>), grid, dim3(enc_threads<NW>()), 0, stream,    \
+                     k_cache, start, n_new, R, W, codes, meta, mbf, status, s.n_kv_heads,       \
+                     s.max_ctx, tpw)
+  const bool kf32 = s.kv_dtype == HHR_F32;
+  switch (s.code_bits) {
+    case 64: if (kf32) HHR_ENC(true, 2); else HHR_ENC(false, 2); break;
+    case 256: if (kf32) HHR_ENC(true, 8); else HHR_ENC(false, 8); break;
+    default: if (kf32) HHR_ENC(true, 4); else HHR_ENC(false, 4); break;
+  }
+#undef HHR_ENC
   return hipGetLastError();
 }
 
@@ -252,8 +267,16 @@ hipError_t launch_append_last_row(const hhr_shape& s, const void* k_cache,
 hipError_t launch_encode_queries(const hhr_shape& s, const float* q, const float* R,
                                  const float* W, float* q_rot, uint32_t* q_codes,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(k_encode_queries, dim3(s.batch * s.n_kv_heads), dim3(kQeThreads), 0, stream,
-                     q, R, W, q_rot, q_codes, s.n_q_heads, s.n_kv_heads);
+  const dim3 grid(s.batch * s.n_kv_heads);
+  if (s.code_bits == 64)
+    hipLaunchKernelGGL(k_encode_queries<2>, grid, dim3(kQeThreads), 0, stream, q, R, W, q_rot,
+                       q_codes, s.n_q_heads, s.n_kv_heads);
+  else if (s.code_bits == 256)
+    hipLaunchKernelGGL(k_encode_queries<8>, grid, dim3(kQeThreads), 0, stream, q, R, W, q_rot,
+                       q_codes, s.n_q_heads, s.n_kv_heads);
+  else
+    hipLaunchKernelGGL(k_encode_queries<4>, grid, dim3(kQeThreads), 0, stream, q, R, W, q_rot,
+                       q_codes, s.n_q_heads, s.n_kv_heads);
   return hipGetLastError();
 }
 

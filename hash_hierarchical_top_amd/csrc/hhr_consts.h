@@ -5,6 +5,7 @@ namespace hhr {
 
 constexpr int kD = 128;    // head_dim
 constexpr int kNW = 4;     // 32-bit words per 128-bit code (appendix Table 4 of HHR: 128 bits)
+constexpr int kMaxNW = 8;  // widest code: 256 bits (HHR appendix Figure 10 sweeps the width)
 constexpr int kPS = 16;    // page size
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kMaxG = 16;  // query heads per KV head

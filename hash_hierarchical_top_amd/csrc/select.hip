@@ -78,15 +78,17 @@ __device__ __forceinline__ int kept_pages(const int32_t* kept_count, int bg, int
   return L > 0 ? max(0, min(kept_count[bg], p_max)) : 0;
 }
 
-// Distances of one 64-page chunk of one (b, g): grid (chunks, B*Hkv).
+// Distances of one 64-page chunk of one (b, g) for NW-word codes: grid
+// (chunks, B*Hkv).
+template <int NW>
 __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
     const uint32_t* __restrict__ q_codes, const uint32_t* __restrict__ codes,
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, int p_max, int Hq, int Hkv, int Lcap,
     uint16_t* __restrict__ dist, int* __restrict__ hist, uint16_t* __restrict__ cum) {
-  __shared__ HamDistSmem sm;
+  __shared__ HamDistSmem<NW> sm;
   const int bg = blockIdx.y;
-  ham_dist_chunk<kHamDistThreads, false>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, blockIdx.x, p_max,
+  ham_dist_chunk<kHamDistThreads, false, NW>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, blockIdx.x, p_max,
                                          seq_len, kept_count, q_codes, codes, kept, dist, hist,
                                          cum, sm);
 }
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kHamSelThreads) void k_ham_select(
     const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, int p_max, int top_k, int Hq, int Hkv, int Lcap,
     const uint16_t* __restrict__ dist, int* __restrict__ hist, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ sel_count, uint32_t* __restrict__ status) {
+    int32_t* __restrict__ sel_count, uint32_t* __restrict__ status, int code_bits) {
   __shared__ HamSmem sm;
   const int bg = blockIdx.x;
   const int b = bg / Hkv;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kHamSelThreads) void k_ham_select(
   const int L = checked_len(seq_len, b, Lcap, g == 0 ? status : nullptr);
   const int P = kept_pages(kept_count, bg, L, p_max);
   ham_select<kHamSelThreads, false>(b, g, Hq, Hkv, P, top_k, p_max, kept, false, dist, hist,
-                                    sel_idx, sel_count, sm);
+                                    sel_idx, sel_count, sm, code_bits);
 }
 
 }  // namespace
@@ -137,9 +139,17 @@ hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const ui
                            const int32_t* seq_len, const int32_t* kept,
                            const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
                            uint16_t* cum, hipStream_t stream) {
-  hipLaunchKernelGGL(k_ham_dist, dim3(ham_chunks(p_max), s.batch * s.n_kv_heads),
-                     dim3(kHamDistThreads), 0, stream, q_codes, codes, seq_len, kept, kept_count,
-                     p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, dist, hist, cum);
+  const dim3 grid(ham_chunks(p_max), s.batch * s.n_kv_heads);
+#define HHR_HAM_DIST(NW)                                                                      \
+  hipLaunchKernelGGL(k_ham_dist<NW>, grid, dim3(kHamDistThreads), 0, stream, q_codes, codes, \
+                     seq_len, kept, kept_count, p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, \
+                     dist, hist, cum)
+  switch (s.code_bits) {
+    case 64: HHR_HAM_DIST(2); break;
+    case 256: HHR_HAM_DIST(8); break;
+    default: HHR_HAM_DIST(4); break;
+  }
+#undef HHR_HAM_DIST
   return hipGetLastError();
 }
 
@@ -154,7 +164,7 @@ hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, cons
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_ham_select, dim3(s.batch * s.n_kv_heads), dim3(kHamSelThreads), 0, stream,
                      seq_len, kept, kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads,
-                     s.max_ctx, dist, hist, sel_idx, sel_count, status);
+                     s.max_ctx, dist, hist, sel_idx, sel_count, status, s.code_bits);
   return hipGetLastError();
 }
 

@@ -16,45 +16,56 @@
 namespace hhr {
 
 // ============================================================== S2: query
-// Columns 0..127 of [R | W] give q' = q R, columns 128..255 give the sign
-// bits of q W.  Every output (head h, column c) is computed the same way:
-// 8 partial sums over the input dims 16 k .. 16 k + 15 (sequential FMAs),
-// then the partials added in LDS in order k = 0..7.  NT threads share the
-// (column, k) work items, CPT = 8 NCOL / NT adjacent columns each, so a thread
-// holds 16 CPT matrix values in registers and the result does not depend on
-// NT or on NCOL (256: rotation and codes; 128: rotation only).
+// Columns 0..127 of [R | W] give q' = q R, columns 128 .. 128 + 32 NW - 1
+// give the sign bits of q W (W is [128][32 NW]).  Every output (head h,
+// column c) is computed the same way: 8 partial sums over the input dims
+// 16 k .. 16 k + 15 (sequential FMAs), then the partials added in LDS in
+// order k = 0..7.  NT threads share the (column, k) work items, CPT adjacent
+// columns each (the fewest of 1, 2, 4 that cover the columns; threads past
+// them idle), so a thread holds 16 CPT matrix values in registers and the
+// result does not depend on NT or on NCOL (128 + 32 NW: rotation and codes;
+// 128: rotation only).
 // rot(h, col, v) receives q'; code(h, word, bits) receives 32 code bits.
 // With extra_row (a KF32/bf16 key row of length 128, or NULL) it is encoded
 // the same way as row h = G after the G queries.  Every thread of the
 // workgroup must call (barriers).
-constexpr int kQeThreads = 512;
+constexpr int kQeThreads = 1024;
 constexpr int kQeChunk = 4;  // rows (query heads, then the extra key) per reduction round
 
 struct QencSmem {
   float sq[kMaxG + 1][kD];
-  float red[8][kQeChunk][2 * kD];
+  float red[8][kQeChunk][kD + 32 * kMaxNW];
 };
 
-template <int NCOL, int NT, typename Rot, typename Code>
+template <int NCOL, int NT>
+constexpr int qenc_cpt() {
+  return 8 * NCOL <= NT ? 1 : 8 * NCOL <= 2 * NT ? 2 : 4;
+}
+
+template <int NCOL, int NT, typename Rot, typename Code, int NW = kNW>
 __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
                           const float* __restrict__ R, const float* __restrict__ W,
                           QencSmem& sm, Rot rot, Code code, const void* extra_row = nullptr,
                           bool extra_f32 = false) {
-  static_assert(NCOL == kD || NCOL == 2 * kD, "rotation, or rotation and codes");
-  constexpr int CPT = 8 * NCOL / NT;  // columns per thread
-  static_assert(CPT == 1 || CPT == 2 || CPT == 4, "8 NCOL / NT columns per thread");
+  static_assert(NCOL == kD || NCOL == kD + 32 * NW, "rotation, or rotation and codes");
+  static_assert(NCOL % 64 == 0, "a wave's outputs stay in one row");
+  constexpr int CPT = qenc_cpt<NCOL, NT>();  // columns per thread
+  static_assert(8 * NCOL <= CPT * NT, "too many columns for the workgroup");
   constexpr int kGroupsC = NCOL / CPT;
+  constexpr int kCB = 32 * NW;  // W's row length
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
-  const int cg = tid % kGroupsC;
-  const int dg = tid / kGroupsC;  // 0..7
-  const int c0 = CPT * cg;        // first column in [0, NCOL)
-  const float* M = (c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kD + (c0 - kD));
+  const bool active = tid < 8 * kGroupsC;  // threads past the work items only reduce
+  const int cg = active ? tid % kGroupsC : 0;
+  const int dg = active ? tid / kGroupsC : 0;  // 0..7
+  const int c0 = CPT * cg;                     // first column in [0, NCOL)
+  const float* M = c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kCB + (c0 - kD);
+  const int mstride = c0 < kD ? kD : kCB;
   float m[16][CPT];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float* row = M + (size_t)(16 * dg + j) * kD;
+    const float* row = M + (size_t)(16 * dg + j) * mstride;
     if constexpr (CPT == 4) {
       const floatx4 v = *(const floatx4*)row;
 #pragma unroll
@@ -88,8 +99,10 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
           for (int k = 0; k < CPT; ++k) acc[k] = fmaf(x, m[j][k], acc[k]);
         }
       }
+      if (active) {
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) sm.red[dg][hh][c0 + k] = acc[k];
+        for (int k = 0; k < CPT; ++k) sm.red[dg][hh][c0 + k] = acc[k];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -117,19 +130,19 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
   }
 }
 
-// q' and the codes of one (b, g) to global memory.
-template <bool COH>
+// q' and the codes (NW words each) of one (b, g) to global memory.
+template <bool COH, int NW = kNW>
 __device__ void qenc_group(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
                            const float* __restrict__ R, const float* __restrict__ W,
                            float* q_rot, uint32_t* q_codes, QencSmem& sm) {
   const int G = Hq / Hkv;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * kD;
-  qenc_core<2 * kD, kQeThreads>(
-      b, g, Hq, Hkv, q, R, W, sm,
-      [&](int h, int col, float v) { Mem<COH>::st(q_rot + qbase + (size_t)h * kD + col, v); },
-      [&](int h, int word, uint32_t bits) {
-        Mem<COH>::st(q_codes + ((size_t)b * Hq + (size_t)g * G + h) * kNW + word, bits);
-      });
+  auto rot = [&](int h, int col, float v) { Mem<COH>::st(q_rot + qbase + (size_t)h * kD + col, v); };
+  auto code = [&](int h, int word, uint32_t bits) {
+    Mem<COH>::st(q_codes + ((size_t)b * Hq + (size_t)g * G + h) * NW + word, bits);
+  };
+  qenc_core<kD + 32 * NW, kQeThreads, decltype(rot), decltype(code), NW>(b, g, Hq, Hkv, q, R, W,
+                                                                         sm, rot, code);
 }
 
 // ============================================================== S3: bound
@@ -366,14 +379,19 @@ __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den
 // hold its 64 output ranks from two entries per block (pick_window).  (Stored
 // bin-major instead, the pick's loads coalesce but the 2-byte stores scatter
 // over a cache line each, which costs more than it saves.)
-constexpr int kHamBins = 128 * kMaxG + 1;  // 2049
+// H = 0 .. 32 NW G: 32 NW G + 1 bins for NW-word codes and G heads.
+template <int NW>
+constexpr int ham_bins_max() { return 32 * NW * kMaxG + 1; }
+constexpr int kHamBins = ham_bins_max<kNW>();         // 2049: the 128-bit composite path
+constexpr int kHamBinsMax = ham_bins_max<kMaxNW>();   // 4097
 constexpr int kHistCopies = 4;
 constexpr int kHamChunk = kHamChunkPages * kPS;  // 1024 candidates
 
+template <int NW>
 struct HamDistSmem {
-  int hist[kHistCopies][kHamBins];
+  int hist[kHistCopies][ham_bins_max<NW>()];
   int skept[kHamChunkPages];
-  __attribute__((aligned(16))) uint32_t sq[kMaxG * kNW];
+  __attribute__((aligned(16))) uint32_t sq[kMaxG * NW];
 };
 
 // 16-byte load; the coherent form is four agent-scope dword loads.
@@ -392,21 +410,22 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 // [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts added
 // atomically); cum (or NULL) [B][Hkv][ham_cum_blocks(p_max)][128 G + 1] u16.
 // Item j of every thread lies in block 4k + j, whose histogram is LDS copy j.
-// All threads call.
-template <int NT, bool COH>
+// Codes are NW 32-bit words.  All threads call.
+template <int NT, bool COH, int NW = kNW>
 __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, int p_max,
                                const int32_t* seq_len, const int32_t* kept_count,
                                const uint32_t* q_codes, const uint32_t* __restrict__ codes,
                                const int32_t* kept, uint16_t* dist, int* hist, uint16_t* cum,
-                               HamDistSmem& sm) {
+                               HamDistSmem<NW>& sm) {
   constexpr int kItems = kHamChunk / NT;
   static_assert(NT == kCumBlock && kItems == kHistCopies, "item j = block j = LDS copy j");
+  static_assert(NW == 2 || NW == 4 || NW == 8, "64-, 128- or 256-bit codes");
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
-  const int nbins = 128 * G + 1;
+  const int nbins = 32 * NW * G + 1;
   const int page0 = k * kHamChunkPages;
   // kept pages and query codes are loaded before the kept count is known
   // (addresses clamped into the buffers), so they share its round trip
@@ -414,7 +433,7 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   uint32_t qw = 0u;
   if (tid < kHamChunkPages)
     kp = Mem<COH>::ld(kept + (size_t)bg * p_max + min(page0 + tid, p_max - 1));
-  if (tid < G * kNW) qw = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * kNW + tid);
+  if (tid < G * NW) qw = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * NW + tid);
   const int L0 = seq_len[b];
   const int L = (L0 < 0 || L0 > Lcap) ? 0 : L0;
   const int P = L > 0 ? max(0, min(kept_count[bg], p_max)) : 0;
@@ -423,14 +442,13 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   const int npg = min(kHamChunkPages, P - page0);
   const int ncl = npg * kPS;  // candidates in this chunk
   if (tid < npg) sm.skept[tid] = kp;
-  if (tid < G * kNW) sm.sq[tid] = qw;
+  if (tid < G * NW) sm.sq[tid] = qw;
   for (int i = tid; i < kHistCopies * nbins; i += NT) sm.hist[i / nbins][i % nbins] = 0;
   __syncthreads();
 
-  const uint32_t* cb = codes + (size_t)bg * Lcap * kNW;
-  const u32x4* sq4 = reinterpret_cast<const u32x4*>(sm.sq);
+  const uint32_t* cb = codes + (size_t)bg * Lcap * NW;
   const int lastc = max(ncl - 1, 0);
-  u32x4 code[kItems];
+  uint32_t code[kItems][NW];
   bool ok[kItems];
   uint32_t h[kItems];
 #pragma unroll
@@ -439,15 +457,29 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
     const int page = sm.skept[min(c, lastc) >> 4];
     const int t = page * kPS + (c & 15);
     ok[j] = c < ncl && (unsigned)page < (unsigned)Np && t < L;
-    code[j] = *(const u32x4*)(cb + (size_t)(ok[j] ? t : 0) * kNW);
+    const uint32_t* src = cb + (size_t)(ok[j] ? t : 0) * NW;
+    if constexpr (NW == 2) {
+      const u32x2 v = *(const u32x2*)src;
+      code[j][0] = v[0];
+      code[j][1] = v[1];
+    } else {
+#pragma unroll
+      for (int v4 = 0; v4 < NW / 4; ++v4) {
+        const u32x4 v = *(const u32x4*)(src + 4 * v4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) code[j][4 * v4 + i] = v[i];
+      }
+    }
     h[j] = 0u;
   }
   for (int qh = 0; qh < G; ++qh) {
-    const u32x4 q = sq4[qh];
+    uint32_t q[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) q[i] = sm.sq[qh * NW + i];
 #pragma unroll
     for (int j = 0; j < kItems; ++j)
-      h[j] += __popc(code[j][0] ^ q[0]) + __popc(code[j][1] ^ q[1]) + __popc(code[j][2] ^ q[2]) +
-              __popc(code[j][3] ^ q[3]);
+#pragma unroll
+      for (int i = 0; i < NW; ++i) h[j] += __popc(code[j][i] ^ q[i]);
   }
   uint16_t* dc = dist + (size_t)bg * p_max * kPS + (size_t)page0 * kPS;
 #pragma unroll
@@ -478,7 +510,7 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
 }
 
 struct HamSmem {
-  int hist[kHamBins];
+  int hist[kHamBinsMax];
   union {
     __attribute__((aligned(16))) uint16_t hval[kMaxCand];      // H of candidate c
     __attribute__((aligned(16))) float scores[kMaxCtx / kPS];  // page scores (S4)
@@ -495,12 +527,13 @@ struct HamSmem {
 template <int NT, bool COH>
 __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int p_max,
                            const int32_t* kept, bool skept_ready, const uint16_t* dist,
-                           int* hist, int32_t* sel_idx, int32_t* sel_count, HamSmem& sm) {
+                           int* hist, int32_t* sel_idx, int32_t* sel_count, HamSmem& sm,
+                           int code_bits = 32 * kNW) {
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
   const int ncand = P * kPS;
-  const int nbins = 128 * G + 1;
+  const int nbins = code_bits * G + 1;
 
   // gather: kept pages, distances (8 per 16-byte load), summed histograms
   if (!skept_ready)

@@ -197,10 +197,13 @@ def make_hhr_inputs(batch: int, n_q_heads: int, n_kv_heads: int, seq_lens: Seque
     return out
 
 
-def make_workload_inputs(name: str, make_v: bool = True) -> Dict[str, np.ndarray]:
+def make_workload_inputs(name: str, make_v: bool = True,
+                         code_bits: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of a named workload; code_bits overrides its projection width."""
     w = WORKLOADS[name]
     return make_hhr_inputs(w.batch, w.n_q_heads, w.n_kv_heads, seq_lens_for(w), w.max_ctx,
-                           w.kv_dtype, w.seed, w.head_dim, w.code_bits, make_v=make_v)
+                           w.kv_dtype, w.seed, w.head_dim,
+                           w.code_bits if code_bits is None else code_bits, make_v=make_v)
 
 
 # --------------------------------------------------------------------------- #
@@ -319,4 +322,20 @@ def small_hhr_cases() -> List[dict]:
         dict(name="bf16_g8_bigk", batch=2, n_q_heads=16, n_kv_heads=2, seq_lens=[700, 333],
              max_ctx=1024, kv_dtype="bf16", seed=14, keep_num=1, keep_den=2, keep_abs=0,
              top_k=4096),
+    ]
+
+
+def small_code_bits_cases() -> List[dict]:
+    """Parity cases at the other code widths: 64 bits, and 256 bits with G = 16 (the
+    largest summed distance, 4096) and with top_k above the candidate count."""
+    return [
+        dict(name="bf16_g4_c64", batch=3, n_q_heads=8, n_kv_heads=2, seq_lens=[5003, 1, 2049],
+             max_ctx=6144, kv_dtype="bf16", seed=21, keep_num=1, keep_den=4, keep_abs=0,
+             top_k=512, code_bits=64),
+        dict(name="f32_g16_c256", batch=2, n_q_heads=16, n_kv_heads=1, seq_lens=[3000, 777],
+             max_ctx=3008, kv_dtype="f32", seed=22, keep_num=0, keep_den=1, keep_abs=48,
+             top_k=300, code_bits=256),
+        dict(name="bf16_g8_c256_bigk", batch=2, n_q_heads=16, n_kv_heads=2,
+             seq_lens=[700, 333], max_ctx=1024, kv_dtype="bf16", seed=23, keep_num=1,
+             keep_den=2, keep_abs=0, top_k=4096, code_bits=256),
     ]

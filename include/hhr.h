@@ -35,7 +35,7 @@
  *   - Layouts are dense row-major C arrays; the bracketed shapes below list
  *     dimensions outermost first.  B = batch, Hq = query heads, Hkv = KV
  *     heads, d = head_dim (128), Lcap = max_ctx, ps = page_size (16),
- *     NpCap = Lcap / ps, nw = code_bits / 32 (4).
+ *     NpCap = Lcap / ps, nw = code_bits / 32 (2, 4 or 8).
  *   - Device-side data errors (a seq_len outside [0, Lcap], a selected
  *     position outside [0, Lcap)) never fault: the offending sequence is
  *     treated as empty / the position is skipped, and a bit is set in the
@@ -84,7 +84,8 @@ typedef enum {
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
 /* Shape of one attention layer's KV cache and its retrieval metadata.
- * Supported: head_dim == 128, code_bits == 128 (Table 4 of [HHR]),
+ * Supported: head_dim == 128, code_bits 64, 128 or 256 (Table 4 of [HHR]
+ * uses 128; appendix Figure 10 of [HHR] varies the number of hash bits),
  * page_size == 16, max_ctx a multiple of 16 in [16, 262144],
  * n_q_heads a multiple of n_kv_heads with G = n_q_heads / n_kv_heads <= 16. */
 typedef struct {

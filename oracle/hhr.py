@@ -9,7 +9,9 @@ that prune low-logit pages; a head-wise learned projection W_h (Learned Hash
 Projection, LHP) gives the codes that rank keys inside the surviving pages;
 attention then runs over only the selected keys.  Figure 1 ("Overview") orders
 the stages coarse (GKR) then fine (LHP).  Figure 2's caption fixes the hash as
-a projection followed by sign(.).  Appendix Table 4 fixes 128-bit codes.  The
+a projection followed by sign(.).  Appendix Table 4 fixes 128-bit codes and
+appendix Figure 10 varies the number of bits; the functions here take any multiple
+of 32 bits, the width of W's last axis.  The
 HATA abstract adds that codes only need to give the relative q.k order,
 which is what a top-k needs.
 

@@ -56,7 +56,7 @@ class Pipeline:
     """Buffers and stage-by-stage calls of the HIP path for one workload."""
 
     def __init__(self, H, inp, kv_dtype, n_q_heads, n_kv_heads, max_ctx, keep_num, keep_den,
-                 keep_abs, top_k, with_v=True, meta_dtype="f32"):
+                 keep_abs, top_k, with_v=True, meta_dtype="f32", code_bits=128):
         self.H = H
         self.inp = inp
         self.kv_dtype = kv_dtype
@@ -66,8 +66,10 @@ class Pipeline:
         self.keep = (keep_num, keep_den, keep_abs)
         self.top_k = top_k
         self.meta_dtype = meta_dtype
+        self.NW = code_bits // 32
+        assert inp["W"].shape[-1] == code_bits
         self.shape = H.make_shape(B, n_q_heads, n_kv_heads, max_ctx, kv_dtype,
-                                  meta_dtype=meta_dtype)
+                                  code_bits=code_bits, meta_dtype=meta_dtype)
         self.d = upload_hhr(inp if with_v else {k: v for k, v in inp.items() if k != "V"},
                             kv_dtype)
         NpCap = max_ctx // 16
@@ -75,11 +77,11 @@ class Pipeline:
         self.p_max = H.hhr_keep_count(NpCap, keep_num, keep_den, keep_abs)
         i32 = dict(dtype=torch.int32, device=dev())
         f32 = dict(dtype=torch.float32, device=dev())
-        self.codes = torch.zeros((B, n_kv_heads, max_ctx, 4), **i32)
+        self.codes = torch.zeros((B, n_kv_heads, max_ctx, self.NW), **i32)
         self.meta = torch.zeros(H.meta_shape(self.shape),
                                 **(f32 if meta_dtype == "f32" else i32))
         self.q_rot = torch.zeros((B, n_q_heads, 128), **f32)
-        self.q_codes = torch.zeros((B, n_q_heads, 4), **i32)
+        self.q_codes = torch.zeros((B, n_q_heads, self.NW), **i32)
         self.scores = torch.full((B, n_kv_heads, NpCap), float("nan"), **f32)
         self.kept = torch.zeros((B, n_kv_heads, self.p_max), **i32)
         self.kept_count = torch.zeros((B, n_kv_heads), **i32)

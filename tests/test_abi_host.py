@@ -115,6 +115,19 @@ def test_shape_errors(H):
     s.page_size = 32
     assert _status(H.hhr_encode_queries, s, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0) == \
         H.HHR_ERR_UNSUPPORTED
+    for bits in (0, 32, 96, 192, 512):
+        s = H.make_shape(**good, code_bits=bits)
+        assert _status(H.hhr_encode_queries, s, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0) == \
+            H.HHR_ERR_UNSUPPORTED, bits
+
+
+def test_workspace_grows_with_code_bits(H):
+    """Query codes (nw words per query head) and the H histograms (code_bits * G + 1 bins per
+    KV head) scale with the code width; every other region is the same."""
+    sizes = {bits: H.hhr_workspace_size(H.make_shape(2, 32, 8, 131072, "bf16", code_bits=bits),
+                                        1, 8, 0, 4096)
+             for bits in (64, 128, 256)}
+    assert 0 < sizes[64] < sizes[128] < sizes[256]
 
 
 def test_pointer_errors(H):

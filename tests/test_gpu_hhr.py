@@ -1,8 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, stage by
 stage (conditioned oracle: each stage fed the GPU's own upstream outputs) and
 end to end (with excused-mismatch accounting), on small seeded cases that span
-several tiles, ragged tails, GQA 1/4/8, an empty-ish sequence and top_k above
-the candidate count.
+several tiles, ragged tails, GQA 1/4/8/16, an empty-ish sequence, top_k above
+the candidate count and 64-, 128- and 256-bit codes.
 """
 import functools
 import math
@@ -17,15 +17,20 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-CASES = synth.small_hhr_cases()
+CASES = synth.small_hhr_cases() + synth.small_code_bits_cases()
 
 
-def _pipeline(H, case, with_v=True):
-    inp = synth.make_hhr_inputs(case["batch"], case["n_q_heads"], case["n_kv_heads"],
-                                case["seq_lens"], case["max_ctx"], case["kv_dtype"], case["seed"])
-    return U.Pipeline(H, inp, case["kv_dtype"], case["n_q_heads"], case["n_kv_heads"],
+def _inputs(case):
+    return synth.make_hhr_inputs(case["batch"], case["n_q_heads"], case["n_kv_heads"],
+                                 case["seq_lens"], case["max_ctx"], case["kv_dtype"],
+                                 case["seed"], code_bits=case.get("code_bits", 128))
+
+
+def _pipeline(H, case, with_v=True, meta_dtype="f32"):
+    return U.Pipeline(H, _inputs(case), case["kv_dtype"], case["n_q_heads"], case["n_kv_heads"],
                       case["max_ctx"], case["keep_num"], case["keep_den"], case["keep_abs"],
-                      case["top_k"], with_v=with_v)
+                      case["top_k"], with_v=with_v, meta_dtype=meta_dtype,
+                      code_bits=case.get("code_bits", 128))
 
 
 def _atol(kv_dtype):
@@ -343,11 +348,7 @@ def test_decode_append(gpu_lib, case, meta_dtype):
     """One fused append + decode step per sequence (one-launch coarse stage), including a
     one-key sequence, a key that opens a page and keys that extend a partial page."""
     print(f"\n[gpu decode_append] {case['name']} meta={meta_dtype}", flush=True)
-    inp = synth.make_hhr_inputs(case["batch"], case["n_q_heads"], case["n_kv_heads"],
-                                case["seq_lens"], case["max_ctx"], case["kv_dtype"], case["seed"])
-    p = U.Pipeline(gpu_lib, inp, case["kv_dtype"], case["n_q_heads"], case["n_kv_heads"],
-                   case["max_ctx"], case["keep_num"], case["keep_den"], case["keep_abs"],
-                   case["top_k"], meta_dtype=meta_dtype)
+    p = _pipeline(gpu_lib, case, meta_dtype=meta_dtype)
     lens, codes0, meta0, sel, sc, out = _decode_append_run(gpu_lib, p)
     pairs = [(b, g) for b in range(p.B) for g in range(p.Hkv)]
     _check_decode_append(p, lens, meta_dtype, codes0, meta0, sel, sc, out, pairs)

@@ -72,18 +72,36 @@ def test_unpack_inverts_pack():
     assert np.array_equal(O.unpack_bits(O.pack_bits(bits)), bits)
 
 
-def test_hamming_closed_form():
-    """H = sum_h (b - <sigma_qh, sigma_k>)/2 with sigma in {+-1}^b taken from the float projections."""
-    rng = _rng(2)
+@pytest.mark.parametrize("nbits", [64, 128, 256])
+def test_hamming_closed_form(nbits):
+    """H = sum_h (b - <sigma_qh, sigma_k>)/2 with sigma in {+-1}^b taken from the float
+    projections, for b-bit codes."""
+    rng = _rng(2 + nbits)
     for G in (1, 4, 16):
-        W = rng.standard_normal((128, 128))
+        W = rng.standard_normal((128, nbits))
         q = rng.standard_normal((G, 128))
         K = rng.standard_normal((50, 128))
-        H = O.hamming(O.hash_codes(q, W), O.hash_codes(K, W))
+        qc, kc = O.hash_codes(q, W), O.hash_codes(K, W)
+        assert qc.shape == (G, nbits // 32) and kc.shape == (50, nbits // 32)
+        H = O.hamming(qc, kc)
         sq = np.where(q @ W >= 0, 1.0, -1.0)
         sk = np.where(K @ W >= 0, 1.0, -1.0)
-        closed = ((128.0 - sk @ sq.T) / 2.0).sum(axis=1)
+        closed = ((nbits - sk @ sq.T) / 2.0).sum(axis=1)
         assert np.array_equal(H, closed.astype(np.int64))
+        assert H.max() <= nbits * G
+
+
+def test_hamming_extremes_at_every_width():
+    """Identical codes give 0, complementary codes give the full width per query head."""
+    for nbits in (64, 128, 256):
+        bits = _rng(nbits).random((3, nbits)) < 0.5
+        c = O.pack_bits(bits)
+        assert O.hamming(c[:1], c[:1]).tolist() == [0]
+        assert O.hamming(c[:1], O.pack_bits(~bits[:1])).tolist() == [nbits]
+        # three query heads against the complement of head 0: nbits + the two others'
+        # distances to head 0's complement, counted bit by bit
+        want = nbits + int((bits[1] == bits[0]).sum()) + int((bits[2] == bits[0]).sum())
+        assert O.hamming(c, O.pack_bits(~bits[:1])).tolist() == [want]
 
 
 def test_codes_scale_invariant():
