@@ -34,6 +34,51 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// min / max by med3 against an infinity: med3(x, y, -inf) = min(x, y) and
+// med3(x, y, +inf) = max(x, y) for non-NaN x, y.  v_med3 needs no NaN
+// canonicalisation of its operands, which IEEE-mode minnum / maxnum add.  The
+// infinity must come from opaque_inf(): a literal would let the compiler fold
+// med3 back into minnum / maxnum.
+__device__ __forceinline__ float opaque_inf() {
+  float r;
+  asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(r));
+  return r;
+}
+__device__ __forceinline__ float med_min(float a, float b, float inf) {
+  return __builtin_amdgcn_fmed3f(a, b, -inf);
+}
+__device__ __forceinline__ float med_max(float a, float b, float inf) {
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+
+// gfx950 lane swaps: with both operands x, v_permlane32_swap leaves {x[l],
+// x[l ^ 32]} in the two results of every lane l, v_permlane16_swap {x[l],
+// x[l ^ 16]}.  One VALU instruction each, no LDS.
+__device__ __forceinline__ float fmin_swap32(float x, float inf) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return med_min(__uint_as_float(p[0]), __uint_as_float(p[1]), inf);
+}
+__device__ __forceinline__ float fmax_swap32(float x, float inf) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return med_max(__uint_as_float(p[0]), __uint_as_float(p[1]), inf);
+}
+__device__ __forceinline__ float fmin_swap16(float x, float inf) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return med_min(__uint_as_float(p[0]), __uint_as_float(p[1]), inf);
+}
+__device__ __forceinline__ float fmax_swap16(float x, float inf) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return med_max(__uint_as_float(p[0]), __uint_as_float(p[1]), inf);
+}
+__device__ __forceinline__ uint32_t or_swap32(uint32_t x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return p[0] | p[1];
+}
+__device__ __forceinline__ uint32_t or_swap16(uint32_t x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return p[0] | p[1];
+}
+
 // Directed rounding f32 -> bf16 bits.  A bf16 value is the upper half of an
 // f32 pattern, so dropping the lower half rounds the magnitude down (toward
 // zero).  Rounding toward -inf is that for x >= 0 and one step up in magnitude
