@@ -72,48 +72,101 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
   reps[((size_t)b * (Lcap / block) + blk) * kD + d] = acc / (float)(r1 - r0);
 }
 
-// H2: 16 blocks per workgroup; thread (bl = tid/16, hg = tid%16) takes heads
-// hg, hg+16, hg+32, hg+48 of block bl, and the 16 threads of a block reduce.
-// shared: every query row b reads the one cache (row 0) of reps, as in prefill.
-__global__ __launch_bounds__(256) void k_hisa_block_scores(
+// H2 on MFMA.  One wave per 16 blocks of one query:
+//   D[h][blk] = sum_d e4m3(q8[h][d]) rep[blk][d]
+// as 4 head tiles x 4 K-steps of 16x16x32 bf16 MFMAs: the fp8 query is exact
+// in bf16, the f32 representative is split into bf16 hi + lo (two MFMAs, f32
+// sums).  Then s_blk = sum_h w_h ReLU(q_scale_h D[h][blk]).  Lane (lrow,
+// lgrp) holds D of block lrow for heads 16 mt + 4 lgrp + j: it sums its 16
+// heads in that order, and two lane-swap adds sum the four lane groups.  Waves
+// are independent (no LDS, no barrier): a wave past the last block exits.
+constexpr int kBsWaves = 4;
+
+__device__ __forceinline__ float add_swap32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_swap16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// 8 fp8 e4m3fn values -> 8 bf16 (exact: 4 significant bits, exponents in range)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = v[i >> 1] >> (16 * (i & 1));
+    const uint32_t lo = __float_as_uint(e4m3fn_to_f32(word & 0xFFu)) >> 16;
+    const uint32_t hi = __float_as_uint(e4m3fn_to_f32((word >> 8) & 0xFFu)) >> 16;
+    r[i] = lo | (hi << 16);
+  }
+  return as_bf16x8(r);
+}
+
+__global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
     const int32_t* __restrict__ seq_len, float* __restrict__ block_scores,
     uint32_t* __restrict__ status, int Hi, int Lcap, int block, int shared) {
-  __shared__ float sq[kMaxIndexHeads][kD + 1];
-  __shared__ float srep[16][kD];
   const int b = blockIdx.y;
   const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 ? status : nullptr);
   const int Nb = (L + block - 1) / block;
   const int NbCap = Lcap / block;
-  const int blk0 = blockIdx.x * 16;
-  if (blk0 >= Nb) return;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < Hi * kD; i += 256) {
-    const int h = i / kD, d = i % kD;
-    sq[h][d] = q_scale[(size_t)b * Hi + h] * e4m3fn_to_f32(q8[((size_t)b * Hi + h) * kD + d]);
-  }
-  for (int i = tid; i < 16 * kD; i += 256) {
-    const int bl = i / kD, d = i % kD;
-    srep[bl][d] =
-        (blk0 + bl < Nb) ? reps[((size_t)(shared ? 0 : b) * NbCap + blk0 + bl) * kD + d] : 0.f;
-  }
-  __syncthreads();
-  const int bl = tid >> 4;
-  const int hg = tid & 15;
-  float part = 0.f;
+  const int wv = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int lrow = l & 15;
+  const int lgrp = l >> 4;
+  const int blk0 = (blockIdx.x * kBsWaves + wv) * 16;
+  if (blk0 >= Nb) return;  // wave-uniform
+  // B: the representative of block blk0 + lrow (the last block past the end),
+  // dims 32 ks + 8 lgrp + [0, 8)
+  const float* rb = reps + ((size_t)(shared ? 0 : b) * NbCap + min(blk0 + lrow, Nb - 1)) * kD;
+  bf16x8 bhi[4], blo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = hg + 16 * i;
-    if (h < Hi) {
-      float dot = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < kD; ++d) dot = fmaf(sq[h][d], srep[bl][d], dot);
-      part = fmaf(w[(size_t)b * Hi + h], fmaxf(dot, 0.f), part);
+  for (int ks = 0; ks < 4; ++ks) {
+    const floatx4 x0 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
+    const floatx4 x1 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
+    u32x4 hv, lv;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(jj < 2 ? x0[2 * jj] : x1[2 * jj - 4], h0, l0);
+      split_bf16(jj < 2 ? x0[2 * jj + 1] : x1[2 * jj - 3], h1, l1);
+      hv[jj] = h0 | (h1 << 16);
+      lv[jj] = l0 | (l1 << 16);
+    }
+    bhi[ks] = as_bf16x8(hv);
+    blo[ks] = as_bf16x8(lv);
+  }
+  // A: head 16 mt + lrow of the query (heads >= Hi are zero)
+  const uint8_t* qb = q8 + (size_t)b * Hi * kD;
+  floatx4 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int h = 16 * mt + lrow;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x2 raw = {0u, 0u};
+      if (h < Hi) raw = *(const u32x2*)(qb + (size_t)h * kD + 32 * ks + 8 * lgrp);
+      const bf16x8 a = e4m3x8_to_bf16x8(raw);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi[ks], acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo[ks], acc[mt], 0, 0, 0);
     }
   }
-  part = row_sum16(part);
-  if (hg == 0 && blk0 + bl < Nb) block_scores[(size_t)b * NbCap + blk0 + bl] = part;
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 16 * mt + 4 * lgrp + j;
+      if (h < Hi)
+        part = fmaf(w[(size_t)b * Hi + h],
+                    fmaxf(acc[mt][j] * q_scale[(size_t)b * Hi + h], 0.f), part);
+    }
+  part = add_swap16(add_swap32(part));
+  if (lgrp == 0 && blk0 + lrow < Nb) block_scores[(size_t)b * NbCap + blk0 + lrow] = part;
 }
 
 // H3: exact top keep_blocks blocks of one query (thread tid takes a run of consecutive blocks).
@@ -143,73 +196,111 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   if (tid == 0) kept_count[b] = cnt;
 }
 
-// H4: token scores of one kept block on fp8 MFMA.  D[token][head] =
-// sum_d e4m3(k8[token][d]) e4m3(q8[head][d]) (exact products, f32 sums), then
-// s_t = sum_h w_h ReLU(D * (q_scale_h * k_scale_t)).  Wave w takes the
-// 16-token tiles w, w+4, ... of the block; 4 head tiles x 4 K-steps per tile.
+// H4: token scores on fp8 MFMA.  A workgroup takes the kept-block slots
+// [slot0, slot0 + nslot) of one query row; its waves take the 16-token tiles of
+// those blocks in turn.  Per tile, the transposed product
+//   D[h][t] = sum_d e4m3(q8[h][d]) e4m3(k8[t][d])   (exact products, f32 sums)
+// runs as 4 head tiles x 4 K-steps; lane (lrow, lgrp) holds D for token lrow
+// and heads 16 ht + 4 lgrp + j, so
+//   s_t = k_scale_t * sum_h (w_h q_scale_h) ReLU(D[h][t])
+// (the scales are positive, so they factor out of the ReLU) is 16 in-lane
+// steps and two lane-swap adds.  The query's fragments and weights stay in
+// registers for all its tiles; each wave keeps the key fragments of its next
+// two tiles in flight.
 typedef long fp8x8;
+constexpr int kTsWaves = 8;
 
-__global__ __launch_bounds__(256) void k_hisa_token_scores(
+__global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
-    float* __restrict__ token_scores, int Hi, int Lcap, int block, int shared) {
-  const int b = blockIdx.y;
-  const int slot = blockIdx.x;
+    float* __restrict__ token_scores, int Hi, int Lcap, int block, int shared, int nslot,
+    int nrows, int xcd_rows) {
+  // xcd_rows: rows in contiguous runs per XCD (workgroups go round-robin over
+  // the eight XCDs; the grid has 8 x ceil(nrows / 8) rows): neighbouring rows
+  // keep mostly the same blocks and share an L2
+  const int by = blockIdx.y;
+  const int b = xcd_rows ? (by % 8) * (gridDim.y / 8) + by / 8 : by;
+  if (b >= nrows) return;
+  const int slot0 = blockIdx.x * nslot;
   int L = seq_len[b];
   if (L < 0 || L > Lcap) L = 0;
   const int kc = min(kept_count[b], keep_blocks);
-  if (slot >= kc) return;
-  const int blk = kept[(size_t)b * keep_blocks + slot];
-  if (blk < 0) return;
-  const int t0 = blk * block;
+  const int slot1 = min(slot0 + nslot, kc);
+  if (slot0 >= slot1) return;
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int l = tid & 63;
   const int lrow = l & 15;
   const int lgrp = l >> 4;
 
-  fp8x8 bq[4][4];
-  float wq[4], sqh[4];
+  // A: head 16 ht + lrow; this lane's 16 heads for the epilogue: 16 ht + 4 lgrp + j
+  fp8x8 aq[4][4];
+  float wsq[4][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int h = 16 * nt + lrow;
-    wq[nt] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
-    sqh[nt] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = 16 * ht + lrow;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bq[nt][ks] = h < Hi ? *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp) : 0;
+      aq[ht][ks] = h < Hi ? *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp) : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int he = 16 * ht + 4 * lgrp + j;
+      wsq[ht][j] = he < Hi ? w[(size_t)b * Hi + he] * q_scale[(size_t)b * Hi + he] : 0.f;
+    }
   }
   const size_t cb = shared ? 0 : (size_t)b;  // the query row's cache
   const uint8_t* kb = k8 + cb * Lcap * kD;
   const float* ksb = k_scale + cb * Lcap;
-  float* ts = token_scores + ((size_t)b * keep_blocks + slot) * block;
-  const int ntile = block / 16;
-  for (int mt = wv; mt < ntile; mt += 4) {
-    const int ta = t0 + 16 * mt + lrow;  // A row of this lane
-    fp8x8 a[4];
+  const int tiles_per_block = block / 16;
+  const int ntiles = (slot1 - slot0) * tiles_per_block;
+  // key fragments of tile i (token row of this lane; rows past L read row 0)
+  auto tile_token = [&](int i) {
+    const int slot = slot0 + i / tiles_per_block;
+    const int blk = kept[(size_t)b * keep_blocks + slot];
+    return blk * block + 16 * (i % tiles_per_block) + lrow;
+  };
+  auto load_tile = [&](int i, fp8x8 (&kf)[4]) {
+    const int t = tile_token(i);
+    const size_t row = (t >= 0 && t < L) ? (size_t)t : 0;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      a[ks] = ta < L ? *(const fp8x8*)(kb + (size_t)ta * kD + 32 * ks + 8 * lgrp) : 0;
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *(const fp8x8*)(kb + row * kD + 32 * ks + 8 * lgrp);
+  };
+  int i = wv;
+  fp8x8 kf[4], k1[4];
+  if (i < ntiles) load_tile(i, kf);
+  if (i + kTsWaves < ntiles) load_tile(i + kTsWaves, k1);
+  for (; i < ntiles; i += kTsWaves) {
+    fp8x8 k2[4];
+    if (i + 2 * kTsWaves < ntiles) load_tile(i + 2 * kTsWaves, k2);
     floatx4 acc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < 4; ++ht) {
+      acc[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a[ks], bq[nt][ks], acc[nt], 0, 0, 0);
+        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aq[ht][ks], kf[ks], acc[ht], 0, 0, 0);
+    }
+    const int t = tile_token(i);
+    const bool valid = t >= 0 && t < L;
+    const float sk = valid ? ksb[t] : 0.f;
+    const float inf = opaque_inf();
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part = fmaf(wsq[ht][j], med_max(acc[ht][j], 0.f, inf), part);
+    part = add_swap16(add_swap32(part)) * sk;
+    if (lgrp == 0) {
+      const int slot = slot0 + i / tiles_per_block;
+      token_scores[((size_t)b * keep_blocks + slot) * block + 16 * (i % tiles_per_block) + lrow] =
+          valid ? part : -__builtin_huge_valf();
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tt = t0 + 16 * mt + 4 * lgrp + j;
-      const float sk = tt < L ? ksb[tt] : 0.f;
-      float part = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        part = fmaf(wq[nt], fmaxf(acc[nt][j] * (sqh[nt] * sk), 0.f), part);
-      part = row_sum16(part);
-      if (lrow == 0) ts[16 * mt + 4 * lgrp + j] = tt < L ? part : -__builtin_huge_valf();
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = k1[ks];
+      k1[ks] = k2[ks];
     }
   }
 }
@@ -270,7 +361,8 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const int32_t* seq_len, float* block_scores,
                                     uint32_t* status, hipStream_t stream, bool shared) {
   const int NbCap = s.max_ctx / s.block;
-  hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + 15) / 16, s.batch), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + 16 * kBsWaves - 1) / (16 * kBsWaves), s.batch),
+                     dim3(64 * kBsWaves), 0, stream,
                      q8, q_scale, w, reps, seq_len, block_scores, status, s.n_index_heads,
                      s.max_ctx, s.block, shared ? 1 : 0);
   return hipGetLastError();
@@ -293,9 +385,17 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                                   int32_t* sel_count, float* token_scores, uint32_t* status,
                                   hipStream_t stream, bool shared) {
   (void)status;
-  hipLaunchKernelGGL(k_hisa_token_scores, dim3(keep_blocks, s.batch), dim3(256), 0, stream, q8,
+  // enough workgroups to fill the chip: a run of kept blocks per workgroup,
+  // all of a row's blocks once there are many rows
+  const int nsplit = std::max(1, std::min<int>(keep_blocks, (512 + s.batch - 1) / s.batch));
+  const int nslot = (keep_blocks + nsplit - 1) / nsplit;
+  // many rows: spread them over the 8 XCDs in contiguous runs
+  const int xcd_rows = s.batch >= 64;
+  const int rows = xcd_rows ? (s.batch + 7) / 8 * 8 : s.batch;
+  hipLaunchKernelGGL(k_hisa_token_scores, dim3(nsplit, rows), dim3(64 * kTsWaves), 0, stream, q8,
                      q_scale, w, k8, k_scale, seq_len, kept, kept_count, keep_blocks,
-                     token_scores, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0);
+                     token_scores, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0, nslot,
+                     s.batch, xcd_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_hisa_topk, dim3(s.batch), dim3(kHisaThreads), 0, stream, token_scores,
