@@ -72,14 +72,15 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
   reps[((size_t)b * (Lcap / block) + blk) * kD + d] = acc / (float)(r1 - r0);
 }
 
-// H2 on MFMA.  One wave per 16 blocks of one query:
+// H2 on MFMA.  A wave takes groups of 16 blocks of one query:
 //   D[h][blk] = sum_d e4m3(q8[h][d]) rep[blk][d]
 // as 4 head tiles x 4 K-steps of 16x16x32 bf16 MFMAs: the fp8 query is exact
 // in bf16, the f32 representative is split into bf16 hi + lo (two MFMAs, f32
 // sums).  Then s_blk = sum_h w_h ReLU(q_scale_h D[h][blk]).  Lane (lrow,
 // lgrp) holds D of block lrow for heads 16 mt + 4 lgrp + j: it sums its 16
-// heads in that order, and two lane-swap adds sum the four lane groups.  Waves
-// are independent (no LDS, no barrier): a wave past the last block exits.
+// heads in that order, and two lane-swap adds sum the four lane groups.  The
+// workgroup converts the query to bf16 once, into LDS; after that barrier the
+// waves are independent, and a wave past the last block stops.
 constexpr int kBsWaves = 4;
 
 __device__ __forceinline__ float add_swap32(float x) {
@@ -91,82 +92,101 @@ __device__ __forceinline__ float add_swap16(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// 8 fp8 e4m3fn values -> 8 bf16 (exact: 4 significant bits, exponents in range)
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 v) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t word = v[i >> 1] >> (16 * (i & 1));
-    const uint32_t lo = __float_as_uint(e4m3fn_to_f32(word & 0xFFu)) >> 16;
-    const uint32_t hi = __float_as_uint(e4m3fn_to_f32((word >> 8) & 0xFFu)) >> 16;
-    r[i] = lo | (hi << 16);
-  }
-  return as_bf16x8(r);
-}
-
 __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
     const int32_t* __restrict__ seq_len, float* __restrict__ block_scores,
-    uint32_t* __restrict__ status, int Hi, int Lcap, int block, int shared) {
+    uint32_t* __restrict__ status, int Hi, int Lcap, int block, int shared, int gpw) {
+  // the query in bf16, converted once per workgroup (rows padded against bank
+  // conflicts; heads >= Hi are zero)
+  __shared__ __attribute__((aligned(16))) uint16_t sq[kMaxIndexHeads][kD + 8];
   const int b = blockIdx.y;
   const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 ? status : nullptr);
   const int Nb = (L + block - 1) / block;
   const int NbCap = Lcap / block;
-  const int wv = threadIdx.x >> 6;
-  const int l = threadIdx.x & 63;
+  const int wg_blk0 = blockIdx.x * kBsWaves * gpw * 16;
+  if (wg_blk0 >= Nb) return;  // block-uniform, before the barrier
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int l = tid & 63;
   const int lrow = l & 15;
   const int lgrp = l >> 4;
-  const int blk0 = (blockIdx.x * kBsWaves + wv) * 16;
-  if (blk0 >= Nb) return;  // wave-uniform
-  // B: the representative of block blk0 + lrow (the last block past the end),
-  // dims 32 ks + 8 lgrp + [0, 8)
-  const float* rb = reps + ((size_t)(shared ? 0 : b) * NbCap + min(blk0 + lrow, Nb - 1)) * kD;
-  bf16x8 bhi[4], blo[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const floatx4 x0 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
-    const floatx4 x1 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
-    u32x4 hv, lv;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(jj < 2 ? x0[2 * jj] : x1[2 * jj - 4], h0, l0);
-      split_bf16(jj < 2 ? x0[2 * jj + 1] : x1[2 * jj - 3], h1, l1);
-      hv[jj] = h0 | (h1 << 16);
-      lv[jj] = l0 | (l1 << 16);
-    }
-    bhi[ks] = as_bf16x8(hv);
-    blo[ks] = as_bf16x8(lv);
-  }
-  // A: head 16 mt + lrow of the query (heads >= Hi are zero)
   const uint8_t* qb = q8 + (size_t)b * Hi * kD;
-  floatx4 acc[4];
+  for (int i = tid; i < kMaxIndexHeads * kD / 4; i += 64 * kBsWaves) {
+    const int h = i / (kD / 4);
+    const int d = 4 * (i % (kD / 4));
+    const uint32_t v = h < Hi ? *(const uint32_t*)(qb + (size_t)h * kD + d) : 0u;
+    u32x2 pk;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int h = 16 * mt + lrow;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x2 raw = {0u, 0u};
-      if (h < Hi) raw = *(const u32x2*)(qb + (size_t)h * kD + 32 * ks + 8 * lgrp);
-      const bf16x8 a = e4m3x8_to_bf16x8(raw);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi[ks], acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo[ks], acc[mt], 0, 0, 0);
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t lo = __float_as_uint(e4m3fn_to_f32((v >> (16 * k)) & 0xFFu)) >> 16;
+      const uint32_t hi = __float_as_uint(e4m3fn_to_f32((v >> (16 * k + 8)) & 0xFFu)) >> 16;
+      pk[k] = lo | (hi << 16);
     }
+    *(u32x2*)&sq[h][d] = pk;
   }
-  float part = 0.f;
+  __syncthreads();
+  // A: head 16 mt + lrow, dims 32 ks + 8 lgrp + [0, 8)
+  bf16x8 aq[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      aq[mt][ks] = as_bf16x8(*(const u32x4*)&sq[16 * mt + lrow][32 * ks + 8 * lgrp]);
+  // this lane's 16 heads in the epilogue: 16 mt + 4 lgrp + j
+  float wh[4][4], sh[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int h = 16 * mt + 4 * lgrp + j;
-      if (h < Hi)
-        part = fmaf(w[(size_t)b * Hi + h],
-                    fmaxf(acc[mt][j] * q_scale[(size_t)b * Hi + h], 0.f), part);
+      wh[mt][j] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
+      sh[mt][j] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
     }
-  part = add_swap16(add_swap32(part));
-  if (lgrp == 0 && blk0 + lrow < Nb) block_scores[(size_t)b * NbCap + blk0 + lrow] = part;
+  const float inf = opaque_inf();
+  for (int grp = 0; grp < gpw; ++grp) {
+    const int blk0 = wg_blk0 + (grp * kBsWaves + wv) * 16;
+    if (blk0 >= Nb) break;  // wave-uniform; no barrier follows
+    // B: the representative of block blk0 + lrow (the last block past the
+    // end), dims 32 ks + 8 lgrp + [0, 8)
+    const float* rb =
+        reps + ((size_t)(shared ? 0 : b) * NbCap + min(blk0 + lrow, Nb - 1)) * kD;
+    bf16x8 bhi[4], blo[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const floatx4 x0 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
+      const floatx4 x1 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
+      u32x4 hv, lv;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16(jj < 2 ? x0[2 * jj] : x1[2 * jj - 4], h0, l0);
+        split_bf16(jj < 2 ? x0[2 * jj + 1] : x1[2 * jj - 3], h1, l1);
+        hv[jj] = h0 | (h1 << 16);
+        lv[jj] = l0 | (l1 << 16);
+      }
+      bhi[ks] = as_bf16x8(hv);
+      blo[ks] = as_bf16x8(lv);
+    }
+    floatx4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[mt][ks], bhi[ks], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[mt][ks], blo[ks], acc[mt], 0, 0, 0);
+      }
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        part = fmaf(wh[mt][j], med_max(acc[mt][j] * sh[mt][j], 0.f, inf), part);
+    part = add_swap16(add_swap32(part));
+    if (lgrp == 0 && blk0 + lrow < Nb) block_scores[(size_t)b * NbCap + blk0 + lrow] = part;
+  }
 }
 
 // H3: exact top keep_blocks blocks of one query (thread tid takes a run of consecutive blocks).
@@ -361,10 +381,13 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const int32_t* seq_len, float* block_scores,
                                     uint32_t* status, hipStream_t stream, bool shared) {
   const int NbCap = s.max_ctx / s.block;
-  hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + 16 * kBsWaves - 1) / (16 * kBsWaves), s.batch),
-                     dim3(64 * kBsWaves), 0, stream,
-                     q8, q_scale, w, reps, seq_len, block_scores, status, s.n_index_heads,
-                     s.max_ctx, s.block, shared ? 1 : 0);
+  // many queries: each workgroup covers 4 groups of 16 blocks per wave, so the
+  // query conversion is shared; few: one group per wave for parallelism
+  const int gpw = s.batch >= 64 ? 4 : 1;
+  const int per_wg = 16 * kBsWaves * gpw;
+  hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + per_wg - 1) / per_wg, s.batch),
+                     dim3(64 * kBsWaves), 0, stream, q8, q_scale, w, reps, seq_len, block_scores,
+                     status, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0, gpw);
   return hipGetLastError();
 }
 
