@@ -424,3 +424,33 @@ def test_keep_all_pages_and_k_equal_L_is_dense_attention(gpu_lib):
     ref = torch.nn.functional.scaled_dot_product_attention(
         q[:, None, :], K[None].expand(4, -1, -1), V[None].expand(4, -1, -1))[:, 0]
     assert (p.out[0].double().cpu() - ref).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("code_bits", [64, 256])
+def test_long_append_other_code_widths(gpu_lib, code_bits):
+    """A 40,000-key append at 64- and 256-bit codes: the bf16 encoder runs several key tiles
+    per workgroup (its LDS ring with tiles in flight), with its wave count and load waits
+    for that width.  Sampled codes and page metadata against the oracle."""
+    print(f"\n[gpu long append] code_bits={code_bits}", flush=True)
+    L, Lcap, Hq, Hkv = 40000, 40960, 8, 2
+    inp = synth.make_hhr_inputs(1, Hq, Hkv, [L], Lcap, "bf16", 31, code_bits=code_bits,
+                                make_v=False)
+    p = U.Pipeline(gpu_lib, inp, "bf16", Hq, Hkv, Lcap, 1, 8, 0, 256, with_v=False,
+                   code_bits=code_bits)
+    p.append_all()
+    torch.cuda.synchronize()
+    assert p.status() == 0
+    codes = U.u32(p.codes)
+    rng = np.random.Generator(np.random.PCG64(5))
+    Np = O.n_pages(L, 16)
+    for g in range(Hkv):
+        K = p.K_valid(0, g)
+        rows = np.unique(np.concatenate([rng.choice(L, 3000, replace=False), [0, L - 1]]))
+        U.check_code_bits(K[rows], p.inp["W"][g], codes[0, g, rows])
+        meta = p.meta[0, g].cpu().numpy().astype(np.float64)
+        R = p.inp["R"][g].astype(np.float64)
+        for pg in np.unique(np.concatenate([rng.choice(Np, 200, replace=False), [0, Np - 1]])):
+            Kp = K[pg * 16:min(L, pg * 16 + 16)]
+            want = O.page_minmax(O.rotate(Kp, R), 16)[0]
+            tol = 3e-5 * (np.abs(Kp) @ np.abs(R)).max()
+            assert np.abs(meta[pg] - want).max() <= tol, (g, pg)

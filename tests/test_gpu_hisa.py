@@ -323,20 +323,25 @@ def _margin_ok(scores, k):
     return abs(s[k - 1] - s[k]) > SCORE_EXCUSE * max(abs(s[k - 1]), 1e-30)
 
 
+@pytest.mark.parametrize("n_rand", [41, 150], ids=["rows48", "rows150"])
 @pytest.mark.parametrize("keep_all", [False, True])
-def test_prefill_select(gpu_lib, keep_all):
+def test_prefill_select(gpu_lib, keep_all, n_rand):
     """Query rows at positions across a 4000-key cache (first token, block edges, the end)
     against one shared cache: equal, bit for bit, to hhr_hisa_select on per-row copies of
     the cache and of its shared pooled representatives; equal to the oracle's prefill
     selection on every row whose block and token cut-offs have no near-tie; with every
-    block kept, equal to the flat indexer on each row's prefix."""
+    block kept, equal to the flat indexer on each row's prefix.  With 64 rows or more the
+    block scores cover four 16-block groups per wave and the token scores map rows to
+    XCDs in runs (a row count that is not a multiple of 8 leaves padding rows)."""
     H = gpu_lib
-    print(f"\n[gpu hisa prefill] keep_all={keep_all}", flush=True)
+    print(f"\n[gpu hisa prefill] keep_all={keep_all} n_rand={n_rand}", flush=True)
     Hi, blk, Lcap, L, top_k = 16, 64, 4096, 4000, 300
     keep = Lcap // blk if keep_all else 8
     rng = np.random.default_rng(61)
     pos = np.unique(np.concatenate([[0, 62, 63, 64, 127, 128, L - 1],
-                                    rng.integers(0, L, 41)]))
+                                    rng.integers(0, L, n_rand)]))
+    while n_rand > 64 and pos.size % 8 != 3:  # > 64 rows, not a multiple of 8
+        pos = np.delete(pos, pos.size // 2)
     q_len = (pos + 1).astype(np.int32)
     M = q_len.size
     src = synth.make_hisa_inputs(Hi, L, Lcap, 4, 62, block=blk, make_kv=False)
