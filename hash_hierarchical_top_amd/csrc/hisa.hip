@@ -203,11 +203,8 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   int32_t* out = kept + (size_t)b * keep_blocks;
   const float* sc = block_scores + (size_t)b * NbCap;
   __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
-#pragma unroll
-  for (int i = 0; i < kHisaItems; ++i) {
-    const int c = i * kHisaThreads + tid;
-    sbuf[c] = sc[min(c, max(Nb - 1, 0))];
-  }
+  // only the Nb candidates: the selection reads no slot past them
+  for (int c = tid; c < Nb; c += kHisaThreads) sbuf[c] = sc[c];
   __syncthreads();
   const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
       sbuf, Nb, [](int) { return true; }, keep_blocks, sh,
@@ -346,16 +343,17 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
   __syncthreads();
   const float* ts = token_scores + (size_t)b * keep_blocks * block;
   __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
-#pragma unroll
-  for (int i = 0; i < kHisaItems; ++i) {
-    const int c = i * kHisaThreads + tid;
-    sbuf[c] = ts[min(c, max(ncand - 1, 0))];
+  // only the ncand candidates (whole blocks, 16-byte aligned runs): the
+  // selection reads no slot past them
+  {
+    const floatx4* ts4 = reinterpret_cast<const floatx4*>(ts);
+    floatx4* sb4 = reinterpret_cast<floatx4*>(sbuf);
+    for (int i = tid; i < ncand / 4; i += kHisaThreads) sb4[i] = ts4[i];
   }
   __syncthreads();
-  auto present = [&](int c) {
-    const int blk = skept[c / block];
-    return blk >= 0 && blk * block + c % block < L;
-  };
+  // the token-score pass wrote -inf for every slot past the sequence end and a
+  // finite score for every token of it
+  auto present = [&](int c) { return sbuf[c] != -__builtin_huge_valf(); };
   int32_t* out = sel_idx + (size_t)b * top_k;
   const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
       sbuf, ncand, present, top_k, sh,
