@@ -218,6 +218,7 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
   w.attn_part = take(attn_part_bytes(s, w.n_split));
+  w.ham_all = take(BHkv * (size_t)s.max_ctx * sizeof(uint16_t));
   w.total = off;
   *ws = w;
   return true;
@@ -439,6 +440,7 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->dist = reinterpret_cast<uint16_t*>(base + ws->ham_dist);
   buf->chist = reinterpret_cast<int*>(base + ws->ham_hist);
   buf->cum = reinterpret_cast<uint16_t*>(base + ws->ham_cum);
+  buf->hall = reinterpret_cast<uint16_t*>(base + ws->ham_all);
   return HHR_OK;
 }
 
@@ -535,8 +537,12 @@ static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int3
   hhr::Workspace ws;
   hhr::CompositeBuffers buf;
   // Few attention workgroups: each picks its own keys (no selection launch).
-  // Many: the one-workgroup-per-(b, g) selection, then plain attention, which
-  // costs less than every workgroup repeating the pick.  Same results.
+  // Many: the selection first (in the coarse launch when that is one launch,
+  // else one workgroup per (b, g)), then plain attention, which costs less
+  // than every workgroup repeating the pick.  Same results.  (With few
+  // attention workgroups the pick also beats the one-launch selection at
+  // 128K: its distance launch and pick cost less than the selection's
+  // single-CU tail plus a separate attention launch.)
   hhr::Workspace probe;
   hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &probe);
   // The in-attention pick reads 128-bit-code histograms only.

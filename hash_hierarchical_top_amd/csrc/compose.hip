@@ -32,6 +32,9 @@ constexpr int kScoreThreads = 1024;
 // the coarse stage runs staged instead (query encode, bounds, top-P).
 constexpr int kScoreToppMaxWgs = 2 * 256;
 constexpr int kScorePagesPerWg = (kScoreThreads / kWave) * kScorePagesPerWave;  // 256
+// Polls (about a microsecond each) before the top-P workgroup of the
+// one-launch selection gives up waiting for the other workgroups' distances.
+constexpr int kFineSpinMax = 1 << 20;
 
 __device__ __forceinline__ int clamped_len(const int32_t* seq_len, int b, int Lcap,
                                            uint32_t* status) {
@@ -57,18 +60,50 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n_wg, in
   return *s_last != 0;
 }
 
+// Thread 0 polls *p (agent scope) until it reaches want, giving up after
+// kFineSpinMax polls (HHR_DEV_TIMEOUT); the workgroup then meets at a
+// barrier.  Used only to wait for workgroups that are already running.
+__device__ __forceinline__ void wait_count(const uint32_t* p, uint32_t want, uint32_t* status);
+
+struct ScoreRotSmem {
+  QencSmem qe;
+  float qrot[kMaxG][kD];
+  float xnew[kD];  // the appended key's rotation (APPEND)
+};
+
+__device__ __forceinline__ void wait_count(const uint32_t* p, uint32_t want, uint32_t* status) {
+  if (threadIdx.x == 0) {
+    uint32_t n = ld_agent_u32(p);
+    for (int spin = 0; n < want && spin < kFineSpinMax; ++spin) {
+      __builtin_amdgcn_s_sleep(2);
+      n = ld_agent_u32(p);
+    }
+    if (n < want) atomicOr(status, HHR_DEV_TIMEOUT);
+  }
+  __syncthreads();
+}
+
 struct ScoreTopSmem {
   union {
-    struct {
-      QencSmem qe;
-      float qrot[kMaxG][kD];
-      float xnew[kD];  // the appended key's rotation (APPEND)
-    } rot;
+    ScoreRotSmem rot;
     struct {
       __attribute__((aligned(16))) float sbuf[kMaxCtx / kPS];
       TopScratch top;
     } sel;
   };
+};
+
+// With the fine stage: the top-P stages the bounds in fine.scores and emits
+// the kept pages into fine.skept, then the distances of their keys replace
+// the bounds (fine.hval).  The query codes stay outside the union.
+struct ScoreFineSmem {
+  union {
+    ScoreRotSmem rot;
+    HamSmem fine;
+  };
+  __attribute__((aligned(16))) uint32_t qc[kMaxG * kNW];
+  // the top-P workgroup's own pages' distances (ham_wave_dist's packing)
+  __attribute__((aligned(16))) uint16_t own_h[kScorePagesPerWg * kPS];
 };
 
 // Folds the appended key's rotation x (LDS, 128 dims) into page pn's metadata
@@ -134,7 +169,16 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 // {min, max} (or starts the page with it) in registers before the bound, and
 // stores the page's metadata back.  Nothing else touches that page, so no
 // other workgroup can see it half-updated.
-template <bool MBF, bool APPEND>
+//
+// FINE (S5 + S6 as well): every workgroup also encodes the query codes.
+// After the first hand-off every other workgroup computes H for every key of
+// its own pages (ham_page_wave) while the top-P runs, and counts itself in on
+// a second counter.  The top-P workgroup then waits for that count, gathers
+// the kept pages' distances (computing those of its own pages on the spot),
+// takes the exact top-k by (H, position) and writes sel_idx and sel_count.
+// So the fine stage costs one gather after the top-P instead of two further
+// launches.
+template <bool MBF, bool APPEND, bool FINE>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
     const float* __restrict__ R, const float* __restrict__ W, void* __restrict__ meta,
@@ -143,8 +187,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     float* __restrict__ scores, float2* __restrict__ wave_range,
     uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
-    uint32_t* __restrict__ status) {
-  __shared__ ScoreTopSmem sm;
+    uint32_t* __restrict__ status, const uint32_t* __restrict__ ham_codes,
+    uint16_t* __restrict__ hall, int top_k, int32_t* __restrict__ sel_idx,
+    int32_t* __restrict__ sel_count) {
+  using Smem = std::conditional_t<FINE, ScoreFineSmem, ScoreTopSmem>;
+  __shared__ Smem sm;
   __shared__ int s_last;
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
@@ -175,20 +222,23 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
         sm.rot.xnew[col] = v;
     };
     auto code_key = [&](int h, int word, uint32_t bits) {
-      if (h == G)
+      if (h == G) {
         crow[word] = bits;
-      else if (blockIdx.x == 0)
-        q_codes[cbase + (size_t)h * kNW + word] = bits;
+      } else {
+        if constexpr (FINE) sm.qc[h * kNW + word] = bits;
+        if (blockIdx.x == 0) q_codes[cbase + (size_t)h * kNW + word] = bits;
+      }
     };
     qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, rot_key, code_key, key,
                                      kv_f32 != 0);
     if (wave_has && pb + kScorePagesPerWave > Np - 1)  // wave-uniform: the last page's wave
       merge_appended_row<MBF>(bg, NpCap, Np - 1, pb, (L - 1) % kPS == 0, sm.rot.xnew, meta, pl);
-  } else if (blockIdx.x == 0) {
+  } else if (blockIdx.x == 0 || (FINE && wg_has)) {
     const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
     qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
                       [&](int h, int word, uint32_t bits) {
-                        q_codes[cbase + (size_t)h * kNW + word] = bits;
+                        if constexpr (FINE) sm.qc[h * kNW + word] = bits;
+                        if (blockIdx.x == 0) q_codes[cbase + (size_t)h * kNW + word] = bits;
                       });
   } else if (wg_has) {
     qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
@@ -212,24 +262,78 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       Mem<true>::st(dst + 1, hi);
     }
   }
-  if (!arrive_last(ctl, gridDim.x, &s_last)) return;
+  const bool last1 = arrive_last(ctl, gridDim.x, &s_last);
+  if (!FINE && !last1) return;
 
-  const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
+  int P = 0;
   int32_t* out = kept + (size_t)bg * p_max;
-  for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
-  if (tid == 0) kept_count[bg] = P;
-  if (P == 0) return;
-  // the range of all bounds from the waves' published {lo, hi}, one per thread
-  static_assert(kMaxCtx / kPS / kScorePagesPerWave <= kScoreThreads, "one wave range per thread");
-  const int n_waves = (Np + kScorePagesPerWave - 1) / kScorePagesPerWave;
-  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-  if (tid < n_waves) {
-    const float* src = reinterpret_cast<const float*>(wr + tid);
-    lo = Mem<true>::ld(src);
-    hi = Mem<true>::ld(src + 1);
+  const int own_lo = blockIdx.x * kScorePagesPerWg;
+  // FINE: this workgroup's own pages' distances into LDS, their code loads
+  // sharing the round trip of the top-P's staging loads
+  auto own_dist = [&]() {
+    if constexpr (FINE) {
+      if (wave_has) {
+        u32x4 c[4];
+        ham_wave_codes<kNW>(bg, Lcap, pb, ham_codes, c);
+        uint32_t w[2];
+        ham_wave_dist(L, pb, G, sm.qc, c, w);
+        const int l = tid & (kWave - 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<uint32_t*>(sm.own_h + (pb - own_lo) * kPS + 128 * j + 2 * l) = w[j];
+      }
+    }
+  };
+  if (last1) {
+    P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
+    for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
+    if (tid == 0) kept_count[bg] = P;
+    if (P > 0) {
+      // the range of all bounds from the waves' published {lo, hi}, one per thread
+      static_assert(kMaxCtx / kPS / kScorePagesPerWave <= kScoreThreads,
+                    "one wave range per thread");
+      const int n_waves = (Np + kScorePagesPerWave - 1) / kScorePagesPerWave;
+      float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+      if (tid < n_waves) {
+        const float* src = reinterpret_cast<const float*>(wr + tid);
+        lo = Mem<true>::ld(src);
+        hi = Mem<true>::ld(src + 1);
+      }
+      if constexpr (FINE) {
+        top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
+                                              sm.fine.scores, sm.fine.top,
+                                              [&](int pos, int c) {
+                                                out[pos] = c;
+                                                sm.fine.skept[pos] = c;
+                                              },
+                                              own_dist);
+      } else {
+        top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
+                                              sm.sel.sbuf, sm.sel.top,
+                                              [&](int pos, int c) { out[pos] = c; });
+      }
+    }
   }
-  top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi, sm.sel.sbuf,
-                                        sm.sel.top, [&](int pos, int c) { out[pos] = c; });
+  if constexpr (FINE) {
+    if (!last1) {
+      // H of all keys of this workgroup's pages, then count in and leave
+      if (wave_has) ham_page_wave<kNW>(bg, Lcap, L, pb, G, ham_codes, sm.qc, hall);
+      wait_all_mem();
+      __syncthreads();
+      if (tid == 0) add_agent_u32(ctl + 1, 1u);
+      return;
+    }
+    // The top-P workgroup waits for the others' distances.  Each of them has
+    // already arrived above and waits on nothing before counting in, so the
+    // wait ends; it is bounded all the same (HHR_DEV_TIMEOUT).  Then the
+    // counter goes back to zero: every other workgroup has counted in.
+    wait_count(ctl + 1, gridDim.x - 1u, status);
+    if (tid == 0) st_agent_u32(ctl + 1, 0u);
+    const int nbins = kNW * 32 * G + 1;
+    ham_gather_kept<kScoreThreads>(bg, Lcap, P, nbins, hall, sm.own_h, own_lo,
+                                   own_lo + kScorePagesPerWg, sm.fine);
+    ham_select_core<kScoreThreads, false>(bg, P, top_k, nbins, sel_idx, sel_count, sm.fine);
+  }
 }
 
 // S6 + S7 for hhr_decode.  grid (n_split, B*Hkv), 256 threads: workgroup j
@@ -283,18 +387,25 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_merge(
 
 }  // namespace
 
+bool one_launch_select(const hhr_shape& s) {
+  const long long wgs = (long long)((s.max_ctx / kPS + kScorePagesPerWg - 1) / kScorePagesPerWg) *
+                        s.batch * s.n_kv_heads;
+  return wgs <= kScoreToppMaxWgs && s.code_bits == 32 * kNW;
+}
+
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
                              const CompositeBuffers& buf, hipStream_t stream,
-                             const AppendArgs* app) {
+                             const AppendArgs* app, const FineArgs* fine) {
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
-  if ((long long)grid.x * grid.y > kScoreToppMaxWgs || s.code_bits != 32 * kNW) {
+  if (!one_launch_select(s)) {
     // many rounds of one-CU workgroups: the launch boundaries of the staged
     // stages cost less than the latency each round would leave exposed.  The
     // fused kernel encodes 128-bit query codes only; other widths run staged.
+    if (fine) return hipErrorInvalidValue;  // callers check one_launch_select first
     hipError_t e = hipSuccess;
     if (app)
       e = launch_append_last_row(s, app->k_cache, seq_len, R, W, app->codes, app->meta,
@@ -311,20 +422,33 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
   const void* kc = app ? app->k_cache : nullptr;
   uint32_t* cd = app ? app->codes : nullptr;
   const int kf32 = s.kv_dtype == HHR_F32;
-#define HHR_SCORE_TOPP(MBF, APP)                                                                 \
-  hipLaunchKernelGGL((k_score_topp<MBF, APP>), grid, dim3(kScoreThreads), 0, stream, q, seq_len, \
-                     R, W, m, kc, kf32, cd, keep_num, keep_den, keep_abs, p_max, s.n_q_heads,    \
-                     s.n_kv_heads, s.max_ctx, buf.scores, buf.wave_range, buf.q_codes, buf.kept, \
-                     buf.kept_count, buf.counters, buf.status)
+  const uint32_t* hc = fine ? fine->codes : nullptr;
+  uint16_t* hall = fine ? buf.hall : nullptr;
+  const int tk = fine ? fine->top_k : 0;
+  int32_t* si = fine ? fine->sel_idx : nullptr;
+  int32_t* sc = fine ? fine->sel_count : nullptr;
+#define HHR_SCORE_TOPP(MBF, APP, FIN)                                                          \
+  hipLaunchKernelGGL((k_score_topp<MBF, APP, FIN>), grid, dim3(kScoreThreads), 0, stream, q,   \
+                     seq_len, R, W, m, kc, kf32, cd, keep_num, keep_den, keep_abs, p_max,      \
+                     s.n_q_heads, s.n_kv_heads, s.max_ctx, buf.scores, buf.wave_range,         \
+                     buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status, hc, hall, \
+                     tk, si, sc)
+#define HHR_SCORE_TOPP_F(MBF, APP)     \
+  if (fine)                            \
+    HHR_SCORE_TOPP(MBF, APP, true);    \
+  else                                 \
+    HHR_SCORE_TOPP(MBF, APP, false);
   const bool mbf = s.meta_dtype == HHR_BF16;
-  if (mbf && app)
-    HHR_SCORE_TOPP(true, true);
-  else if (mbf)
-    HHR_SCORE_TOPP(true, false);
-  else if (app)
-    HHR_SCORE_TOPP(false, true);
-  else
-    HHR_SCORE_TOPP(false, false);
+  if (mbf && app) {
+    HHR_SCORE_TOPP_F(true, true)
+  } else if (mbf) {
+    HHR_SCORE_TOPP_F(true, false)
+  } else if (app) {
+    HHR_SCORE_TOPP_F(false, true)
+  } else {
+    HHR_SCORE_TOPP_F(false, false)
+  }
+#undef HHR_SCORE_TOPP_F
 #undef HHR_SCORE_TOPP
   return hipGetLastError();
 }
@@ -336,6 +460,12 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,
                                    hipStream_t stream, const AppendArgs* app) {
+  if (finish && one_launch_select(s)) {
+    // S2..S6 in one launch
+    const FineArgs fine{codes, top_k, sel_idx, sel_count};
+    return launch_score_topp(s, q, seq_len, R, W, meta, keep_num, keep_den, keep_abs, p_max, buf,
+                             stream, app, &fine);
+  }
   hipError_t e = launch_score_topp(s, q, seq_len, R, W, meta, keep_num, keep_den, keep_abs,
                                    p_max, buf, stream, app);
   if (e != hipSuccess) return e;

@@ -21,7 +21,8 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // holds the device status word at offset 0.
 struct Workspace {
   size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, ham_cum = 0, q_rot = 0, q_codes = 0,
-         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, total = 0;
+         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, ham_all = 0,
+         total = 0;
   int32_t p_max = 0, n_split = 0;
 };
 
@@ -95,6 +96,15 @@ struct CompositeBuffers {
   uint16_t* dist;
   int* chist;
   uint16_t* cum;  // per-block cumulative H histograms (hhr_decode's pick)
+  uint16_t* hall;  // H of every key [B*Hkv][Lcap] (the one-launch selection)
+};
+// The fine stage of the one-launch selection: codes to score, and where the
+// selection goes.
+struct FineArgs {
+  const uint32_t* codes;
+  int32_t top_k;
+  int32_t* sel_idx;
+  int32_t* sel_count;
 };
 // A key appended at row seq_len[b] - 1 of every sequence, to be encoded (its
 // code and its page's metadata) by the coarse stage before it bounds the page.
@@ -106,11 +116,17 @@ struct AppendArgs {
 
 // k_score_topp alone (S2..S4): kept pages, counts and query codes into buf;
 // with app, the appended keys are encoded first.
+// With fine, S5 + S6 run in the same launch and write the selection (only
+// when one_launch_select(s)).
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
                              const CompositeBuffers& buf, hipStream_t stream,
-                             const AppendArgs* app = nullptr);
+                             const AppendArgs* app = nullptr, const FineArgs* fine = nullptr);
+// True when the coarse stage runs as one launch (k_score_topp): the scoring
+// grid is at most two rounds of one workgroup per CU and codes are 128-bit.
+// hhr_select and hhr_decode then run S2..S6 in that launch.
+bool one_launch_select(const hhr_shape& s);
 // S1 for the single row seq_len[b] - 1 of every sequence with seq_len[b] >= 1.
 hipError_t launch_append_last_row(const hhr_shape& s, const void* k_cache,
                                   const int32_t* seq_len, const float* R, const float* W,

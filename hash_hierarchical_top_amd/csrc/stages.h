@@ -318,9 +318,16 @@ __device__ int top_pages_core(const float* sc, int Np, int P, float* sbuf, TopSc
 // passes a (lo, hi) that bounds some of the scores (+inf, -inf for none), and
 // together they bound all of them.  The range is reduced in the barrier that
 // the staging needs anyway, so there is no pass over the scores to find it.
-template <int NT, bool COH, typename Emit>
+// mid() runs once, after the first staging loads are issued and before their
+// values are used, so that work of the caller's with loads of its own shares
+// their round trip.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <int NT, bool COH, typename Emit, typename Mid = NoMid>
 __device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
-                                TopScratch& sh, Emit emit) {
+                                TopScratch& sh, Emit emit, Mid mid = Mid()) {
   constexpr int kB = 8;
   const int tid = threadIdx.x;
   const int last = max(Np - 1, 0);
@@ -331,6 +338,7 @@ __device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float 
     float x[kB];
 #pragma unroll
     for (int j = 0; j < kB; ++j) x[j] = Mem<COH>::ld(sc + min(c0 + j * NT + tid, last));
+    if (c0 == 0) mid();
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
       const int c = c0 + j * NT + tid;
@@ -509,8 +517,12 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   }
 }
 
+// The gather's spread histogram needs (nbins + 1) x (sub-bins) words: 16
+// sub-bins for 128-bit codes and 4-head groups.
+constexpr int kHamHistCap = 16 * (32 * kNW * 4 + 2);
+
 struct HamSmem {
-  int hist[kHamBinsMax];
+  int hist[kHamHistCap > kHamBinsMax ? kHamHistCap : kHamBinsMax];
   union {
     __attribute__((aligned(16))) uint16_t hval[kMaxCand];      // H of candidate c
     __attribute__((aligned(16))) float scores[kMaxCtx / kPS];  // page scores (S4)
@@ -520,6 +532,10 @@ struct HamSmem {
   int scan[17];
   TopScratch top;
 };
+
+template <int NT, bool COH>
+__device__ void ham_select_core(int bg, int P, int top_k, int nbins, int32_t* sel_idx,
+                                int32_t* sel_count, HamSmem& sm);
 
 // Selection of (b, g) from the distances and histogram its distance chunks
 // wrote; leaves the histogram zero.  If skept_ready, sm.skept already holds
@@ -551,6 +567,18 @@ __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int 
     Mem<COH>::st(hb + i, 0);
   }
   __syncthreads();
+  ham_select_core<NT, COH>(bg, P, top_k, nbins, sel_idx, sel_count, sm);
+}
+
+// The cut and the ordered compaction of ham_select, once sm.hist holds the
+// histogram of the valid candidates over H = 0 .. nbins - 1, sm.hval their
+// distances (0xFFFF for an invalid row) and sm.skept the P kept pages, all
+// behind a barrier.  Writes sel_idx[bg][0 .. top_k) and sel_count[bg].
+template <int NT, bool COH>
+__device__ void ham_select_core(int bg, int P, int top_k, int nbins, int32_t* sel_idx,
+                                int32_t* sel_count, HamSmem& sm) {
+  const int tid = threadIdx.x;
+  const int ncand = P * kPS;
 
   // threshold over bins in ascending H
   {
@@ -611,18 +639,167 @@ __device__ void ham_select(int b, int g, int Hq, int Hkv, int P, int top_k, int 
   int gb, eb;
   run_offsets<NT>(gt, eq, sm.top, gb, eb);
   int32_t* out = sel_idx + (size_t)bg * top_k;
-  auto emit = [&](int pos, int c) { Mem<COH>::st(out + pos, sm.skept[c >> 4] * kPS + (c & 15)); };
 #pragma unroll 1
   for (int j = 0; j < nv8; ++j) {
     const u32x4 hw = run8[j];
+    const int cj = c0 + 8 * j;  // 8 candidates of one kept page
+    const int base = sm.skept[min(cj, max(ncand - 1, 0)) >> 4] * kPS - (cj & ~15);
+    auto emit = [&](int pos, int c) { Mem<COH>::st(out + pos, base + c); };
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = c0 + 8 * j + e;
-      emit_ordered(cls_of(hw, e, c), c, need_eq, gb, eb, emit);
-    }
+    for (int e = 0; e < 8; ++e) emit_ordered(cls_of(hw, e, cj + e), cj + e, need_eq, gb, eb, emit);
   }
   for (int i = count + tid; i < top_k; i += NT) Mem<COH>::st(out + i, -1);
   if (tid == 0) Mem<COH>::st(sel_count + bg, count);
+}
+
+// ------------------------------------- S5 over every page, then S6 from LDS
+// The one-launch selection (k_score_topp with the fine stage) computes H for
+// every key of every page while the top-P runs, so that only a gather of the
+// kept pages' distances remains after it.
+//
+// H of every key of the 16 pages [pb, pb + 16) of (b, g), by one wave, in
+// two steps (so that the loads can be issued early).  Lane l takes keys
+// 2l, 2l + 1 and 128 + 2l, 128 + 2l + 1 of the wave's 256, so every store of
+// the packed result writes 256 contiguous bytes (two distances per 32-bit
+// word: word j holds rows t_base + 128 j + 2 l and the next one).
+template <int NW>
+__device__ __forceinline__ void ham_wave_codes(int bg, int Lcap, int pb,
+                                               const uint32_t* __restrict__ codes, u32x4 c[4]) {
+  static_assert(NW == 4, "the one-launch selection reads 128-bit codes");
+  const int l = threadIdx.x & (kWave - 1);
+  const int t_base = pb * kPS;
+  const uint32_t* cb = codes + (size_t)bg * Lcap * NW;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = t_base + 128 * (k >> 1) + 2 * l + (k & 1);
+    c[k] = *(const u32x4*)(cb + (size_t)min(t, Lcap - 1) * NW);
+  }
+}
+
+// The summed distances of ham_wave_codes' keys to the G query codes sq (LDS),
+// packed; a row at or past L gets 0xFFFF.
+__device__ __forceinline__ void ham_wave_dist(int L, int pb, int G, const uint32_t* sq,
+                                              const u32x4 c[4], uint32_t w[2]) {
+  const int l = threadIdx.x & (kWave - 1);
+  uint32_t h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 1
+  for (int qh = 0; qh < G; ++qh) {
+    const u32x4 q = *(const u32x4*)(sq + qh * kNW);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[k] += __popc(c[k][i] ^ q[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t0 = pb * kPS + 128 * j + 2 * l;
+    const uint32_t v0 = t0 < L ? h[2 * j] : 0xFFFFu;
+    const uint32_t v1 = t0 + 1 < L ? h[2 * j + 1] : 0xFFFFu;
+    w[j] = v0 | (v1 << 16);
+  }
+}
+
+// ham_wave_codes + ham_wave_dist, stored to hall [B*Hkv][Lcap] u16 with
+// agent-scope stores (a workgroup of the same launch reads them).
+template <int NW>
+__device__ __forceinline__ void ham_page_wave(int bg, int Lcap, int L, int pb, int G,
+                                              const uint32_t* __restrict__ codes,
+                                              const uint32_t* sq, uint16_t* hall) {
+  const int l = threadIdx.x & (kWave - 1);
+  u32x4 c[4];
+  ham_wave_codes<NW>(bg, Lcap, pb, codes, c);
+  uint32_t w[2];
+  ham_wave_dist(L, pb, G, sq, c, w);
+  const int t_end = min((pb + kScorePagesPerWave) * kPS, Lcap);
+  uint16_t* hb = hall + (size_t)bg * Lcap;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t0 = pb * kPS + 128 * j + 2 * l;  // even, and t_end is a multiple of 16
+    if (t0 < t_end) Mem<true>::st(reinterpret_cast<uint32_t*>(hb + t0), w[j]);
+  }
+}
+
+// 16 bytes at byte offset off of buf (whose size is bytes), loaded with the
+// sc1 cache policy: coherent with agent-scope stores of other workgroups of
+// the same launch, like an agent-scope atomic load, but as one dwordx4.
+__device__ __forceinline__ u32x4 ld_sc1_x4(const void* buf, uint32_t bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(buf), (short)0, (int)bytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16 /* sc1 */);
+}
+
+// Sub-bins per H value of the gather's LDS histogram: lane l adds into copy
+// l % S (copy-major: word k (nbins + 1) + H), so lanes of one instruction
+// that hit the same H rarely hit the same word, and the fold reads
+// consecutive words across lanes.
+__device__ __forceinline__ int ham_spread(int nbins) {
+  int S = 16;
+  while (S > 1 && (nbins + 1) * S > kHamHistCap) S >>= 1;
+  return S;
+}
+
+// The distances of the P kept pages sm.skept[0 .. P) (ascending) into sm.hval
+// (candidate c = kept slot c / 16, row c % 16) and their histogram over
+// H = 0 .. nbins - 1 into sm.hist, ready for ham_select_core.  Two lanes per
+// kept page, 8 rows each, every load of a thread issued before any is used.
+// Pages in [own_lo, own_hi) are this workgroup's own: their distances are in
+// LDS (own_h, 16 per page from own_lo); every other page's come from hall,
+// written by the other workgroups of this launch.  All NT threads call;
+// sm.skept and own_h must be behind a barrier.
+template <int NT>
+__device__ void ham_gather_kept(int bg, int Lcap, int P, int nbins, const uint16_t* hall,
+                                const uint16_t* own_h, int own_lo, int own_hi, HamSmem& sm) {
+  constexpr int kTasks = 2 * (kMaxCand / kPS) / NT;  // half-pages per thread, at most
+  static_assert(kTasks * NT == 2 * (kMaxCand / kPS), "half-pages split evenly");
+  const int tid = threadIdx.x;
+  const int S = ham_spread(nbins);
+  const int stride = nbins + 1;  // bin nbins takes the 0xFFFF rows
+  int* hc = sm.hist + (tid & (S - 1)) * stride;
+  for (int i = tid; i < stride * S; i += NT) sm.hist[i] = 0;
+  const uint16_t* hb = hall + (size_t)bg * Lcap;
+  const uint32_t hbytes = (uint32_t)Lcap * 2u;
+  u32x4 h8[kTasks];
+#pragma unroll
+  for (int j = 0; j < kTasks; ++j) {
+    const int i = tid + j * NT;
+    const int page = sm.skept[min(i >> 1, max(P - 1, 0))];
+    const int half = 8 * (i & 1);  // first of this lane's 8 rows in the page
+    if (i < 2 * P) {
+      if (page >= own_lo && page < own_hi)
+        h8[j] = *reinterpret_cast<const u32x4*>(own_h + (page - own_lo) * kPS + half);
+      else
+        h8[j] = ld_sc1_x4(hb, hbytes, (uint32_t)(page * kPS + half) * 2u);
+    }
+  }
+  __syncthreads();  // the histogram is clear
+#pragma unroll
+  for (int j = 0; j < kTasks; ++j) {
+    const int i = tid + j * NT;
+    if (i >= 2 * P) continue;
+    reinterpret_cast<u32x4*>(sm.hval)[i] = h8[j];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      atomicAdd(hc + min((int)(h8[j][w] & 0xFFFFu), nbins), 1);
+      atomicAdd(hc + min((int)(h8[j][w] >> 16), nbins), 1);
+    }
+  }
+  __syncthreads();
+  // fold the copies: read every bin's total first, then overwrite copy 0
+  constexpr int kFold = (kHamBinsMax + NT - 1) / NT;
+  int tot[kFold];
+#pragma unroll
+  for (int j = 0; j < kFold; ++j) {
+    const int bin = tid + j * NT;
+    int t = 0;
+    if (bin < nbins)
+      for (int k = 0; k < S; ++k) t += sm.hist[k * stride + bin];
+    tot[j] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kFold; ++j)
+    if (tid + j * NT < nbins) sm.hist[tid + j * NT] = tot[j];
+  __syncthreads();
 }
 
 // The 64 selected positions of output chunk [k0, k0 + 64) of (b, g), found

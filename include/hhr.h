@@ -78,8 +78,10 @@ typedef enum {
 #define HHR_DEV_BAD_SEQ_LEN 0x1u  /* a seq_len was < 0 or > max_ctx           */
 #define HHR_DEV_BAD_INDEX 0x2u    /* a selected position was outside [0,Lcap) */
 #define HHR_DEV_TIMEOUT 0x4u      /* a wait between workgroups of one launch gave up
-                                     (results of that call are unspecified); reserved:
-                                     no current kernel waits on another workgroup */
+                                     (results of that call are unspecified).  Only the
+                                     one-launch selection waits: its top-P workgroup
+                                     waits for the other workgroups of its (b, g), all
+                                     of which are already running */
 
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
@@ -249,7 +251,12 @@ hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_
 
 /* ---------------------------------------------------- S2..S6 and S2..S7 */
 /* hhr_select: S2..S6 in one stream-ordered call; intermediates live in the
- * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk. */
+ * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk.  When the
+ * coarse stage fits one launch (at most 2 x 256 scoring workgroups of 256
+ * pages, 128-bit codes) the fine stage runs in it too: every workgroup also
+ * scores all keys of its own pages against the query codes while the top-P
+ * runs, and the top-P workgroup then takes the top-k from the kept pages'
+ * distances.  Otherwise it runs as separate launches.  Same results. */
 hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
                       const void* page_meta, int32_t keep_num, int32_t keep_den,
