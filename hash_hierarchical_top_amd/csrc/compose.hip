@@ -300,17 +300,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
         hi = Mem<true>::ld(src + 1);
       }
       if constexpr (FINE) {
-        top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
-                                              sm.fine.scores, sm.fine.top,
-                                              [&](int pos, int c) {
-                                                out[pos] = c;
-                                                sm.fine.skept[pos] = c;
-                                              },
-                                              own_dist);
+        top_pages_strided<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
+                                               sm.fine.scores, sm.fine.top,
+                                               [&](int pos, int c) {
+                                                 out[pos] = c;
+                                                 sm.fine.skept[pos] = c;
+                                               },
+                                               own_dist);
       } else {
-        top_pages_ranged<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
-                                              sm.sel.sbuf, sm.sel.top,
-                                              [&](int pos, int c) { out[pos] = c; });
+        top_pages_strided<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
+                                               sm.sel.sbuf, sm.sel.top,
+                                               [&](int pos, int c) { out[pos] = c; });
       }
     }
   }

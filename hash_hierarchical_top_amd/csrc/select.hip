@@ -66,8 +66,9 @@ __global__ __launch_bounds__(kTopPThreads) void k_top_pages(
   for (int i = P + tid; i < p_max; i += kTopPThreads) out[i] = -1;
   if (tid == 0) kept_count[bg] = P;
   if (P == 0) return;
-  top_pages_core<kTopPThreads, false>(scores + (size_t)bg * (Lcap / kPS), Np, P, sbuf,
-                                                  sh, [&](int pos, int c) { out[pos] = c; });
+  top_pages_strided<kTopPThreads, false>(scores + (size_t)bg * (Lcap / kPS), Np, P,
+                                         __builtin_huge_valf(), -__builtin_huge_valf(), sbuf, sh,
+                                         [&](int pos, int c) { out[pos] = c; });
 }
 
 // ------------------------------------------------------------------ S5+S6

@@ -287,62 +287,32 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
 }
 
 // ============================================================== S4: prune
-// Exact top-P of Np page scores in one workgroup of NT threads.  The scores
-// are first staged into LDS with coalesced loads (page c = i*NT + tid, eight
-// loads in flight per thread, addresses clamped instead of branched); the
-// selection then reads each thread's run of pages from there.  sbuf holds
-// kMaxCtx / kPS floats.  emit(pos, page) with pos ascending in page.
-template <int NT, bool COH, typename Emit>
-__device__ int top_pages_core(const float* sc, int Np, int P, float* sbuf, TopScratch& sh,
-                              Emit emit) {
-  constexpr int kB = 8;
-  const int tid = threadIdx.x;
-  const int last = max(Np - 1, 0);
-#pragma unroll 1
-  for (int c0 = 0; c0 < Np; c0 += kB * NT) {
-    float x[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j) x[j] = Mem<COH>::ld(sc + min(c0 + j * NT + tid, last));
-#pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int c = c0 + j * NT + tid;
-      if (c < Np) sbuf[c] = x[j];
-    }
-  }
-  __syncthreads();
-  return top_largest_lds<NT, kMaxCtx / kPS / (4 * NT)>(sbuf, Np, [](int) { return true; }, P,
-                                                         sh, emit);
-}
-
-// top_pages_core with the range of the scores given in pieces: every thread
-// passes a (lo, hi) that bounds some of the scores (+inf, -inf for none), and
-// together they bound all of them.  The range is reduced in the barrier that
-// the staging needs anyway, so there is no pass over the scores to find it.
-// mid() runs once, after the first staging loads are issued and before their
+// Exact top-P of Np page scores in one workgroup of NT threads
+// (top_largest_strided): thread t loads pages j NT + t, so the loads coalesce
+// and the scores stay in registers.  The range is the given pieces (lo, hi)
+// together with this thread's own scores (pass +inf, -inf to take it from the
+// scores alone).  mid() runs once, after the loads are issued and before their
 // values are used, so that work of the caller's with loads of its own shares
-// their round trip.
+// their round trip.  sbuf (kMaxCtx / kPS floats, LDS) serves only the radix
+// fallback.  emit(pos, page) with pos ascending in page.
 struct NoMid {
   __device__ void operator()() const {}
 };
 
-template <int NT, bool COH, typename Emit, typename Mid = NoMid>
-__device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
-                                TopScratch& sh, Emit emit, Mid mid = Mid()) {
-  constexpr int kB = 8;
+template <int NT, int NV, bool COH, typename Emit, typename Mid>
+__device__ int top_pages_strided_nv(const float* sc, int Np, int P, float lo, float hi,
+                                    float* sbuf, TopScratch& sh, Emit& emit, Mid& mid) {
   const int tid = threadIdx.x;
   const int last = max(Np - 1, 0);
-  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the barrier below
-  if (tid == 0) sh.list_n = 0;
-#pragma unroll 1
-  for (int c0 = 0; c0 < Np; c0 += kB * NT) {
-    float x[kB];
+  float x[NV];
 #pragma unroll
-    for (int j = 0; j < kB; ++j) x[j] = Mem<COH>::ld(sc + min(c0 + j * NT + tid, last));
-    if (c0 == 0) mid();
+  for (int j = 0; j < NV; ++j) x[j] = Mem<COH>::ld(sc + min(j * NT + tid, last));
+  mid();
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int c = c0 + j * NT + tid;
-      if (c < Np) sbuf[c] = x[j];
+  for (int j = 0; j < NV; ++j) {
+    if (j * NT + tid < Np) {
+      lo = fminf(lo, x[j]);
+      hi = fmaxf(hi, x[j]);
     }
   }
   lo = wave_min(lo);
@@ -351,15 +321,29 @@ __device__ int top_pages_ranged(const float* sc, int Np, int P, float lo, float 
     sh.w_min[tid / kWave] = lo;
     sh.w_max[tid / kWave] = hi;
   }
-  __syncthreads();
+  __syncthreads();  // also orders the caller's clearing of sh.hist and sh.list_n
   float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
 #pragma unroll
   for (int k = 0; k < NT / kWave; ++k) {
     vmin = fminf(vmin, sh.w_min[k]);
     vmax = fmaxf(vmax, sh.w_max[k]);
   }
-  return top_largest_ranged<NT, kMaxCtx / kPS / (4 * NT)>(sbuf, Np, [](int) { return true; }, P,
-                                                            vmin, vmax, Np, sh, emit, true);
+  return top_largest_strided<NT, NV>(x, Np, P, vmin, vmax, sbuf, sh, emit);
+}
+
+template <int NT, bool COH, typename Emit, typename Mid = NoMid>
+__device__ int top_pages_strided(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
+                                 TopScratch& sh, Emit emit, Mid mid = Mid()) {
+  static_assert(16 * NT >= kMaxCtx / kPS, "16 pages per thread cover the largest context");
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the range barrier
+  if (tid == 0) sh.list_n = 0;
+  const int nv = (Np + NT - 1) / NT;  // block-uniform
+  if (nv <= 1) return top_pages_strided_nv<NT, 1, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
+  if (nv <= 2) return top_pages_strided_nv<NT, 2, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
+  if (nv <= 4) return top_pages_strided_nv<NT, 4, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
+  if (nv <= 8) return top_pages_strided_nv<NT, 8, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
+  return top_pages_strided_nv<NT, 16, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
 }
 
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {

@@ -30,8 +30,11 @@ namespace hhr {
 constexpr int kLinBins = 2048;
 constexpr int kLinListMax = 512;
 
+constexpr int kStridedCnt = 256;  // (slot, wave) counts of top_largest_strided
+
 struct TopScratch {
   int hist[kLinBins];
+  uint32_t cnt[kStridedCnt];
   float list_v[kLinListMax];
   int list_n;
   float w_min[16], w_max[16];
@@ -417,6 +420,183 @@ __device__ int top_largest_fixed(const float* sbuf, int n, Present present, int 
   for (int i = 0; i < 4 * nv4; ++i) {
     const int k = (int)(cls >> (2 * i)) & 3;
     if (k != 0) emit_ordered(k, c0 + i, need_eq, gb, eb, emit);
+  }
+  return Pe;
+}
+
+// ---------------------------------------------------------------------------
+// The same selection with the scores in registers and strided ownership:
+// thread t of NT holds candidate j NT + t in x[j] (j < NV), the layout that
+// coalesced loads give, so the scores are never staged through LDS.  Output
+// positions come from per-slot wave ballots (a lane's rank among the wave's
+// taken candidates of slot j) and one exclusive prefix over the (slot, wave)
+// counts, whose order j, wave, lane is the candidate order.  This costs a few
+// vector instructions per candidate where the run-based compaction spends
+// tens, and the top-P of one (b, g) runs on a single CU bound by its vector
+// throughput.  vmin <= every score <= vmax; sh.hist and sh.list_n must be
+// zero behind a barrier; sbuf (4 NT NV floats in LDS) is used only by the
+// radix fallback.  Candidates c >= n are absent.  Returns min(P, n).  All NT
+// threads call.
+template <int NT, int NV, typename Emit>
+__device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmin, float vmax,
+                                   float* sbuf, TopScratch& sh, Emit& emit) {
+  constexpr int NWAVES = NT / kWave;
+  constexpr int NE = NV * NWAVES;  // (slot, wave) entries
+  static_assert(NE <= kStridedCnt, "slot counts fit TopScratch::cnt");
+  constexpr int PER = (NE + kWave - 1) / kWave;
+  static_assert(PER <= 4, "at most 4 entries per lane");
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = tid % kWave;
+  const int Pe = min(P, n);
+  if (Pe <= 0) return 0;  // block-uniform
+  const bool all = Pe >= n;
+
+  // bins, linear in value: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)),
+  // non-decreasing in v; -1 for an absent candidate
+  const float range = vmax - vmin;
+  const float inv = range > 0.f ? (float)kLinBins / range : 0.f;
+  int bin[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const float f = (x[j] - vmin) * inv;
+    const int bb = f < (float)kLinBins ? max((int)f, 0) : kLinBins - 1;
+    const bool present = j * NT + tid < n;
+    bin[j] = present ? bb : -1;
+    if (present && !all) atomicAdd(&sh.hist[bb], 1);
+  }
+
+  // cut-off: mode 0 = every present candidate, 1 = bin >= bstar, 2 = bin >
+  // bstar or (bin == bstar and key >= T, ties by need_eq), 3 = key >= T
+  int mode = 0, need_eq = 0, bstar = 0;
+  uint32_t T = 0u;
+  if (!all) {
+    __syncthreads();
+    {
+      constexpr int PERB = kLinBins / NT > 0 ? kLinBins / NT : 1;
+      int local = 0;
+#pragma unroll
+      for (int j = 0; j < PERB; ++j) {
+        const int d = kLinBins - 1 - (tid * PERB + j);
+        if (d >= 0) local += sh.hist[d];
+      }
+      int tot;
+      int run = block_exclusive_scan<NT, int>(local, sh.scan, &tot);
+#pragma unroll
+      for (int j = 0; j < PERB; ++j) {
+        const int d = kLinBins - 1 - (tid * PERB + j);
+        if (d >= 0) {
+          const int c = sh.hist[d];
+          if (run < Pe && run + c >= Pe) {
+            sh.bstar = d;
+            sh.above = run;
+          }
+          run += c;
+        }
+      }
+    }
+    __syncthreads();
+    bstar = sh.bstar;
+    const int need = Pe - sh.above;  // 1 <= need <= hist[b*]
+    const int cstar = sh.hist[bstar];
+    if (need == cstar) {
+      mode = 1;
+    } else if (cstar <= kLinListMax) {
+      mode = 2;
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        if (bin[j] == bstar) sh.list_v[atomicAdd(&sh.list_n, 1)] = x[j];
+      __syncthreads();
+      // T = the value with (#greater in b*) < need <= (#greater) + (#equal)
+      for (int j = tid; j < cstar; j += NT) {
+        const float vj = sh.list_v[j];
+        int gtr = 0, eql = 0;
+#pragma unroll 1
+        for (int k = 0; k < cstar; ++k) {
+          const float vk = sh.list_v[k];
+          gtr += vk > vj;
+          eql += vk == vj;
+        }
+        if (gtr < need && need <= gtr + eql) {  // all equal copies agree
+          sh.T = orderable_key(vj);
+          sh.need_eq = need - gtr;
+        }
+      }
+      __syncthreads();
+      T = sh.T;
+      need_eq = sh.need_eq;
+    } else {
+      mode = 3;  // radix over the keys of the whole set, read back from LDS
+#pragma unroll
+      for (int j = 0; j < NV; ++j) sbuf[j * NT + tid] = x[j];
+      __syncthreads();
+      radix_cutoff<NT>(
+          [&](int i) -> uint32_t {
+            const int c = i * NT + tid;
+            return c < n ? orderable_key(sbuf[c]) : 0u;
+          },
+          NV, Pe, sh);
+      T = sh.T;
+      need_eq = sh.need_eq;
+    }
+  }
+
+  // classes (1 = inside the cut, 2 = on it) and each lane's rank among its
+  // wave's candidates of the same class and slot
+  int cls[NV];
+  uint32_t rank[NV];  // rank in class 1 | rank in class 2 << 16
+  const uint64_t below = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    int k = 0;
+    if (bin[j] >= 0) {
+      if (mode == 0) {
+        k = 1;
+      } else if (mode == 1) {
+        k = bin[j] >= bstar ? 1 : 0;
+      } else if (mode == 2 && bin[j] != bstar) {
+        k = bin[j] > bstar ? 1 : 0;
+      } else {
+        const uint32_t key = orderable_key(x[j]);
+        k = key > T ? 1 : (key == T ? 2 : 0);
+      }
+    }
+    cls[j] = k;
+    const uint64_t b1 = __ballot(k == 1);
+    const uint64_t b2 = __ballot(k == 2);
+    rank[j] = (uint32_t)popc64(b1 & below) | ((uint32_t)popc64(b2 & below) << 16);
+    if (l == 0) sh.cnt[j * NWAVES + w] = (uint32_t)popc64(b1) | ((uint32_t)popc64(b2) << 16);
+  }
+  __syncthreads();
+  // exclusive prefix over entries e = j NWAVES + w (lane l holds entries
+  // PER l .. PER l + PER - 1); both 16-bit halves stay below 65536
+  uint32_t pre[PER];
+  {
+    uint32_t v[PER], local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = PER * l + i;
+      v[i] = e < NE ? sh.cnt[e] : 0u;
+      local += v[i];
+    }
+    uint32_t run = wave_inclusive_scan(local) - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      pre[i] = run;
+      run += v[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = j * NWAVES + w;  // wave-uniform
+    const int r = e % PER;
+    uint32_t p = pre[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i)
+      if (r == i) p = pre[i];
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)p, e / PER) + rank[j];
+    const int gb = (int)(base & 0xFFFFu), eb = (int)(base >> 16);
+    if (cls[j] == 1 || (cls[j] == 2 && eb < need_eq)) emit(gb + min(eb, need_eq), j * NT + tid);
   }
   return Pe;
 }
