@@ -202,13 +202,10 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   const int tid = threadIdx.x;
   int32_t* out = kept + (size_t)b * keep_blocks;
   const float* sc = block_scores + (size_t)b * NbCap;
-  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
-  // only the Nb candidates: the selection reads no slot past them
-  for (int c = tid; c < Nb; c += kHisaThreads) sbuf[c] = sc[c];
-  __syncthreads();
-  const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
-      sbuf, Nb, [](int) { return true; }, keep_blocks, sh,
-      [&](int pos, int c) { out[pos] = c; });
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];  // radix fallback only
+  const int cnt = top_strided<kHisaThreads, false>(sc, Nb, Nb, keep_blocks, AllPresent(),
+                                                   __builtin_huge_valf(), -__builtin_huge_valf(),
+                                                   sbuf, sh, [&](int pos, int c) { out[pos] = c; });
   for (int i = cnt + tid; i < keep_blocks; i += kHisaThreads) out[i] = -1;
   if (tid == 0) kept_count[b] = cnt;
 }
@@ -339,25 +336,21 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
   const int kc = L > 0 ? min(kept_count[b], keep_blocks) : 0;
   const int ncand = kc * block;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kc; i += kHisaThreads) skept[i] = kept[(size_t)b * keep_blocks + i];
-  __syncthreads();
   const float* ts = token_scores + (size_t)b * keep_blocks * block;
-  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];
-  // only the ncand candidates (whole blocks, 16-byte aligned runs): the
-  // selection reads no slot past them
-  {
-    const floatx4* ts4 = reinterpret_cast<const floatx4*>(ts);
-    floatx4* sb4 = reinterpret_cast<floatx4*>(sbuf);
-    for (int i = tid; i < ncand / 4; i += kHisaThreads) sb4[i] = ts4[i];
-  }
-  __syncthreads();
-  // the token-score pass wrote -inf for every slot past the sequence end and a
-  // finite score for every token of it
-  auto present = [&](int c) { return sbuf[c] != -__builtin_huge_valf(); };
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];  // radix fallback only
+  // the kept blocks (for the output positions) load with the scores; the
+  // scores load before the kept count is known (clamped to the buffer), and
+  // only the first ncand are candidates.  The token-score pass wrote -inf for
+  // every slot past the sequence end and a finite score for every token of it.
+  auto load_kept = [&]() {
+    for (int i = tid; i < kc; i += kHisaThreads) skept[i] = kept[(size_t)b * keep_blocks + i];
+  };
+  auto present = [](float v) { return v != -__builtin_huge_valf(); };
   int32_t* out = sel_idx + (size_t)b * top_k;
-  const int cnt = top_largest_lds<kHisaThreads, kHisaMaxCand / (4 * kHisaThreads)>(
-      sbuf, ncand, present, top_k, sh,
-      [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; });
+  const int cnt = top_strided<kHisaThreads, false>(
+      ts, keep_blocks * block, ncand, top_k, present, __builtin_huge_valf(),
+      -__builtin_huge_valf(), sbuf, sh,
+      [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; }, load_kept);
   for (int i = cnt + tid; i < top_k; i += kHisaThreads) out[i] = -1;
   if (tid == 0) sel_count[b] = cnt;
 }

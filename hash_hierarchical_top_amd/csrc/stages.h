@@ -295,55 +295,11 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
 // values are used, so that work of the caller's with loads of its own shares
 // their round trip.  sbuf (kMaxCtx / kPS floats, LDS) serves only the radix
 // fallback.  emit(pos, page) with pos ascending in page.
-struct NoMid {
-  __device__ void operator()() const {}
-};
-
-template <int NT, int NV, bool COH, typename Emit, typename Mid>
-__device__ int top_pages_strided_nv(const float* sc, int Np, int P, float lo, float hi,
-                                    float* sbuf, TopScratch& sh, Emit& emit, Mid& mid) {
-  const int tid = threadIdx.x;
-  const int last = max(Np - 1, 0);
-  float x[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) x[j] = Mem<COH>::ld(sc + min(j * NT + tid, last));
-  mid();
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    if (j * NT + tid < Np) {
-      lo = fminf(lo, x[j]);
-      hi = fmaxf(hi, x[j]);
-    }
-  }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  if ((tid & (kWave - 1)) == 0) {
-    sh.w_min[tid / kWave] = lo;
-    sh.w_max[tid / kWave] = hi;
-  }
-  __syncthreads();  // also orders the caller's clearing of sh.hist and sh.list_n
-  float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
-#pragma unroll
-  for (int k = 0; k < NT / kWave; ++k) {
-    vmin = fminf(vmin, sh.w_min[k]);
-    vmax = fmaxf(vmax, sh.w_max[k]);
-  }
-  return top_largest_strided<NT, NV>(x, Np, P, vmin, vmax, sbuf, sh, emit);
-}
-
 template <int NT, bool COH, typename Emit, typename Mid = NoMid>
 __device__ int top_pages_strided(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
                                  TopScratch& sh, Emit emit, Mid mid = Mid()) {
   static_assert(16 * NT >= kMaxCtx / kPS, "16 pages per thread cover the largest context");
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the range barrier
-  if (tid == 0) sh.list_n = 0;
-  const int nv = (Np + NT - 1) / NT;  // block-uniform
-  if (nv <= 1) return top_pages_strided_nv<NT, 1, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
-  if (nv <= 2) return top_pages_strided_nv<NT, 2, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
-  if (nv <= 4) return top_pages_strided_nv<NT, 4, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
-  if (nv <= 8) return top_pages_strided_nv<NT, 8, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
-  return top_pages_strided_nv<NT, 16, COH>(sc, Np, P, lo, hi, sbuf, sh, emit, mid);
+  return top_strided<NT, COH>(sc, Np, Np, P, AllPresent(), lo, hi, sbuf, sh, emit, mid);
 }
 
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {

@@ -1,16 +1,17 @@
 // Ordered exact top-P inside one workgroup: the P largest scores, ties to the
 // lower candidate index, emitted in ascending candidate order.  Internal header.
 //
-// Layout: the scores sit in LDS; thread tid owns a run of consecutive
-// candidates, read as float4, so the whole selection works from registers and
-// the output order follows from one block scan.
+// Layout: thread t of NT holds candidates j NT + t (j < NV) in registers, the
+// layout that coalesced loads give, so the scores are never staged through
+// LDS; the selection is bound by one CU's vector throughput, so it spends as
+// few instructions per candidate as it can.
 //
 // The selection is described by a cut-off (T, need_eq) on orderable keys:
 // candidate c is taken iff key > T, or key == T and fewer than need_eq keys
 // equal to T precede it (in c order).  Two ways find the cut-off:
-//   * linear histogram (the usual case): after a block min / max, one pass
-//     bins the scores into 2048 bins linear in value -- bin(v) = (int)((v -
-//     vmin) * 2048 / (vmax - vmin)) is non-decreasing in v because each step
+//   * linear histogram (the usual case): given the range [vmin, vmax], one
+//     pass bins the scores into 2048 bins linear in value -- bin(v) = (int)((v
+//     - vmin) * 2048 / (vmax - vmin)) is non-decreasing in v because each step
 //     of the float arithmetic is monotone, so a higher bin holds only larger
 //     scores.  If the whole threshold bin b* (count above < P <= count
 //     through b*) is taken, the cut is "bin >= b*"; otherwise b* usually
@@ -18,9 +19,9 @@
 //   * radix select over orderable keys (when b* holds more than
 //     kLinListMax scores, e.g. many equal values): 11-bit digits of
 //     key - kmin from the highest bit in which keys differ.
-// Then an ordered compaction over the per-thread runs: each thread counts
-// its taken candidates (strictly inside the cut, and on it) and one block
-// scan of the packed pair gives every run its output offset.
+// Output positions come from per-slot wave ballots and one prefix over the
+// (slot, wave) counts, whose order is the candidate order.  run_offsets and
+// emit_ordered serve the per-thread-run compaction of the fine top-k.
 #pragma once
 
 #include "hhr_device.h"
@@ -167,263 +168,6 @@ __device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& g
   eb += cls == 2 ? 1 : 0;
 }
 
-// The min(P, #present) largest present scores of sbuf[0..n), ties to the
-// lower index; emit(pos, c) for each taken candidate c, pos = its rank in
-// ascending c.  present(c) tells whether candidate c < n exists.  Thread tid
-// owns candidates [4*nv4*tid, 4*nv4*(tid+1)) with nv4 = ceil(n / (4*NT)) <=
-// MAXV4; sbuf must hold 4*NT*MAXV4 floats, 16-byte aligned (slots past n are
-// read but never used).  Scores must be finite (-0 counts as +0).  Returns
-// the number taken.  All threads call.
-//
-// Every pass over the data is vector-throughput bound on one CU, so each
-// slot's bin is computed once and kept in registers (16 bits per slot):
-// the cut is then decided from the bins, and only members of the threshold
-// bin compare values.
-template <int NT, int MAXV4, typename Present, typename Emit>
-__device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
-                                  float vmax, int n_valid, TopScratch& sh, Emit emit,
-                                  bool hist_clear = false);
-
-template <int NT, int MAXV4, typename Present, typename Emit>
-__device__ int top_largest_lds(const float* sbuf, int n, Present present, int P, TopScratch& sh,
-                               Emit emit) {
-  constexpr int NWAVES = NT / kWave;
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int l = tid % kWave;
-  const int nv4 = (n + 4 * NT - 1) / (4 * NT);
-  const int c0 = 4 * nv4 * tid;
-  const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
-  auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
-
-  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
-    if (j < nv4) {
-      const float4 t = run4[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = c0 + 4 * j + e;
-        if (c < n && present(c)) {
-          mn = fminf(mn, val(t, e));
-          mx = fmaxf(mx, val(t, e));
-          ++cnt;
-        }
-      }
-    }
-  }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  cnt = wave_sum_i(cnt);
-  if (l == 0) {
-    sh.w_min[w] = mn;
-    sh.w_max[w] = mx;
-    sh.w_n[w] = cnt;
-  }
-  __syncthreads();
-  float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
-  int n_valid = 0;
-#pragma unroll
-  for (int k = 0; k < NWAVES; ++k) {
-    vmin = fminf(vmin, sh.w_min[k]);
-    vmax = fmaxf(vmax, sh.w_max[k]);
-    n_valid += sh.w_n[k];
-  }
-  return top_largest_ranged<NT, MAXV4>(sbuf, n, present, P, vmin, vmax, n_valid, sh, emit);
-}
-
-// The same selection with the range of the present scores given: vmin <=
-// every present score <= vmax, and n_valid = #present.  Each thread reads only
-// its own run of sbuf, so a caller that writes its own run needs no barrier
-// before the call.  hist_clear: the caller has already zeroed sh.hist and
-// sh.list_n before a barrier (saving a barrier here).
-template <int NT, int NV4, typename Present, typename Emit>
-__device__ int top_largest_fixed(const float* sbuf, int n, Present present, int P, float vmin,
-                                 float vmax, int n_valid, TopScratch& sh, Emit& emit,
-                                 bool hist_clear);
-
-// Dispatch on the run length nv4 = ceil(n / (4 NT)) (block-uniform), so that
-// every per-slot loop is exactly as long as the live run: these passes are
-// vector-throughput bound, and dead slots cost as much as live ones.
-template <int NT, int MAXV4, typename Present, typename Emit>
-__device__ int top_largest_ranged(const float* sbuf, int n, Present present, int P, float vmin,
-                                  float vmax, int n_valid, TopScratch& sh, Emit emit,
-                                  bool hist_clear) {
-  static_assert(MAXV4 >= 1 && MAXV4 <= 8, "run length");
-  const int nv4 = max((n + 4 * NT - 1) / (4 * NT), 1);
-#define HHR_TOP_CASE(k)                                                                      \
-  if (MAXV4 >= (k) && nv4 == (k))                                                            \
-    return top_largest_fixed<NT, ((k) <= MAXV4 ? (k) : 1)>(sbuf, n, present, P, vmin, vmax, \
-                                                           n_valid, sh, emit, hist_clear);
-  HHR_TOP_CASE(1)
-  HHR_TOP_CASE(2)
-  HHR_TOP_CASE(3)
-  HHR_TOP_CASE(4)
-  HHR_TOP_CASE(5)
-  HHR_TOP_CASE(6)
-  HHR_TOP_CASE(7)
-  HHR_TOP_CASE(8)
-#undef HHR_TOP_CASE
-  return 0;  // unreachable for n <= 4 NT MAXV4
-}
-
-template <int NT, int NV4, typename Present, typename Emit>
-__device__ int top_largest_fixed(const float* sbuf, int n, Present present, int P, float vmin,
-                                 float vmax, int n_valid, TopScratch& sh, Emit& emit,
-                                 bool hist_clear) {
-  constexpr int MAXV4 = NV4;
-  constexpr int MAXV = 4 * MAXV4;
-  static_assert(MAXV <= 32, "2 class bits per slot in 64 bits");
-  constexpr uint32_t kAbsent = 0xFFFFu;  // bin code of an absent slot
-  const int tid = threadIdx.x;
-  constexpr int nv4 = NV4;
-  const int c0 = 4 * nv4 * tid;
-  const float4* run4 = reinterpret_cast<const float4*>(sbuf) + nv4 * tid;
-  auto val = [&](const float4& t, int e) { return e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w; };
-  auto is_present = [&](int c) { return c < n && present(c); };
-
-  const int Pe = min(P, n_valid);
-  if (Pe <= 0) return 0;  // block-uniform
-  if (!hist_clear) {
-    for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;
-    if (tid == 0) sh.list_n = 0;
-    __syncthreads();
-  }
-
-  // bins: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)) is monotone in v
-  const float range = vmax - vmin;
-  const float inv = range > 0.f ? (float)kLinBins / range : 0.f;
-  uint32_t bins[MAXV / 2];  // two 16-bit bin codes per word
-  const bool all = Pe >= n_valid;
-#pragma unroll
-  for (int j = 0; j < MAXV4; ++j) {
-    uint32_t b4[4];
-    if (j < nv4) {
-      const float4 t = run4[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t bb = kAbsent;
-        if (is_present(c0 + 4 * j + e)) {
-          const float f = (val(t, e) - vmin) * inv;
-          bb = (uint32_t)min(max(f < (float)kLinBins ? (int)f : kLinBins - 1, 0), kLinBins - 1);
-          if (!all) atomicAdd(&sh.hist[bb], 1);
-        }
-        b4[e] = bb;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b4[e] = kAbsent;
-    }
-    bins[2 * j] = b4[0] | (b4[1] << 16);
-    bins[2 * j + 1] = b4[2] | (b4[3] << 16);
-  }
-  auto bin_at = [&](int i) { return (bins[i >> 1] >> (16 * (i & 1))) & 0xFFFFu; };
-
-  // cut-off: mode 0 = every present slot, 1 = bin >= bstar, 2 = bin > bstar or
-  // (bin == bstar and key >= T, ties by need_eq)
-  int mode = 0, need_eq = 0;
-  uint32_t bstar = 0, T = 0u;
-  if (!all) {
-    __syncthreads();
-    {
-      constexpr int PER = kLinBins / NT > 0 ? kLinBins / NT : 1;
-      int local = 0;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int d = kLinBins - 1 - (tid * PER + j);
-        if (d >= 0) local += sh.hist[d];
-      }
-      int tot;
-      int run = block_exclusive_scan<NT, int>(local, sh.scan, &tot);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int d = kLinBins - 1 - (tid * PER + j);
-        if (d >= 0) {
-          const int c = sh.hist[d];
-          if (run < Pe && run + c >= Pe) {
-            sh.bstar = d;
-            sh.above = run;
-          }
-          run += c;
-        }
-      }
-    }
-    __syncthreads();
-    bstar = (uint32_t)sh.bstar;
-    const int need = Pe - sh.above;  // 1 <= need <= hist[b*]
-    const int cstar = sh.hist[bstar];
-    if (need == cstar) {
-      mode = 1;
-    } else if (cstar <= kLinListMax) {
-      mode = 2;
-#pragma unroll
-      for (int i = 0; i < MAXV; ++i)
-        if (bin_at(i) == bstar) sh.list_v[atomicAdd(&sh.list_n, 1)] = sbuf[c0 + i];
-      __syncthreads();
-      // T = the value with (#greater in b*) < need <= (#greater) + (#equal)
-      for (int j = tid; j < cstar; j += NT) {
-        const float vj = sh.list_v[j];
-        int gtr = 0, eql = 0;
-#pragma unroll 1
-        for (int k = 0; k < cstar; ++k) {
-          const float vk = sh.list_v[k];
-          gtr += vk > vj;
-          eql += vk == vj;
-        }
-        if (gtr < need && need <= gtr + eql) {  // all equal copies agree
-          sh.T = orderable_key(vj);
-          sh.need_eq = need - gtr;
-        }
-      }
-      __syncthreads();
-      T = sh.T;
-      need_eq = sh.need_eq;
-    } else {
-      mode = 3;  // radix over the keys of the whole set
-      radix_cutoff<NT>(
-          [&](int i) -> uint32_t {
-            const int c = c0 + i;
-            return is_present(c) ? orderable_key(sbuf[c]) : 0u;
-          },
-          4 * nv4, Pe, sh);
-      T = sh.T;
-      need_eq = sh.need_eq;
-    }
-  }
-  // classify each slot once (2 bits: 1 = inside the cut, 2 = on it)
-  uint64_t cls = 0;
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const uint32_t bb = bin_at(i);
-    int k = 0;
-    if (bb != kAbsent) {
-      if (mode == 0) {
-        k = 1;
-      } else if (mode == 1) {
-        k = bb >= bstar ? 1 : 0;
-      } else if (mode == 2 && bb != bstar) {
-        k = bb > bstar ? 1 : 0;
-      } else {  // key comparison: mode 3, or a member of the threshold bin
-        const uint32_t key = orderable_key(sbuf[c0 + i]);
-        k = key > T ? 1 : (key == T ? 2 : 0);
-      }
-    }
-    cls |= (uint64_t)k << (2 * i);
-    gt += k == 1;
-    eq += k == 2;
-  }
-  int gb, eb;
-  run_offsets<NT>(gt, eq, sh, gb, eb);
-#pragma unroll 1
-  for (int i = 0; i < 4 * nv4; ++i) {
-    const int k = (int)(cls >> (2 * i)) & 3;
-    if (k != 0) emit_ordered(k, c0 + i, need_eq, gb, eb, emit);
-  }
-  return Pe;
-}
-
 // ---------------------------------------------------------------------------
 // The same selection with the scores in registers and strided ownership:
 // thread t of NT holds candidate j NT + t in x[j] (j < NV), the layout that
@@ -433,13 +177,15 @@ __device__ int top_largest_fixed(const float* sbuf, int n, Present present, int 
 // counts, whose order j, wave, lane is the candidate order.  This costs a few
 // vector instructions per candidate where the run-based compaction spends
 // tens, and the top-P of one (b, g) runs on a single CU bound by its vector
-// throughput.  vmin <= every score <= vmax; sh.hist and sh.list_n must be
-// zero behind a barrier; sbuf (4 NT NV floats in LDS) is used only by the
-// radix fallback.  Candidates c >= n are absent.  Returns min(P, n).  All NT
-// threads call.
-template <int NT, int NV, typename Emit>
-__device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmin, float vmax,
-                                   float* sbuf, TopScratch& sh, Emit& emit) {
+// throughput.  Candidate j NT + t is present iff it is below n and
+// present(x[j]); n_valid counts the present ones, and vmin <= every present
+// score <= vmax.  sh.hist and sh.list_n must be zero behind a barrier; sbuf
+// (NT NV floats in LDS) is used only by the radix fallback.  Returns
+// min(P, n_valid).  All NT threads call.
+template <int NT, int NV, typename Present, typename Emit>
+__device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Present present,
+                                   int P, float vmin, float vmax, float* sbuf, TopScratch& sh,
+                                   Emit& emit) {
   constexpr int NWAVES = NT / kWave;
   constexpr int NE = NV * NWAVES;  // (slot, wave) entries
   static_assert(NE <= kStridedCnt, "slot counts fit TopScratch::cnt");
@@ -448,9 +194,9 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmi
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = tid % kWave;
-  const int Pe = min(P, n);
+  const int Pe = min(P, n_valid);
   if (Pe <= 0) return 0;  // block-uniform
-  const bool all = Pe >= n;
+  const bool all = Pe >= n_valid;
 
   // bins, linear in value: bin(v) = (int)((v - vmin) * 2048 / (vmax - vmin)),
   // non-decreasing in v; -1 for an absent candidate
@@ -461,9 +207,9 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmi
   for (int j = 0; j < NV; ++j) {
     const float f = (x[j] - vmin) * inv;
     const int bb = f < (float)kLinBins ? max((int)f, 0) : kLinBins - 1;
-    const bool present = j * NT + tid < n;
-    bin[j] = present ? bb : -1;
-    if (present && !all) atomicAdd(&sh.hist[bb], 1);
+    const bool pres = j * NT + tid < n && present(x[j]);
+    bin[j] = pres ? bb : -1;
+    if (pres && !all) atomicAdd(&sh.hist[bb], 1);
   }
 
   // cut-off: mode 0 = every present candidate, 1 = bin >= bstar, 2 = bin >
@@ -533,7 +279,7 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmi
       radix_cutoff<NT>(
           [&](int i) -> uint32_t {
             const int c = i * NT + tid;
-            return c < n ? orderable_key(sbuf[c]) : 0u;
+            return c < n && present(sbuf[c]) ? orderable_key(sbuf[c]) : 0u;
           },
           NV, Pe, sh);
       T = sh.T;
@@ -599,6 +345,81 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int P, float vmi
     if (cls[j] == 1 || (cls[j] == 2 && eb < need_eq)) emit(gb + min(eb, need_eq), j * NT + tid);
   }
   return Pe;
+}
+
+// ---------------------------------------------------------------------------
+// Loading front end of top_largest_strided.  mid() runs once, after the loads
+// are issued and before their values are used, so that work of the caller's
+// with loads of its own shares their round trip.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+struct AllPresent {
+  __device__ bool operator()(float) const { return true; }
+};
+
+// Loads candidates j NT + t (j < NV) of src into registers (COH: agent-scope;
+// addresses clamped to src[0 .. n_load)), runs mid(), then reduces the range
+// of the present candidates (below n, with the given pieces lo, hi) and their
+// count in one barrier, and selects with top_largest_strided.  The caller
+// must have zeroed sh.hist and sh.list_n.
+template <int NT, int NV, bool COH, typename Present, typename Emit, typename Mid>
+__device__ int top_strided_nv(const float* src, int n_load, int n, int P, Present& present,
+                              float lo, float hi, float* sbuf, TopScratch& sh, Emit& emit,
+                              Mid& mid) {
+  const int tid = threadIdx.x;
+  const int last = max(n_load - 1, 0);
+  float x[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) x[j] = Mem<COH>::ld(src + min(j * NT + tid, last));
+  mid();
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool pres = j * NT + tid < n && present(x[j]);
+    cnt += __popcll(__ballot(pres));
+    if (pres) {
+      lo = fminf(lo, x[j]);
+      hi = fmaxf(hi, x[j]);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if ((tid & (kWave - 1)) == 0) {
+    sh.w_min[tid / kWave] = lo;
+    sh.w_max[tid / kWave] = hi;
+    sh.w_n[tid / kWave] = cnt;
+  }
+  __syncthreads();  // also orders the caller's clearing of sh.hist and sh.list_n
+  float vmin = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
+  int n_valid = 0;
+#pragma unroll
+  for (int k = 0; k < NT / kWave; ++k) {
+    vmin = fminf(vmin, sh.w_min[k]);
+    vmax = fmaxf(vmax, sh.w_max[k]);
+    n_valid += sh.w_n[k];
+  }
+  return top_largest_strided<NT, NV>(x, n, n_valid, present, P, vmin, vmax, sbuf, sh, emit);
+}
+
+// The P largest of src[0 .. n) (those present), ties to the lower index,
+// emitted in ascending index.  n_load (>= n, <= 16 NT, block-uniform and
+// known before n may be) bounds the loads, so they need not wait for n.
+template <int NT, bool COH, typename Present, typename Emit, typename Mid = NoMid>
+__device__ int top_strided(const float* src, int n_load, int n, int P, Present present, float lo,
+                           float hi, float* sbuf, TopScratch& sh, Emit emit, Mid mid = Mid()) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the range barrier
+  if (tid == 0) sh.list_n = 0;
+  const int nv = (n_load + NT - 1) / NT;
+#define HHR_TOP_STRIDED(V) \
+  return top_strided_nv<NT, V, COH>(src, n_load, n, P, present, lo, hi, sbuf, sh, emit, mid)
+  if (nv <= 1) HHR_TOP_STRIDED(1);
+  if (nv <= 2) HHR_TOP_STRIDED(2);
+  if (nv <= 4) HHR_TOP_STRIDED(4);
+  if (nv <= 8) HHR_TOP_STRIDED(8);
+  HHR_TOP_STRIDED(16);
+#undef HHR_TOP_STRIDED
 }
 
 }  // namespace hhr
