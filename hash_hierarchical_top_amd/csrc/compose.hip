@@ -32,6 +32,11 @@ constexpr int kScoreThreads = 1024;
 // the coarse stage runs staged instead (query encode, bounds, top-P).
 constexpr int kScoreToppMaxWgs = 2 * 256;
 constexpr int kScorePagesPerWg = (kScoreThreads / kWave) * kScorePagesPerWave;  // 256
+// With few pages (short contexts, small batches) a workgroup scores only 128
+// or 64 pages (its first 8 or 4 waves), so that the scoring grid still covers
+// the chip's 256 CUs; the top-P workgroup always has all 1024 threads.
+constexpr int kScoreMinPagesPerWg = 4 * kScorePagesPerWave;  // 64
+constexpr int kScoreTargetWgs = 256;
 // Polls (about a microsecond each) before the top-P workgroup of the
 // one-launch selection gives up waiting for the other workgroups' distances.
 constexpr int kFineSpinMax = 1 << 20;
@@ -157,8 +162,9 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
   }
 }
 
-// S2 + S3 + S4.  grid (ceil(NpCap / 256), B*Hkv), 1024 threads: 16 waves x 16
-// pages.  Each workgroup rotates its group's queries itself (64 KiB of R from
+// S2 + S3 + S4.  grid (ceil(NpCap / ppw), B*Hkv), 1024 threads: the first
+// ppw / 16 of the 16 waves score 16 pages each (ppw = 256, or 128 or 64 when
+// the grid would not cover the chip).  Each workgroup rotates its group's queries itself (64 KiB of R from
 // L2, issued after its metadata loads so both are in flight together);
 // workgroup 0 of each (b, g) also writes the query codes.
 //
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
     uint32_t* __restrict__ status, const uint32_t* __restrict__ ham_codes,
     uint16_t* __restrict__ hall, int top_k, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ sel_count) {
+    int32_t* __restrict__ sel_count, int ppw) {
   using Smem = std::conditional_t<FINE, ScoreFineSmem, ScoreTopSmem>;
   __shared__ Smem sm;
   __shared__ int s_last;
@@ -201,14 +207,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   const int NpCap = Lcap / kPS;
   const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
   const int Np = (L + kPS - 1) / kPS;
-  const int pb = blockIdx.x * kScorePagesPerWg + (tid >> 6) * kScorePagesPerWave;
-  const bool wave_has = pb < Np;                                    // wave-uniform
-  const bool wg_has = (int)blockIdx.x * kScorePagesPerWg < Np;      // block-uniform
+  const int pb = blockIdx.x * ppw + (tid >> 6) * kScorePagesPerWave;
+  const bool wave_has = (tid >> 6) * kScorePagesPerWave < ppw && pb < Np;  // wave-uniform
+  const bool wg_has = (int)blockIdx.x * ppw < Np;                   // block-uniform
   PageLoads<1> pl;
   if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
   // the workgroup holding the last page, when a key was appended (block-uniform)
-  const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / kScorePagesPerWg;
+  const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / ppw;
   if (owner) {
     const size_t krow = ((size_t)bg * Lcap + (size_t)(L - 1)) * kD;
     const void* key = kv_f32 ? (const void*)((const float*)kcache + krow)
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
 
   int P = 0;
   int32_t* out = kept + (size_t)bg * p_max;
-  const int own_lo = blockIdx.x * kScorePagesPerWg;
+  const int own_lo = blockIdx.x * ppw;
   // FINE: this workgroup's own pages' distances into LDS, their code loads
   // sharing the round trip of the top-P's staging loads
   auto own_dist = [&]() {
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     if (tid == 0) st_agent_u32(ctl + 1, 0u);
     const int nbins = kNW * 32 * G + 1;
     ham_gather_kept<kScoreThreads>(bg, Lcap, P, nbins, hall, sm.own_h, own_lo,
-                                   own_lo + kScorePagesPerWg, sm.fine);
+                                   own_lo + ppw, sm.fine);
     ham_select_core<kScoreThreads, false>(bg, P, top_k, nbins, sel_idx, sel_count, sm.fine);
   }
 }
@@ -387,6 +393,17 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_merge(
 
 }  // namespace
 
+// Pages per scoring workgroup: 256, halved (down to 64) while the grid would
+// have fewer workgroups than the chip has CUs.
+static int score_pages_per_wg(const hhr_shape& s) {
+  const int NpCap = s.max_ctx / kPS;
+  const long long BG = (long long)s.batch * s.n_kv_heads;
+  int ppw = kScorePagesPerWg;
+  while (ppw > kScoreMinPagesPerWg && (long long)((NpCap + ppw - 1) / ppw) * BG < kScoreTargetWgs)
+    ppw /= 2;
+  return ppw;
+}
+
 bool one_launch_select(const hhr_shape& s) {
   const long long wgs = (long long)((s.max_ctx / kPS + kScorePagesPerWg - 1) / kScorePagesPerWg) *
                         s.batch * s.n_kv_heads;
@@ -400,7 +417,8 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
                              const AppendArgs* app, const FineArgs* fine) {
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
-  const dim3 grid((NpCap + kScorePagesPerWg - 1) / kScorePagesPerWg, BG);
+  const int ppw = score_pages_per_wg(s);
+  const dim3 grid((NpCap + ppw - 1) / ppw, BG);
   if (!one_launch_select(s)) {
     // many rounds of one-CU workgroups: the launch boundaries of the staged
     // stages cost less than the latency each round would leave exposed.  The
@@ -432,7 +450,7 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
                      seq_len, R, W, m, kc, kf32, cd, keep_num, keep_den, keep_abs, p_max,      \
                      s.n_q_heads, s.n_kv_heads, s.max_ctx, buf.scores, buf.wave_range,         \
                      buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status, hc, hall, \
-                     tk, si, sc)
+                     tk, si, sc, ppw)
 #define HHR_SCORE_TOPP_F(MBF, APP)     \
   if (fine)                            \
     HHR_SCORE_TOPP(MBF, APP, true);    \
