@@ -110,6 +110,8 @@ WORKLOADS: Dict[str, HHRWorkload] = {
     "llama8b_32k": HHRWorkload("llama8b_32k", 1, 32, 8, 32768, "bf16", 1, 4, 0, 2048, 1001),
     # same shape at 128K context, keep 12.5% of pages
     "llama8b_128k": HHRWorkload("llama8b_128k", 1, 32, 8, 131072, "bf16", 1, 8, 0, 4096, 1002),
+    # same shape at 64K context (a test size between the two: 4096 pages per KV head)
+    "llama8b_64k": HHRWorkload("llama8b_64k", 1, 32, 8, 65536, "bf16", 1, 8, 0, 4096, 1005),
     # batched ragged decode, 16 sequences of 8K..64K
     "llama8b_ragged_b16": HHRWorkload("llama8b_ragged_b16", 16, 32, 8, 65536, "bf16", 1, 4, 0,
                                       2048, 1003, min_len=8192),

@@ -140,6 +140,18 @@ class Pipeline:
         assert self.H.hhr_read_device_status(ws) == 0
         return kept, kc, qc
 
+    def select(self):
+        """hhr_select into fresh buffers (and a workspace of its own)."""
+        sel = torch.full_like(self.sel, 12345)
+        sc = torch.full_like(self.sel_count, -3)
+        ws = torch.zeros(self.H.hhr_workspace_size(self.shape, *self.keep, self.top_k),
+                         dtype=torch.uint8, device=dev())
+        self.H.hhr_select(self.shape, self.d["q"], self.d["seq_len"], self.d["R"], self.d["W"],
+                          self.codes, self.meta, *self.keep, self.top_k, sel, sc, ws)
+        torch.cuda.synchronize()
+        assert self.H.hhr_read_device_status(ws) == 0
+        return sel, sc
+
     def status(self):
         return self.H.hhr_read_device_status(self.ws)
 

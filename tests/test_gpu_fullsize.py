@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, on sampled outputs the oracle computes one
-by one: the 4K f32 single-head case, the 32K and 128K Llama-3.1-8B-shaped
+by one: the 4K f32 single-head case, the 32K, 64K and 128K Llama-3.1-8B-shaped
 decode steps (the 128K one as bench.py times it) and the 16-sequence ragged
-batch.
+batch.  The coarse launch scores 64, 128 and 256 pages per workgroup at 32K,
+64K and 128K respectively.
 
 For a few sampled (sequence, KV head) pairs: key codes and page metadata of
 sampled keys and pages, the query encoding, every page bound (conditioned on
@@ -20,7 +21,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = ["tiny_f32_4k", "llama8b_32k", "llama8b_128k", "llama8b_ragged_b16"]
+WORKLOADS = ["tiny_f32_4k", "llama8b_32k", "llama8b_64k", "llama8b_128k", "llama8b_ragged_b16"]
 
 
 def _pairs(w, seq_len):
@@ -143,6 +144,13 @@ def test_select_pages_equals_stages(full):
     kept, kc, qc = p.select_pages()
     assert torch.equal(kept, p.kept) and torch.equal(kc, p.kept_count)
     assert torch.equal(qc, p.q_codes)
+
+
+def test_select_equals_stages(full):
+    """hhr_select (one launch on all but the ragged batch) equals the staged selection."""
+    name, w, p, h, pairs = full
+    sel, sc = p.select()
+    assert torch.equal(sc, p.sel_count) and torch.equal(sel, p.sel)
 
 
 def test_decode_and_graph_replays_equal_stages(full):
