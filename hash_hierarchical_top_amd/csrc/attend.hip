@@ -1,8 +1,11 @@
 // S7 sparse decode: softmax attention over only the selected K/V rows
 // [HHR abstract: hash-based sparse attention], split over 64-key chunks of the
 // selected set with an online-softmax (m, l, o) combine.  k_attn runs one
-// chunk per workgroup (attn_chunk); k_attn_combine merges one (b, g, query
-// head) per workgroup of kCombThreads threads (attn_combine).
+// chunk per workgroup (attn_chunk), or, when a group has many query heads and
+// the grid is small, one chunk for 4 of the heads per workgroup (grid.z picks
+// the heads: the 64 rows are gathered once per head group, and each wave then
+// attends one head instead of several); k_attn_combine merges one (b, g,
+// query head) per workgroup of kCombThreads threads (attn_combine).
 
 #include "hhr_device.h"
 #include "hhr_internal.h"
@@ -23,10 +26,12 @@ __global__ __launch_bounds__(256) void k_attn(
   const int cnt = max(0, min(sel_count[bg], top_k));
   const int k0 = blockIdx.x * kCh;
   if (k0 >= cnt) return;
+  const int hper = (Hq / Hkv + gridDim.z - 1) / gridDim.z;  // query heads per workgroup
+  const int h_lo = blockIdx.z * hper;
   attn_chunk<KF32, false>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, top_k, k0, min(kCh, cnt - k0), scale,
                           q, kcache, vcache, sel_idx,
                           part + ((size_t)bg * n_split + blockIdx.x) * kMaxG * kPartStride, status,
-                          sm);
+                          sm, h_lo, h_lo + hper);
 }
 
 __global__ __launch_bounds__(kCombThreads) void k_attn_combine(
@@ -46,7 +51,12 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
                                 const int32_t* sel_count, int32_t top_k, float scale, float* out,
                                 float* part, int32_t n_split, uint32_t* status,
                                 hipStream_t stream) {
-  dim3 grid(n_split, s.batch * s.n_kv_heads);
+  // more than 4 query heads per KV head and fewer chunks than CUs: split the
+  // heads over grid.z, 4 per workgroup (one per wave)
+  const int G = s.n_q_heads / s.n_kv_heads;
+  const long long chunks = (long long)n_split * s.batch * s.n_kv_heads;
+  const int hsplit = (G > 4 && chunks < 256) ? (G + 3) / 4 : 1;
+  dim3 grid(n_split, s.batch * s.n_kv_heads, hsplit);
   if (s.kv_dtype == HHR_F32)
     hipLaunchKernelGGL(k_attn<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache, sel_idx,
                        sel_count, part, status, s.n_q_heads, s.n_kv_heads, s.max_ctx, top_k,

@@ -898,7 +898,9 @@ __device__ __forceinline__ int pick_window(int bg, int P, int p_max, int nbins, 
 // (o~, m, l): o~_h = sum_i e^(x_hi - m_h) V_i, m_h = max_i x_hi,
 // l_h = sum_i e^(x_hi - m_h), x_hi = q_h . K_i * scale.
 // All threads of the workgroup must call (barriers); each 256-thread group
-// passes its own chunk (nk = 0 for an idle group).
+// passes its own chunk (nk = 0 for an idle group).  Only query heads
+// [h_lo, h_hi) of the group are attended and their partials written, so that
+// several workgroups can share one chunk's heads when the group is large.
 constexpr int kCh = kAttnChunk;      // 64 selected keys per chunk
 constexpr int kPartStride = kD + 2;  // o~[128], m, l
 constexpr int kRowPad = 8;           // LDS row padding (bank spread), in elements
@@ -918,7 +920,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
                            float scale, const float* __restrict__ q,
                            const void* __restrict__ kcache, const void* __restrict__ vcache,
                            const int32_t* sel_idx, float* pout, uint32_t* status,
-                           AttnSmem<KF32>& sm) {
+                           AttnSmem<KF32>& sm, int h_lo = 0, int h_hi = kMaxG) {
   typedef typename AttnSmem<KF32>::ET ET;
   constexpr int kStride = kD + kRowPad;
   constexpr int kVec = 16 / sizeof(ET);              // elements per 16-byte load
@@ -941,6 +943,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     }
     sm.sidx[tq] = idx;
   }
+  const int h_end = min(h_hi, G);  // this workgroup's query heads [h_lo, h_end)
   for (int i = tq; i < G * kD; i += 256)
     sm.sq[i / kD][i % kD] = q[((size_t)b * Hq + (size_t)g * G) * kD + i];
   __syncthreads();
@@ -972,7 +975,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   __syncthreads();
 
   // logits: thread (key = l, head group w) -> heads w, w+4, ...
-  for (int h = w; h < G; h += 4) {
+  for (int h = h_lo + w; h < h_end; h += 4) {
     const ET* row = sm.rows + l * kStride;
     float dot = 0.f;
 #pragma unroll 4
@@ -999,7 +1002,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     const int c = tq + 256 * i;
     *(u32x4*)(sm.rows + (c / kChunksPerRow) * kStride + (c % kChunksPerRow) * kVec) = vreg[i];
   }
-  for (int h = w; h < G; h += 4) {
+  for (int h = h_lo + w; h < h_end; h += 4) {
     const float x = sm.sp[h][l];
     const float m = wave_max(x);
     const float p = (x == -__builtin_huge_valf()) ? 0.f : expf(x - m);
@@ -1014,7 +1017,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
 
   // partial o~_h[d] = sum_k p_h[k] V[k][d]: lane owns dims {2l, 2l+1}, wave w heads w, w+4, ...
   if (nk > 0) {
-    for (int h = w; h < G; h += 4) {
+    for (int h = h_lo + w; h < h_end; h += 4) {
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll 8
       for (int k = 0; k < kCh; ++k) {
