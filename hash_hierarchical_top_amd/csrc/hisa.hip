@@ -101,27 +101,63 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   // conflicts; heads >= Hi are zero)
   __shared__ __attribute__((aligned(16))) uint16_t sq[kMaxIndexHeads][kD + 8];
   const int b = blockIdx.y;
-  const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 ? status : nullptr);
-  const int Nb = (L + block - 1) / block;
   const int NbCap = Lcap / block;
   const int wg_blk0 = blockIdx.x * kBsWaves * gpw * 16;
-  if (wg_blk0 >= Nb) return;  // block-uniform, before the barrier
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int l = tid & 63;
   const int lrow = l & 15;
   const int lgrp = l >> 4;
+  // The query, its weights and scales and the first group's representatives
+  // load before the row's length is known (every address stays inside its
+  // buffer; rows past the end are computed and never stored), so they share
+  // that round trip.
+  constexpr int kQWords = kMaxIndexHeads * kD / 4 / (64 * kBsWaves);
+  static_assert(kQWords * 64 * kBsWaves == kMaxIndexHeads * kD / 4, "query words per thread");
   const uint8_t* qb = q8 + (size_t)b * Hi * kD;
-  for (int i = tid; i < kMaxIndexHeads * kD / 4; i += 64 * kBsWaves) {
+  uint32_t qv[kQWords];
+#pragma unroll
+  for (int k = 0; k < kQWords; ++k) {
+    const int i = tid + k * 64 * kBsWaves;
+    const int h = i / (kD / 4);
+    qv[k] = h < Hi ? *(const uint32_t*)(qb + (size_t)h * kD + 4 * (i % (kD / 4))) : 0u;
+  }
+  // this lane's 16 heads in the epilogue: 16 mt + 4 lgrp + j
+  float wh[4][4], sh[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 16 * mt + 4 * lgrp + j;
+      wh[mt][j] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
+      sh[mt][j] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
+    }
+  // B rows: the representative of block blk0 + lrow, dims 32 ks + 8 lgrp + [0, 8)
+  const float* repb = reps + (size_t)(shared ? 0 : b) * NbCap * kD;
+  floatx4 x0[4], x1[4];
+  auto load_reps = [&](int row) {
+    const float* rb = repb + (size_t)row * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      x0[ks] = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
+      x1[ks] = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
+    }
+  };
+  load_reps(min(wg_blk0 + wv * 16 + lrow, NbCap - 1));
+  const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 ? status : nullptr);
+  const int Nb = (L + block - 1) / block;
+  if (wg_blk0 >= Nb) return;  // block-uniform, before the barrier
+#pragma unroll
+  for (int k = 0; k < kQWords; ++k) {
+    const int i = tid + k * 64 * kBsWaves;
     const int h = i / (kD / 4);
     const int d = 4 * (i % (kD / 4));
-    const uint32_t v = h < Hi ? *(const uint32_t*)(qb + (size_t)h * kD + d) : 0u;
     u32x2 pk;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t lo = __float_as_uint(e4m3fn_to_f32((v >> (16 * k)) & 0xFFu)) >> 16;
-      const uint32_t hi = __float_as_uint(e4m3fn_to_f32((v >> (16 * k + 8)) & 0xFFu)) >> 16;
-      pk[k] = lo | (hi << 16);
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t lo = __float_as_uint(e4m3fn_to_f32((qv[k] >> (16 * kk)) & 0xFFu)) >> 16;
+      const uint32_t hi = __float_as_uint(e4m3fn_to_f32((qv[k] >> (16 * kk + 8)) & 0xFFu)) >> 16;
+      pk[kk] = lo | (hi << 16);
     }
     *(u32x2*)&sq[h][d] = pk;
   }
@@ -133,35 +169,20 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       aq[mt][ks] = as_bf16x8(*(const u32x4*)&sq[16 * mt + lrow][32 * ks + 8 * lgrp]);
-  // this lane's 16 heads in the epilogue: 16 mt + 4 lgrp + j
-  float wh[4][4], sh[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 16 * mt + 4 * lgrp + j;
-      wh[mt][j] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
-      sh[mt][j] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
-    }
   const float inf = opaque_inf();
   for (int grp = 0; grp < gpw; ++grp) {
     const int blk0 = wg_blk0 + (grp * kBsWaves + wv) * 16;
     if (blk0 >= Nb) break;  // wave-uniform; no barrier follows
-    // B: the representative of block blk0 + lrow (the last block past the
-    // end), dims 32 ks + 8 lgrp + [0, 8)
-    const float* rb =
-        reps + ((size_t)(shared ? 0 : b) * NbCap + min(blk0 + lrow, Nb - 1)) * kD;
+    if (grp > 0) load_reps(min(blk0 + lrow, Nb - 1));
     bf16x8 bhi[4], blo[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const floatx4 x0 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
-      const floatx4 x1 = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
       u32x4 hv, lv;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         uint32_t h0, l0, h1, l1;
-        split_bf16(jj < 2 ? x0[2 * jj] : x1[2 * jj - 4], h0, l0);
-        split_bf16(jj < 2 ? x0[2 * jj + 1] : x1[2 * jj - 3], h1, l1);
+        split_bf16(jj < 2 ? x0[ks][2 * jj] : x1[ks][2 * jj - 4], h0, l0);
+        split_bf16(jj < 2 ? x0[ks][2 * jj + 1] : x1[ks][2 * jj - 3], h1, l1);
         hv[jj] = h0 | (h1 << 16);
         lv[jj] = l0 | (l1 << 16);
       }
@@ -238,17 +259,16 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   const int b = xcd_rows ? (by % 8) * (gridDim.y / 8) + by / 8 : by;
   if (b >= nrows) return;
   const int slot0 = blockIdx.x * nslot;
-  int L = seq_len[b];
-  if (L < 0 || L > Lcap) L = 0;
-  const int kc = min(kept_count[b], keep_blocks);
-  const int slot1 = min(slot0 + nslot, kc);
-  if (slot0 >= slot1) return;
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int l = tid & 63;
   const int lrow = l & 15;
   const int lgrp = l >> 4;
+  const int tiles_per_block = block / 16;
 
+  // The query's fragments and weights and the block of this wave's first tile
+  // load before the row's length and kept count are known (every address
+  // stays inside its buffer), so they share that round trip.
   // A: head 16 ht + lrow; this lane's 16 heads for the epilogue: 16 ht + 4 lgrp + j
   fp8x8 aq[4][4];
   float wsq[4][4];
@@ -264,15 +284,22 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
       wsq[ht][j] = he < Hi ? w[(size_t)b * Hi + he] * q_scale[(size_t)b * Hi + he] : 0.f;
     }
   }
+  const int pslot = min(slot0 + wv / tiles_per_block, keep_blocks - 1);
+  const int pblk = kept[(size_t)b * keep_blocks + pslot];
+  int L = seq_len[b];
+  if (L < 0 || L > Lcap) L = 0;
+  const int kc = min(kept_count[b], keep_blocks);
+  const int slot1 = min(slot0 + nslot, kc);
+  if (slot0 >= slot1) return;
+
   const size_t cb = shared ? 0 : (size_t)b;  // the query row's cache
   const uint8_t* kb = k8 + cb * Lcap * kD;
   const float* ksb = k_scale + cb * Lcap;
-  const int tiles_per_block = block / 16;
   const int ntiles = (slot1 - slot0) * tiles_per_block;
   // key fragments of tile i (token row of this lane; rows past L read row 0)
   auto tile_token = [&](int i) {
     const int slot = slot0 + i / tiles_per_block;
-    const int blk = kept[(size_t)b * keep_blocks + slot];
+    const int blk = slot == pslot ? pblk : kept[(size_t)b * keep_blocks + slot];
     return blk * block + 16 * (i % tiles_per_block) + lrow;
   };
   auto load_tile = [&](int i, fp8x8 (&kf)[4]) {
