@@ -17,7 +17,10 @@ Readings where the pages are silent:
     dequantized value = scale * e4m3fn(code);
   * ties: larger score first, then lower block / token index;
   * "exact" top-k means exact within the kept blocks (the coarse stage is a
-    heuristic; its agreement with the flat indexer is measured by IoU).
+    heuristic; its agreement with the flat indexer is measured by IoU);
+  * a prefill query row at position p is causal in both stages: it sees tokens
+    t <= p only, so its partly visible last block is pooled over its visible rows,
+    and it selects what a decode query with p + 1 tokens in the cache selects.
 """
 from __future__ import annotations
 
@@ -97,13 +100,23 @@ def select(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, keep_blocks: i
 def prefill_select(q8, q_scale, w, k8, k_scale, cache_len: int, q_len: int, block: int,
                    keep_blocks: int, top_k: int) -> Dict[str, np.ndarray]:
     """HISA selection for one query row of a prefill chunk [HISA abstract: the
-    indexer's per-layer O(L^2) case].  The index-key cache holds cache_len rows and
-    its block representatives are pooled once over them; the row sees tokens
-    t < q_len (its position + 1): the coarse filter scores the blocks that hold its
-    prefix with those representatives, the token stage only its prefix."""
+    indexer's per-layer O(L^2) case, where every query scans its whole prefix].
+
+    The index-key cache holds cache_len rows; the row sits at position q_len - 1 and
+    sees only tokens t < q_len, in both stages.  Coarse stage: a block wholly inside
+    the prefix is represented by the mean of all its rows (what pooling the shared
+    cache gives); the row's last block, when only partly visible, by the mean of its
+    visible rows t < q_len alone.  So no key after the row's position enters its
+    selection, and the row selects what a decode query with a sequence of q_len
+    tokens would.  Fine stage: the indexer on the kept blocks' tokens t < q_len.
+    """
     q = dequantize(q8, q_scale)
     keys = dequantize(np.asarray(k8)[:cache_len], np.asarray(k_scale)[:cache_len])
-    reps = pooled_reps(keys, block)[:(q_len + block - 1) // block]
+    n_full = q_len // block                          # blocks wholly visible to the row
+    reps = pooled_reps(keys, block)[:n_full]
+    if q_len % block:                                # the row's partly visible last block
+        partial = keys[n_full * block:q_len].mean(axis=0)
+        reps = np.concatenate([reps, partial[None, :]], axis=0)
     S = indexer_scores(q, w, reps)
     blocks = top_largest(S, np.arange(reps.shape[0]), keep_blocks)
     cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
@@ -111,18 +124,6 @@ def prefill_select(q8, q_scale, w, k8, k_scale, cache_len: int, q_len: int, bloc
     s = indexer_scores(q, w, keys[cand])
     sel = top_largest(s, cand, top_k)
     return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s, sel=sel)
-
-
-def select_in_blocks(q8, q_scale, w, k8, k_scale, seq_len: int, block: int, blocks,
-                     top_k: int) -> Dict[str, np.ndarray]:
-    """Fine stage alone, on given kept blocks."""
-    q = dequantize(q8, q_scale)
-    blocks = np.asarray(blocks, dtype=np.int64)
-    cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
-    cand = cand[cand < seq_len]
-    keys = dequantize(np.asarray(k8)[cand], np.asarray(k_scale)[cand])
-    s = indexer_scores(q, w, keys)
-    return dict(cand=cand, token_scores=s, sel=top_largest(s, cand, top_k))
 
 
 def flat_select(q8, q_scale, w, k8, k_scale, seq_len: int, top_k: int) -> np.ndarray:

@@ -386,3 +386,14 @@ def test_bf16_outward_metadata_keeps_the_bound_valid():
     true = (K @ Q.T).sum(axis=1)
     for p in range(s16.size):
         assert s16[p] >= true[p * 16:(p + 1) * 16].max() - 1e-9
+
+
+def test_recall_worked_values():
+    """recall = |selected & exact| / |exact| (HHR Figure 4: top-k key recall)."""
+    assert O.recall([1, 2, 3, 4], [2, 4, 6, 8]) == 0.5
+    # more or fewer selected than exact: the denominator is the exact set
+    assert O.recall([5], [1, 2, 3, 5]) == 0.25
+    assert O.recall([1, 2, 3, 4, 5, 6], [1, 2]) == 1.0
+    assert O.recall([7, 9], [1, 2, 3]) == 0.0
+    assert O.recall([], [1]) == 0.0
+    assert O.recall([3], []) == 1.0

@@ -112,15 +112,56 @@ def test_prefill_row_at_the_cache_end_is_the_decode_selection():
         assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["blocks"], b["blocks"])
 
 
+@pytest.mark.parametrize("q_len", [1, 63, 64, 65, 500, 900])
+def test_prefill_row_is_the_decode_selection_at_its_length(q_len):
+    """Causal prefill: row r of a chunk over a 900-key cache selects exactly what a decode
+    query with a sequence of q_len[r] tokens selects (the decode path pools the prefix
+    keys[:q_len] itself, so a partly visible last block is pooled over its visible rows)."""
+    q8, qs, wt, k8, ks = _prefill_inputs()
+    a = O.prefill_select(q8, qs, wt, k8, ks, 900, q_len, 64, 3, 150)
+    b = O.select(q8, qs, wt, k8, ks, q_len, 64, 3, 150)
+    assert a["reps"].shape == b["reps"].shape
+    assert np.allclose(a["reps"], b["reps"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(a["block_scores"], b["block_scores"], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(a["blocks"], b["blocks"])
+    assert np.array_equal(a["cand"], b["cand"])
+    assert np.array_equal(a["sel"], b["sel"])
+
+
+def test_prefill_row_does_not_see_future_keys():
+    """Rewriting every key at or after the row's position (the rest of its last block
+    included) leaves the row's representatives, block scores and selection unchanged."""
+    q8, qs, wt, k8, ks = _prefill_inputs()
+    rng = np.random.default_rng(77)
+    for q_len in (1, 40, 64, 100, 511):
+        k8b, ksb = k8.copy(), ks.copy()
+        junk8, junks = synth.quantize_rows_e4m3(
+            (5.0 * rng.standard_normal((900 - q_len, 128))).astype(np.float32))
+        k8b[q_len:], ksb[q_len:] = junk8, junks
+        a = O.prefill_select(q8, qs, wt, k8, ks, 900, q_len, 64, 2, 40)
+        b = O.prefill_select(q8, qs, wt, k8b, ksb, 900, q_len, 64, 2, 40)
+        assert np.array_equal(a["reps"], b["reps"])
+        assert np.array_equal(a["block_scores"], b["block_scores"])
+        assert np.array_equal(a["sel"], b["sel"])
+
+
 def test_prefill_row_sees_only_its_prefix():
     q8, qs, wt, k8, ks = _prefill_inputs()
+    keys = O.dequantize(k8[:900], ks[:900])
+    full = O.pooled_reps(keys, 64)
     for q_len in (1, 63, 64, 65, 500):
         r = O.prefill_select(q8, qs, wt, k8, ks, 900, q_len, 64, 4, 300)
         assert r["sel"].size == min(300, r["cand"].size) and np.all(r["sel"] < q_len)
         assert r["blocks"].size == min(4, -(-q_len // 64)) and np.all(r["blocks"] * 64 < q_len)
-        # the partly visible last block is scored with the mean over the whole cache block
-        full = O.pooled_reps(O.dequantize(k8[:900], ks[:900]), 64)
-        assert np.array_equal(r["reps"], full[:-(-q_len // 64)])
+        # blocks wholly inside the prefix keep the cache's pooled representative; a partly
+        # visible last block is the mean of its visible rows (worked: q_len = 1 is row 0)
+        nf = q_len // 64
+        assert np.array_equal(r["reps"][:nf], full[:nf])
+        if q_len % 64:
+            assert np.allclose(r["reps"][nf], keys[nf * 64:q_len].mean(axis=0), rtol=0,
+                               atol=1e-15)
+    assert np.array_equal(O.prefill_select(q8, qs, wt, k8, ks, 900, 1, 64, 4, 300)["reps"],
+                          keys[:1])
 
 
 def test_prefill_keep_all_blocks_is_the_flat_indexer_on_the_prefix():

@@ -145,7 +145,16 @@ def _outward_inward(meta):
     return out
 
 
+def _recall_over_selected(selected, exact):
+    """divides by the number selected instead of the exact set's size"""
+    selected = np.asarray(selected)
+    if selected.size == 0:
+        return 1.0
+    return float(np.intersect1d(selected, np.asarray(exact)).size) / float(selected.size)
+
+
 MUTANTS = [
+    ("recall", _recall_over_selected),
     ("bf16_round", _bf16_round_fine),
     ("bf16_round", _bf16_round_toward_zero),
     ("bf16_outward", _outward_inward),
@@ -199,30 +208,46 @@ def _top_largest_high_ties(s, ids, k):
     return np.sort(ids[np.lexsort((-ids, -s))[:k]])
 
 
-def _prefill_reps_of_prefix(q8, q_scale, w, k8, k_scale, cache_len, q_len, block, keep_blocks,
-                            top_k):
-    """the other reading: pool the row's own prefix instead of the shared cache"""
-    return OH.select(q8, q_scale, w, k8, k_scale, q_len, block, keep_blocks, top_k)
-
-
-def _prefill_no_causal_mask(q8, q_scale, w, k8, k_scale, cache_len, q_len, block, keep_blocks,
-                            top_k):
-    """the token stage scans the kept blocks up to the cache end"""
+def _prefill_whole_block_mean(q8, q_scale, w, k8, k_scale, cache_len, q_len, block,
+                              keep_blocks, top_k):
+    """the non-causal reading: the row's partly visible last block is scored with the mean
+    of the whole cache block, keys after the row's position included"""
     q = OH.dequantize(q8, q_scale)
     keys = OH.dequantize(np.asarray(k8)[:cache_len], np.asarray(k_scale)[:cache_len])
     reps = OH.pooled_reps(keys, block)[:(q_len + block - 1) // block]
     S = OH.indexer_scores(q, w, reps)
     blocks = OH.top_largest(S, np.arange(reps.shape[0]), keep_blocks)
     cand = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
-    cand = cand[cand < cache_len]
+    cand = cand[cand < q_len]
     s = OH.indexer_scores(q, w, keys[cand])
     return dict(reps=reps, block_scores=S, blocks=blocks, cand=cand, token_scores=s,
                 sel=OH.top_largest(s, cand, top_k))
 
 
+def _prefill_no_causal_mask(q8, q_scale, w, k8, k_scale, cache_len, q_len, block, keep_blocks,
+                            top_k):
+    """the token stage scans the kept blocks up to the cache end"""
+    r = OH.__dict__["_prefill_orig"](q8, q_scale, w, k8, k_scale, cache_len, q_len, block,
+                                     keep_blocks, top_k)
+    q = OH.dequantize(q8, q_scale)
+    keys = OH.dequantize(np.asarray(k8)[:cache_len], np.asarray(k_scale)[:cache_len])
+    cand = (r["blocks"][:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    cand = cand[cand < cache_len]
+    s = OH.indexer_scores(q, w, keys[cand])
+    return dict(r, cand=cand, token_scores=s, sel=OH.top_largest(s, cand, top_k))
+
+
+def _prefill_prefix_of_cache_rows(q8, q_scale, w, k8, k_scale, cache_len, q_len, block,
+                                  keep_blocks, top_k):
+    """an off-by-one on the row's prefix: it sees tokens t <= q_len (one key too many)"""
+    return OH.__dict__["_prefill_orig"](q8, q_scale, w, k8, k_scale, cache_len,
+                                        min(q_len + 1, cache_len), block, keep_blocks, top_k)
+
+
 HISA_MUTANTS = [
-    ("prefill_select", _prefill_reps_of_prefix),
+    ("prefill_select", _prefill_whole_block_mean),
     ("prefill_select", _prefill_no_causal_mask),
+    ("prefill_select", _prefill_prefix_of_cache_rows),
     ("e4m3fn_decode", _decode_no_subnormal),
     ("e4m3fn_decode", _decode_bias8),
     ("pooled_reps", _reps_sum),
@@ -235,4 +260,5 @@ HISA_MUTANTS = [
                          ids=[f"{a}:{m.__name__}" for a, m in HISA_MUTANTS])
 def test_hisa_pins_catch_mutant(attr, mutant):
     OH._dec_orig = OH.e4m3fn_decode
+    OH._prefill_orig = OH.prefill_select
     assert _caught(PH, OH, attr, mutant) is not None, f"no pin catches mutant {mutant.__name__}"
