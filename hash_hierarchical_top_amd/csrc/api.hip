@@ -240,6 +240,7 @@ bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t t
   w.kept_blocks = take(B * keep_blocks * sizeof(int32_t));
   w.kept_count = take(B * sizeof(int32_t));
   w.token_scores = take(B * (size_t)keep_blocks * s.block * sizeof(float));
+  w.tail_reps = take(B * kD * sizeof(float));
   w.total = off;
   *ws = w;
   return true;
@@ -716,8 +717,9 @@ static hhr_status hisa_select_impl(const hhr_hisa_shape* shape, const uint8_t* q
   int32_t* kc = reinterpret_cast<int32_t*>(base + ws.kept_count);
   float* ts = reinterpret_cast<float*>(base + ws.token_scores);
   hipStream_t st = as_stream(stream);
+  float* tail = shared ? reinterpret_cast<float*>(base + ws.tail_reps) : nullptr;
   HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status, st,
-                                           shared),
+                                           k8, k_scale, tail),
              "hisa_block_scores launch");
   HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, bs, seq_len, keep_blocks, kept, kc, status, st),
              "hisa_top_blocks launch");

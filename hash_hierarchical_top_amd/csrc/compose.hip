@@ -206,15 +206,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   const int tid = threadIdx.x;
   const int NpCap = Lcap / kPS;
   const int pb = blockIdx.x * ppw + (tid >> 6) * kScorePagesPerWave;
-  // the metadata loads go out before the sequence length arrives: a wave
-  // inside the capacity loads its pages (clamped to the (b, g)'s last page
-  // slot); pages past the end are computed and never stored
+  // a wave loads its pages' metadata only once the sequence length says they
+  // exist (clamped to the last one), so a short sequence in a long cache reads
+  // only its own pages
   const bool wave_in = (tid >> 6) * kScorePagesPerWave < ppw && pb < NpCap;  // wave-uniform
-  PageLoads<1> pl;
-  if (wave_in) score_load<MBF, 1>(bg, NpCap, NpCap, pb, meta, pl);
   const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
   const int Np = (L + kPS - 1) / kPS;
   const bool wave_has = wave_in && pb < Np;          // wave-uniform
+  PageLoads<1> pl;
+  if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   const bool wg_has = (int)blockIdx.x * ppw < Np;  // block-uniform
   auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
   // the workgroup holding the last page, when a key was appended (block-uniform)

@@ -154,7 +154,8 @@ constexpr size_t kCtrlTicketsOffset = 64;
 
 // ---- HISA ----
 struct HisaWorkspace {
-  size_t ctrl = 0, block_scores = 0, kept_blocks = 0, kept_count = 0, token_scores = 0, total = 0;
+  size_t ctrl = 0, block_scores = 0, kept_blocks = 0, kept_count = 0, token_scores = 0,
+         tail_reps = 0, total = 0;
 };
 bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t top_k,
                          HisaWorkspace* ws);
@@ -165,7 +166,11 @@ hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const fl
 hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const float* q_scale, const float* w, const float* reps,
                                     const int32_t* seq_len, float* block_scores,
-                                    uint32_t* status, hipStream_t stream, bool shared = false);
+                                    uint32_t* status, hipStream_t stream,
+                                    const uint8_t* k8 = nullptr, const float* k_scale = nullptr,
+                                    float* tail = nullptr);
+// (With tail: query rows against one shared cache; each row's partly visible
+// last block is first pooled over its visible rows into tail [B][128].)
 hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_scores,
                                   const int32_t* seq_len, int32_t keep_blocks, int32_t* kept,
                                   int32_t* kept_count, uint32_t* status, hipStream_t stream);

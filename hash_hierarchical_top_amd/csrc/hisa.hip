@@ -43,6 +43,17 @@ __device__ __forceinline__ int checked_len(const int32_t* seq_len, int b, int Lc
   return L;
 }
 
+// Mean of dimension d over index-key rows [r0, r1) (r1 > r0) of one cache:
+// sum_t k_scale[t] * e4m3(k8[t][d]) accumulated in row order, then divided by
+// the row count.  Both the block pooling and a prefill row's partly visible
+// block use it, so equal rows give bit-identical means.
+__device__ __forceinline__ float pool_mean(const uint8_t* __restrict__ kb,
+                                           const float* __restrict__ sb, int r0, int r1, int d) {
+  float acc = 0.f;
+  for (int t = r0; t < r1; ++t) acc = fmaf(sb[t], e4m3fn_to_f32(kb[(size_t)t * kD + d]), acc);
+  return acc / (float)(r1 - r0);
+}
+
 // H1: one workgroup (128 threads = dims) per touched block.
 __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8,
                                                   const float* __restrict__ k_scale,
@@ -65,11 +76,26 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
   const int r0 = blk * block;
   const int r1 = min(r0 + block, e);
   const int d = threadIdx.x;
-  const uint8_t* kb = k8 + (size_t)b * Lcap * kD;
-  const float* sb = k_scale + (size_t)b * Lcap;
-  float acc = 0.f;
-  for (int t = r0; t < r1; ++t) acc = fmaf(sb[t], e4m3fn_to_f32(kb[(size_t)t * kD + d]), acc);
-  reps[((size_t)b * (Lcap / block) + blk) * kD + d] = acc / (float)(r1 - r0);
+  reps[((size_t)b * (Lcap / block) + blk) * kD + d] =
+      pool_mean(k8 + (size_t)b * Lcap * kD, k_scale + (size_t)b * Lcap, r0, r1, d);
+}
+
+// Prefill rows against one shared cache: row r sees tokens t < q_len[r], so
+// when q_len[r] is not a multiple of the block, its last block is only partly
+// visible and is represented by the mean of its visible rows
+// [block * floor(q_len / block), q_len) alone, never by the cache's pooled
+// block (which holds later keys).  One workgroup (128 threads = dims) per row
+// writes that mean to tail[r]; rows ending on a block edge write nothing.
+__global__ __launch_bounds__(kD) void k_hisa_pool_tail(const uint8_t* __restrict__ k8,
+                                                       const float* __restrict__ k_scale,
+                                                       const int32_t* __restrict__ q_len,
+                                                       float* __restrict__ tail, int Lcap,
+                                                       int block) {
+  const int r = blockIdx.x;
+  const int L = q_len[r];
+  if (L <= 0 || L > Lcap || L % block == 0) return;  // bad lengths: the scorer flags them
+  const int r0 = L / block * block;
+  tail[(size_t)r * kD + threadIdx.x] = pool_mean(k8, k_scale, r0, L, threadIdx.x);
 }
 
 // H2 on MFMA.  A wave takes groups of 16 blocks of one query:
@@ -95,8 +121,9 @@ __device__ __forceinline__ float add_swap16(float x) {
 __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
-    const int32_t* __restrict__ seq_len, float* __restrict__ block_scores,
-    uint32_t* __restrict__ status, int Hi, int Lcap, int block, int shared, int gpw) {
+    const int32_t* __restrict__ seq_len, const float* __restrict__ tail,
+    float* __restrict__ block_scores, uint32_t* __restrict__ status, int Hi, int Lcap, int block,
+    int shared, int gpw) {
   // the query in bf16, converted once per workgroup (rows padded against bank
   // conflicts; heads >= Hi are zero)
   __shared__ __attribute__((aligned(16))) uint16_t sq[kMaxIndexHeads][kD + 8];
@@ -132,21 +159,28 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
       wh[mt][j] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
       sh[mt][j] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
     }
-  // B rows: the representative of block blk0 + lrow, dims 32 ks + 8 lgrp + [0, 8)
+  // B rows: the representative of block blk0 + lrow, dims 32 ks + 8 lgrp + [0, 8).
+  // Shared cache (prefill rows): a row's partly visible last block is its own
+  // tail mean (k_hisa_pool_tail), not the cache's pooled block.
   const float* repb = reps + (size_t)(shared ? 0 : b) * NbCap * kD;
   floatx4 x0[4], x1[4];
-  auto load_reps = [&](int row) {
-    const float* rb = repb + (size_t)row * kD;
+  auto load_rep_row = [&](const float* rb) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       x0[ks] = *(const floatx4*)(rb + 32 * ks + 8 * lgrp);
       x1[ks] = *(const floatx4*)(rb + 32 * ks + 8 * lgrp + 4);
     }
   };
-  load_reps(min(wg_blk0 + wv * 16 + lrow, NbCap - 1));
+  load_rep_row(repb + (size_t)min(wg_blk0 + wv * 16 + lrow, NbCap - 1) * kD);
   const int L = checked_len(seq_len, b, Lcap, blockIdx.x == 0 ? status : nullptr);
   const int Nb = (L + block - 1) / block;
+  // the block (of this launch's row b) whose representative is the row's tail mean, or -1
+  const int tail_blk = shared && L % block != 0 ? Nb - 1 : -1;
+  auto load_reps = [&](int row) {
+    load_rep_row(row == tail_blk ? tail + (size_t)b * kD : repb + (size_t)row * kD);
+  };
   if (wg_blk0 >= Nb) return;  // block-uniform, before the barrier
+  if (wg_blk0 + wv * 16 + lrow == tail_blk) load_reps(tail_blk);
 #pragma unroll
   for (int k = 0; k < kQWords; ++k) {
     const int i = tid + k * 64 * kBsWaves;
@@ -397,15 +431,24 @@ hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const fl
 hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const float* q_scale, const float* w, const float* reps,
                                     const int32_t* seq_len, float* block_scores,
-                                    uint32_t* status, hipStream_t stream, bool shared) {
+                                    uint32_t* status, hipStream_t stream, const uint8_t* k8,
+                                    const float* k_scale, float* tail) {
+  const bool shared = tail != nullptr;
+  if (shared) {
+    hipLaunchKernelGGL(k_hisa_pool_tail, dim3(s.batch), dim3(kD), 0, stream, k8, k_scale,
+                       seq_len, tail, s.max_ctx, s.block);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int NbCap = s.max_ctx / s.block;
   // many queries: each workgroup covers 4 groups of 16 blocks per wave, so the
   // query conversion is shared; few: one group per wave for parallelism
   const int gpw = s.batch >= 64 ? 4 : 1;
   const int per_wg = 16 * kBsWaves * gpw;
   hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + per_wg - 1) / per_wg, s.batch),
-                     dim3(64 * kBsWaves), 0, stream, q8, q_scale, w, reps, seq_len, block_scores,
-                     status, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0, gpw);
+                     dim3(64 * kBsWaves), 0, stream, q8, q_scale, w, reps, seq_len, tail,
+                     block_scores, status, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0,
+                     gpw);
   return hipGetLastError();
 }
 

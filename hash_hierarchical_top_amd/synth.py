@@ -240,14 +240,17 @@ HISA_PREFILL_WORKLOADS: Dict[str, Tuple[str, int]] = {
 
 
 def make_hisa_prefill_rows(name: str, ctx: int = 0) -> Dict[str, np.ndarray]:
-    """q8 [M][Hi][d], q_scale [M][Hi], w [M][Hi] and q_len [M] (positions + 1 spread over
-    [1, ctx], ctx defaulting to the workload's)."""
+    """q8 [M][Hi][d], q_scale [M][Hi], w [M][Hi] and q_len [M]: the rows' positions + 1,
+    drawn uniformly over [1, ctx] (seeded, ascending; the last row is the prompt's last
+    token), so most rows end inside a block; ctx defaults to the workload's."""
     base, rows = HISA_PREFILL_WORKLOADS[name]
     w = HISA_WORKLOADS[base]
     ctx = ctx or w.ctx
     parts = [make_hisa_inputs(w.n_index_heads, 1, 16, 0, w.seed + 1000 + r, w.head_dim,
                               block=16, make_kv=False) for r in range(rows)]
-    q_len = ((np.arange(rows, dtype=np.int64) + 1) * ctx // rows).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 999))
+    q_len = np.sort(rng.integers(1, ctx + 1, rows)).astype(np.int32)
+    q_len[-1] = ctx
     return dict(q8=np.stack([x["q8"] for x in parts]),
                 q_scale=np.stack([x["q_scale"] for x in parts]),
                 w=np.stack([x["w"] for x in parts]), q_len=q_len)

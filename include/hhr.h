@@ -89,7 +89,15 @@ typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
  * Supported: head_dim == 128, code_bits 64, 128 or 256 (Table 4 of [HHR]
  * uses 128; appendix Figure 10 of [HHR] varies the number of hash bits),
  * page_size == 16, max_ctx a multiple of 16 in [16, 262144],
- * n_q_heads a multiple of n_kv_heads with G = n_q_heads / n_kv_heads <= 16. */
+ * n_q_heads a multiple of n_kv_heads with G = n_q_heads / n_kv_heads <= 16,
+ * batch * n_kv_heads <= 65535.
+ * Selection limits (the entry points taking keep and top_k parameters return
+ * HHR_ERR_UNSUPPORTED beyond them, and hhr_workspace_size returns 0):
+ *   - candidates per (b, g): p_max * 16 <= 32768, where p_max =
+ *     hhr_keep_count(max_ctx / 16, keep_num, keep_den, keep_pages_abs) is the
+ *     kept-page count of a full cache (so max_ctx 262144 allows keeping at most
+ *     1/8 of the pages, max_ctx 32768 all of them);
+ *   - 1 <= top_k <= 32768. */
 typedef struct {
   int32_t batch;
   int32_t n_q_heads;
@@ -250,7 +258,11 @@ hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------- S2..S6 and S2..S7 */
-/* hhr_select: S2..S6 in one stream-ordered call; intermediates live in the
+/* hhr_select: S2..S6 in one stream-ordered call, the coarse-to-fine
+ * retrieval of [HHR abstract] (GKR page bounds prune the pages, then LHP
+ * codes rank the keys of the surviving pages by Hamming distance; [HHR]
+ * Figure 1 orders the stages coarse then fine; [HATA abstract]: the codes
+ * need only order q.k, which a top-k needs).  Intermediates live in the
  * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk.  When the
  * coarse stage fits one launch (at most 2 x 256 scoring workgroups of 256
  * pages, 128-bit codes) the fine stage runs in it too: every workgroup also
@@ -264,9 +276,13 @@ hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq
                       int32_t* sel_count, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* hhr_decode: one decode step, S2..S7: select, then attend over the selected
- * keys with softmax scale `scale` (1/sqrt(128) for the usual scaling).
- * sel_idx / sel_count receive the selection; out receives o. */
+/* hhr_decode: one decode step, S2..S7: select as hhr_select, then attend
+ * over only the selected keys ([HHR abstract]: hash-based sparse attention,
+ * with the exact q.k logits; the codes only select) with softmax scale
+ * `scale` (1/sqrt(128) for the usual scaling).  sel_idx / sel_count receive
+ * the selection; out receives o.  Arguments and limits as for hhr_select and
+ * hhr_sparse_decode; the workspace is hhr_workspace_size(shape, keep_num,
+ * keep_den, keep_pages_abs, top_k) bytes. */
 hhr_status hhr_decode(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
                       const void* page_meta, const void* k_cache, const void* v_cache,
@@ -299,7 +315,9 @@ hhr_status hhr_decode_append(const hhr_shape* shape, const float* q, const int32
  * head_dim 128 scored against one fp8 index key per past token; blocks of
  * `block` tokens are pooled for the coarse stage.                  [HISA]
  * Supported: head_dim == 128, n_index_heads in [1, 64], block a multiple of
- * 16 in [16, 1024], max_ctx a multiple of block, max_ctx / block <= 16384. */
+ * 16 in [16, 1024], max_ctx a multiple of block, max_ctx / block <= 16384,
+ * max_ctx <= 2^24, batch <= 65535.  Selection limits (HHR_ERR_UNSUPPORTED
+ * beyond them): keep_blocks * block <= 16384 candidates, 1 <= top_k <= 16384. */
 typedef struct {
   int32_t batch;
   int32_t n_index_heads;
@@ -350,8 +368,13 @@ hhr_status hhr_hisa_token_topk(const hhr_hisa_shape* shape, const uint8_t* q8,
 
 size_t hhr_hisa_workspace_size(const hhr_hisa_shape* shape, int32_t keep_blocks, int32_t top_k);
 
-/* H2..H5 in one stream-ordered call.  The selected positions then feed
- * hhr_sparse_decode with an hhr_shape of n_kv_heads = 1. */
+/* H2..H5 in one stream-ordered call: the HISA selection of [HISA abstract]
+ * (a block-level coarse filter over pooled representatives, then the
+ * original indexer only on the tokens of the kept blocks, keeping an exact
+ * token-level top-k among them).  seq_len [B] int32 in [0, max_ctx]; reps as
+ * hhr_hisa_pool_keys writes them over the sequence's rows; outputs as
+ * hhr_hisa_token_topk.  The selected positions then feed hhr_sparse_decode
+ * with an hhr_shape of n_kv_heads = 1. */
 hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const float* q_scale,
                            const float* w, const uint8_t* k8, const float* k_scale,
                            const float* reps, const int32_t* seq_len, int32_t keep_blocks,
@@ -360,11 +383,15 @@ hhr_status hhr_hisa_select(const hhr_hisa_shape* shape, const uint8_t* q8, const
 
 /* Prefill indexer: H2..H5 for a chunk of query rows against ONE shared index-key
  * cache, each row over its own causal prefix (the O(L^2) per-layer case the
- * HISA abstract names).  Row r sees tokens t < q_len[r] (its position + 1): the
- * coarse filter scores blocks blk < ceil(q_len[r] / block) with the shared
- * pooled representatives (pooled once over the cache by hhr_hisa_pool_keys, so
- * a row's last, partly visible block is scored with the whole block's mean),
- * the token stage scores only tokens t < q_len[r].       [HISA abstract]
+ * HISA abstract names).  Row r sees tokens t < q_len[r] (its position + 1), and
+ * nothing after it, in both stages: the coarse filter scores the blocks
+ * blk < ceil(q_len[r] / block), a block wholly inside the prefix with the shared
+ * pooled representative (pooled once over the cache by hhr_hisa_pool_keys) and
+ * the row's partly visible last block with the mean of its visible rows only
+ * (computed by the call, the same arithmetic as hhr_hisa_pool_keys); the token
+ * stage scores only tokens t < q_len[r].  So row r selects exactly what
+ * hhr_hisa_select selects for a sequence of q_len[r] tokens whose
+ * representatives were pooled over those tokens.             [HISA abstract]
  *   shape.batch = M query rows; max_ctx = the cache capacity
  *   q8 [M][Hi][d] uint8, q_scale [M][Hi] f32 (> 0), w [M][Hi] f32 (>= 0)
  *   k8 [Lcap][d] uint8, k_scale [Lcap] f32, reps [Lcap/block][d] f32 (shared)

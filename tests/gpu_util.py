@@ -23,6 +23,17 @@ from oracle import hhr as O
 CODE_EXCUSE = 1e-4
 PAGE_EXCUSE = 1e-4
 
+# Excused mismatches per test, written to a JSON file at the end of the session
+# (tests/conftest.py): {test name: {counter: total}}.
+EXCUSED: dict = {}
+
+
+def record_excused(name: str, **counts) -> None:
+    """Adds counts of excused mismatches (code bits, pages, blocks, tokens, ...) under name."""
+    rec = EXCUSED.setdefault(name, {})
+    for k, v in counts.items():
+        rec[k] = rec.get(k, 0) + int(v)
+
 
 def dev():
     return torch.device("cuda", 0)
@@ -211,3 +222,57 @@ def check_kept_pages(oracle_scores: np.ndarray, P: int, got: np.ndarray) -> int:
     far = diff[np.abs(oracle_scores[diff] - sP) > band]
     assert far.size == 0, f"kept pages differ outside the excuse band: {far[:8]}"
     return int(diff.size)
+
+
+def _threshold(H: np.ndarray, k: int) -> int:
+    """The k-th smallest value of H (the cut of a top-k by smallest H), or a value above
+    every H when there are at most k of them."""
+    if H.size <= k:
+        return 1 << 30
+    return int(np.sort(H)[k - 1])
+
+
+def explain_selection(res: dict, sel_gpu, kept_gpu, codes_gpu, qcodes_gpu, L: int,
+                      top_k: int) -> dict:
+    """Every difference between the GPU selection and the oracle's selection from raw
+    inputs (res = oracle.hhr.select(...)) must be explained by an excused item: a kept
+    page inside the page band; a key whose code differs from the oracle's (bits inside the
+    code band, checked by check_code_bits); a query code that differs; or the displacement
+    of the top-k cut that such an item causes (a position whose distance lies between the
+    GPU's and the oracle's cut).  With no excused item the selections must be identical.
+    Returns the counts: excused pages, keys with excused code bits among the candidates,
+    query code words, and the differing selected positions by explanation."""
+    P = res["n_keep"]
+    n_pages = check_kept_pages(res["scores"], P, kept_gpu)
+    ex_pages = set(np.setxor1d(res["kept"], kept_gpu).tolist())
+    codes_or = res["enc"]["codes"]
+    key_mis = np.flatnonzero(np.any(np.asarray(codes_gpu)[:L] != codes_or[:L], axis=-1))
+    cand_gpu = O.candidates(np.asarray(kept_gpu, np.int64), L, 16)
+    cand_or = res["cand"]
+    ex_keys = set(key_mis.tolist()) & (set(cand_gpu.tolist()) | set(cand_or.tolist()))
+    q_mis = int(np.sum(np.asarray(qcodes_gpu) != res["qcodes"]))
+    H_gpu = O.hamming(qcodes_gpu, np.asarray(codes_gpu)[cand_gpu])
+    hg = dict(zip(cand_gpu.tolist(), H_gpu.tolist()))
+    ho = dict(zip(cand_or.tolist(), res["H"].tolist()))
+    T_lo, T_hi = sorted((_threshold(H_gpu, top_k), _threshold(res["H"], top_k)))
+    any_excused = bool(ex_pages) or bool(ex_keys) or q_mis > 0
+    diff = np.setxor1d(np.asarray(sel_gpu, np.int64), res["sel"])
+    counts = dict(pages=n_pages, key_codes=len(ex_keys), query_code_words=q_mis,
+                  sel_diff=int(diff.size), by_page=0, by_key_code=0, by_query_code=0,
+                  by_cut=0)
+    if not any_excused:
+        assert diff.size == 0, f"selection differs with nothing excused: {diff[:8]}"
+        return counts
+    for t in diff.tolist():
+        if t // 16 in ex_pages:
+            counts["by_page"] += 1
+        elif t in ex_keys:
+            counts["by_key_code"] += 1
+        elif q_mis:
+            counts["by_query_code"] += 1
+        elif any(T_lo <= h.get(t, -1) <= T_hi for h in (hg, ho)):
+            counts["by_cut"] += 1
+        else:
+            raise AssertionError(f"unexplained selection difference at position {t}: H gpu "
+                                 f"{hg.get(t)}, oracle {ho.get(t)}, cuts {T_lo}..{T_hi}")
+    return counts

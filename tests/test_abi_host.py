@@ -220,3 +220,43 @@ def test_hisa_errors(H):
                    FAKE, FAKE, FAKE, workspace_bytes=1 << 30, stream=0) == H.HHR_ERR_UNSUPPORTED
     assert _status(H.hhr_hisa_pool_keys, good, FAKE, FAKE, FAKE, FAKE, -1, FAKE,
                    stream=0) == H.HHR_ERR_INVALID_ARG
+
+
+def test_documented_selection_limits(H):
+    """The header's selection limits: p_max * 16 <= 32768 candidates per (b, g) and
+    top_k <= 32768 (HISA: keep_blocks * block and top_k <= 16384).  At the limit the
+    workspace size is positive; one step past it every entry point returns
+    HHR_ERR_UNSUPPORTED and hhr_workspace_size returns 0."""
+    at = H.make_shape(1, 32, 8, 32768, "bf16")       # 2048 pages, all kept: 32768 candidates
+    past = H.make_shape(1, 32, 8, 32784, "bf16")     # 2049 pages: 32784 candidates
+    assert H.hhr_workspace_size(at, 1, 1, 0, 4096) > 0
+    assert H.hhr_workspace_size(at, 1, 1, 0, 32768) > 0
+    assert H.hhr_workspace_size(past, 1, 1, 0, 4096) == 0
+    assert H.hhr_workspace_size(past, 0, 1, 2049, 4096) == 0
+    assert H.hhr_workspace_size(past, 0, 1, 2048, 4096) > 0
+    assert H.hhr_workspace_size(at, 1, 1, 0, 32769) == 0
+    # 262144 keys: keeping 1/8 of the pages is the most that fits
+    assert H.hhr_workspace_size(H.make_shape(1, 32, 8, 262144, "bf16"), 1, 8, 0, 4096) > 0
+    assert H.hhr_workspace_size(H.make_shape(1, 32, 8, 262144, "bf16"), 1, 4, 0, 4096) == 0
+    big = 1 << 34
+    sel = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for shape, keep, k in ((past, (1, 1, 0), 4096), (past, (0, 1, 2049), 4096),
+                           (at, (1, 1, 0), 32769)):
+        assert _status(H.hhr_select, shape, *sel, *keep, k, FAKE, FAKE, FAKE,
+                       workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED
+        assert _status(H.hhr_decode, shape, *sel, FAKE, FAKE, *keep, k, 0.088, FAKE, FAKE, FAKE,
+                       FAKE, workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED
+        if shape is past:  # hhr_select_pages takes no top_k: only the page limit applies
+            assert _status(H.hhr_select_pages, shape, FAKE, FAKE, FAKE, FAKE, FAKE, *keep, FAKE,
+                           FAKE, None, FAKE, workspace_bytes=big, stream=0) == \
+                H.HHR_ERR_UNSUPPORTED
+    assert _status(H.hhr_sparse_decode, at, FAKE, FAKE, FAKE, FAKE, FAKE, 32769, 0.088, FAKE,
+                   FAKE, workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED
+    assert _status(H.hhr_hamming_topk, past, FAKE, FAKE, FAKE, FAKE, FAKE, 2049, 64, FAKE, FAKE,
+                   None, FAKE, workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED
+    hs = H.make_hisa_shape(1, 64, 128, 131072)
+    assert H.hhr_hisa_workspace_size(hs, 128, 2048) > 0       # 16384 candidates
+    assert H.hhr_hisa_workspace_size(hs, 129, 2048) == 0
+    assert H.hhr_hisa_workspace_size(hs, 64, 16385) == 0
+    assert _status(H.hhr_hisa_select, hs, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16385,
+                   FAKE, FAKE, FAKE, workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED

@@ -66,7 +66,8 @@ def test_codes_and_meta_sampled(full):
         Np = O.n_pages(L, 16)
         K = p.K_valid(b, g)
         rows = np.unique(np.concatenate([rng.choice(L, min(L, 2048), replace=False), [L - 1]]))
-        U.check_code_bits(K[rows], p.inp["W"][g], h["codes"][b, g, rows])
+        n = U.check_code_bits(K[rows], p.inp["W"][g], h["codes"][b, g, rows])
+        U.record_excused(f"full_{name}_sampled_key_codes", keys=rows.size, code_bits=n)
         pages = np.unique(np.concatenate([rng.choice(Np, min(Np, 64), replace=False),
                                           [0, Np - 1]]))
         meta = p.meta[b, g].cpu().numpy().astype(np.float64)
@@ -102,15 +103,26 @@ def test_page_bounds_and_top_pages_conditioned(full):
         assert h["kept"][b, g, :P].tolist() == O.top_pages(h["scores"][b, g, :Np], P).tolist()
 
 
-def test_top_pages_against_unconditioned_oracle(full):
+def test_end_to_end_against_unconditioned_oracle(full):
+    """The oracle's whole selection from raw inputs on sampled (b, g): kept pages within the
+    page band, and every selected position that differs explained by an excused page, an
+    excused code bit or the cut displacement it causes (every key encoded by the oracle, so
+    the codes of all candidates are compared); the counts are recorded."""
     name, w, p, h, pairs = full
+    total = {}
     for b, g in pairs[:2]:
         L = int(p.inp["seq_len"][b])
-        Np = O.n_pages(L, 16)
-        enc = O.encode_keys(p.K_valid(b, g), p.inp["R"][g], p.inp["W"][g], 16)
-        qe = O.encode_query(p.q_group(b, g), p.inp["R"][g], p.inp["W"][g])
-        s = O.page_scores(qe["qrot"], enc["meta"])
-        U.check_kept_pages(s, O.keep_count(Np, *p.keep), h["kept"][b, g, :h["kept_count"][b, g]])
+        res = O.select(p.q_group(b, g), p.K_valid(b, g), p.inp["R"][g], p.inp["W"][g], 16,
+                       *p.keep, p.top_k)
+        n = int(h["sel_count"][b, g])
+        assert n == len(res["sel"])
+        c = U.explain_selection(res, h["sel"][b, g, :n], h["kept"][b, g, :res["n_keep"]],
+                                h["codes"][b, g], h["q_codes"][b, g * p.G:(g + 1) * p.G], L,
+                                p.top_k)
+        for k, v in c.items():
+            total[k] = total.get(k, 0) + v
+    print(f"excused ({name}): {total}")
+    U.record_excused(f"full_{name}_e2e", **total)
 
 
 def test_hamming_topk_conditioned_exact(full):

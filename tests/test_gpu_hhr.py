@@ -71,6 +71,7 @@ def test_append_codes_and_meta(run):
                 err = np.abs(meta[b, g, pg] - enc["meta"][pg]).max()
                 assert err <= tol, (b, g, pg, err, tol)
     print(f"excused code bits: {excused}")
+    U.record_excused(f"hhr_codes_{case['name']}", code_bits=excused)
 
 
 def test_encode_queries(run):
@@ -160,25 +161,29 @@ def test_sparse_decode_conditioned(run):
 
 
 def test_end_to_end_against_unconditioned_oracle(run):
-    """Selection from raw inputs: kept pages may differ only inside the excuse band; where no
-    excused difference occurred anywhere upstream, selected positions are identical."""
+    """Selection from raw inputs: every position where the GPU's selection differs from the
+    oracle's must be explained by an excused page, an excused code bit or the cut
+    displacement one causes; the counts are recorded."""
     case, p = run
     sel = p.sel.cpu().numpy()
+    sc = p.sel_count.cpu().numpy()
     kept = p.kept.cpu().numpy()
     codes = U.u32(p.codes)
     q_codes = U.u32(p.q_codes)
+    total = {}
     for b in range(p.B):
         L = int(p.inp["seq_len"][b])
         for g in range(p.Hkv):
             K = p.K_valid(b, g)
             res = O.select(p.q_group(b, g), K, p.inp["R"][g], p.inp["W"][g], 16, *p.keep,
                            p.top_k)
-            P = res["n_keep"]
-            n_page_diff = U.check_kept_pages(res["scores"], P, kept[b, g, :P])
-            same_codes = (np.array_equal(codes[b, g, :L], res["enc"]["codes"]) and
-                          np.array_equal(q_codes[b, g * p.G:(g + 1) * p.G], res["qcodes"]))
-            if n_page_diff == 0 and same_codes:
-                assert sel[b, g, :len(res["sel"])].tolist() == res["sel"].tolist()
+            assert sc[b, g] == len(res["sel"])
+            c = U.explain_selection(res, sel[b, g, :sc[b, g]], kept[b, g, :res["n_keep"]],
+                                    codes[b, g], q_codes[b, g * p.G:(g + 1) * p.G], L, p.top_k)
+            for k, v in c.items():
+                total[k] = total.get(k, 0) + v
+    print(f"excused: {total}")
+    U.record_excused(f"hhr_e2e_{case['name']}", **total)
 
 
 def test_decode_composite_equals_stages(run, gpu_lib):
