@@ -7,7 +7,20 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hhr_internal.h"
+
+// Scratch of hhr_decode_no_alloc: the decode workspace (control block,
+// distances, histograms, bounds, kept pages, attention partials) in a
+// file-scope device array, for callers that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: host code
+// uses only the per-device address from hipGetSymbolAddress (no_alloc_scratch).
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+}
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -263,7 +276,7 @@ const char* hhr_status_string(int32_t status) {
 
 const char* hhr_last_error(void) { return g_err; }
 
-int32_t hhr_abi_version(void) { return 4; }
+int32_t hhr_abi_version(void) { return 5; }
 
 int32_t hhr_keep_count(int32_t n_pages, int32_t keep_num, int32_t keep_den,
                        int32_t keep_pages_abs) {
@@ -481,7 +494,8 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
                               int32_t* sel_count, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, bool finish, hhr::Workspace* layout,
                               hhr::CompositeBuffers* bufs,
-                              const hhr::AppendArgs* app = nullptr) {
+                              const hhr::AppendArgs* app = nullptr,
+                              uint32_t* status_word = nullptr) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_keep(keep_num, keep_den, keep_abs));
   HHR_TRY(check_top_k(top_k));
@@ -498,6 +512,7 @@ static hhr_status select_impl(const hhr_shape* shape, const float* q, const int3
   hhr::CompositeBuffers buf;
   HHR_TRY(composite_buffers(*shape, keep_num, keep_den, keep_abs, top_k, workspace,
                             workspace_bytes, &ws, &buf));
+  if (status_word) buf.status = status_word;  // device errors go there instead
   HHR_LAUNCH(hhr::launch_select_composite(*shape, q, seq_len, R, W, codes, page_meta, keep_num,
                                           keep_den, keep_abs, ws.p_max, top_k, sel_idx,
                                           sel_count, buf, finish, stream, app),
@@ -527,7 +542,7 @@ static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int3
                               int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
                               int32_t top_k, float scale, int32_t* sel_idx, int32_t* sel_count,
                               float* out, void* workspace, size_t workspace_bytes, void* stream,
-                              bool append) {
+                              bool append, uint32_t* status_word = nullptr) {
   HHR_TRY(check_shape(shape));
   HHR_TRY(check_ptr(k_cache, "k_cache"));
   HHR_TRY(check_ptr(v_cache, "v_cache"));
@@ -552,7 +567,8 @@ static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int3
                         hhr::kPickInAttentionMaxWgs;
   HHR_TRY(select_impl(shape, q, seq_len, R, W, codes, page_meta, keep_num, keep_den,
                       keep_pages_abs, top_k, sel_idx, sel_count, workspace, workspace_bytes,
-                      as_stream(stream), !pick, &ws, &buf, append ? &app : nullptr));
+                      as_stream(stream), !pick, &ws, &buf, append ? &app : nullptr,
+                      status_word));
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.attn_part);
   if (pick)
     HHR_LAUNCH(hhr::launch_attend_picked(*shape, q, k_cache, v_cache, seq_len, ws.p_max, top_k,
@@ -589,6 +605,81 @@ hhr_status hhr_decode_append(const hhr_shape* shape, const float* q, const int32
                      workspace_bytes, stream, true);
 }
 
+
+}  // extern "C"
+
+// ------------------------------------------------------------- no-alloc decode
+namespace {
+
+// Clears n 32-bit words (the control block that must start each call at zero).
+// A kernel rather than hipMemsetAsync, so that a captured graph replays it
+// exactly.
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* __restrict__ p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+hhr_status no_alloc_scratch(void** ptr) {
+  int dev = 0;
+  HHR_LAUNCH(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HHR_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    HHR_LAUNCH(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(HHR_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return HHR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hhr_no_alloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+hhr_status hhr_decode_no_alloc(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                               const float* R, const float* W, const uint32_t* codes,
+                               const void* page_meta, const void* k_cache, const void* v_cache,
+                               int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                               int32_t top_k, float scale, int32_t* sel_idx, int32_t* sel_count,
+                               float* out, uint32_t* status_word, void* stream) {
+  // every host check of hhr_decode, before anything is enqueued
+  HHR_TRY(check_shape(shape));
+  HHR_TRY(check_keep(keep_num, keep_den, keep_pages_abs));
+  HHR_TRY(check_top_k(top_k));
+  for (const void* p : {(const void*)q, (const void*)seq_len, (const void*)R, (const void*)W,
+                        (const void*)codes, page_meta, k_cache, v_cache, (const void*)sel_idx,
+                        (const void*)sel_count, (const void*)out})
+    HHR_TRY(check_ptr(p, "a pointer argument"));
+  HHR_TRY(check_opt_ptr(status_word, "status_word"));
+  if (!(scale > 0.0f) || scale != scale) return fail(HHR_ERR_INVALID_ARG, "scale must be > 0");
+  hhr::Workspace ws;
+  hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &ws);
+  HHR_TRY(check_p_max(ws.p_max));
+  if (ws.total > kNoAllocScratchBytes)
+    return fail(HHR_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of scratch; the library's static scratch holds %zu",
+                ws.total, kNoAllocScratchBytes);
+  void* base = nullptr;
+  HHR_TRY(no_alloc_scratch(&base));
+  // the control block (status word, counters, histograms) starts at zero
+  const uint32_t n_words = (uint32_t)(hhr::ctrl_bytes(*shape) / sizeof(uint32_t));
+  hipLaunchKernelGGL(k_zero_words, dim3((n_words + 1023) / 1024), dim3(256), 0,
+                     as_stream(stream), static_cast<uint32_t*>(base), n_words);
+  HHR_LAUNCH(hipGetLastError(), "zero scratch launch");
+  return decode_impl(shape, q, seq_len, R, W, codes, page_meta, k_cache, v_cache, keep_num,
+                     keep_den, keep_pages_abs, top_k, scale, sel_idx, sel_count, out, base,
+                     kNoAllocScratchBytes, stream, false, status_word);
+}
 
 // ------------------------------------------------------------------ HISA
 size_t hhr_hisa_workspace_size(const hhr_hisa_shape* shape, int32_t keep_blocks, int32_t top_k) {

@@ -22,7 +22,7 @@ HHR_ERR_WORKSPACE = -3
 HHR_ERR_HIP = -4
 HHR_F32 = 0
 HHR_BF16 = 1
-ABI_VERSION = 4  # the include/hhr.h declarations this binding mirrors
+ABI_VERSION = 5  # the include/hhr.h declarations this binding mirrors
 HHR_DEV_BAD_SEQ_LEN = 0x1
 HHR_DEV_BAD_INDEX = 0x2
 
@@ -76,6 +76,9 @@ _SIGS = {
     "hhr_decode_append": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                   c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_size,
                                   c_vp]),
+    "hhr_decode_no_alloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                    c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "hhr_no_alloc_scratch_bytes": (c_size, []),
     "hhr_hisa_workspace_size": (c_size, [c_vp, c_i32, c_i32]),
     "hhr_hisa_pool_keys": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "hhr_hisa_block_scores": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -257,6 +260,19 @@ def hhr_decode_append(shape, q, seq_len, R, W, codes, page_meta, k_cache, v_cach
           _ptr(codes), _ptr(page_meta), _ptr(k_cache), _ptr(v_cache), keep_num, keep_den,
           keep_pages_abs, int(top_k), float(scale), _ptr(sel_idx), _ptr(sel_count), _ptr(out),
           _ptr(workspace), wb, _stream(stream))
+
+
+def hhr_decode_no_alloc(shape, q, seq_len, R, W, codes, page_meta, k_cache, v_cache, keep_num,
+                        keep_den, keep_pages_abs, top_k, scale, sel_idx, sel_count, out,
+                        status_word=None, stream=None) -> None:
+    _call("hhr_decode_no_alloc", ctypes.byref(shape), _ptr(q), _ptr(seq_len), _ptr(R), _ptr(W),
+          _ptr(codes), _ptr(page_meta), _ptr(k_cache), _ptr(v_cache), keep_num, keep_den,
+          keep_pages_abs, int(top_k), float(scale), _ptr(sel_idx), _ptr(sel_count), _ptr(out),
+          _ptr(status_word), _stream(stream))
+
+
+def hhr_no_alloc_scratch_bytes() -> int:
+    return int(load().hhr_no_alloc_scratch_bytes())
 
 
 # --------------------------------------------------------------------- HISA steps

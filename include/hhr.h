@@ -310,6 +310,33 @@ hhr_status hhr_decode_append(const hhr_shape* shape, const float* q, const int32
                              float scale, int32_t* sel_idx, int32_t* sel_count, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* hhr_decode_no_alloc: hhr_decode without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Its scratch is a static device
+ * array of the library, hhr_no_alloc_scratch_bytes() bytes (64 MiB) on every
+ * GPU it runs on, held until the process ends; the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  It clears the
+ * scratch's control block with a small kernel, then runs exactly the kernels
+ * of hhr_decode, so its outputs equal hhr_decode's bit for bit.
+ *   Arguments as for hhr_decode, without workspace / workspace_bytes;
+ *   status_word  device uint32 or NULL: device error bits (HHR_DEV_*) are
+ *                OR-ed into it (the caller clears it); with NULL they are
+ *                dropped.
+ * Returns HHR_ERR_UNSUPPORTED when the shape's workspace
+ * (hhr_workspace_size) exceeds the static scratch.  Every call on one GPU
+ * uses the same scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must not be issued.  The first call
+ * on each device looks up the scratch's address (hipGetSymbolAddress), so
+ * make it outside stream capture. */
+hhr_status hhr_decode_no_alloc(const hhr_shape* shape, const float* q, const int32_t* seq_len,
+                               const float* R, const float* W, const uint32_t* codes,
+                               const void* page_meta, const void* k_cache, const void* v_cache,
+                               int32_t keep_num, int32_t keep_den, int32_t keep_pages_abs,
+                               int32_t top_k, float scale, int32_t* sel_idx, int32_t* sel_count,
+                               float* out, uint32_t* status_word, void* stream);
+/* Bytes of the static scratch behind hhr_decode_no_alloc.  Pure host. */
+size_t hhr_no_alloc_scratch_bytes(void);
+
 /* ================================================================ HISA  */
 /* Shape of a HISA indexer: per query, n_index_heads fp8 index heads of
  * head_dim 128 scored against one fp8 index key per past token; blocks of

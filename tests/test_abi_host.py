@@ -260,3 +260,26 @@ def test_documented_selection_limits(H):
     assert H.hhr_hisa_workspace_size(hs, 64, 16385) == 0
     assert _status(H.hhr_hisa_select, hs, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 16385,
                    FAKE, FAKE, FAKE, workspace_bytes=big, stream=0) == H.HHR_ERR_UNSUPPORTED
+
+
+def test_no_alloc_decode_host_checks(H):
+    """hhr_decode_no_alloc: the static scratch holds 64 MiB; a shape whose workspace is larger
+    is rejected with HHR_ERR_UNSUPPORTED before anything reaches the GPU, as are bad
+    arguments (the ragged 16-sequence 64K workload, 63.8 MiB, fits)."""
+    assert H.hhr_no_alloc_scratch_bytes() == 64 << 20
+    fits = H.make_shape(16, 32, 8, 65536, "bf16")
+    assert 0 < H.hhr_workspace_size(fits, 1, 4, 0, 2048) <= 64 << 20
+    big = H.make_shape(32, 32, 8, 65536, "bf16")
+    assert H.hhr_workspace_size(big, 1, 4, 0, 2048) > 64 << 20
+    args = (FAKE,) * 8
+    assert _status(H.hhr_decode_no_alloc, big, *args, 1, 4, 0, 2048, 0.088, FAKE, FAKE, FAKE,
+                   None, stream=0) == H.HHR_ERR_UNSUPPORTED
+    assert "static scratch" in H.load().hhr_last_error().decode()
+    assert _status(H.hhr_decode_no_alloc, fits, *args, 1, 4, 0, 2048, 0.0, FAKE, FAKE, FAKE,
+                   None, stream=0) == H.HHR_ERR_INVALID_ARG
+    assert _status(H.hhr_decode_no_alloc, fits, *args, 1, 4, 0, 2048, 0.088, FAKE, None, FAKE,
+                   None, stream=0) == H.HHR_ERR_INVALID_ARG
+    assert _status(H.hhr_decode_no_alloc, fits, *args, 1, 4, 0, 2048, 0.088, FAKE, FAKE, FAKE,
+                   FAKE + 4, stream=0) == H.HHR_ERR_INVALID_ARG
+    assert _status(H.hhr_decode_no_alloc, fits, *args, 0, 4, 0, 2048, 0.088, FAKE, FAKE, FAKE,
+                   None, stream=0) == H.HHR_ERR_INVALID_ARG
