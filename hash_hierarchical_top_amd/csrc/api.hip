@@ -126,7 +126,7 @@ hhr_status check_p_max(int32_t p_max) {
 }
 
 size_t attn_part_bytes(const hhr_shape& s, int32_t n_split) {
-  return (size_t)s.batch * s.n_kv_heads * n_split * hhr::kMaxG * (hhr::kD + 2) * sizeof(float);
+  return (size_t)s.batch * s.n_kv_heads * n_split * hhr::kMaxG * hhr::kPartStride * sizeof(float);
 }
 
 int32_t n_split_for(int32_t top_k) { return (top_k + hhr::kAttnChunk - 1) / hhr::kAttnChunk; }
@@ -195,7 +195,7 @@ HamScratch ham_scratch(const hhr_shape& s, int32_t p_max) {
 
 AttnWorkspace attn_workspace(const hhr_shape& s, int32_t top_k) {
   AttnWorkspace a;
-  a.tickets = kAlign;
+  a.counters = kAlign;
   a.part = ctrl_bytes(s);
   a.total = a.part + align_up(attn_part_bytes(s, n_split_for(top_k)));
   return a;
@@ -231,7 +231,6 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
   w.attn_part = take(attn_part_bytes(s, w.n_split));
-  w.ham_all = take(BHkv * (size_t)s.max_ctx * sizeof(uint16_t));
   w.total = off;
   *ws = w;
   return true;
@@ -454,7 +453,6 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->dist = reinterpret_cast<uint16_t*>(base + ws->ham_dist);
   buf->chist = reinterpret_cast<int*>(base + ws->ham_hist);
   buf->cum = reinterpret_cast<uint16_t*>(base + ws->ham_cum);
-  buf->hall = reinterpret_cast<uint16_t*>(base + ws->ham_all);
   return HHR_OK;
 }
 
@@ -552,13 +550,11 @@ static hhr_status decode_impl(const hhr_shape* shape, const float* q, const int3
   hhr::AppendArgs app{k_cache, const_cast<uint32_t*>(codes), const_cast<void*>(page_meta)};
   hhr::Workspace ws;
   hhr::CompositeBuffers buf;
-  // Few attention workgroups: each picks its own keys (no selection launch).
-  // Many: the selection first (in the coarse launch when that is one launch,
-  // else one workgroup per (b, g)), then plain attention, which costs less
-  // than every workgroup repeating the pick.  Same results.  (With few
-  // attention workgroups the pick also beats the one-launch selection at
-  // 128K: its distance launch and pick cost less than the selection's
-  // single-CU tail plus a separate attention launch.)
+  // The coarse stage and the distances, then attention.  With few attention
+  // chunks each attention workgroup picks its own keys from the distances and
+  // their histogram (no selection launch); with many, one selection workgroup
+  // per (b, g) runs first, which costs less than every attention workgroup
+  // repeating the pick.  Same results.
   hhr::Workspace probe;
   hhr::make_workspace(*shape, keep_num, keep_den, keep_pages_abs, top_k, &probe);
   // The in-attention pick reads 128-bit-code histograms only.

@@ -10,6 +10,10 @@ constexpr int kPS = 16;    // page size
 constexpr int kWave = 64;  // CDNA wavefront width
 constexpr int kMaxG = 16;  // query heads per KV head
 
+// Split-K attention partial of one (b, g, chunk, query head): o~[128], m, l,
+// padded so that each partial starts on a 16-byte boundary.
+constexpr int kPartStride = kD + 4;
+
 // Fine top-k distance chunks: 64 kept pages (1024 candidates) per workgroup.
 constexpr int kHamChunkPages = 64;
 constexpr int ham_chunks(int pages) { return (pages + kHamChunkPages - 1) / kHamChunkPages; }

@@ -245,6 +245,26 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* lds, T* total) {
 // and read with agent-scope (sc1) accesses, which the L2 does not hold stale,
 // and a producer publishes with s_waitcnt(0) + a relaxed agent-scope atomic.
 // Mem<false> is the plain path for data that only crosses kernel boundaries.
+//
+// Why the relaxed hand-off (arrive_last) is ordered.  The HIP memory model
+// would express it as a release (producer) and an acquire (consumer) at agent
+// scope; on this part those compile to an L2 writeback (release) and an L2
+// invalidate (acquire) around the atomic, which only matter for data that may
+// sit in an L2 line: data written by plain stores (dirty in the producer's
+// XCD's L2) or read by plain loads (possibly stale in the consumer's).  Every
+// value handed over inside a launch here is written with agent-scope stores
+// and read with agent-scope loads (Mem<true>, ld_sc1_x4): such accesses are
+// performed at the memory side, never through a stale or dirty L2 line, so
+// there is nothing to write back or invalidate.  What remains is completion
+// order: each producer wave waits with s_waitcnt(0) until its agent-scope
+// stores are acknowledged (performed at the memory side), the workgroup meets
+// at a barrier (which the compiler does not move memory accesses across),
+// and only then does one thread add to the counter with an agent-scope
+// atomic, itself performed at the memory side after those stores.  The
+// workgroup that reads the final count therefore issues its agent-scope
+// loads after every producer's stores were performed.  Nobody waits for
+// anybody: the last arriver is the one that finds all the others done, so
+// there is no scheduling hazard either.
 template <bool COH>
 struct Mem {
   template <typename T>
@@ -270,6 +290,21 @@ __device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
 }
 // Wait until every memory access this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Publishes this workgroup's agent-scope stores and counts it in on *counter;
+// true in the workgroup that arrives last (n_wg arrivals), which also puts the
+// counter back to zero for the next call.  All threads call.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n_wg, int* s_last) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = add_agent_u32(counter, 1u);
+    *s_last = prev == n_wg - 1u;
+    if (*s_last) st_agent_u32(counter, 0u);
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
 
 }  // namespace hhr
 

@@ -21,8 +21,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // holds the device status word at offset 0.
 struct Workspace {
   size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, ham_cum = 0, q_rot = 0, q_codes = 0,
-         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, ham_all = 0,
-         total = 0;
+         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, total = 0;
   int32_t p_max = 0, n_split = 0;
 };
 
@@ -34,13 +33,15 @@ struct HamScratch {
 };
 HamScratch ham_scratch(const hhr_shape& s, int32_t p_max);
 constexpr int kCountersPerGroup = 8;  // control words per (b, g) after the first 256 bytes
+constexpr int kScoreCounter = 0;      // k_score_topp's arrivals
 // hhr_decode lets every attention workgroup pick its own keys while there are
 // at most this many of them (B * Hkv * top_k / 64), else it selects first.
 constexpr int kPickInAttentionMaxWgs = 1024;
 
-// Workspace of hhr_sparse_decode alone: control block, tickets, partials.
+// Workspace of hhr_sparse_decode alone: control block (its counters at the
+// offset every layout uses), partials.
 struct AttnWorkspace {
-  size_t tickets = 0, part = 0, total = 0;
+  size_t counters = 0, part = 0, total = 0;
 };
 AttnWorkspace attn_workspace(const hhr_shape& s, int32_t top_k);
 size_t ctrl_bytes(const hhr_shape& s);
@@ -82,7 +83,7 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
 // the last-arriving workgroup of each (b, g), then S5, then S6 (or, for
 // hhr_decode, S6 + S7 with every attention workgroup picking its own keys).
 // counters: kCountersPerGroup words per (b, g) (zero before and after every
-// call), the first of which counts k_score_topp's arrivals.  wave_range:
+// call): word kScoreCounter counts k_score_topp's arrivals.  wave_range:
 // {smallest, largest} bound of each 16-page wave, [B*Hkv][NpCap/16].
 struct CompositeBuffers {
   uint32_t* status;
@@ -96,15 +97,6 @@ struct CompositeBuffers {
   uint16_t* dist;
   int* chist;
   uint16_t* cum;  // per-block cumulative H histograms (hhr_decode's pick)
-  uint16_t* hall;  // H of every key [B*Hkv][Lcap] (the one-launch selection)
-};
-// The fine stage of the one-launch selection: codes to score, and where the
-// selection goes.
-struct FineArgs {
-  const uint32_t* codes;
-  int32_t top_k;
-  int32_t* sel_idx;
-  int32_t* sel_count;
 };
 // A key appended at row seq_len[b] - 1 of every sequence, to be encoded (its
 // code and its page's metadata) by the coarse stage before it bounds the page.
@@ -114,18 +106,16 @@ struct AppendArgs {
   void* meta;
 };
 
-// k_score_topp alone (S2..S4): kept pages, counts and query codes into buf;
-// with app, the appended keys are encoded first.
-// With fine, S5 + S6 run in the same launch and write the selection (only
-// when one_launch_select(s)).
+// The coarse stage (S2..S4): kept pages, counts and query codes into buf;
+// with app, the appended keys are encoded first.  One launch (k_score_topp)
+// when one_launch_select(s), else staged launches.
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
                              const CompositeBuffers& buf, hipStream_t stream,
-                             const AppendArgs* app = nullptr, const FineArgs* fine = nullptr);
+                             const AppendArgs* app = nullptr);
 // True when the coarse stage runs as one launch (k_score_topp): the scoring
 // grid is at most two rounds of one workgroup per CU and codes are 128-bit.
-// hhr_select and hhr_decode then run S2..S6 in that launch.
 bool one_launch_select(const hhr_shape& s);
 // S1 for the single row seq_len[b] - 1 of every sequence with seq_len[b] >= 1.
 hipError_t launch_append_last_row(const hhr_shape& s, const void* k_cache,

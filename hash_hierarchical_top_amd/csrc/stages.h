@@ -321,12 +321,9 @@ __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den
 //     for the next call), finds the smallest H value T whose cumulative count
 //     reaches top_k and how many candidates with H == T are taken, then
 //     compacts in candidate order.
-// For hhr_decode the distance stage also writes, per block of 256 candidates,
-// the cumulative histogram cum[blk][i] = #(H <= i) over the block's valid
-// candidates (u16), so that each attention workgroup can find the blocks that
-// hold its 64 output ranks from two entries per block (pick_window).  (Stored
-// bin-major instead, the pick's loads coalesce but the 2-byte stores scatter
-// over a cache line each, which costs more than it saves.)
+// For hhr_decode the selection stage is replaced by the attention workgroups:
+// each finds its own output ranks from the distances and the histogram
+// (pick_window).
 // H = 0 .. 32 NW G: 32 NW G + 1 bins for NW-word codes and G heads.
 template <int NW>
 constexpr int ham_bins_max() { return 32 * NW * kMaxG + 1; }
@@ -357,8 +354,9 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 // c < 16 P, P = the (b, g)'s kept count (nothing to do past it).  dist
 // [B][Hkv][p_max*16] u16; hist [B][Hkv][128 G + 1] (counts added
 // atomically); cum (or NULL) [B][Hkv][ham_cum_blocks(p_max)][128 G + 1] u16.
-// Item j of every thread lies in block 4k + j, whose histogram is LDS copy j.
-// Codes are NW 32-bit words.  All threads call.
+// Item j of every thread lies in block 4k + j of 256 candidates, whose
+// histogram is LDS copy j (fewer conflicting adds); the copies are summed
+// before the global adds.  Codes are NW 32-bit words.  All threads call.
 template <int NT, bool COH, int NW = kNW>
 __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, int p_max,
                                const int32_t* seq_len, const int32_t* kept_count,
@@ -371,8 +369,6 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   const int G = Hq / Hkv;
   const int bg = b * Hkv + g;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int l = tid & 63;
   const int nbins = 32 * NW * G + 1;
   const int page0 = k * kHamChunkPages;
   // kept pages and query codes are loaded before the kept count is known
@@ -446,6 +442,8 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   }
   // cumulative histogram of block 4k + w by wave w, 64 bins per wave scan, so
   // each store instruction writes 128 contiguous bytes
+  const int w = tid >> 6;
+  const int l = tid & 63;
   if (cum == nullptr || w * kCumBlock >= ncl) return;  // wave-uniform; no barrier follows
   uint16_t* row = cum + ((size_t)bg * ham_cum_blocks(p_max) + (size_t)k * kHistCopies + w) * nbins;
   int carry = 0;
@@ -457,7 +455,7 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   }
 }
 
-// The gather's spread histogram needs (nbins + 1) x (sub-bins) words: 16
+// The fine stage's spread histogram needs (nbins + 1) x (sub-bins) words: 16
 // sub-bins for 128-bit codes and 4-head groups.
 constexpr int kHamHistCap = 16 * (32 * kNW * 4 + 2);
 
@@ -592,73 +590,6 @@ __device__ void ham_select_core(int bg, int P, int top_k, int nbins, int32_t* se
   if (tid == 0) Mem<COH>::st(sel_count + bg, count);
 }
 
-// ------------------------------------- S5 over every page, then S6 from LDS
-// The one-launch selection (k_score_topp with the fine stage) computes H for
-// every key of every page while the top-P runs, so that only a gather of the
-// kept pages' distances remains after it.
-//
-// H of every key of the 16 pages [pb, pb + 16) of (b, g), by one wave, in
-// two steps (so that the loads can be issued early).  Lane l takes keys
-// 2l, 2l + 1 and 128 + 2l, 128 + 2l + 1 of the wave's 256, so every store of
-// the packed result writes 256 contiguous bytes (two distances per 32-bit
-// word: word j holds rows t_base + 128 j + 2 l and the next one).
-template <int NW>
-__device__ __forceinline__ void ham_wave_codes(int bg, int Lcap, int pb,
-                                               const uint32_t* __restrict__ codes, u32x4 c[4]) {
-  static_assert(NW == 4, "the one-launch selection reads 128-bit codes");
-  const int l = threadIdx.x & (kWave - 1);
-  const int t_base = pb * kPS;
-  const uint32_t* cb = codes + (size_t)bg * Lcap * NW;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int t = t_base + 128 * (k >> 1) + 2 * l + (k & 1);
-    c[k] = *(const u32x4*)(cb + (size_t)min(t, Lcap - 1) * NW);
-  }
-}
-
-// The summed distances of ham_wave_codes' keys to the G query codes sq (LDS),
-// packed; a row at or past L gets 0xFFFF.
-__device__ __forceinline__ void ham_wave_dist(int L, int pb, int G, const uint32_t* sq,
-                                              const u32x4 c[4], uint32_t w[2]) {
-  const int l = threadIdx.x & (kWave - 1);
-  uint32_t h[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 1
-  for (int qh = 0; qh < G; ++qh) {
-    const u32x4 q = *(const u32x4*)(sq + qh * kNW);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[k] += __popc(c[k][i] ^ q[i]);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t0 = pb * kPS + 128 * j + 2 * l;
-    const uint32_t v0 = t0 < L ? h[2 * j] : 0xFFFFu;
-    const uint32_t v1 = t0 + 1 < L ? h[2 * j + 1] : 0xFFFFu;
-    w[j] = v0 | (v1 << 16);
-  }
-}
-
-// ham_wave_codes + ham_wave_dist, stored to hall [B*Hkv][Lcap] u16 with
-// agent-scope stores (a workgroup of the same launch reads them).
-template <int NW>
-__device__ __forceinline__ void ham_page_wave(int bg, int Lcap, int L, int pb, int G,
-                                              const uint32_t* __restrict__ codes,
-                                              const uint32_t* sq, uint16_t* hall) {
-  const int l = threadIdx.x & (kWave - 1);
-  u32x4 c[4];
-  ham_wave_codes<NW>(bg, Lcap, pb, codes, c);
-  uint32_t w[2];
-  ham_wave_dist(L, pb, G, sq, c, w);
-  const int t_end = min((pb + kScorePagesPerWave) * kPS, Lcap);
-  uint16_t* hb = hall + (size_t)bg * Lcap;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t0 = pb * kPS + 128 * j + 2 * l;  // even, and t_end is a multiple of 16
-    if (t0 < t_end) Mem<true>::st(reinterpret_cast<uint32_t*>(hb + t0), w[j]);
-  }
-}
-
 // 16 bytes at byte offset off of buf (whose size is bytes), loaded with the
 // sc1 cache policy: coherent with agent-scope stores of other workgroups of
 // the same launch, like an agent-scope atomic load, but as one dwordx4.
@@ -668,150 +599,136 @@ __device__ __forceinline__ u32x4 ld_sc1_x4(const void* buf, uint32_t bytes, uint
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16 /* sc1 */);
 }
 
-// Sub-bins per H value of the gather's LDS histogram: lane l adds into copy
-// l % S (copy-major: word k (nbins + 1) + H), so lanes of one instruction
-// that hit the same H rarely hit the same word, and the fold reads
-// consecutive words across lanes.
-__device__ __forceinline__ int ham_spread(int nbins) {
-  int S = 16;
-  while (S > 1 && (nbins + 1) * S > kHamHistCap) S >>= 1;
-  return S;
+// seq_len[b], or 0 (and HHR_DEV_BAD_SEQ_LEN in *status, if given) when it is
+// outside [0, Lcap].
+__device__ __forceinline__ int clamped_len(const int32_t* seq_len, int b, int Lcap,
+                                           uint32_t* status) {
+  const int L = seq_len[b];
+  if (L < 0 || L > Lcap) {
+    if (status && threadIdx.x == 0) atomicOr(status, HHR_DEV_BAD_SEQ_LEN);
+    return 0;
+  }
+  return L;
 }
 
-// The distances of the P kept pages sm.skept[0 .. P) (ascending) into sm.hval
-// (candidate c = kept slot c / 16, row c % 16) and their histogram over
-// H = 0 .. nbins - 1 into sm.hist, ready for ham_select_core.  Two lanes per
-// kept page, 8 rows each, every load of a thread issued before any is used.
-// Pages in [own_lo, own_hi) are this workgroup's own: their distances are in
-// LDS (own_h, 16 per page from own_lo); every other page's come from hall,
-// written by the other workgroups of this launch.  All NT threads call;
-// sm.skept and own_h must be behind a barrier.
-template <int NT>
-__device__ void ham_gather_kept(int bg, int Lcap, int P, int nbins, const uint16_t* hall,
-                                const uint16_t* own_h, int own_lo, int own_hi, HamSmem& sm) {
-  constexpr int kTasks = 2 * (kMaxCand / kPS) / NT;  // half-pages per thread, at most
-  static_assert(kTasks * NT == 2 * (kMaxCand / kPS), "half-pages split evenly");
-  const int tid = threadIdx.x;
-  const int S = ham_spread(nbins);
-  const int stride = nbins + 1;  // bin nbins takes the 0xFFFF rows
-  int* hc = sm.hist + (tid & (S - 1)) * stride;
-  for (int i = tid; i < stride * S; i += NT) sm.hist[i] = 0;
-  const uint16_t* hb = hall + (size_t)bg * Lcap;
-  const uint32_t hbytes = (uint32_t)Lcap * 2u;
-  u32x4 h8[kTasks];
-#pragma unroll
-  for (int j = 0; j < kTasks; ++j) {
-    const int i = tid + j * NT;
-    const int page = sm.skept[min(i >> 1, max(P - 1, 0))];
-    const int half = 8 * (i & 1);  // first of this lane's 8 rows in the page
-    if (i < 2 * P) {
-      if (page >= own_lo && page < own_hi)
-        h8[j] = *reinterpret_cast<const u32x4*>(own_h + (page - own_lo) * kPS + half);
-      else
-        h8[j] = ld_sc1_x4(hb, hbytes, (uint32_t)(page * kPS + half) * 2u);
-    }
-  }
-  __syncthreads();  // the histogram is clear
-#pragma unroll
-  for (int j = 0; j < kTasks; ++j) {
-    const int i = tid + j * NT;
-    if (i >= 2 * P) continue;
-    reinterpret_cast<u32x4*>(sm.hval)[i] = h8[j];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      atomicAdd(hc + min((int)(h8[j][w] & 0xFFFFu), nbins), 1);
-      atomicAdd(hc + min((int)(h8[j][w] >> 16), nbins), 1);
-    }
-  }
-  __syncthreads();
-  // fold the copies: read every bin's total first, then overwrite copy 0
-  constexpr int kFold = (kHamBinsMax + NT - 1) / NT;
-  int tot[kFold];
-#pragma unroll
-  for (int j = 0; j < kFold; ++j) {
-    const int bin = tid + j * NT;
-    int t = 0;
-    if (bin < nbins)
-      for (int k = 0; k < S; ++k) t += sm.hist[k * stride + bin];
-    tot[j] = t;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kFold; ++j)
-    if (tid + j * NT < nbins) sm.hist[tid + j * NT] = tot[j];
-  __syncthreads();
-}
+// The selected positions of output ranks [k0, k0 + 64) of (b, g), found
+// without the compacted selection, from what k_ham_dist wrote: the distances
+// (candidate c = kept slot c / 16, row c % 16, in position order), their H
+// histogram and, per block of 256 candidates, the cumulative histogram.
+// Candidate c is taken iff H < T, or H == T and fewer than `need` candidates
+// with H == T precede it, T and need being the cut of the whole histogram.
+//   pick_load (at kernel start, with the caller's other loads): the sequence
+//     length and kept count, this thread's histogram bins, and -- guessed
+//     from the window's place among the output ranks, as if the taken
+//     candidates were spread evenly -- kPickPre blocks of distances and kept
+//     pages around the window, so that usually no later load is needed.
+//   pick_window: the cut (block scan of the histogram); per block, from two
+//     entries of its cumulative histogram, the counts below and at the cut and
+//     so its first output rank (wave 0); then every block that reaches into
+//     the window places its taken candidates, ranked within the block by wave
+//     ballots (prefetched blocks all at once; others loaded here).
+// The result is sidx[i] = the position of output rank k0 + i (-1 past the
+// selection); pick_window returns the selection size min(top_k, #valid).
+// All NT = 256 threads call both.
+constexpr int kPickPre = 8;  // blocks prefetched
+constexpr int kPickMaxPer = (kHamBins + 255) / 256;  // histogram bins per thread
 
-// The 64 selected positions of output chunk [k0, k0 + 64) of (b, g), found
-// without the compacted list.  The cut (T, need) comes from the H histogram:
-// candidate c is taken iff H < T, or H == T and fewer than `need` candidates
-// with H == T precede it.  Two entries of each block's cumulative histogram
-// give its counts below and at T; wave scans over the blocks give every
-// block its first output rank, so only the blocks that reach into the chunk
-// (usually one or two) are read, one packed block scan each, to place their
-// taken candidates.  The result is sidx[i] = the position of output rank
-// k0 + i (-1 past the selection); returns the selection size
-// min(top_k, #valid).  Reads dist, hist, cum and kept written by earlier
-// launches.  All NT threads call.
-constexpr int kPickMaxBlocks = 4;  // blocks read per round trip
+struct PickRegs {
+  int P;
+  int cnt_bin[kPickMaxPer];
+  int pb0;  // first prefetched block
+  uint32_t h[kPickPre];
+  int pg[kPickPre];
+};
 
 struct PickSmem {
   int scan[17];
-  uint32_t uscan[17];
   int s_T, s_need, s_blo, s_bhi;
   int blk_first[2 * kWave];  // first output rank of each block
   int blk_eq[2 * kWave];     // candidates with H == T in earlier blocks
+  int wcnt[kPickPre][4];     // per block and wave: (H < T) | (H == T) << 16
 };
 
 template <int NT>
-__device__ __forceinline__ int pick_window(int bg, int P, int p_max, int nbins, int top_k, int k0,
-                                           const int32_t* kept, const uint16_t* dist,
-                                           const int* hist, const uint16_t* cum, int* sidx,
-                                           PickSmem& ps) {
+__device__ __forceinline__ void pick_load(int b, int bg, int p_max, int Lcap, int nbins,
+                                          int top_k, int k0, const int32_t* seq_len,
+                                          const int32_t* kept, const int32_t* kept_count,
+                                          const uint16_t* dist, const int* hist,
+                                          uint32_t* status, PickRegs& pr) {
   static_assert(NT == kCumBlock, "one candidate of a block per thread");
-  constexpr int kMaxPer = (kHamBins + NT - 1) / NT;
   const int tid = threadIdx.x;
-  const int ncand = P * kPS;
-  const int nblk = (ncand + kCumBlock - 1) / kCumBlock;  // <= 2 * kWave
-  // the cut: smallest T with #(H <= T) >= top_k, and how many H == T are taken
+  const int L = clamped_len(seq_len, b, Lcap, status);
+  const int kc = kept_count[bg];
   const int* hb = hist + (size_t)bg * nbins;
   const int per = (nbins + NT - 1) / NT;
+#pragma unroll
+  for (int i = 0; i < kPickMaxPer; ++i) {
+    const int v = hb[min(tid * per + i, nbins - 1)];
+    pr.cnt_bin[i] = (i < per && tid * per + i < nbins) ? v : 0;
+  }
+  const int P = L > 0 ? max(0, min(kc, p_max)) : 0;
+  pr.P = P;
+  const int ncand = P * kPS;
+  const int nblk = (ncand + kCumBlock - 1) / kCumBlock;
+  const int est = max(min(top_k, ncand), 1);
+  const int guess = (int)((int64_t)k0 * ncand / est) / kCumBlock;
+  pr.pb0 = max(0, min(guess - kPickPre / 2 + 1, nblk - kPickPre));
+  const uint16_t* db = dist + (size_t)bg * p_max * kPS;
+  const int32_t* kb = kept + (size_t)bg * p_max;
+  const int lastc = max(ncand - 1, 0);
+#pragma unroll
+  for (int u = 0; u < kPickPre; ++u) {
+    const int c = min((pr.pb0 + u) * kCumBlock + tid, lastc);
+    pr.h[u] = db[c];
+    pr.pg[u] = kb[c >> 4];
+  }
+}
+
+__device__ __forceinline__ int pick_window(int p_max, int nbins, int top_k, int k0,
+                                           const int32_t* kept, const uint16_t* dist,
+                                           const uint16_t* cum, int bg, const PickRegs& pr,
+                                           int* sidx, PickSmem& ps) {
+  constexpr int NT = kCumBlock;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int P = pr.P;
+  const int ncand = P * kPS;
+  const int nblk = (ncand + kCumBlock - 1) / kCumBlock;  // <= 2 * kWave
+  const int per = (nbins + NT - 1) / NT;
   const int b0 = tid * per;
-  int cnt_bin[kMaxPer];
+  if (tid < kAttnChunk) sidx[tid] = -1;
+  // the cut: smallest T with #(H <= T) >= top_k, and how many H == T are taken
   int local = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
-    cnt_bin[i] = (i < per && b0 + i < nbins) ? hb[min(b0 + i, nbins - 1)] : 0;
-    local += cnt_bin[i];
-  }
+  for (int i = 0; i < kPickMaxPer; ++i) local += pr.cnt_bin[i];
   int total;
   const int ex = block_exclusive_scan<NT, int>(local, ps.scan, &total);
   if (tid == 0) {
     ps.s_T = nbins;  // every valid H is < nbins: take all valid candidates
     ps.s_need = 0;
   }
-  if (tid < kAttnChunk) sidx[tid] = -1;
   __syncthreads();
   if (total > top_k) {
     int run = ex;
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      if (run < top_k && run + cnt_bin[i] >= top_k && cnt_bin[i] > 0) {
+    for (int i = 0; i < kPickMaxPer; ++i) {
+      if (run < top_k && run + pr.cnt_bin[i] >= top_k && pr.cnt_bin[i] > 0) {
         ps.s_T = b0 + i;
         ps.s_need = top_k - run;
       }
-      run += cnt_bin[i];
+      run += pr.cnt_bin[i];
     }
   }
   __syncthreads();
   const int Th = ps.s_T;
   const int need = ps.s_need;
   const int count = min(top_k, total);
+  if (k0 >= count) return count;  // block-uniform: nothing in the window
 
   // wave 0: per block, #(H < T) and #(H == T) from its cumulative histogram,
   // then its first output rank; the window's blocks are [s_blo, s_bhi]
-  if (tid < kWave) {
-    const int l = tid;
+  if (w == 0) {
     const uint16_t* cb = cum + (size_t)bg * ham_cum_blocks(p_max) * nbins;
     int lt[2], eq[2];
 #pragma unroll
@@ -854,35 +771,56 @@ __device__ __forceinline__ int pick_window(int bg, int P, int p_max, int nbins, 
   }
   __syncthreads();
   const int blo = ps.s_blo, bhi = ps.s_bhi;
+  const uint64_t below = lanemask_lt();
+  // rank of this thread's candidate of block blk (distance hv) within the
+  // block from the wave ballots and the earlier waves' counts in ps.wcnt[u]
+  auto place = [&](int u, int blk, uint32_t hv, int page, uint32_t in_wave) {
+    uint32_t before = in_wave;
+    for (int v = 0; v < w; ++v) before += (uint32_t)ps.wcnt[u][v];
+    const int lt_b = (int)(before & 0xFFFFu), eq_b = (int)(before >> 16);
+    const int r = max(need - ps.blk_eq[blk], 0);  // ties still to take at the block start
+    const bool tk = hv < (uint32_t)Th || (hv == (uint32_t)Th && eq_b < r);
+    const int pos = ps.blk_first[blk] + lt_b + min(eq_b, r) - k0;
+    const int c = blk * kCumBlock + tid;
+    if (tk && pos >= 0 && pos < kAttnChunk) sidx[pos] = page * kPS + (c & 15);
+  };
+  auto ballots = [&](int u, uint32_t hv) -> uint32_t {
+    const uint64_t blt = __ballot(hv < (uint32_t)Th);
+    const uint64_t beq = __ballot(hv == (uint32_t)Th);
+    if (l == 0) ps.wcnt[u][w] = (int)((uint32_t)popc64(blt) | ((uint32_t)popc64(beq) << 16));
+    return (uint32_t)popc64(blt & below) | ((uint32_t)popc64(beq & below) << 16);
+  };
+  // prefetched blocks that reach into the window, all at once
+  uint32_t inw[kPickPre];
+#pragma unroll
+  for (int u = 0; u < kPickPre; ++u) {
+    const int blk = pr.pb0 + u;
+    const uint32_t hv = blk * kCumBlock + tid < ncand ? pr.h[u] : 0xFFFFu;
+    inw[u] = ballots(u, hv);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPickPre; ++u) {
+    const int blk = pr.pb0 + u;
+    if (blk >= blo && blk <= bhi) {  // block-uniform
+      const uint32_t hv = blk * kCumBlock + tid < ncand ? pr.h[u] : 0xFFFFu;
+      place(u, blk, hv, pr.pg[u], inw[u]);
+    }
+  }
+  // the window's blocks that were not prefetched (a guess that missed)
   const uint16_t* db = dist + (size_t)bg * p_max * kPS;
   const int32_t* kb = kept + (size_t)bg * p_max;
 #pragma unroll 1
-  for (int bb = blo; bb <= bhi; bb += kPickMaxBlocks) {  // block-uniform
-    uint32_t h[kPickMaxBlocks];
-    int pg[kPickMaxBlocks];
-#pragma unroll
-    for (int u = 0; u < kPickMaxBlocks; ++u) {
-      const int c = min((bb + u) * kCumBlock + tid, max(ncand - 1, 0));
-      h[u] = db[c];
-      pg[u] = kb[c >> 4];
-    }
-#pragma unroll
-    for (int u = 0; u < kPickMaxBlocks; ++u) {
-      const int blk = bb + u;
-      if (blk > bhi) break;  // block-uniform
-      const int c = blk * kCumBlock + tid;
-      const uint32_t hv = c < ncand ? h[u] : 0xFFFFu;
-      const uint32_t ltf = hv < (uint32_t)Th ? 1u : 0u;
-      const uint32_t eqf = hv == (uint32_t)Th ? 1u : 0u;
-      uint32_t tot;
-      const uint32_t pre = block_exclusive_scan<NT, uint32_t>(ltf | (eqf << 16), ps.uscan, &tot);
-      const int lt_b = (int)(pre & 0xFFFFu), eq_b = (int)(pre >> 16);
-      const int r = max(need - ps.blk_eq[blk], 0);  // ties still to take at the block start
-      const bool tk = ltf || (eqf && eq_b < r);
-      const int pos = ps.blk_first[blk] + lt_b + min(eq_b, r);
-      if (tk && pos >= k0 && pos < k0 + kAttnChunk) sidx[pos - k0] = pg[u] * kPS + (c & 15);
-      __syncthreads();  // ps.uscan is reused by the next scan
-    }
+  for (int blk = blo; blk <= bhi; ++blk) {  // block-uniform
+    if (blk >= pr.pb0 && blk < pr.pb0 + kPickPre) continue;
+    const int c = blk * kCumBlock + tid;
+    const int cc = min(c, max(ncand - 1, 0));
+    const uint32_t hv = c < ncand ? (uint32_t)db[cc] : 0xFFFFu;
+    const int page = kb[cc >> 4];
+    __syncthreads();  // ps.wcnt[0] is free
+    const uint32_t iw = ballots(0, hv);
+    __syncthreads();
+    place(0, blk, hv, page, iw);
   }
   __syncthreads();
   return count;
@@ -897,12 +835,12 @@ __device__ __forceinline__ int pick_window(int bg, int P, int p_max, int nbins, 
 // writes the unnormalised partial
 // (o~, m, l): o~_h = sum_i e^(x_hi - m_h) V_i, m_h = max_i x_hi,
 // l_h = sum_i e^(x_hi - m_h), x_hi = q_h . K_i * scale.
+// The group's queries come from q, or, with q_ready, are already in sm.sq.
 // All threads of the workgroup must call (barriers); each 256-thread group
 // passes its own chunk (nk = 0 for an idle group).  Only query heads
 // [h_lo, h_hi) of the group are attended and their partials written, so that
 // several workgroups can share one chunk's heads when the group is large.
 constexpr int kCh = kAttnChunk;      // 64 selected keys per chunk
-constexpr int kPartStride = kD + 2;  // o~[128], m, l
 constexpr int kRowPad = 8;           // LDS row padding (bank spread), in elements
 
 template <bool KF32>
@@ -920,7 +858,8 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
                            float scale, const float* __restrict__ q,
                            const void* __restrict__ kcache, const void* __restrict__ vcache,
                            const int32_t* sel_idx, float* pout, uint32_t* status,
-                           AttnSmem<KF32>& sm, int h_lo = 0, int h_hi = kMaxG) {
+                           AttnSmem<KF32>& sm, int h_lo = 0, int h_hi = kMaxG,
+                           bool q_ready = false) {
   typedef typename AttnSmem<KF32>::ET ET;
   constexpr int kStride = kD + kRowPad;
   constexpr int kVec = 16 / sizeof(ET);              // elements per 16-byte load
@@ -944,8 +883,9 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     sm.sidx[tq] = idx;
   }
   const int h_end = min(h_hi, G);  // this workgroup's query heads [h_lo, h_end)
-  for (int i = tq; i < G * kD; i += 256)
-    sm.sq[i / kD][i % kD] = q[((size_t)b * Hq + (size_t)g * G) * kD + i];
+  if (!q_ready)  // else the caller filled sm.sq
+    for (int i = tq; i < G * kD; i += 256)
+      sm.sq[i / kD][i % kD] = q[((size_t)b * Hq + (size_t)g * G) * kD + i];
   __syncthreads();
 
   // gather: every thread issues all of its K and V loads before storing any
@@ -1055,7 +995,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
 // weights are known, so up to 64 chunks cost one round trip.
 constexpr int kCombThreads = 128;
 constexpr int kCombGroups = kCombThreads / (kD / 4);  // 4 chunk groups
-constexpr int kCombMaxChunks = kMaxCand / kCh;        // 512
+constexpr int kCombMaxChunks = kMaxCand / kCh;  // 512
 
 struct CombSmem {
   float f[kCombMaxChunks];

@@ -47,8 +47,7 @@
  *     It starts with a control block: the device status word at offset 0;
  *     bytes 64..255, eight words per (b, g) from offset 256 and then one
  *     H histogram per (b, g) (the fine top-k's) are reserved and zero
- *     between calls.  Every call leaves them zero again (after an
- *     HHR_DEV_TIMEOUT, zero the workspace before reusing it); the status word
+ *     between calls.  Every call leaves them zero again; the status word
  *     keeps its error bits until hhr_read_device_status clears it.  The
  *     control block sits at the same offsets in every HHR layout and every
  *     other region follows it, so one workspace may serve every HHR entry
@@ -77,11 +76,9 @@ typedef enum {
 /* Device status bits (hhr_read_device_status). */
 #define HHR_DEV_BAD_SEQ_LEN 0x1u  /* a seq_len was < 0 or > max_ctx           */
 #define HHR_DEV_BAD_INDEX 0x2u    /* a selected position was outside [0,Lcap) */
-#define HHR_DEV_TIMEOUT 0x4u      /* a wait between workgroups of one launch gave up
-                                     (results of that call are unspecified).  Only the
-                                     one-launch selection waits: its top-P workgroup
-                                     waits for the other workgroups of its (b, g), all
-                                     of which are already running */
+#define HHR_DEV_TIMEOUT 0x4u      /* reserved: no kernel of this version waits for
+                                     another workgroup (hand-offs between workgroups
+                                     go to whichever arrives last), so it is never set */
 
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
@@ -265,10 +262,10 @@ hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_
  * need only order q.k, which a top-k needs).  Intermediates live in the
  * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk.  When the
  * coarse stage fits one launch (at most 2 x 256 scoring workgroups of 256
- * pages, 128-bit codes) the fine stage runs in it too: every workgroup also
- * scores all keys of its own pages against the query codes while the top-P
- * runs, and the top-P workgroup then takes the top-k from the kept pages'
- * distances.  Otherwise it runs as separate launches.  Same results. */
+ * pages, 128-bit codes) the fine stage runs in it too: the workgroup that
+ * takes the top-P then computes the distances of the kept pages' keys from
+ * their codes and takes the top-k.  Otherwise it runs as separate launches.
+ * Same results. */
 hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
                       const void* page_meta, int32_t keep_num, int32_t keep_den,
