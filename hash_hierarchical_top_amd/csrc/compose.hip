@@ -107,14 +107,16 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 
 // S2 + S3 + S4.  grid (ceil(NpCap / ppw), B*Hkv), 1024 threads: the first
 // ppw / 16 of the 16 waves score 16 pages each (ppw = 256, or 128 or 64 when
-// the grid would not cover the chip).  Each workgroup rotates its group's queries itself (64 KiB of R from
-// L2, issued after its metadata loads so both are in flight together);
-// workgroup 0 of each (b, g) also writes the query codes.
+// the grid would not cover the chip).  Each workgroup rotates its group's
+// queries itself (64 KiB of R from L2, issued after its metadata loads so both
+// are in flight together); workgroup 0 of each (b, g) also writes the query
+// codes, once its bounds are done (the sign bits need W's columns in
+// registers, which would not fit beside the metadata).
 //
 // APPEND: row L - 1 of every sequence is a key appended since the last encode
 // (its K row is in kcache).  The workgroup that holds the last page encodes
-// it with its queries (rotation and code bits, the same per-column sums),
-// writes its code, and the wave that holds the page folds it into the page's
+// it with its queries (rotation, and after the bounds its code bits: the same
+// per-column sums), writes its code, and the wave that holds the page folds it into the page's
 // {min, max} (or starts the page with it) in registers before the bound, and
 // stores the page's metadata back.  Nothing else touches that page, so no
 // other workgroup can see it half-updated.
@@ -147,41 +149,30 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   PageLoads<1> pl;
   if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   const bool wg_has = (int)blockIdx.x * ppw < Np;  // block-uniform
-  auto to_lds = [&](int h, int col, float v) { sm.rot.qrot[h][col] = v; };
   // the workgroup holding the last page, when a key was appended (block-uniform)
   const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / ppw;
+  const void* key = nullptr;
+  uint32_t* crow = nullptr;
   if (owner) {
     const size_t krow = ((size_t)bg * Lcap + (size_t)(L - 1)) * kD;
-    const void* key = kv_f32 ? (const void*)((const float*)kcache + krow)
-                             : (const void*)((const uint16_t*)kcache + krow);
-    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
-    uint32_t* crow = codes + ((size_t)bg * Lcap + (size_t)(L - 1)) * kNW;
-    auto rot_key = [&](int h, int col, float v) {
-      if (h < G)
-        sm.rot.qrot[h][col] = v;
-      else
-        sm.rot.xnew[col] = v;
-    };
-    auto code_key = [&](int h, int word, uint32_t bits) {
-      if (h == G) {
-        crow[word] = bits;
-      } else {
-        if (blockIdx.x == 0) q_codes[cbase + (size_t)h * kNW + word] = bits;
-      }
-    };
-    qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, rot_key, code_key, key,
-                                     kv_f32 != 0);
-    if (wave_has && pb + kScorePagesPerWave > Np - 1)  // wave-uniform: the last page's wave
+    key = kv_f32 ? (const void*)((const float*)kcache + krow)
+                 : (const void*)((const uint16_t*)kcache + krow);
+    crow = codes + ((size_t)bg * Lcap + (size_t)(L - 1)) * kNW;
+  }
+  // the rotation of the queries (and of the appended key, as row G) before
+  // the bounds; their code bits once the bounds are done, when the metadata
+  // no longer holds registers
+  if (wg_has || owner) {
+    qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe,
+                                 [&](int h, int col, float v) {
+                                   if (h < G)
+                                     sm.rot.qrot[h][col] = v;
+                                   else
+                                     sm.rot.xnew[col] = v;
+                                 },
+                                 [](int, int, uint32_t) {}, key, kv_f32 != 0);
+    if (owner && wave_has && pb + kScorePagesPerWave > Np - 1)  // the last page's wave
       merge_appended_row<MBF>(bg, NpCap, Np - 1, pb, (L - 1) % kPS == 0, sm.rot.xnew, meta, pl);
-  } else if (blockIdx.x == 0) {
-    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
-    qenc_core<2 * kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
-                      [&](int h, int word, uint32_t bits) {
-                        q_codes[cbase + (size_t)h * kNW + word] = bits;
-                      });
-  } else if (wg_has) {
-    qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe, to_lds,
-                                 [](int, int, uint32_t) {});
   }
   uint32_t* ctl = counters + (size_t)bg * kCountersPerGroup;
   float2* wr = wave_range + (size_t)bg * (NpCap / kScorePagesPerWave);
@@ -200,6 +191,18 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       Mem<true>::st(dst, lo);
       Mem<true>::st(dst + 1, hi);
     }
+  }
+  if (blockIdx.x == 0 || owner) {  // block-uniform
+    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
+    auto code_of = [&](int h, int word, uint32_t bits) {
+      if (h == G)
+        crow[word] = bits;
+      else if (blockIdx.x == 0)
+        q_codes[cbase + (size_t)h * kNW + word] = bits;
+    };
+    auto no_rot = [](int, int, float) {};
+    qenc_core<32 * kNW, kScoreThreads, decltype(no_rot), decltype(code_of), kNW, kD>(
+        b, g, Hq, Hkv, q, R, W, sm.rot.qe, no_rot, code_of, key, kv_f32 != 0);
   }
   const bool last1 = arrive_last(ctl, gridDim.x, &s_last);
   if (!last1) return;

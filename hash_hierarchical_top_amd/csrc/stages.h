@@ -23,8 +23,9 @@ namespace hhr {
 // order k = 0..7.  NT threads share the (column, k) work items, CPT adjacent
 // columns each (the fewest of 1, 2, 4 that cover the columns; threads past
 // them idle), so a thread holds 16 CPT matrix values in registers and the
-// result does not depend on NT or on NCOL (128 + 32 NW: rotation and codes;
-// 128: rotation only).
+// result does not depend on NT or on the column range [COL0, COL0 + NCOL)
+// (0 and 128 + 32 NW: rotation and codes; 0 and 128: rotation only; 128 and
+// 32 NW: codes only).
 // rot(h, col, v) receives q'; code(h, word, bits) receives 32 code bits.
 // With extra_row (a KF32/bf16 key row of length 128, or NULL) it is encoded
 // the same way as row h = G after the G queries.  Every thread of the
@@ -42,12 +43,14 @@ constexpr int qenc_cpt() {
   return 8 * NCOL <= NT ? 1 : 8 * NCOL <= 2 * NT ? 2 : 4;
 }
 
-template <int NCOL, int NT, typename Rot, typename Code, int NW = kNW>
+template <int NCOL, int NT, typename Rot, typename Code, int NW = kNW, int COL0 = 0>
 __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict__ q,
                           const float* __restrict__ R, const float* __restrict__ W,
                           QencSmem& sm, Rot rot, Code code, const void* extra_row = nullptr,
                           bool extra_f32 = false) {
-  static_assert(NCOL == kD || NCOL == kD + 32 * NW, "rotation, or rotation and codes");
+  static_assert((COL0 == 0 && (NCOL == kD || NCOL == kD + 32 * NW)) ||
+                    (COL0 == kD && NCOL == 32 * NW),
+                "rotation, rotation and codes, or codes");
   static_assert(NCOL % 64 == 0, "a wave's outputs stay in one row");
   constexpr int CPT = qenc_cpt<NCOL, NT>();  // columns per thread
   static_assert(8 * NCOL <= CPT * NT, "too many columns for the workgroup");
@@ -59,7 +62,7 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
   const bool active = tid < 8 * kGroupsC;  // threads past the work items only reduce
   const int cg = active ? tid % kGroupsC : 0;
   const int dg = active ? tid / kGroupsC : 0;  // 0..7
-  const int c0 = CPT * cg;                     // first column in [0, NCOL)
+  const int c0 = COL0 + CPT * cg;              // first column in [COL0, COL0 + NCOL)
   const float* M = c0 < kD ? R + (size_t)g * kD * kD + c0 : W + (size_t)g * kD * kCB + (c0 - kD);
   const int mstride = c0 < kD ? kD : kCB;
   float m[16][CPT];
@@ -110,7 +113,7 @@ __device__ void qenc_core(int b, int g, int Hq, int Hkv, const float* __restrict
       const int o = tid + NT * pass;  // (row hh, column col) of this round
       if (o >= kOut) break;           // wave-uniform: kOut is a multiple of 64
       const int hh = o / NCOL;
-      const int col = o % NCOL;
+      const int col = COL0 + o % NCOL;
       float v = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) v += sm.red[k][hh][col];
