@@ -288,6 +288,13 @@ __device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t add_agent_u32(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A compiler-only barrier for memory operations (no instruction, no wait):
+// loads written before it are issued before it.  Used after a batch of
+// independent loads whose values are consumed under conditions, which the
+// compiler would otherwise turn into one branch per load, each load waited
+// for on its own before the next is issued.
+__device__ __forceinline__ void issue_loads_here() { asm volatile("" ::: "memory"); }
+
 // Wait until every memory access this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 

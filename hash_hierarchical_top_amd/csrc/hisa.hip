@@ -294,6 +294,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   if (b >= nrows) return;
   const int slot0 = blockIdx.x * nslot;
   const int tid = threadIdx.x;
+  __shared__ int skb[kHisaMaxCand / 16];  // kept blocks of this workgroup's slots
   const int wv = tid >> 6;
   const int l = tid & 63;
   const int lrow = l & 15;
@@ -304,19 +305,34 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   // load before the row's length and kept count are known (every address
   // stays inside its buffer), so they share that round trip.
   // A: head 16 ht + lrow; this lane's 16 heads for the epilogue: 16 ht + 4 lgrp + j
+  // (every address clamped into its row and the loads issued together; heads
+  // past Hi are zeroed afterwards)
   fp8x8 aq[4][4];
+  float wq[4][4], sq[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = min(16 * ht + lrow, Hi - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      aq[ht][ks] = *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int he = min(16 * ht + 4 * lgrp + j, Hi - 1);
+      wq[ht][j] = w[(size_t)b * Hi + he];
+      sq[ht][j] = q_scale[(size_t)b * Hi + he];
+    }
+  }
+  issue_loads_here();
   float wsq[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    const int h = 16 * ht + lrow;
+    if (16 * ht + lrow >= Hi) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      aq[ht][ks] = h < Hi ? *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp) : 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int he = 16 * ht + 4 * lgrp + j;
-      wsq[ht][j] = he < Hi ? w[(size_t)b * Hi + he] * q_scale[(size_t)b * Hi + he] : 0.f;
+      for (int ks = 0; ks < 4; ++ks) aq[ht][ks] = 0;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wsq[ht][j] = 16 * ht + 4 * lgrp + j < Hi ? wq[ht][j] * sq[ht][j] : 0.f;
   }
   const int pslot = min(slot0 + wv / tiles_per_block, keep_blocks - 1);
   const int pblk = kept[(size_t)b * keep_blocks + pslot];
@@ -330,25 +346,31 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   const uint8_t* kb = k8 + cb * Lcap * kD;
   const float* ksb = k_scale + cb * Lcap;
   const int ntiles = (slot1 - slot0) * tiles_per_block;
-  // key fragments of tile i (token row of this lane; rows past L read row 0)
+  // this workgroup's kept blocks, so that a tile's token needs no load of its own
+  for (int i = tid; i < slot1 - slot0; i += 64 * kTsWaves)
+    skb[i] = slot0 + i == pslot ? pblk : kept[(size_t)b * keep_blocks + slot0 + i];
+  __syncthreads();
   auto tile_token = [&](int i) {
-    const int slot = slot0 + i / tiles_per_block;
-    const int blk = slot == pslot ? pblk : kept[(size_t)b * keep_blocks + slot];
-    return blk * block + 16 * (i % tiles_per_block) + lrow;
+    return skb[i / tiles_per_block] * block + 16 * (i % tiles_per_block) + lrow;
   };
-  auto load_tile = [&](int i, fp8x8 (&kf)[4]) {
+  // key fragments and scale of tile i (token row of this lane; rows past L
+  // read row 0), all issued together
+  auto load_tile = [&](int i, fp8x8 (&kf)[4], float& ks) {
     const int t = tile_token(i);
     const size_t row = (t >= 0 && t < L) ? (size_t)t : 0;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[ks] = *(const fp8x8*)(kb + row * kD + 32 * ks + 8 * lgrp);
+    for (int k = 0; k < 4; ++k) kf[k] = *(const fp8x8*)(kb + row * kD + 32 * k + 8 * lgrp);
+    ks = ksb[row];
   };
   int i = wv;
   fp8x8 kf[4], k1[4];
-  if (i < ntiles) load_tile(i, kf);
-  if (i + kTsWaves < ntiles) load_tile(i + kTsWaves, k1);
+  float s0 = 0.f, s1 = 0.f;
+  if (i < ntiles) load_tile(i, kf, s0);
+  if (i + kTsWaves < ntiles) load_tile(i + kTsWaves, k1, s1);
   for (; i < ntiles; i += kTsWaves) {
     fp8x8 k2[4];
-    if (i + 2 * kTsWaves < ntiles) load_tile(i + 2 * kTsWaves, k2);
+    float s2 = 0.f;
+    if (i + 2 * kTsWaves < ntiles) load_tile(i + 2 * kTsWaves, k2, s2);
     floatx4 acc[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -359,7 +381,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
     }
     const int t = tile_token(i);
     const bool valid = t >= 0 && t < L;
-    const float sk = valid ? ksb[t] : 0.f;
+    const float sk = valid ? s0 : 0.f;
     const float inf = opaque_inf();
     float part = 0.f;
 #pragma unroll
@@ -377,6 +399,8 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
       kf[ks] = k1[ks];
       k1[ks] = k2[ks];
     }
+    s0 = s1;
+    s1 = s2;
   }
 }
 

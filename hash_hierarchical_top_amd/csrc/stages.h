@@ -665,10 +665,11 @@ __device__ __forceinline__ void pick_load(int b, int bg, int p_max, int Lcap, in
   const int* hb = hist + (size_t)bg * nbins;
   const int per = (nbins + NT - 1) / NT;
 #pragma unroll
-  for (int i = 0; i < kPickMaxPer; ++i) {
-    const int v = hb[min(tid * per + i, nbins - 1)];
-    pr.cnt_bin[i] = (i < per && tid * per + i < nbins) ? v : 0;
-  }
+  for (int i = 0; i < kPickMaxPer; ++i) pr.cnt_bin[i] = hb[min(tid * per + i, nbins - 1)];
+  issue_loads_here();
+#pragma unroll
+  for (int i = 0; i < kPickMaxPer; ++i)
+    if (!(i < per && tid * per + i < nbins)) pr.cnt_bin[i] = 0;
   const int P = L > 0 ? max(0, min(kc, p_max)) : 0;
   pr.P = P;
   const int ncand = P * kPS;
@@ -737,14 +738,18 @@ __device__ __forceinline__ int pick_window(int p_max, int nbins, int top_k, int 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int blk = r * kWave + l;
-      lt[r] = eq[r] = 0;
-      if (blk < nblk) {
-        const uint16_t* row = cb + (size_t)blk * nbins;
-        const int below = Th == 0 ? 0 : (int)row[min(Th, nbins) - 1];
-        const int upto = Th >= nbins ? below : (int)row[Th];
-        lt[r] = below;
-        eq[r] = upto - below;
-      }
+      const uint16_t* row = cb + (size_t)min(blk, max(nblk - 1, 0)) * nbins;
+      lt[r] = row[max(min(Th, nbins) - 1, 0)];
+      eq[r] = row[min(Th, nbins - 1)];
+    }
+    issue_loads_here();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int blk = r * kWave + l;
+      const int below = Th == 0 ? 0 : lt[r];
+      const int upto = Th >= nbins ? below : eq[r];
+      lt[r] = blk < nblk ? below : 0;
+      eq[r] = blk < nblk ? upto - below : 0;
     }
     int lt_carry = 0, eq_carry = 0, lo = 2 * kWave, hi = -1;
 #pragma unroll
@@ -874,21 +879,34 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   const int w = tq >> 6;
   const int l = tq & 63;
 
-  if (sel_idx != nullptr && tq < kCh) {  // else the caller filled sm.sidx (valid or -1)
-    int idx = -1;
-    if (tq < nk) {
-      idx = Mem<COH>::ld(sel_idx + (size_t)bg * top_k + k0 + tq);
-      if (idx < 0 || idx >= Lcap) {
-        if (status) atomicOr(status, HHR_DEV_BAD_INDEX);
-        idx = -1;
-      }
+  // the chunk's positions and the group's queries, loaded together (addresses
+  // clamped into the buffers, values past them dropped afterwards)
+  constexpr int kQPer = kMaxG * kD / 256;
+  float qv[kQPer];
+  int idx = -1;
+  if (!q_ready) {  // else the caller filled sm.sq
+    const float* qg = q + ((size_t)b * Hq + (size_t)g * G) * kD;
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) qv[i] = qg[min(tq + 256 * i, G * kD - 1)];
+  }
+  if (sel_idx != nullptr && tq < kCh)  // else the caller filled sm.sidx (valid or -1)
+    idx = Mem<COH>::ld(sel_idx + (size_t)bg * top_k + k0 + min(tq, max(nk - 1, 0)));
+  issue_loads_here();
+  if (sel_idx != nullptr && tq < kCh) {
+    if (tq >= nk) {
+      idx = -1;
+    } else if (idx < 0 || idx >= Lcap) {
+      if (status) atomicOr(status, HHR_DEV_BAD_INDEX);
+      idx = -1;
     }
     sm.sidx[tq] = idx;
   }
   const int h_end = min(h_hi, G);  // this workgroup's query heads [h_lo, h_end)
-  if (!q_ready)  // else the caller filled sm.sq
-    for (int i = tq; i < G * kD; i += 256)
-      sm.sq[i / kD][i % kD] = q[((size_t)b * Hq + (size_t)g * G) * kD + i];
+  if (!q_ready) {
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i)
+      if (tq + 256 * i < G * kD) sm.sq[(tq + 256 * i) / kD][(tq + 256 * i) % kD] = qv[i];
+  }
   __syncthreads();
 
   // gather: every thread issues all of its K and V loads before storing any
@@ -1038,33 +1056,33 @@ __device__ void attn_combine(int b, int g, int h, int Hq, int Hkv, int ns, int n
       v[j] = ld_f32x4<COH>(pb + sc * sstride + 4 * d4);
     }
   };
-  if (ns > 0) load_batch(sgrp);
-  // chunk weights: wave 0 (chunks s = l, l + 64, ...)
-  if (tid < kWave) {
-    const float* ph = pb + kD;
-    if (ns <= kWave) {
-      const int sc = min(l, max(ns - 1, 0));
-      const float ms = l < ns ? Mem<COH>::ld(ph + sc * sstride) : -__builtin_huge_valf();
-      const float ls_ = l < ns ? Mem<COH>::ld(ph + sc * sstride + 1) : 0.f;
-      const float M = wave_max(ms);
-      const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
-      if (l < ns) sm.f[l] = f;
-      const float ls = wave_sum(fmaf(f, ls_, 0.f));
-      if (l == 0) sm.lsum = ls;
-    } else {
-      float M = -__builtin_huge_valf();
-      for (int s = l; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(ph + s * sstride));
-      M = wave_max(M);
-      float ls = 0.f;
-      for (int s = l; s < ns; s += kWave) {
-        const float ms = Mem<COH>::ld(ph + s * sstride);
-        const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
-        sm.f[s] = f;
-        ls = fmaf(f, Mem<COH>::ld(ph + s * sstride + 1), ls);
-      }
-      ls = wave_sum(ls);
-      if (l == 0) sm.lsum = ls;
+  // chunk weights (chunks s = l, l + 64, ...; every wave computes them, wave
+  // 0 stores them).  The (m, l) of chunk l load first, then the first
+  // partials, all without branches, so that waiting for the weights does not
+  // wait for the partials.
+  const float* ph = pb + kD;
+  const int sc0 = min(l, max(ns - 1, 0));
+  const float m0 = Mem<COH>::ld(ph + sc0 * sstride);
+  const float l0 = Mem<COH>::ld(ph + sc0 * sstride + 1);
+  load_batch(sgrp);
+  {
+    float M = l < ns ? m0 : -__builtin_huge_valf();
+    for (int s = l + kWave; s < ns; s += kWave) M = fmaxf(M, Mem<COH>::ld(ph + s * sstride));
+    M = wave_max(M);
+    float ls = 0.f;
+    if (l < ns) {
+      const float f = (m0 == -__builtin_huge_valf()) ? 0.f : expf(m0 - M);
+      if (tid < kWave) sm.f[l] = f;
+      ls = fmaf(f, l0, 0.f);
     }
+    for (int s = l + kWave; s < ns; s += kWave) {
+      const float ms = Mem<COH>::ld(ph + s * sstride);
+      const float f = (ms == -__builtin_huge_valf()) ? 0.f : expf(ms - M);
+      if (tid < kWave) sm.f[s] = f;
+      ls = fmaf(f, Mem<COH>::ld(ph + s * sstride + 1), ls);
+    }
+    ls = wave_sum(ls);
+    if (tid == 0) sm.lsum = ls;
   }
   __syncthreads();
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
