@@ -857,6 +857,10 @@ struct AttnSmem {
   __attribute__((aligned(16))) ET rows[kCh * (kD + kRowPad)];
   float sq[kMaxG][kD];
   float sp[kMaxG][kCh];
+  // bf16 hi + lo of the queries and numerators (MFMA A operands; rows padded
+  // by 16 bytes, since an operand read walks down 16 rows)
+  __attribute__((aligned(16))) uint16_t sqh[kMaxG][kD + 8], sql[kMaxG][kD + 8];
+  __attribute__((aligned(16))) uint16_t sph[kMaxG][kCh + 8], spl[kMaxG][kCh + 8];
   int sidx[kCh];
   float sm[kMaxG], sl[kMaxG];
 };
@@ -922,6 +926,20 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     kreg[i] = *(const u32x4*)(kb + (size_t)idx * kD + cc * kVec);
     vreg[i] = *(const u32x4*)(vb + (size_t)idx * kD + cc * kVec);
   }
+  if constexpr (!KF32) {
+    // while they are in flight: the queries as bf16 hi + lo for the MFMA
+    // logits, 16 rows (zero outside [h_lo, h_end)), 8 values per thread
+    const int r = tq >> 4;
+    const int c0 = 8 * (tq & 15);
+    const bool hrow = r >= h_lo && r < h_end;
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split_bf16(hrow ? sm.sq[r][c0 + j] : 0.f, hi[j], lo[j]);
+    *(u32x4*)&sm.sqh[r][c0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                   hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+    *(u32x4*)&sm.sql[r][c0] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                   lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+  }
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int c = tq + 256 * i;
@@ -935,6 +953,32 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   }
   __syncthreads();
 
+  if constexpr (!KF32) {
+    // logits on MFMA (bf16 keys): S[h][key] for 16 query-head rows (those
+    // outside [h_lo, h_end) are zero) and wave w's 16 keys 16 w .. 16 w + 15,
+    // K = 128 dims in 4 steps of 32.  A = the queries as bf16 hi + lo (lane:
+    // head lrow, dims 32 ks + 8 lgrp ..), B = the key rows as stored
+    // (lane: key 16 w + lrow, the same dims); D: lane holds S[4 lgrp + i][key].
+    const int lrow = l & 15;
+    const int lgrp = l >> 4;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      const bf16x8 ahi = as_bf16x8(*(const u32x4*)&sm.sqh[lrow][32 * ks + 8 * lgrp]);
+      const bf16x8 alo = as_bf16x8(*(const u32x4*)&sm.sql[lrow][32 * ks + 8 * lgrp]);
+      const bf16x8 bk =
+          as_bf16x8(*(const u32x4*)(sm.rows + (16 * w + lrow) * kStride + 32 * ks + 8 * lgrp));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bk, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bk, acc, 0, 0, 0);
+    }
+    const int key = 16 * w + lrow;
+    const bool kval = key < nk && sm.sidx[key] >= 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * lgrp + i;
+      if (h >= h_lo && h < h_end) sm.sp[h][key] = kval ? acc[i] * scale : -__builtin_huge_valf();
+    }
+  } else {
   // logits: thread (key = l, head group w) -> heads w, w+4, ...
   for (int h = h_lo + w; h < h_end; h += 4) {
     const ET* row = sm.rows + l * kStride;
@@ -955,6 +999,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     }
     sm.sp[h][l] = (l < nk && sm.sidx[l] >= 0) ? dot * scale : -__builtin_huge_valf();
   }
+  }
   __syncthreads();
 
   // V rows replace K rows; chunk softmax numerators (one wave per head, lane = key)
@@ -969,6 +1014,12 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     const float p = (x == -__builtin_huge_valf()) ? 0.f : expf(x - m);
     const float s = wave_sum(p);
     sm.sp[h][l] = p;
+    if constexpr (!KF32) {  // the numerators as bf16 hi + lo for the MFMA PV
+      uint32_t hi, lo;
+      split_bf16(p, hi, lo);
+      sm.sph[h][l] = (uint16_t)hi;
+      sm.spl[h][l] = (uint16_t)lo;
+    }
     if (l == 0) {
       sm.sm[h] = m;
       sm.sl[h] = s;
@@ -976,6 +1027,53 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   }
   __syncthreads();
 
+  if constexpr (!KF32) {
+    // partial o~_h[d] = sum_k p_h[k] V[k][d] on MFMA (bf16 values): 16
+    // query-head rows (outside [h_lo, h_end) zero), wave w's dims 32 w ..
+    // 32 w + 31 as two column tiles, K = the 64 keys in 2 steps of 32.  A = the
+    // numerators as bf16 hi + lo (lane: head lrow, keys 32 ks + 8 lgrp ..),
+    // B = V (lane: dim 16 nt + lrow, the same keys, read down the rows);
+    // D: lane holds o~[4 lgrp + i][16 nt + lrow].
+    if (nk > 0) {
+      const int lrow = l & 15;
+      const int lgrp = l >> 4;
+      const bool hrow = lrow >= h_lo && lrow < h_end;
+      bf16x8 phi[2], plo[2];
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < kCh / 32; ++ks) {
+        const u32x4 a = *(const u32x4*)&sm.sph[lrow][32 * ks + 8 * lgrp];
+        const u32x4 b = *(const u32x4*)&sm.spl[lrow][32 * ks + 8 * lgrp];
+        phi[ks] = as_bf16x8(hrow ? a : z);
+        plo[ks] = as_bf16x8(hrow ? b : z);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int d = 32 * w + 16 * t + lrow;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kCh / 32; ++ks) {
+          const ET* col = sm.rows + (32 * ks + 8 * lgrp) * kStride + d;
+          uint32_t v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = col[j * kStride];
+          const bf16x8 bv = as_bf16x8(u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16),
+                                            v[4] | (v[5] << 16), v[6] | (v[7] << 16)});
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[ks], bv, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], bv, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 4 * lgrp + i;
+          if (h >= h_lo && h < h_end) Mem<COH>::st(pout + h * kPartStride + d, acc[i]);
+        }
+      }
+      if (tq >= h_lo && tq < h_end) {
+        Mem<COH>::st(pout + tq * kPartStride + kD, sm.sm[tq]);
+        Mem<COH>::st(pout + tq * kPartStride + kD + 1, sm.sl[tq]);
+      }
+    }
+  } else {
   // partial o~_h[d] = sum_k p_h[k] V[k][d]: lane owns dims {2l, 2l+1}, wave w heads w, w+4, ...
   if (nk > 0) {
     for (int h = h_lo + w; h < h_end; h += 4) {
@@ -1003,6 +1101,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
         Mem<COH>::st(pout + h * kPartStride + kD + 1, sm.sl[h]);
       }
     }
+  }
   }
 }
 
