@@ -51,11 +51,14 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
                                 const int32_t* sel_count, int32_t top_k, float scale, float* out,
                                 float* part, int32_t n_split, uint32_t* status,
                                 hipStream_t stream) {
-  // more than 4 query heads per KV head and fewer chunks than CUs: split the
-  // heads over grid.z, 4 per workgroup (one per wave)
+  // f32 caches with more than 4 query heads per KV head and fewer chunks than
+  // CUs: split the heads over grid.z, 4 per workgroup (one per wave).  bf16
+  // caches take all 16 head rows in each MFMA, so a split would only repeat
+  // the chunk's gather.
   const int G = s.n_q_heads / s.n_kv_heads;
   const long long chunks = (long long)n_split * s.batch * s.n_kv_heads;
-  const int hsplit = (G > 4 && chunks < 256) ? (G + 3) / 4 : 1;
+  const int hsplit =
+      (s.kv_dtype == HHR_F32 && G > 4 && chunks < 256) ? (G + 3) / 4 : 1;
   dim3 grid(n_split, s.batch * s.n_kv_heads, hsplit);
   if (s.kv_dtype == HHR_F32)
     hipLaunchKernelGGL(k_attn<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache, sel_idx,

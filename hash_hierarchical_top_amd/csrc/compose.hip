@@ -258,9 +258,7 @@ __global__ __launch_bounds__(256) void k_attn_pick(
   const float* qg = q + ((size_t)b * Hq + (size_t)g * G) * kD;
 #pragma unroll
   for (int i = 0; i < kQPer; ++i) qv[i] = qg[min(tid + 256 * i, G * kD - 1)];
-#pragma unroll
-  for (int i = 0; i < kQPer; ++i)
-    if (tid + 256 * i < G * kD) sm.sq[(tid + 256 * i) / kD][(tid + 256 * i) % kD] = qv[i];
+  attn_put_q(sm, qv, G);
   const int count = pick_window(p_max, nbins, top_k, k0, kept, dist, cum, bg, pr, sm.sidx, ps);
   if (tid < kCh && k0 + tid < top_k) sel_idx[(size_t)bg * top_k + k0 + tid] = sm.sidx[tid];
   if (blockIdx.x == 0 && tid == 0) sel_count[bg] = count;

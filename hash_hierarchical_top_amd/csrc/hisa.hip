@@ -146,19 +146,29 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
 #pragma unroll
   for (int k = 0; k < kQWords; ++k) {
     const int i = tid + k * 64 * kBsWaves;
-    const int h = i / (kD / 4);
-    qv[k] = h < Hi ? *(const uint32_t*)(qb + (size_t)h * kD + 4 * (i % (kD / 4))) : 0u;
+    const int h = min(i / (kD / 4), Hi - 1);
+    qv[k] = *(const uint32_t*)(qb + (size_t)h * kD + 4 * (i % (kD / 4)));
   }
   // this lane's 16 heads in the epilogue: 16 mt + 4 lgrp + j
+  // (addresses clamped and all loads issued together; heads past Hi zeroed after)
   float wh[4][4], sh[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int h = 16 * mt + 4 * lgrp + j;
-      wh[mt][j] = h < Hi ? w[(size_t)b * Hi + h] : 0.f;
-      sh[mt][j] = h < Hi ? q_scale[(size_t)b * Hi + h] : 0.f;
+      const int h = min(16 * mt + 4 * lgrp + j, Hi - 1);
+      wh[mt][j] = w[(size_t)b * Hi + h];
+      sh[mt][j] = q_scale[(size_t)b * Hi + h];
     }
+  issue_loads_here();
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (16 * mt + 4 * lgrp + j >= Hi) wh[mt][j] = sh[mt][j] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kQWords; ++k)
+    if ((tid + k * 64 * kBsWaves) / (kD / 4) >= Hi) qv[k] = 0u;
   // B rows: the representative of block blk0 + lrow, dims 32 ks + 8 lgrp + [0, 8).
   // Shared cache (prefill rows): a row's partly visible last block is its own
   // tail mean (k_hisa_pool_tail), not the cache's pooled block.

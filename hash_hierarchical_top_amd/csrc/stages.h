@@ -843,7 +843,8 @@ __device__ __forceinline__ int pick_window(int p_max, int nbins, int top_k, int 
 // writes the unnormalised partial
 // (o~, m, l): o~_h = sum_i e^(x_hi - m_h) V_i, m_h = max_i x_hi,
 // l_h = sum_i e^(x_hi - m_h), x_hi = q_h . K_i * scale.
-// The group's queries come from q, or, with q_ready, are already in sm.sq.
+// The group's queries come from q, or, with q_ready, are already in sm
+// (attn_put_q).
 // All threads of the workgroup must call (barriers); each 256-thread group
 // passes its own chunk (nk = 0 for an idle group).  Only query heads
 // [h_lo, h_hi) of the group are attended and their partials written, so that
@@ -854,16 +855,48 @@ constexpr int kRowPad = 8;           // LDS row padding (bank spread), in elemen
 template <bool KF32>
 struct AttnSmem {
   typedef typename std::conditional<KF32, float, uint16_t>::type ET;
+  static constexpr int kQRows = KF32 ? kMaxG : 1;   // f32 queries (f32 caches only)
+  static constexpr int kBRows = KF32 ? 1 : kMaxG;   // bf16 hi + lo operands (bf16 caches)
   __attribute__((aligned(16))) ET rows[kCh * (kD + kRowPad)];
-  float sq[kMaxG][kD];
+  float sq[kQRows][kD];
   float sp[kMaxG][kCh];
-  // bf16 hi + lo of the queries and numerators (MFMA A operands; rows padded
-  // by 16 bytes, since an operand read walks down 16 rows)
-  __attribute__((aligned(16))) uint16_t sqh[kMaxG][kD + 8], sql[kMaxG][kD + 8];
-  __attribute__((aligned(16))) uint16_t sph[kMaxG][kCh + 8], spl[kMaxG][kCh + 8];
+  // bf16 hi + lo of the queries (until the logits are done), then of the
+  // softmax numerators: the MFMA A operands, rows padded by 16 bytes since an
+  // operand read walks down 16 rows
+  union {
+    struct {
+      __attribute__((aligned(16))) uint16_t h[kBRows][kD + 8], l[kBRows][kD + 8];
+    } q;
+    struct {
+      __attribute__((aligned(16))) uint16_t h[kBRows][kCh + 8], l[kBRows][kCh + 8];
+    } p;
+  } ab;
   int sidx[kCh];
   float sm[kMaxG], sl[kMaxG];
 };
+
+// Puts the group's queries into sm: element e = tq + 256 i of the G x 128
+// query block is qv[i] (e past the block: ignored).  f32 caches keep them as
+// f32, bf16 caches as the bf16 hi + lo MFMA operands.  All 256 threads call
+// (no barrier).
+template <bool KF32, int NQ>
+__device__ __forceinline__ void attn_put_q(AttnSmem<KF32>& sm, const float (&qv)[NQ], int G) {
+  const int tq = threadIdx.x & 255;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = tq + 256 * i;
+    if (e < G * kD) {
+      if constexpr (KF32) {
+        sm.sq[e / kD][e % kD] = qv[i];
+      } else {
+        uint32_t hi, lo;
+        split_bf16(qv[i], hi, lo);
+        sm.ab.q.h[e / kD][e % kD] = (uint16_t)hi;
+        sm.ab.q.l[e / kD][e % kD] = (uint16_t)lo;
+      }
+    }
+  }
+}
 
 template <bool KF32, bool COH>
 __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, int k0, int nk,
@@ -906,11 +939,7 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     sm.sidx[tq] = idx;
   }
   const int h_end = min(h_hi, G);  // this workgroup's query heads [h_lo, h_end)
-  if (!q_ready) {
-#pragma unroll
-    for (int i = 0; i < kQPer; ++i)
-      if (tq + 256 * i < G * kD) sm.sq[(tq + 256 * i) / kD][(tq + 256 * i) % kD] = qv[i];
-  }
+  if (!q_ready) attn_put_q(sm, qv, G);
   __syncthreads();
 
   // gather: every thread issues all of its K and V loads before storing any
@@ -925,20 +954,6 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     const int idx = max(sm.sidx[r], 0);
     kreg[i] = *(const u32x4*)(kb + (size_t)idx * kD + cc * kVec);
     vreg[i] = *(const u32x4*)(vb + (size_t)idx * kD + cc * kVec);
-  }
-  if constexpr (!KF32) {
-    // while they are in flight: the queries as bf16 hi + lo for the MFMA
-    // logits, 16 rows (zero outside [h_lo, h_end)), 8 values per thread
-    const int r = tq >> 4;
-    const int c0 = 8 * (tq & 15);
-    const bool hrow = r >= h_lo && r < h_end;
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) split_bf16(hrow ? sm.sq[r][c0 + j] : 0.f, hi[j], lo[j]);
-    *(u32x4*)&sm.sqh[r][c0] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                   hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-    *(u32x4*)&sm.sql[r][c0] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                   lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
   }
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
@@ -961,11 +976,15 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     // (lane: key 16 w + lrow, the same dims); D: lane holds S[4 lgrp + i][key].
     const int lrow = l & 15;
     const int lgrp = l >> 4;
+    const bool hrow = lrow >= h_lo && lrow < h_end;
+    const u32x4 z = {0u, 0u, 0u, 0u};
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ++ks) {
-      const bf16x8 ahi = as_bf16x8(*(const u32x4*)&sm.sqh[lrow][32 * ks + 8 * lgrp]);
-      const bf16x8 alo = as_bf16x8(*(const u32x4*)&sm.sql[lrow][32 * ks + 8 * lgrp]);
+      const u32x4 qh = *(const u32x4*)&sm.ab.q.h[lrow][32 * ks + 8 * lgrp];
+      const u32x4 ql = *(const u32x4*)&sm.ab.q.l[lrow][32 * ks + 8 * lgrp];
+      const bf16x8 ahi = as_bf16x8(hrow ? qh : z);
+      const bf16x8 alo = as_bf16x8(hrow ? ql : z);
       const bf16x8 bk =
           as_bf16x8(*(const u32x4*)(sm.rows + (16 * w + lrow) * kStride + 32 * ks + 8 * lgrp));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bk, acc, 0, 0, 0);
@@ -1017,8 +1036,8 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
     if constexpr (!KF32) {  // the numerators as bf16 hi + lo for the MFMA PV
       uint32_t hi, lo;
       split_bf16(p, hi, lo);
-      sm.sph[h][l] = (uint16_t)hi;
-      sm.spl[h][l] = (uint16_t)lo;
+      sm.ab.p.h[h][l] = (uint16_t)hi;  // the query operands are no longer read
+      sm.ab.p.l[h][l] = (uint16_t)lo;
     }
     if (l == 0) {
       sm.sm[h] = m;
@@ -1042,8 +1061,8 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int ks = 0; ks < kCh / 32; ++ks) {
-        const u32x4 a = *(const u32x4*)&sm.sph[lrow][32 * ks + 8 * lgrp];
-        const u32x4 b = *(const u32x4*)&sm.spl[lrow][32 * ks + 8 * lgrp];
+        const u32x4 a = *(const u32x4*)&sm.ab.p.h[lrow][32 * ks + 8 * lgrp];
+        const u32x4 b = *(const u32x4*)&sm.ab.p.l[lrow][32 * ks + 8 * lgrp];
         phi[ks] = as_bf16x8(hrow ? a : z);
         plo[ks] = as_bf16x8(hrow ? b : z);
       }
