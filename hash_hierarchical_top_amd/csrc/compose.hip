@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
     uint32_t* __restrict__ status, int ppw) {
   __shared__ ScoreTopSmem sm;
-  __shared__ int s_last;
+  __shared__ uint32_t s_order;
   const int bg = blockIdx.y;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
@@ -151,17 +151,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   const bool wg_has = (int)blockIdx.x * ppw < Np;  // block-uniform
   // the workgroup holding the last page, when a key was appended (block-uniform)
   const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / ppw;
-  const void* key = nullptr;
-  uint32_t* crow = nullptr;
-  if (owner) {
+  const void* key = nullptr;  // the appended key's row
+  uint32_t* crow = nullptr;   // and its code
+  if (APPEND && L > 0) {
     const size_t krow = ((size_t)bg * Lcap + (size_t)(L - 1)) * kD;
     key = kv_f32 ? (const void*)((const float*)kcache + krow)
                  : (const void*)((const uint16_t*)kcache + krow);
     crow = codes + ((size_t)bg * Lcap + (size_t)(L - 1)) * kNW;
   }
-  // the rotation of the queries (and of the appended key, as row G) before
-  // the bounds; their code bits once the bounds are done, when the metadata
-  // no longer holds registers
+  // the rotation of the queries (and, in the owner, of the appended key as row
+  // G) before the bounds
   if (wg_has || owner) {
     qenc_core<kD, kScoreThreads>(b, g, Hq, Hkv, q, R, W, sm.rot.qe,
                                  [&](int h, int col, float v) {
@@ -170,7 +169,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
                                    else
                                      sm.rot.xnew[col] = v;
                                  },
-                                 [](int, int, uint32_t) {}, key, kv_f32 != 0);
+                                 [](int, int, uint32_t) {}, owner ? key : nullptr,
+                                 kv_f32 != 0);
     if (owner && wave_has && pb + kScorePagesPerWave > Np - 1)  // the last page's wave
       merge_appended_row<MBF>(bg, NpCap, Np - 1, pb, (L - 1) % kPS == 0, sm.rot.xnew, meta, pl);
   }
@@ -192,19 +192,26 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       Mem<true>::st(dst + 1, hi);
     }
   }
-  if (blockIdx.x == 0 || owner) {  // block-uniform
-    const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
+  // The code bits of the queries (and of the appended key, as row G) need W's
+  // columns in registers, which would not fit beside the metadata; the first
+  // workgroup of the (b, g) to finish its bounds computes them while the
+  // others still run, off the top-P's path (the last arriver does it after
+  // the top-P only when it is also the first, a grid of one).
+  const size_t cbase = ((size_t)b * Hq + (size_t)g * G) * kNW;
+  auto code_pass = [&]() {
     auto code_of = [&](int h, int word, uint32_t bits) {
       if (h == G)
         crow[word] = bits;
-      else if (blockIdx.x == 0)
+      else
         q_codes[cbase + (size_t)h * kNW + word] = bits;
     };
     auto no_rot = [](int, int, float) {};
     qenc_core<32 * kNW, kScoreThreads, decltype(no_rot), decltype(code_of), kNW, kD>(
         b, g, Hq, Hkv, q, R, W, sm.rot.qe, no_rot, code_of, key, kv_f32 != 0);
-  }
-  const bool last1 = arrive_last(ctl, gridDim.x, &s_last);
+  };
+  const uint32_t order = arrive_order(ctl, gridDim.x, &s_order);
+  const bool last1 = order == gridDim.x - 1u;
+  if (order == 0u && !last1) code_pass();  // block-uniform
   if (!last1) return;
   int32_t* out = kept + (size_t)bg * p_max;
   const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
@@ -224,6 +231,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     top_pages_strided<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
                                            sm.sel.sbuf, sm.sel.top,
                                            [&](int pos, int c) { out[pos] = c; });
+  }
+  if (order == 0u) {  // block-uniform: a grid of one workgroup
+    __syncthreads();  // the top-P's LDS is reused
+    code_pass();
   }
 }
 

@@ -299,6 +299,23 @@ __device__ __forceinline__ void issue_loads_here() { asm volatile("" ::: "memory
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Publishes this workgroup's agent-scope stores and counts it in on *counter;
+// returns its place in the arrival order (0 = first, n_wg - 1 = last; the
+// last also puts the counter back to zero for the next call).  All threads
+// call.
+__device__ __forceinline__ uint32_t arrive_order(uint32_t* counter, uint32_t n_wg,
+                                                 uint32_t* s_order) {
+  wait_all_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = add_agent_u32(counter, 1u);
+    *s_order = prev;
+    if (prev == n_wg - 1u) st_agent_u32(counter, 0u);
+  }
+  __syncthreads();
+  return *s_order;
+}
+
+// Publishes this workgroup's agent-scope stores and counts it in on *counter;
 // true in the workgroup that arrives last (n_wg arrivals), which also puts the
 // counter back to zero for the next call.  All threads call.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n_wg, int* s_last) {
