@@ -248,6 +248,7 @@ bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t t
   };
   const size_t B = (size_t)s.batch;
   w.ctrl = take(kAlign);
+  w.counters = take(B * kHisaCounters * sizeof(uint32_t));
   w.block_scores = take(B * (s.max_ctx / s.block) * sizeof(float));
   w.kept_blocks = take(B * keep_blocks * sizeof(int32_t));
   w.kept_count = take(B * sizeof(int32_t));
@@ -805,14 +806,27 @@ static hhr_status hisa_select_impl(const hhr_hisa_shape* shape, const uint8_t* q
   float* ts = reinterpret_cast<float*>(base + ws.token_scores);
   hipStream_t st = as_stream(stream);
   float* tail = shared ? reinterpret_cast<float*>(base + ws.tail_reps) : nullptr;
-  HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status, st,
-                                           k8, k_scale, tail),
-             "hisa_block_scores launch");
-  HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, bs, seq_len, keep_blocks, kept, kc, status, st),
-             "hisa_top_blocks launch");
-  HHR_LAUNCH(hhr::launch_hisa_token_topk(*shape, q8, q_scale, w, k8, k_scale, seq_len, kept, kc,
-                                         keep_blocks, top_k, sel_idx, sel_count, ts, status, st,
-                                         shared),
+  // H3 inside the block-score launch when the rows are few and short enough
+  if (hhr::hisa_fused_top_blocks(*shape)) {
+    uint32_t* counters = reinterpret_cast<uint32_t*>(base + ws.counters);
+    HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status,
+                                             st, k8, k_scale, tail, keep_blocks, kept, kc,
+                                             counters),
+               "hisa_block_scores launch");
+  } else {
+    HHR_LAUNCH(hhr::launch_hisa_block_scores(*shape, q8, q_scale, w, reps, seq_len, bs, status,
+                                             st, k8, k_scale, tail),
+               "hisa_block_scores launch");
+    HHR_LAUNCH(hhr::launch_hisa_top_blocks(*shape, bs, seq_len, keep_blocks, kept, kc, status,
+                                           st),
+               "hisa_top_blocks launch");
+  }
+  // H5 inside the token-score launch when the rows are few
+  HHR_LAUNCH(hhr::launch_hisa_token_topk(
+                 *shape, q8, q_scale, w, k8, k_scale, seq_len, kept, kc, keep_blocks, top_k,
+                 sel_idx, sel_count, ts, status, st, shared,
+                 hhr::hisa_fused_topk(*shape) ? reinterpret_cast<uint32_t*>(base + ws.counters)
+                                              : nullptr),
              "hisa_token_topk launch");
   return ok();
 }

@@ -144,9 +144,15 @@ constexpr size_t kCtrlTicketsOffset = 64;
 
 // ---- HISA ----
 struct HisaWorkspace {
-  size_t ctrl = 0, block_scores = 0, kept_blocks = 0, kept_count = 0, token_scores = 0,
-         tail_reps = 0, total = 0;
+  size_t ctrl = 0, counters = 0, block_scores = 0, kept_blocks = 0, kept_count = 0,
+         token_scores = 0, tail_reps = 0, total = 0;
 };
+// Arrival counters per HISA query row (zero between calls): [0] the block
+// scores' (fused H3), [1] the token scores' (fused H5).
+constexpr int kHisaCounters = 2;
+// Rows up to which H3 runs inside the block-score launch (hisa_fused_top_blocks).
+constexpr int kHisaFusedMaxRows = 64;
+bool hisa_fused_top_blocks(const hhr_hisa_shape& s);
 bool make_hisa_workspace(const hhr_hisa_shape& s, int32_t keep_blocks, int32_t top_k,
                          HisaWorkspace* ws);
 
@@ -158,7 +164,9 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const int32_t* seq_len, float* block_scores,
                                     uint32_t* status, hipStream_t stream,
                                     const uint8_t* k8 = nullptr, const float* k_scale = nullptr,
-                                    float* tail = nullptr);
+                                    float* tail = nullptr, int32_t keep_blocks = 0,
+                                    int32_t* kept = nullptr, int32_t* kept_count = nullptr,
+                                    uint32_t* counters = nullptr);
 // (With tail: query rows against one shared cache; each row's partly visible
 // last block is first pooled over its visible rows into tail [B][128].)
 hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_scores,
@@ -170,6 +178,9 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                                   const int32_t* kept, const int32_t* kept_count,
                                   int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
                                   int32_t* sel_count, float* token_scores, uint32_t* status,
-                                  hipStream_t stream, bool shared = false);
+                                  hipStream_t stream, bool shared = false,
+                                  uint32_t* counters = nullptr);
+// Rows up to which H5 runs inside the token-score launch (counters non-NULL).
+bool hisa_fused_topk(const hhr_hisa_shape& s);
 
 }  // namespace hhr

@@ -7,6 +7,8 @@
 // Indexer score: s(x) = sum_h w_h ReLU(qhat_h . x), fp8 e4m3fn operands with
 // one positive f32 scale per row.
 
+#include <type_traits>
+
 #include "hhr_device.h"
 #include "hhr_internal.h"
 #include "topk_device.h"
@@ -118,15 +120,31 @@ __device__ __forceinline__ float add_swap16(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// TOP: H3 in the same launch.  Every workgroup publishes its block scores
+// (agent-scope stores) and counts in on its row's counter; the last one to
+// arrive takes the row's top keep_blocks blocks (as k_hisa_top_blocks does,
+// with this workgroup's threads), so H3 needs no launch of its own.  Only for
+// rows of at most kBsTopMax blocks.
+constexpr int kBsTopMax = 16 * 64 * kBsWaves;  // top_strided's limit at this width
+
+struct BsTopSmem {
+  __attribute__((aligned(16))) float sbuf[kBsTopMax];  // radix fallback only
+  TopScratch sh;
+};
+
+template <bool TOP>
 __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
     const int32_t* __restrict__ seq_len, const float* __restrict__ tail,
     float* __restrict__ block_scores, uint32_t* __restrict__ status, int Hi, int Lcap, int block,
-    int shared, int gpw) {
+    int shared, int gpw, int keep_blocks, int32_t* __restrict__ kept,
+    int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters) {
   // the query in bf16, converted once per workgroup (rows padded against bank
   // conflicts; heads >= Hi are zero)
   __shared__ __attribute__((aligned(16))) uint16_t sq[kMaxIndexHeads][kD + 8];
+  __shared__ typename std::conditional<TOP, BsTopSmem, char>::type top_sm;
+  __shared__ int s_last;
   const int b = blockIdx.y;
   const int NbCap = Lcap / block;
   const int wg_blk0 = blockIdx.x * kBsWaves * gpw * 16;
@@ -149,23 +167,16 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     const int h = min(i / (kD / 4), Hi - 1);
     qv[k] = *(const uint32_t*)(qb + (size_t)h * kD + 4 * (i % (kD / 4)));
   }
-  // this lane's 16 heads in the epilogue: 16 mt + 4 lgrp + j
-  // (addresses clamped and all loads issued together; heads past Hi zeroed after)
-  float wh[4][4], sh[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = min(16 * mt + 4 * lgrp + j, Hi - 1);
-      wh[mt][j] = w[(size_t)b * Hi + h];
-      sh[mt][j] = q_scale[(size_t)b * Hi + h];
-    }
+  // the weights and scales once per workgroup (one load per thread, zero past
+  // Hi), into LDS after the barrier below; lane (lrow, lgrp) takes those of
+  // its 16 epilogue heads 16 mt + 4 lgrp + j from there
+  __shared__ float sw[kMaxIndexHeads], ss[kMaxIndexHeads];
+  float w_ = 0.f, s_ = 0.f;
+  if (tid < Hi) {
+    w_ = w[(size_t)b * Hi + tid];
+    s_ = q_scale[(size_t)b * Hi + tid];
+  }
   issue_loads_here();
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (16 * mt + 4 * lgrp + j >= Hi) wh[mt][j] = sh[mt][j] = 0.f;
 #pragma unroll
   for (int k = 0; k < kQWords; ++k)
     if ((tid + k * 64 * kBsWaves) / (kD / 4) >= Hi) qv[k] = 0u;
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   auto load_reps = [&](int row) {
     load_rep_row(row == tail_blk ? tail + (size_t)b * kD : repb + (size_t)row * kD);
   };
-  if (wg_blk0 >= Nb) return;  // block-uniform, before the barrier
+  if (!TOP && wg_blk0 >= Nb) return;  // block-uniform, before the barrier
   if (wg_blk0 + wv * 16 + lrow == tail_blk) load_reps(tail_blk);
 #pragma unroll
   for (int k = 0; k < kQWords; ++k) {
@@ -205,7 +216,19 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     }
     *(u32x2*)&sq[h][d] = pk;
   }
+  if (tid < kMaxIndexHeads) {
+    sw[tid] = w_;
+    ss[tid] = s_;
+  }
   __syncthreads();
+  float wh[4][4], sh[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wh[mt][j] = sw[16 * mt + 4 * lgrp + j];
+      sh[mt][j] = ss[16 * mt + 4 * lgrp + j];
+    }
   // A: head 16 mt + lrow, dims 32 ks + 8 lgrp + [0, 8)
   bf16x8 aq[4][4];
 #pragma unroll
@@ -250,7 +273,18 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
       for (int j = 0; j < 4; ++j)
         part = fmaf(wh[mt][j], med_max(acc[mt][j] * sh[mt][j], 0.f, inf), part);
     part = add_swap16(add_swap32(part));
-    if (lgrp == 0 && blk0 + lrow < Nb) block_scores[(size_t)b * NbCap + blk0 + lrow] = part;
+    if (lgrp == 0 && blk0 + lrow < Nb) Mem<TOP>::st(block_scores + (size_t)b * NbCap + blk0 + lrow, part);
+  }
+  if constexpr (TOP) {
+    if (!arrive_last(counters + (size_t)b * kHisaCounters, gridDim.x, &s_last)) return;
+    // H3 of row b from every workgroup's published scores
+    int32_t* out = kept + (size_t)b * keep_blocks;
+    const int cnt = top_strided<64 * kBsWaves, true>(
+        block_scores + (size_t)b * NbCap, Nb, Nb, keep_blocks, AllPresent(),
+        __builtin_huge_valf(), -__builtin_huge_valf(), top_sm.sbuf, top_sm.sh,
+        [&](int pos, int c) { out[pos] = c; });
+    for (int i = cnt + tid; i < keep_blocks; i += 64 * kBsWaves) out[i] = -1;
+    if (tid == 0) kept_count[b] = cnt;
   }
 }
 
@@ -286,16 +320,32 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
 // steps and two lane-swap adds.  The query's fragments and weights stay in
 // registers for all its tiles; each wave keeps the key fragments of its next
 // two tiles in flight.
+//
+// TOPK: H5 in the same launch (few rows).  Every workgroup publishes its token
+// scores (agent-scope stores) and counts in on its row's counter; the last to
+// arrive takes the row's exact top-k as k_hisa_topk does, with its 16 waves.
 typedef long fp8x8;
-constexpr int kTsWaves = 8;
+constexpr int kTsWaves = 8;      // the plain variant
+constexpr int kTsTopWaves = 16;  // with H5: k_hisa_topk's width
 
-__global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
+struct TsTopSmem {
+  __attribute__((aligned(16))) float sbuf[kHisaMaxCand];  // radix fallback only
+  TopScratch sh;
+};
+
+template <int WAVES, bool TOPK>
+__global__ __launch_bounds__(64 * WAVES) void k_hisa_token_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
     float* __restrict__ token_scores, int Hi, int Lcap, int block, int shared, int nslot,
-    int nrows, int xcd_rows) {
+    int nrows, int xcd_rows, int top_k, int32_t* __restrict__ sel_idx,
+    int32_t* __restrict__ sel_count, uint32_t* __restrict__ counters) {
+  static_assert(!TOPK || 64 * WAVES == kHisaThreads, "H5 runs at k_hisa_topk's width");
+  constexpr int kTsWavesT = WAVES;
+  __shared__ typename std::conditional<TOPK, TsTopSmem, char>::type top_sm;
+  __shared__ int s_last;
   // xcd_rows: rows in contiguous runs per XCD (workgroups go round-robin over
   // the eight XCDs; the grid has 8 x ceil(nrows / 8) rows): neighbouring rows
   // keep mostly the same blocks and share an L2
@@ -311,55 +361,49 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   const int lgrp = l >> 4;
   const int tiles_per_block = block / 16;
 
-  // The query's fragments and weights and the block of this wave's first tile
-  // load before the row's length and kept count are known (every address
-  // stays inside its buffer), so they share that round trip.
-  // A: head 16 ht + lrow; this lane's 16 heads for the epilogue: 16 ht + 4 lgrp + j
-  // (every address clamped into its row and the loads issued together; heads
-  // past Hi are zeroed afterwards)
-  fp8x8 aq[4][4];
-  float wq[4][4], sq[4][4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = min(16 * ht + lrow, Hi - 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      aq[ht][ks] = *(const fp8x8*)(q8 + ((size_t)b * Hi + h) * kD + 32 * ks + 8 * lgrp);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int he = min(16 * ht + 4 * lgrp + j, Hi - 1);
-      wq[ht][j] = w[(size_t)b * Hi + he];
-      sq[ht][j] = q_scale[(size_t)b * Hi + he];
-    }
+  // The query (fp8, Hi x 128 bytes), its weights and scales and this
+  // workgroup's kept blocks load once per workgroup, coalesced and all
+  // together, before the row's length and kept count are known (addresses
+  // clamped into the buffers); the waves then take their fragments from LDS.
+  __shared__ __attribute__((aligned(16))) uint8_t sq8[kMaxIndexHeads][kD + 16];
+  __shared__ float swsq[kMaxIndexHeads];
+  u32x4 qc = {0u, 0u, 0u, 0u};
+  const int nq16 = Hi * kD / 16;  // 16-byte chunks of the query
+  if (tid < nq16) qc = *(const u32x4*)(q8 + (size_t)b * Hi * kD + 16 * tid);
+  float wv_ = 0.f, sv_ = 0.f;
+  if (tid < Hi) {
+    wv_ = w[(size_t)b * Hi + tid];
+    sv_ = q_scale[(size_t)b * Hi + tid];
   }
-  issue_loads_here();
+  int L = seq_len[b];
+  const int kc = min(kept_count[b], keep_blocks);
+  // (a run longer than the workgroup, prefill only, takes further rounds)
+  for (int i = tid; i < nslot; i += 64 * WAVES)
+    skb[i] = kept[(size_t)b * keep_blocks + min(slot0 + i, keep_blocks - 1)];
+  if (tid < nq16) *(u32x4*)&sq8[(16 * tid) / kD][(16 * tid) % kD] = qc;
+  if (tid < kMaxIndexHeads) swsq[tid] = tid < Hi ? wv_ * sv_ : 0.f;
+  __syncthreads();
+  // A: head 16 ht + lrow (zero past Hi); this lane's 16 heads for the
+  // epilogue: 16 ht + 4 lgrp + j
+  fp8x8 aq[4][4];
   float wsq[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    if (16 * ht + lrow >= Hi) {
+    const bool hv = 16 * ht + lrow < Hi;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) aq[ht][ks] = 0;
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      aq[ht][ks] = hv ? *(const fp8x8*)&sq8[16 * ht + lrow][32 * ks + 8 * lgrp] : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      wsq[ht][j] = 16 * ht + 4 * lgrp + j < Hi ? wq[ht][j] * sq[ht][j] : 0.f;
+    for (int j = 0; j < 4; ++j) wsq[ht][j] = swsq[16 * ht + 4 * lgrp + j];
   }
-  const int pslot = min(slot0 + wv / tiles_per_block, keep_blocks - 1);
-  const int pblk = kept[(size_t)b * keep_blocks + pslot];
-  int L = seq_len[b];
   if (L < 0 || L > Lcap) L = 0;
-  const int kc = min(kept_count[b], keep_blocks);
   const int slot1 = min(slot0 + nslot, kc);
-  if (slot0 >= slot1) return;
-
+  if (!TOPK && slot0 >= slot1) return;
+  if (slot0 < slot1) {  // block-uniform
   const size_t cb = shared ? 0 : (size_t)b;  // the query row's cache
   const uint8_t* kb = k8 + cb * Lcap * kD;
   const float* ksb = k_scale + cb * Lcap;
   const int ntiles = (slot1 - slot0) * tiles_per_block;
-  // this workgroup's kept blocks, so that a tile's token needs no load of its own
-  for (int i = tid; i < slot1 - slot0; i += 64 * kTsWaves)
-    skb[i] = slot0 + i == pslot ? pblk : kept[(size_t)b * keep_blocks + slot0 + i];
-  __syncthreads();
   auto tile_token = [&](int i) {
     return skb[i / tiles_per_block] * block + 16 * (i % tiles_per_block) + lrow;
   };
@@ -376,11 +420,11 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
   fp8x8 kf[4], k1[4];
   float s0 = 0.f, s1 = 0.f;
   if (i < ntiles) load_tile(i, kf, s0);
-  if (i + kTsWaves < ntiles) load_tile(i + kTsWaves, k1, s1);
-  for (; i < ntiles; i += kTsWaves) {
+  if (i + kTsWavesT < ntiles) load_tile(i + kTsWavesT, k1, s1);
+  for (; i < ntiles; i += kTsWavesT) {
     fp8x8 k2[4];
     float s2 = 0.f;
-    if (i + 2 * kTsWaves < ntiles) load_tile(i + 2 * kTsWaves, k2, s2);
+    if (i + 2 * kTsWavesT < ntiles) load_tile(i + 2 * kTsWavesT, k2, s2);
     floatx4 acc[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -401,8 +445,10 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
     part = add_swap16(add_swap32(part)) * sk;
     if (lgrp == 0) {
       const int slot = slot0 + i / tiles_per_block;
-      token_scores[((size_t)b * keep_blocks + slot) * block + 16 * (i % tiles_per_block) + lrow] =
-          valid ? part : -__builtin_huge_valf();
+      Mem<TOPK>::st(
+          token_scores + ((size_t)b * keep_blocks + slot) * block + 16 * (i % tiles_per_block) +
+              lrow,
+          valid ? part : -__builtin_huge_valf());
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -411,6 +457,26 @@ __global__ __launch_bounds__(64 * kTsWaves) void k_hisa_token_scores(
     }
     s0 = s1;
     s1 = s2;
+  }
+  }
+  if constexpr (TOPK) {
+    if (!arrive_last(counters + (size_t)b * kHisaCounters + 1, gridDim.x, &s_last)) return;
+    // H5 of row b from every workgroup's published scores (k_hisa_topk's steps)
+    const int kcv = L > 0 ? kc : 0;
+    const int ncand = kcv * block;
+    const float* ts = token_scores + (size_t)b * keep_blocks * block;
+    auto load_kept = [&]() {  // skb is free now: all of the row's kept blocks
+      for (int i = tid; i < kcv; i += 64 * WAVES) skb[i] = kept[(size_t)b * keep_blocks + i];
+    };
+    auto present = [](float v) { return v != -__builtin_huge_valf(); };
+    int32_t* out = sel_idx + (size_t)b * top_k;
+    __syncthreads();  // every wave is done with skb
+    const int cnt = top_strided<64 * WAVES, true>(
+        ts, keep_blocks * block, ncand, top_k, present, __builtin_huge_valf(),
+        -__builtin_huge_valf(), top_sm.sbuf, top_sm.sh,
+        [&](int pos, int c) { out[pos] = skb[c / block] * block + c % block; }, load_kept);
+    for (int i = cnt + tid; i < top_k; i += 64 * WAVES) out[i] = -1;
+    if (tid == 0) sel_count[b] = cnt;
   }
 }
 
@@ -462,11 +528,16 @@ hipError_t launch_hisa_pool(const hhr_hisa_shape& s, const uint8_t* k8, const fl
   return hipGetLastError();
 }
 
+bool hisa_fused_top_blocks(const hhr_hisa_shape& s) {
+  return s.batch <= kHisaFusedMaxRows && s.max_ctx / s.block <= kBsTopMax;
+}
+
 hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
                                     const float* q_scale, const float* w, const float* reps,
                                     const int32_t* seq_len, float* block_scores,
                                     uint32_t* status, hipStream_t stream, const uint8_t* k8,
-                                    const float* k_scale, float* tail) {
+                                    const float* k_scale, float* tail, int32_t keep_blocks,
+                                    int32_t* kept, int32_t* kept_count, uint32_t* counters) {
   const bool shared = tail != nullptr;
   if (shared) {
     hipLaunchKernelGGL(k_hisa_pool_tail, dim3(s.batch), dim3(kD), 0, stream, k8, k_scale,
@@ -479,10 +550,16 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
   // query conversion is shared; few: one group per wave for parallelism
   const int gpw = s.batch >= 64 ? 4 : 1;
   const int per_wg = 16 * kBsWaves * gpw;
-  hipLaunchKernelGGL(k_hisa_block_scores, dim3((NbCap + per_wg - 1) / per_wg, s.batch),
-                     dim3(64 * kBsWaves), 0, stream, q8, q_scale, w, reps, seq_len, tail,
-                     block_scores, status, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0,
-                     gpw);
+  const dim3 grid((NbCap + per_wg - 1) / per_wg, s.batch);
+  if (kept != nullptr)  // H3 in this launch (hisa_fused_top_blocks)
+    hipLaunchKernelGGL(k_hisa_block_scores<true>, grid, dim3(64 * kBsWaves), 0, stream, q8,
+                       q_scale, w, reps, seq_len, tail, block_scores, status, s.n_index_heads,
+                       s.max_ctx, s.block, shared ? 1 : 0, gpw, keep_blocks, kept, kept_count,
+                       counters);
+  else
+    hipLaunchKernelGGL(k_hisa_block_scores<false>, grid, dim3(64 * kBsWaves), 0, stream, q8,
+                       q_scale, w, reps, seq_len, tail, block_scores, status, s.n_index_heads,
+                       s.max_ctx, s.block, shared ? 1 : 0, gpw, 0, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -495,14 +572,27 @@ hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_sc
   return hipGetLastError();
 }
 
+bool hisa_fused_topk(const hhr_hisa_shape& s) { return s.batch <= kHisaFusedMaxRows; }
+
 hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                                   const float* q_scale, const float* w, const uint8_t* k8,
                                   const float* k_scale, const int32_t* seq_len,
                                   const int32_t* kept, const int32_t* kept_count,
                                   int32_t keep_blocks, int32_t top_k, int32_t* sel_idx,
                                   int32_t* sel_count, float* token_scores, uint32_t* status,
-                                  hipStream_t stream, bool shared) {
+                                  hipStream_t stream, bool shared, uint32_t* counters) {
   (void)status;
+  if (counters != nullptr) {  // H5 in the token-score launch (hisa_fused_topk)
+    // a workgroup's 16 waves take one tile each: enough kept blocks to fill them
+    const int nslot = std::max(1, kTsTopWaves / (s.block / 16));
+    const int nsplit = (keep_blocks + nslot - 1) / nslot;
+    hipLaunchKernelGGL((k_hisa_token_scores<kTsTopWaves, true>), dim3(nsplit, s.batch),
+                       dim3(64 * kTsTopWaves), 0, stream, q8, q_scale, w, k8, k_scale, seq_len,
+                       kept, kept_count, keep_blocks, token_scores, s.n_index_heads, s.max_ctx,
+                       s.block, shared ? 1 : 0, nslot, s.batch, 0, top_k, sel_idx, sel_count,
+                       counters);
+    return hipGetLastError();
+  }
   // enough workgroups to fill the chip: a run of kept blocks per workgroup,
   // all of a row's blocks once there are many rows
   const int nsplit = std::max(1, std::min<int>(keep_blocks, (512 + s.batch - 1) / s.batch));
@@ -510,10 +600,10 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
   // many rows: spread them over the 8 XCDs in contiguous runs
   const int xcd_rows = s.batch >= 64;
   const int rows = xcd_rows ? (s.batch + 7) / 8 * 8 : s.batch;
-  hipLaunchKernelGGL(k_hisa_token_scores, dim3(nsplit, rows), dim3(64 * kTsWaves), 0, stream, q8,
-                     q_scale, w, k8, k_scale, seq_len, kept, kept_count, keep_blocks,
-                     token_scores, s.n_index_heads, s.max_ctx, s.block, shared ? 1 : 0, nslot,
-                     s.batch, xcd_rows);
+  hipLaunchKernelGGL((k_hisa_token_scores<kTsWaves, false>), dim3(nsplit, rows),
+                     dim3(64 * kTsWaves), 0, stream, q8, q_scale, w, k8, k_scale, seq_len, kept,
+                     kept_count, keep_blocks, token_scores, s.n_index_heads, s.max_ctx, s.block,
+                     shared ? 1 : 0, nslot, s.batch, xcd_rows, 0, nullptr, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_hisa_topk, dim3(s.batch), dim3(kHisaThreads), 0, stream, token_scores,

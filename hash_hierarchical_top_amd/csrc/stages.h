@@ -1021,28 +1021,53 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
   }
   __syncthreads();
 
-  // V rows replace K rows; chunk softmax numerators (one wave per head, lane = key)
+  // V rows replace K rows; chunk softmax numerators
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int c = tq + 256 * i;
     *(u32x4*)(sm.rows + (c / kChunksPerRow) * kStride + (c % kChunksPerRow) * kVec) = vreg[i];
   }
+  if constexpr (!KF32) {
+    // all query heads at once: thread (head tq / 16, keys 4 (tq % 16) ..), the
+    // max and sum over the head's 16 lanes; the numerators go out as the bf16
+    // hi + lo MFMA operands
+    const int h = tq >> 4;
+    const int k4 = 4 * (tq & 15);
+    if (h >= h_lo && h < h_end) {
+      const floatx4 x = *(const floatx4*)&sm.sp[h][k4];
+      float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+      float p[4], s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (x[i] == -__builtin_huge_valf()) ? 0.f : expf(x[i] - m);
+        s += p[i];
+      }
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_bf16(p[i], hi[i], lo[i]);
+      *(u32x2*)&sm.ab.p.h[h][k4] = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *(u32x2*)&sm.ab.p.l[h][k4] = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      if ((tq & 15) == 0) {
+        sm.sm[h] = m;
+        sm.sl[h] = s;
+      }
+    }
+  } else {
   for (int h = h_lo + w; h < h_end; h += 4) {
     const float x = sm.sp[h][l];
     const float m = wave_max(x);
     const float p = (x == -__builtin_huge_valf()) ? 0.f : expf(x - m);
     const float s = wave_sum(p);
     sm.sp[h][l] = p;
-    if constexpr (!KF32) {  // the numerators as bf16 hi + lo for the MFMA PV
-      uint32_t hi, lo;
-      split_bf16(p, hi, lo);
-      sm.ab.p.h[h][l] = (uint16_t)hi;  // the query operands are no longer read
-      sm.ab.p.l[h][l] = (uint16_t)lo;
-    }
     if (l == 0) {
       sm.sm[h] = m;
       sm.sl[h] = s;
     }
+  }
   }
   __syncthreads();
 
