@@ -456,6 +456,12 @@ def main_hisa(args, torch, hhr, synth, dev):
         torch.cuda.synchronize()
         pool_ms.append(pe[0].elapsed_time(pe[1]))
 
+    if args.copy_probe_mib:  # a plain copy of known size, to calibrate HBM byte counters
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
     def step(i):
         lay = layers[i % args.layers]
         hhr.hhr_hisa_select(hs, q8, q_scale, wt, lay["k8"], lay["ks"], lay["reps"], seq,

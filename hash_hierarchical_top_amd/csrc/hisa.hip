@@ -125,15 +125,16 @@ __device__ __forceinline__ float add_swap16(float x) {
 // arrive takes the row's top keep_blocks blocks (as k_hisa_top_blocks does,
 // with this workgroup's threads), so H3 needs no launch of its own.  Only for
 // rows of at most kBsTopMax blocks.
-constexpr int kBsTopMax = 16 * 64 * kBsWaves;  // top_strided's limit at this width
+constexpr int kBsTopWaves = 8;  // with H3 (16 would spill: 128 VGPRs at 1024 threads)
+constexpr int kBsTopMax = 16 * 64 * kBsTopWaves;  // top_strided's limit at that width
 
 struct BsTopSmem {
   __attribute__((aligned(16))) float sbuf[kBsTopMax];  // radix fallback only
   TopScratch sh;
 };
 
-template <bool TOP>
-__global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
+template <int WAVES, bool TOP>
+__global__ __launch_bounds__(64 * WAVES) void k_hisa_block_scores(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const float* __restrict__ reps,
     const int32_t* __restrict__ seq_len, const float* __restrict__ tail,
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   __shared__ int s_last;
   const int b = blockIdx.y;
   const int NbCap = Lcap / block;
-  const int wg_blk0 = blockIdx.x * kBsWaves * gpw * 16;
+  const int wg_blk0 = blockIdx.x * WAVES * gpw * 16;
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int l = tid & 63;
@@ -157,13 +158,13 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   // load before the row's length is known (every address stays inside its
   // buffer; rows past the end are computed and never stored), so they share
   // that round trip.
-  constexpr int kQWords = kMaxIndexHeads * kD / 4 / (64 * kBsWaves);
-  static_assert(kQWords * 64 * kBsWaves == kMaxIndexHeads * kD / 4, "query words per thread");
+  constexpr int kQWords = kMaxIndexHeads * kD / 4 / (64 * WAVES);
+  static_assert(kQWords * 64 * WAVES == kMaxIndexHeads * kD / 4, "query words per thread");
   const uint8_t* qb = q8 + (size_t)b * Hi * kD;
   uint32_t qv[kQWords];
 #pragma unroll
   for (int k = 0; k < kQWords; ++k) {
-    const int i = tid + k * 64 * kBsWaves;
+    const int i = tid + k * 64 * WAVES;
     const int h = min(i / (kD / 4), Hi - 1);
     qv[k] = *(const uint32_t*)(qb + (size_t)h * kD + 4 * (i % (kD / 4)));
   }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   issue_loads_here();
 #pragma unroll
   for (int k = 0; k < kQWords; ++k)
-    if ((tid + k * 64 * kBsWaves) / (kD / 4) >= Hi) qv[k] = 0u;
+    if ((tid + k * 64 * WAVES) / (kD / 4) >= Hi) qv[k] = 0u;
   // B rows: the representative of block blk0 + lrow, dims 32 ks + 8 lgrp + [0, 8).
   // Shared cache (prefill rows): a row's partly visible last block is its own
   // tail mean (k_hisa_pool_tail), not the cache's pooled block.
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
   if (wg_blk0 + wv * 16 + lrow == tail_blk) load_reps(tail_blk);
 #pragma unroll
   for (int k = 0; k < kQWords; ++k) {
-    const int i = tid + k * 64 * kBsWaves;
+    const int i = tid + k * 64 * WAVES;
     const int h = i / (kD / 4);
     const int d = 4 * (i % (kD / 4));
     u32x2 pk;
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
       aq[mt][ks] = as_bf16x8(*(const u32x4*)&sq[16 * mt + lrow][32 * ks + 8 * lgrp]);
   const float inf = opaque_inf();
   for (int grp = 0; grp < gpw; ++grp) {
-    const int blk0 = wg_blk0 + (grp * kBsWaves + wv) * 16;
+    const int blk0 = wg_blk0 + (grp * WAVES + wv) * 16;
     if (blk0 >= Nb) break;  // wave-uniform; no barrier follows
     if (grp > 0) load_reps(min(blk0 + lrow, Nb - 1));
     bf16x8 bhi[4], blo[4];
@@ -279,11 +280,11 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_hisa_block_scores(
     if (!arrive_last(counters + (size_t)b * kHisaCounters, gridDim.x, &s_last)) return;
     // H3 of row b from every workgroup's published scores
     int32_t* out = kept + (size_t)b * keep_blocks;
-    const int cnt = top_strided<64 * kBsWaves, true>(
+    const int cnt = top_strided<64 * WAVES, true>(
         block_scores + (size_t)b * NbCap, Nb, Nb, keep_blocks, AllPresent(),
         __builtin_huge_valf(), -__builtin_huge_valf(), top_sm.sbuf, top_sm.sh,
         [&](int pos, int c) { out[pos] = c; });
-    for (int i = cnt + tid; i < keep_blocks; i += 64 * kBsWaves) out[i] = -1;
+    for (int i = cnt + tid; i < keep_blocks; i += 64 * WAVES) out[i] = -1;
     if (tid == 0) kept_count[b] = cnt;
   }
 }
@@ -549,15 +550,18 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
   // many queries: each workgroup covers 4 groups of 16 blocks per wave, so the
   // query conversion is shared; few: one group per wave for parallelism
   const int gpw = s.batch >= 64 ? 4 : 1;
-  const int per_wg = 16 * kBsWaves * gpw;
+  const int waves = kept != nullptr ? kBsTopWaves : kBsWaves;
+  const int per_wg = 16 * waves * gpw;
   const dim3 grid((NbCap + per_wg - 1) / per_wg, s.batch);
   if (kept != nullptr)  // H3 in this launch (hisa_fused_top_blocks)
-    hipLaunchKernelGGL(k_hisa_block_scores<true>, grid, dim3(64 * kBsWaves), 0, stream, q8,
+    hipLaunchKernelGGL((k_hisa_block_scores<kBsTopWaves, true>), grid, dim3(64 * kBsTopWaves), 0,
+                       stream, q8,
                        q_scale, w, reps, seq_len, tail, block_scores, status, s.n_index_heads,
                        s.max_ctx, s.block, shared ? 1 : 0, gpw, keep_blocks, kept, kept_count,
                        counters);
   else
-    hipLaunchKernelGGL(k_hisa_block_scores<false>, grid, dim3(64 * kBsWaves), 0, stream, q8,
+    hipLaunchKernelGGL((k_hisa_block_scores<kBsWaves, false>), grid, dim3(64 * kBsWaves), 0,
+                       stream, q8,
                        q_scale, w, reps, seq_len, tail, block_scores, status, s.n_index_heads,
                        s.max_ctx, s.block, shared ? 1 : 0, gpw, 0, nullptr, nullptr, nullptr);
   return hipGetLastError();

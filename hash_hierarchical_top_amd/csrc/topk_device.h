@@ -36,7 +36,7 @@ constexpr int kStridedCnt = 256;  // (slot, wave) counts of top_largest_strided
 struct TopScratch {
   int hist[kLinBins];
   uint32_t cnt[kStridedCnt];
-  float list_v[kLinListMax];
+  __attribute__((aligned(16))) float list_v[kLinListMax + 4];  // + 4: whole 16-byte reads
   int list_n;
   float w_min[16], w_max[16];
   int w_n[16];
@@ -253,15 +253,21 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Pre
       for (int j = 0; j < NV; ++j)
         if (bin[j] == bstar) sh.list_v[atomicAdd(&sh.list_n, 1)] = x[j];
       __syncthreads();
-      // T = the value with (#greater in b*) < need <= (#greater) + (#equal)
+      // T = the value with (#greater in b*) < need <= (#greater) + (#equal);
+      // the list is read four entries per LDS load (entries past cstar are
+      // masked; the list has room for them)
       for (int j = tid; j < cstar; j += NT) {
         const float vj = sh.list_v[j];
         int gtr = 0, eql = 0;
-#pragma unroll 1
-        for (int k = 0; k < cstar; ++k) {
-          const float vk = sh.list_v[k];
-          gtr += vk > vj;
-          eql += vk == vj;
+#pragma unroll 2
+        for (int k0 = 0; k0 < cstar; k0 += 4) {
+          const floatx4 v4 = *(const floatx4*)&sh.list_v[k0];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool in = k0 + i < cstar;
+            gtr += (in && v4[i] > vj) ? 1 : 0;
+            eql += (in && v4[i] == vj) ? 1 : 0;
+          }
         }
         if (gtr < need && need <= gtr + eql) {  // all equal copies agree
           sh.T = orderable_key(vj);
