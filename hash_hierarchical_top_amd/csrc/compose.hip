@@ -270,7 +270,8 @@ __global__ __launch_bounds__(256) void k_attn_pick(
 #pragma unroll
   for (int i = 0; i < kQPer; ++i) qv[i] = qg[min(tid + 256 * i, G * kD - 1)];
   attn_put_q(sm, qv, G);
-  const int count = pick_window(p_max, nbins, top_k, k0, kept, dist, cum, bg, pr, sm.sidx, ps);
+  const int count =
+      pick_window(p_max, nbins, top_k, k0, kept, dist, hist, cum, bg, pr, sm.sidx, ps);
   if (tid < kCh && k0 + tid < top_k) sel_idx[(size_t)bg * top_k + k0 + tid] = sm.sidx[tid];
   if (blockIdx.x == 0 && tid == 0) sel_count[bg] = count;
   if (k0 >= count) return;  // block-uniform

@@ -621,20 +621,22 @@ __device__ __forceinline__ int clamped_len(const int32_t* seq_len, int b, int Lc
 // Candidate c is taken iff H < T, or H == T and fewer than `need` candidates
 // with H == T precede it, T and need being the cut of the whole histogram.
 //   pick_load (at kernel start, with the caller's other loads): the sequence
-//     length and kept count, this thread's histogram bins, and -- guessed
-//     from the window's place among the output ranks, as if the taken
-//     candidates were spread evenly -- kPickPre blocks of distances and kept
-//     pages around the window, so that usually no later load is needed.
-//   pick_window: the cut (block scan of the histogram); per block, from two
-//     entries of its cumulative histogram, the counts below and at the cut and
-//     so its first output rank (wave 0); then every block that reaches into
-//     the window places its taken candidates, ranked within the block by wave
-//     ballots (prefetched blocks all at once; others loaded here).
+//     length and kept count, the histogram (wave 0, kPickMaxPer bins per lane
+//     when 64 lanes hold them all), and -- guessed from the window's place
+//     among the output ranks, as if the taken candidates were spread evenly
+//     -- kPickPre blocks of distances and kept pages around the window, so
+//     that usually no later load is needed.
+//   pick_window: wave 0 alone finds the cut (lane-local runs of bins and one
+//     wave scan) and, per block, from two entries of its cumulative
+//     histogram, the counts below and at the cut and so its first output
+//     rank; after one barrier every block that reaches into the window places
+//     its taken candidates, ranked within the block by wave ballots
+//     (prefetched blocks all at once; others loaded here).
 // The result is sidx[i] = the position of output rank k0 + i (-1 past the
 // selection); pick_window returns the selection size min(top_k, #valid).
 // All NT = 256 threads call both.
 constexpr int kPickPre = 8;  // blocks prefetched
-constexpr int kPickMaxPer = (kHamBins + 255) / 256;  // histogram bins per thread
+constexpr int kPickMaxPer = 9;  // histogram bins per lane of wave 0: 576 >= 128 G + 1 for G <= 4
 
 struct PickRegs {
   int P;
@@ -645,8 +647,7 @@ struct PickRegs {
 };
 
 struct PickSmem {
-  int scan[17];
-  int s_T, s_need, s_blo, s_bhi;
+  int s_T, s_need, s_count, s_blo, s_bhi;
   int blk_first[2 * kWave];  // first output rank of each block
   int blk_eq[2 * kWave];     // candidates with H == T in earlier blocks
   int wcnt[kPickPre][4];     // per block and wave: (H < T) | (H == T) << 16
@@ -663,13 +664,18 @@ __device__ __forceinline__ void pick_load(int b, int bg, int p_max, int Lcap, in
   const int L = clamped_len(seq_len, b, Lcap, status);
   const int kc = kept_count[bg];
   const int* hb = hist + (size_t)bg * nbins;
-  const int per = (nbins + NT - 1) / NT;
+  // wave 0 takes the histogram, kPickMaxPer consecutive bins per lane (when
+  // they fit; else pick_window loads them itself)
+  const int perw = (nbins + kWave - 1) / kWave;
+  if (tid < kWave && perw <= kPickMaxPer) {
 #pragma unroll
-  for (int i = 0; i < kPickMaxPer; ++i) pr.cnt_bin[i] = hb[min(tid * per + i, nbins - 1)];
-  issue_loads_here();
+    for (int i = 0; i < kPickMaxPer; ++i)
+      pr.cnt_bin[i] = hb[min(tid * kPickMaxPer + i, nbins - 1)];
+    issue_loads_here();
 #pragma unroll
-  for (int i = 0; i < kPickMaxPer; ++i)
-    if (!(i < per && tid * per + i < nbins)) pr.cnt_bin[i] = 0;
+    for (int i = 0; i < kPickMaxPer; ++i)
+      if (tid * kPickMaxPer + i >= nbins) pr.cnt_bin[i] = 0;
+  }
   const int P = L > 0 ? max(0, min(kc, p_max)) : 0;
   pr.P = P;
   const int ncand = P * kPS;
@@ -690,94 +696,118 @@ __device__ __forceinline__ void pick_load(int b, int bg, int p_max, int Lcap, in
 
 __device__ __forceinline__ int pick_window(int p_max, int nbins, int top_k, int k0,
                                            const int32_t* kept, const uint16_t* dist,
-                                           const uint16_t* cum, int bg, const PickRegs& pr,
-                                           int* sidx, PickSmem& ps) {
-  constexpr int NT = kCumBlock;
+                                           const int* hist, const uint16_t* cum, int bg,
+                                           const PickRegs& pr, int* sidx, PickSmem& ps) {
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
   const int P = pr.P;
   const int ncand = P * kPS;
   const int nblk = (ncand + kCumBlock - 1) / kCumBlock;  // <= 2 * kWave
-  const int per = (nbins + NT - 1) / NT;
-  const int b0 = tid * per;
   if (tid < kAttnChunk) sidx[tid] = -1;
-  // the cut: smallest T with #(H <= T) >= top_k, and how many H == T are taken
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < kPickMaxPer; ++i) local += pr.cnt_bin[i];
-  int total;
-  const int ex = block_exclusive_scan<NT, int>(local, ps.scan, &total);
-  if (tid == 0) {
-    ps.s_T = nbins;  // every valid H is < nbins: take all valid candidates
-    ps.s_need = 0;
-  }
-  __syncthreads();
-  if (total > top_k) {
-    int run = ex;
-#pragma unroll
-    for (int i = 0; i < kPickMaxPer; ++i) {
-      if (run < top_k && run + pr.cnt_bin[i] >= top_k && pr.cnt_bin[i] > 0) {
-        ps.s_T = b0 + i;
-        ps.s_need = top_k - run;
-      }
-      run += pr.cnt_bin[i];
-    }
-  }
-  __syncthreads();
-  const int Th = ps.s_T;
-  const int need = ps.s_need;
-  const int count = min(top_k, total);
-  if (k0 >= count) return count;  // block-uniform: nothing in the window
 
-  // wave 0: per block, #(H < T) and #(H == T) from its cumulative histogram,
-  // then its first output rank; the window's blocks are [s_blo, s_bhi]
+  // wave 0 alone: the cut -- the smallest T with #(H <= T) >= top_k and how
+  // many H == T are taken -- from lane-local runs of bins and one wave scan;
+  // then, per block, #(H < T) and #(H == T) from its cumulative histogram and
+  // so its first output rank; the window's blocks are [s_blo, s_bhi]
   if (w == 0) {
-    const uint16_t* cb = cum + (size_t)bg * ham_cum_blocks(p_max) * nbins;
-    int lt[2], eq[2];
+    // lane l holds bins [l * perw, l * perw + perw): pick_load's kPickMaxPer
+    // when they fit, else loaded here
+    const int perw = (nbins + kWave - 1) / kWave <= kPickMaxPer ? kPickMaxPer
+                                                                : (nbins + kWave - 1) / kWave;
+    const int* hb = hist + (size_t)bg * nbins;
+    auto bin = [&](int i) -> int {  // lane l's bin l * perw + i, when not in pr.cnt_bin
+      const int bi = l * perw + i;
+      return bi < nbins ? hb[bi] : 0;
+    };
+    int local = 0;
+    if (perw == kPickMaxPer) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int blk = r * kWave + l;
-      const uint16_t* row = cb + (size_t)min(blk, max(nblk - 1, 0)) * nbins;
-      lt[r] = row[max(min(Th, nbins) - 1, 0)];
-      eq[r] = row[min(Th, nbins - 1)];
+      for (int i = 0; i < kPickMaxPer; ++i) local += pr.cnt_bin[i];
+    } else {
+      for (int i = 0; i < perw; ++i) local += bin(i);
     }
-    issue_loads_here();
+    const int incl = wave_inclusive_scan(local);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    int Tl = nbins, needl = 0;
+    const bool mine = total > top_k && incl - local < top_k && incl >= top_k;
+    if (mine) {  // the one lane whose bins cross top_k
+      int run = incl - local;
+      auto step = [&](int i, int c) {
+        if (run < top_k && run + c >= top_k && c > 0) {
+          Tl = l * perw + i;
+          needl = top_k - run;
+        }
+        run += c;
+      };
+      if (perw == kPickMaxPer) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int blk = r * kWave + l;
-      const int below = Th == 0 ? 0 : lt[r];
-      const int upto = Th >= nbins ? below : eq[r];
-      lt[r] = blk < nblk ? below : 0;
-      eq[r] = blk < nblk ? upto - below : 0;
-    }
-    int lt_carry = 0, eq_carry = 0, lo = 2 * kWave, hi = -1;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int blk = r * kWave + l;
-      const int lt_in = wave_inclusive_scan(lt[r]);
-      const int eq_in = wave_inclusive_scan(eq[r]);
-      const int lt_before = lt_carry + lt_in - lt[r];
-      const int eq_before = eq_carry + eq_in - eq[r];
-      const int first = lt_before + min(eq_before, need);
-      const int taken = lt[r] + min(max(need - eq_before, 0), eq[r]);
-      ps.blk_first[blk] = first;
-      ps.blk_eq[blk] = eq_before;
-      if (blk < nblk && taken > 0 && first < k0 + kAttnChunk && first + taken > k0) {
-        lo = min(lo, blk);
-        hi = max(hi, blk);
+        for (int i = 0; i < kPickMaxPer; ++i) step(i, pr.cnt_bin[i]);
+      } else {
+        for (int i = 0; i < perw; ++i) step(i, bin(i));
       }
-      lt_carry += __builtin_amdgcn_readlane(lt_in, kWave - 1);
-      eq_carry += __builtin_amdgcn_readlane(eq_in, kWave - 1);
     }
-    lo = (int)wave_min_u((uint32_t)lo);
-    hi = (int)wave_max_u((uint32_t)(hi + 1)) - 1;
+    const uint64_t who = __ballot(mine);
+    const int src = who ? (int)__builtin_ctzll(who) : 0;
+    // no crossing lane: every valid H is < nbins, take all valid candidates
+    const int Th = who ? __builtin_amdgcn_readlane(Tl, src) : nbins;
+    const int need = who ? __builtin_amdgcn_readlane(needl, src) : 0;
+    const int count = min(top_k, total);
+    int lo = 2 * kWave, hi = -1;
+    if (k0 < count) {  // wave-uniform
+      const uint16_t* cb = cum + (size_t)bg * ham_cum_blocks(p_max) * nbins;
+      int lt[2], eq[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int blk = r * kWave + l;
+        const uint16_t* row = cb + (size_t)min(blk, max(nblk - 1, 0)) * nbins;
+        lt[r] = row[max(min(Th, nbins) - 1, 0)];
+        eq[r] = row[min(Th, nbins - 1)];
+      }
+      issue_loads_here();
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int blk = r * kWave + l;
+        const int below = Th == 0 ? 0 : lt[r];
+        const int upto = Th >= nbins ? below : eq[r];
+        lt[r] = blk < nblk ? below : 0;
+        eq[r] = blk < nblk ? upto - below : 0;
+      }
+      int lt_carry = 0, eq_carry = 0;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int blk = r * kWave + l;
+        const int lt_in = wave_inclusive_scan(lt[r]);
+        const int eq_in = wave_inclusive_scan(eq[r]);
+        const int lt_before = lt_carry + lt_in - lt[r];
+        const int eq_before = eq_carry + eq_in - eq[r];
+        const int first = lt_before + min(eq_before, need);
+        const int taken = lt[r] + min(max(need - eq_before, 0), eq[r]);
+        ps.blk_first[blk] = first;
+        ps.blk_eq[blk] = eq_before;
+        if (blk < nblk && taken > 0 && first < k0 + kAttnChunk && first + taken > k0) {
+          lo = min(lo, blk);
+          hi = max(hi, blk);
+        }
+        lt_carry += __builtin_amdgcn_readlane(lt_in, kWave - 1);
+        eq_carry += __builtin_amdgcn_readlane(eq_in, kWave - 1);
+      }
+      lo = (int)wave_min_u((uint32_t)lo);
+      hi = (int)wave_max_u((uint32_t)(hi + 1)) - 1;
+    }
     if (l == 0) {
+      ps.s_T = Th;
+      ps.s_need = need;
+      ps.s_count = count;
       ps.s_blo = lo;
       ps.s_bhi = hi;
     }
   }
   __syncthreads();
+  const int count = ps.s_count;
+  if (k0 >= count) return count;  // block-uniform: nothing in the window
+  const int Th = ps.s_T;
+  const int need = ps.s_need;
   const int blo = ps.s_blo, bhi = ps.s_bhi;
   const uint64_t below = lanemask_lt();
   // rank of this thread's candidate of block blk (distance hv) within the
@@ -798,13 +828,16 @@ __device__ __forceinline__ int pick_window(int p_max, int nbins, int top_k, int 
     if (l == 0) ps.wcnt[u][w] = (int)((uint32_t)popc64(blt) | ((uint32_t)popc64(beq) << 16));
     return (uint32_t)popc64(blt & below) | ((uint32_t)popc64(beq & below) << 16);
   };
-  // prefetched blocks that reach into the window, all at once
+  // the prefetched blocks that reach into the window, all at once
   uint32_t inw[kPickPre];
 #pragma unroll
   for (int u = 0; u < kPickPre; ++u) {
     const int blk = pr.pb0 + u;
-    const uint32_t hv = blk * kCumBlock + tid < ncand ? pr.h[u] : 0xFFFFu;
-    inw[u] = ballots(u, hv);
+    inw[u] = 0u;
+    if (blk >= blo && blk <= bhi) {  // block-uniform
+      const uint32_t hv = blk * kCumBlock + tid < ncand ? pr.h[u] : 0xFFFFu;
+      inw[u] = ballots(u, hv);
+    }
   }
   __syncthreads();
 #pragma unroll
