@@ -48,11 +48,43 @@ __device__ __forceinline__ int checked_len(const int32_t* seq_len, int b, int Lc
 // Mean of dimension d over index-key rows [r0, r1) (r1 > r0) of one cache:
 // sum_t k_scale[t] * e4m3(k8[t][d]) accumulated in row order, then divided by
 // the row count.  Both the block pooling and a prefill row's partly visible
-// block use it, so equal rows give bit-identical means.
+// block use it, so equal rows give bit-identical means.  The workgroup (128
+// threads = dims) stages the rows in LDS, kPoolRows at a time with every
+// thread's 16-byte loads in flight together; then each thread runs its chain.
+// All threads call (barriers).
+constexpr int kPoolRows = 128;
+
+struct PoolSmem {
+  __attribute__((aligned(16))) uint8_t k[kPoolRows][kD];
+  float s[kPoolRows];
+};
+
 __device__ __forceinline__ float pool_mean(const uint8_t* __restrict__ kb,
-                                           const float* __restrict__ sb, int r0, int r1, int d) {
+                                           const float* __restrict__ sb, int r0, int r1,
+                                           PoolSmem& sm) {
+  constexpr int kChunks = kPoolRows * kD / 16 / kD;  // 16-byte loads per thread per round
+  const int d = threadIdx.x;
   float acc = 0.f;
-  for (int t = r0; t < r1; ++t) acc = fmaf(sb[t], e4m3fn_to_f32(kb[(size_t)t * kD + d]), acc);
+  for (int c0 = r0; c0 < r1; c0 += kPoolRows) {  // block-uniform
+    const int n = min(kPoolRows, r1 - c0);
+    u32x4 v[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int e = d + kD * i;  // 16-byte piece e of the round: row e / 8, piece e % 8
+      v[i] = *(const u32x4*)(kb + (size_t)(c0 + min(e / 8, n - 1)) * kD + 16 * (e % 8));
+    }
+    const float sc = sb[c0 + min(d, n - 1)];
+    __syncthreads();  // the previous round's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int e = d + kD * i;
+      *(u32x4*)&sm.k[e / 8][16 * (e % 8)] = v[i];
+    }
+    sm.s[d] = sc;
+    __syncthreads();
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) acc = fmaf(sm.s[t], e4m3fn_to_f32(sm.k[t][d]), acc);
+  }
   return acc / (float)(r1 - r0);
 }
 
@@ -64,6 +96,7 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
                                                   float* __restrict__ reps,
                                                   uint32_t* __restrict__ status, int Lcap,
                                                   int block) {
+  __shared__ PoolSmem sm;
   const int b = blockIdx.y;
   const int s = start[b];
   const int n = n_new[b];
@@ -78,8 +111,8 @@ __global__ __launch_bounds__(kD) void k_hisa_pool(const uint8_t* __restrict__ k8
   const int r0 = blk * block;
   const int r1 = min(r0 + block, e);
   const int d = threadIdx.x;
-  reps[((size_t)b * (Lcap / block) + blk) * kD + d] =
-      pool_mean(k8 + (size_t)b * Lcap * kD, k_scale + (size_t)b * Lcap, r0, r1, d);
+  const float m = pool_mean(k8 + (size_t)b * Lcap * kD, k_scale + (size_t)b * Lcap, r0, r1, sm);
+  reps[((size_t)b * (Lcap / block) + blk) * kD + d] = m;
 }
 
 // Prefill rows against one shared cache: row r sees tokens t < q_len[r], so
@@ -93,11 +126,12 @@ __global__ __launch_bounds__(kD) void k_hisa_pool_tail(const uint8_t* __restrict
                                                        const int32_t* __restrict__ q_len,
                                                        float* __restrict__ tail, int Lcap,
                                                        int block) {
+  __shared__ PoolSmem sm;
   const int r = blockIdx.x;
   const int L = q_len[r];
   if (L <= 0 || L > Lcap || L % block == 0) return;  // bad lengths: the scorer flags them
   const int r0 = L / block * block;
-  tail[(size_t)r * kD + threadIdx.x] = pool_mean(k8, k_scale, r0, L, threadIdx.x);
+  tail[(size_t)r * kD + threadIdx.x] = pool_mean(k8, k_scale, r0, L, sm);
 }
 
 // H2 on MFMA.  A wave takes groups of 16 blocks of one query:
