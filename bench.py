@@ -260,7 +260,7 @@ def main():
     ms_per_step = total_ms / steps
     value = B * steps / (total_ms / 1e3)
     per_step_us = [rep_ev[r].elapsed_time(rep_ev[r + 1]) * 1e3 / args.layers
-                   for r in range(n_rep)]
+                   for r in range(n_rep)] if graph is not None else []
     dist = None
     if per_step_us:
         pq = np.percentile(per_step_us, [10, 50, 90])

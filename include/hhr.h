@@ -260,12 +260,11 @@ hhr_status hhr_select_pages(const hhr_shape* shape, const float* q, const int32_
  * codes rank the keys of the surviving pages by Hamming distance; [HHR]
  * Figure 1 orders the stages coarse then fine; [HATA abstract]: the codes
  * need only order q.k, which a top-k needs).  Intermediates live in the
- * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk.  When the
- * coarse stage fits one launch (at most 2 x 256 scoring workgroups of 256
- * pages, 128-bit codes) the fine stage runs in it too: the workgroup that
- * takes the top-P then computes the distances of the kept pages' keys from
- * their codes and takes the top-k.  Otherwise it runs as separate launches.
- * Same results. */
+ * workspace.  Outputs sel_idx / sel_count as in hhr_hamming_topk.  The
+ * coarse stage is one launch when it fits (at most 2 x 256 scoring
+ * workgroups of 256 pages, 128-bit codes), else separate launches; the fine
+ * stage is a distance launch and one selection workgroup per (b, g).  Same
+ * results either way. */
 hhr_status hhr_select(const hhr_shape* shape, const float* q, const int32_t* seq_len,
                       const float* R, const float* W, const uint32_t* codes,
                       const void* page_meta, int32_t keep_num, int32_t keep_den,
