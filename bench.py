@@ -20,8 +20,9 @@ calls (which launch it alone) over the same rotating layers; `traffic` is its
 counter-measured HBM bytes per launch from the committed profile, while the
 kernel's sources are unchanged since.  `--meta bf16` runs the same step on
 bfloat16 page metadata rounded outward (half the metadata bytes).
-`cpu_baseline` times the CPU oracle (numpy, 1 thread) on whole decode steps
-of the same workload for a bounded number of seconds.
+`cpu_baseline` times the CPU oracle (numpy fp64) on whole decode steps of the
+same workload for a bounded number of seconds, once with the KV heads spread
+over the host's cores and once on one core.
 """
 from __future__ import annotations
 
@@ -41,41 +42,44 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 
-# Measured HBM traffic of the page-bound scorer comes from a committed counter
-# profile; it is reported only while the kernel sources that build that kernel
-# (the files below) are unchanged since the counters were taken.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_topp_llama8b_128k_hbm_traffic.md")
-SCORER_SOURCES = ["hash_hierarchical_top_amd/csrc/compose.hip",
-                  "hash_hierarchical_top_amd/csrc/stages.h",
-                  "hash_hierarchical_top_amd/csrc/topk_device.h",
-                  "hash_hierarchical_top_amd/csrc/hhr_device.h",
-                  "hash_hierarchical_top_amd/csrc/hhr_internal.h",
-                  "hash_hierarchical_top_amd/csrc/hhr_consts.h"]
+# Measured HBM traffic of a roofline kernel comes from a committed counter profile
+# (a JSON record in a fenced block of the named file under profiles/); it is reported
+# only while the kernel sources that the record lists are unchanged since the counters
+# were taken.
+TRAFFIC_PROFILES = {
+    "llama8b_128k": "score_topp_llama8b_128k_hbm_traffic.md",
+    "llama8b_ragged_b16": "select_pages_ragged_b16_hbm_traffic.md",
+    "hisa_128k": "hisa_token_topk_128k_hbm_traffic.md",
+}
 
 
-def scorer_source_digest() -> str:
+def source_digest(sources) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in SCORER_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, meta_dtype: str):
-    """Calibrated HBM bytes per k_score_topp launch from the counter profile, or None if
-    there is none for this workload and metadata format or the kernel's sources changed
-    since."""
+def measured_traffic(workload: str, kernel: str, meta_dtype: str = "f32"):
+    """Calibrated HBM bytes per launch of `kernel` on `workload` from its counter profile,
+    or None if there is none for this workload, kernel and metadata format, or if the
+    sources listed in the record changed since."""
+    name = TRAFFIC_PROFILES.get(workload)
+    if name is None:
+        return None
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             text = f.read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
     for r in rec if isinstance(rec, list) else [rec]:
-        if (r.get("workload") == workload and r.get("meta_dtype", "f32") == meta_dtype
-                and r.get("source_sha256") == scorer_source_digest()):
+        if (r.get("workload") == workload and r.get("kernel") == kernel
+                and r.get("meta_dtype", "f32") == meta_dtype
+                and r.get("source_sha256") == source_digest(r.get("sources", []))):
             return int(r["traffic_bytes_per_launch"])
     return None
 
@@ -317,12 +321,13 @@ def main():
     # the library runs k_score_topp while the scoring grid is at most two rounds of
     # one 1024-thread workgroup per CU, else the staged coarse launches
     one_launch = -(-NpCap // 256) * B * Hkv <= 512
+    k_name = ("k_score_topp" if one_launch
+              else "hhr_select_pages (k_encode_queries + k_page_scores + k_top_pages)")
     roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.workload, args.meta) if one_launch else None,
-                "kernel": "k_score_topp" if one_launch
-                else "hhr_select_pages (k_encode_queries + k_page_scores + k_top_pages)",
+                "traffic": measured_traffic(args.workload, k_name, args.meta),
+                "kernel": k_name,
                 "bytes_per_launch": k_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}
 
     # the bound computation alone (staged k_page_scores, S3 only), for context
@@ -519,8 +524,9 @@ def main_hisa(args, torch, hhr, synth, dev):
     n_sel = int(cnt.item())
     step_bytes = ((L // blk) * 128 * 4 + w.keep_blocks * blk * (128 + 4) + n_sel * 2 * 128 * 2
                   + Hi * (128 + 8) + Ha * 128 * 4 * 2)
-    # dominant kernel by bytes: the fp8 token scorer + token top-k entry point, timed back to
-    # back on its stream over the rotating layers
+    # dominant kernel by bytes: the fp8 token scorer with the token top-k in its last
+    # workgroup (hhr_hisa_token_topk, one launch at one row), timed back to back on its
+    # stream over the rotating layers
     kept = torch.zeros((1, w.keep_blocks), dtype=torch.int32, device=dev)
     kc = torch.zeros((1,), dtype=torch.int32, device=dev)
     bs = torch.zeros((1, L // blk), dtype=torch.float32, device=dev)
@@ -541,8 +547,9 @@ def main_hisa(args, torch, hhr, synth, dev):
     k_bytes = w.keep_blocks * blk * (128 + 4) + Hi * (128 + 8) + w.keep_blocks * 4 + w.top_k * 4
     roofline = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e6), 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 5), "traffic": None,
-                "kernel": "k_hisa_token_scores + k_hisa_topk (hhr_hisa_token_topk)",
+                "frac": round(k_bytes / (k_ms * 1e6) / HBM_PEAK_GBS, 5),
+                "traffic": measured_traffic(args.workload, "k_hisa_token_scores<16, true>"),
+                "kernel": "k_hisa_token_scores<16, true> (hhr_hisa_token_topk)",
                 "bytes_per_launch": k_bytes, "avg_launch_us": round(k_ms * 1e3, 3),
                 "note": "latency-bound: ~1 MB per launch"}
 

@@ -768,9 +768,16 @@ hhr_status hhr_hisa_token_topk(const hhr_hisa_shape* shape, const uint8_t* q8,
                 ws.total);
   float* ts = token_scores ? token_scores
                            : reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.token_scores);
+  // H5 inside the token-score launch when the rows are few (its arrival
+  // counters live in the workspace)
+  uint32_t* counters =
+      hhr::hisa_fused_topk(*shape)
+          ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws.counters)
+          : nullptr;
   HHR_LAUNCH(hhr::launch_hisa_token_topk(*shape, q8, q_scale, w, k8, k_scale, seq_len,
                                          kept_blocks, kept_count, keep_blocks, top_k, sel_idx,
-                                         sel_count, ts, status_of(workspace), as_stream(stream)),
+                                         sel_count, ts, status_of(workspace), as_stream(stream),
+                                         false, counters),
              "hisa_token_topk launch");
   return ok();
 }

@@ -380,7 +380,11 @@ hhr_status hhr_hisa_top_blocks(const hhr_hisa_shape* shape, const float* block_s
  * top_k by (larger s, lower t), ascending.  [HISA: token-level refinement]
  *   sel_idx [B][top_k] int32 out (-1 padded), sel_count [B] int32 out
  *   token_scores [B][keep_blocks*block] f32 out or NULL (-inf for rows >= seq_len)
- *   workspace >= hhr_hisa_workspace_size(...) */
+ *   workspace >= hhr_hisa_workspace_size(...)
+ * Up to 64 rows this is one launch: the last workgroup of a row to finish its
+ * scores takes that row's top-k (arrival counters in the workspace, zero
+ * between calls); with more rows a score launch, then a top-k launch.  Same
+ * results either way. */
 hhr_status hhr_hisa_token_topk(const hhr_hisa_shape* shape, const uint8_t* q8,
                                const float* q_scale, const float* w, const uint8_t* k8,
                                const float* k_scale, const int32_t* seq_len,
