@@ -190,13 +190,13 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
              max((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
 }
 
-// Lanes below this one in the wave.
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int l = lane_id();
-  return l == 0 ? 0ull : (~0ull >> (64 - l));
-}
-
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+// Set bits of the wave-uniform mask m below this lane.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // Inclusive scan across the wave (32-bit integers): Hillis-Steele inside
 // each 16-lane row with row_shr 1, 2, 4, 8, then row totals carried forward

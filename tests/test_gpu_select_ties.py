@@ -67,3 +67,48 @@ def test_top_pages_exact_on_constructed_scores(gpu_lib):
                 checked += 1
     assert int(status.item()) == 0
     print(f"checked {checked} selections")
+
+
+@pytest.mark.parametrize("group", [4, 3, 8192])
+def test_duplicate_pages_composite_equals_stages(gpu_lib, group):
+    """Keys copied page by page in runs of `group` pages give equal page bounds in runs,
+    so the cut of the top-P falls inside a run of ties (group 8192: every page equal).
+    The one-launch coarse stage of hhr_decode and hhr_select (kept pages handed to the
+    distance launch as bit words) must keep the same pages as the staged top-P, which
+    breaks ties to the lower page: the selections and outputs are bit-identical, and the
+    staged kept pages equal the oracle's top-P of the GPU's own bounds."""
+    print(f"\n[gpu duplicate pages] group={group}", flush=True)
+    from hash_hierarchical_top_amd import synth
+
+    B, Hq, Hkv, Lcap = 2, 8, 2, 8192
+    lens = [8192, 5000]
+    inp = synth.make_hhr_inputs(B, Hq, Hkv, lens, Lcap, "bf16", seed=77)
+    K = inp["K"].reshape(B, Hkv, Lcap // 16, 16, 128)
+    src = (np.arange(Lcap // 16) // group) * group
+    inp["K"] = np.ascontiguousarray(K[:, :, src].reshape(B, Hkv, Lcap, 128))
+    for b, L in enumerate(lens):
+        inp["K"][b, :, L:] = 0
+    p = U.Pipeline(gpu_lib, inp, "bf16", Hq, Hkv, Lcap, 1, 8, 0, 256)
+    p.append_all()
+    p.encode_queries()
+    p.page_scores()
+    p.top_pages()
+    p.hamming_topk()
+    p.sparse_decode()
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        Np = O.n_pages(L, 16)
+        P = O.keep_count(Np, 1, 8, 0)
+        for g in range(Hkv):
+            s = p.scores[b, g, :Np].cpu().numpy().astype(np.float64)
+            assert p.kept[b, g, :P].cpu().tolist() == O.top_pages(s, P).tolist(), (b, g)
+    sel = torch.zeros_like(p.sel)
+    sc = torch.zeros_like(p.sel_count)
+    out = torch.zeros_like(p.out)
+    p.decode(sel, sc, out)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, p.sel_count) and torch.equal(sel, p.sel)
+    assert torch.equal(out, p.out)
+    sel2, sc2 = p.select()
+    assert torch.equal(sc2, p.sel_count) and torch.equal(sel2, p.sel)
+    assert p.status() == 0
