@@ -230,7 +230,6 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.wave_range = take(BHkv * (NpCap / 16) * sizeof(float2));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
-  w.kept_mask = take(BHkv * (size_t)((NpCap + 63) / 64) * sizeof(uint64_t));
   w.attn_part = take(attn_part_bytes(s, w.n_split));
   w.total = off;
   *ws = w;
@@ -398,9 +397,7 @@ hhr_status hhr_hamming_topk(const hhr_shape* shape, const uint32_t* q_codes,
     return fail(HHR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, hs.end);
   char* base = static_cast<char*>(workspace);
   uint16_t* d = dist != nullptr ? dist : reinterpret_cast<uint16_t*>(base + hs.dist);
-  // kept is only read (no mask)
-  HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len,
-                                      const_cast<int32_t*>(kept), nullptr, kept_count, p_max,
+  HHR_LAUNCH(hhr::launch_hamming_topk(*shape, q_codes, codes, seq_len, kept, kept_count, p_max,
                                       top_k, sel_idx, sel_count, d,
                                       reinterpret_cast<int*>(base + hs.hist),
                                       status_of(workspace), as_stream(stream)),
@@ -454,7 +451,6 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->q_codes = reinterpret_cast<uint32_t*>(base + ws->q_codes);
   buf->kept = reinterpret_cast<int32_t*>(base + ws->kept);
   buf->kept_count = reinterpret_cast<int32_t*>(base + ws->kept_count);
-  buf->kept_mask = reinterpret_cast<uint64_t*>(base + ws->kept_mask);
   buf->dist = reinterpret_cast<uint16_t*>(base + ws->ham_dist);
   buf->chist = reinterpret_cast<int*>(base + ws->ham_hist);
   buf->cum = reinterpret_cast<uint16_t*>(base + ws->ham_cum);

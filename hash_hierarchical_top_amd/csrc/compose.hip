@@ -120,11 +120,7 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 // {min, max} (or starts the page with it) in registers before the bound, and
 // stores the page's metadata back.  Nothing else touches that page, so no
 // other workgroup can see it half-updated.
-//
-// MASK: the kept pages go out as words of 64 (kept_mask [B*Hkv][words], bit i
-// of word e = page 64 e + i) instead of as a list, which spares the top-P its
-// per-page output ranks; the distance launch turns them into the list.
-template <bool MBF, bool APPEND, bool MASK>
+template <bool MBF, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
     const float* __restrict__ R, const float* __restrict__ W, void* __restrict__ meta,
@@ -132,8 +128,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     int keep_num, int keep_den, int keep_abs, int p_max, int Hq, int Hkv, int Lcap,
     float* __restrict__ scores, float2* __restrict__ wave_range,
     uint32_t* __restrict__ q_codes, int32_t* __restrict__ kept,
-    int32_t* __restrict__ kept_count, uint64_t* __restrict__ kept_mask,
-    uint32_t* __restrict__ counters, uint32_t* __restrict__ status, int ppw) {
+    int32_t* __restrict__ kept_count, uint32_t* __restrict__ counters,
+    uint32_t* __restrict__ status, int ppw) {
   __shared__ ScoreTopSmem sm;
   __shared__ uint32_t s_order;
   const int bg = blockIdx.y;
@@ -219,8 +215,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   if (!last1) return;
   int32_t* out = kept + (size_t)bg * p_max;
   const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
-  if (!MASK)
-    for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
+  for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
   if (tid == 0) kept_count[bg] = P;
   if (P > 0) {
     // the range of all bounds from the waves' published {lo, hi}, one per thread
@@ -233,16 +228,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       lo = Mem<true>::ld(src);
       hi = Mem<true>::ld(src + 1);
     }
-    if constexpr (MASK) {
-      uint64_t* mw = kept_mask + (size_t)bg * kept_mask_words(NpCap);
-      top_pages_strided<kScoreThreads, true, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
-                                                   sm.sel.sbuf, sm.sel.top,
-                                                   [&](int e, uint64_t m) { mw[e] = m; });
-    } else {
-      top_pages_strided<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
-                                             sm.sel.sbuf, sm.sel.top,
-                                             [&](int pos, int c) { out[pos] = c; });
-    }
+    top_pages_strided<kScoreThreads, true>(scores + (size_t)bg * NpCap, Np, P, lo, hi,
+                                           sm.sel.sbuf, sm.sel.top,
+                                           [&](int pos, int c) { out[pos] = c; });
   }
   if (order == 0u) {  // block-uniform: a grid of one workgroup
     __syncthreads();  // the top-P's LDS is reused
@@ -332,7 +320,7 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
                              const CompositeBuffers& buf, hipStream_t stream,
-                             const AppendArgs* app, bool mask) {
+                             const AppendArgs* app) {
   const int BG = s.batch * s.n_kv_heads;
   const int NpCap = s.max_ctx / kPS;
   const int ppw = score_pages_per_wg(s);
@@ -357,29 +345,20 @@ hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* 
   const void* kc = app ? app->k_cache : nullptr;
   uint32_t* cd = app ? app->codes : nullptr;
   const int kf32 = s.kv_dtype == HHR_F32;
-#define HHR_SCORE_TOPP(MBF, APP, MASK)                                                         \
-  hipLaunchKernelGGL((k_score_topp<MBF, APP, MASK>), grid, dim3(kScoreThreads), 0, stream, q,   \
+#define HHR_SCORE_TOPP(MBF, APP)                                                               \
+  hipLaunchKernelGGL((k_score_topp<MBF, APP>), grid, dim3(kScoreThreads), 0, stream, q,         \
                      seq_len, R, W, m, kc, kf32, cd, keep_num, keep_den, keep_abs, p_max,      \
                      s.n_q_heads, s.n_kv_heads, s.max_ctx, buf.scores, buf.wave_range,         \
-                     buf.q_codes, buf.kept, buf.kept_count, buf.kept_mask, buf.counters,       \
-                     buf.status, ppw)
+                     buf.q_codes, buf.kept, buf.kept_count, buf.counters, buf.status, ppw)
   const bool mbf = s.meta_dtype == HHR_BF16;
-  if (mask) {  // the composite paths; the fused append runs only there
-    if (mbf && app)
-      HHR_SCORE_TOPP(true, true, true);
-    else if (mbf)
-      HHR_SCORE_TOPP(true, false, true);
-    else if (app)
-      HHR_SCORE_TOPP(false, true, true);
-    else
-      HHR_SCORE_TOPP(false, false, true);
-  } else {
-    if (app) return hipErrorInvalidValue;  // the fused append runs in the composite paths only
-    if (mbf)
-      HHR_SCORE_TOPP(true, false, false);
-    else
-      HHR_SCORE_TOPP(false, false, false);
-  }
+  if (mbf && app)
+    HHR_SCORE_TOPP(true, true);
+  else if (mbf)
+    HHR_SCORE_TOPP(true, false);
+  else if (app)
+    HHR_SCORE_TOPP(false, true);
+  else
+    HHR_SCORE_TOPP(false, false);
 #undef HHR_SCORE_TOPP
   return hipGetLastError();
 }
@@ -391,17 +370,14 @@ hipError_t launch_select_composite(const hhr_shape& s, const float* q, const int
                                    int32_t* sel_idx, int32_t* sel_count,
                                    const CompositeBuffers& buf, bool finish,
                                    hipStream_t stream, const AppendArgs* app) {
-  // one-launch coarse stage: kept pages as mask words, listed by the distance launch
-  const bool mask = one_launch_select(s);
   hipError_t e = launch_score_topp(s, q, seq_len, R, W, meta, keep_num, keep_den, keep_abs,
-                                   p_max, buf, stream, app, mask);
+                                   p_max, buf, stream, app);
   if (e != hipSuccess) return e;
-  const uint64_t* km = mask ? buf.kept_mask : nullptr;
   if (finish)
-    return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, km, buf.kept_count,
-                               p_max, top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status,
+    return launch_hamming_topk(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
+                               top_k, sel_idx, sel_count, buf.dist, buf.chist, buf.status,
                                stream);
-  return launch_ham_dist(s, buf.q_codes, codes, seq_len, buf.kept, km, buf.kept_count, p_max,
+  return launch_ham_dist(s, buf.q_codes, codes, seq_len, buf.kept, buf.kept_count, p_max,
                          buf.dist, buf.chist, buf.cum, stream);
 }
 

@@ -21,8 +21,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // holds the device status word at offset 0.
 struct Workspace {
   size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, ham_cum = 0, q_rot = 0, q_codes = 0,
-         scores = 0, wave_range = 0, kept = 0, kept_count = 0, kept_mask = 0, attn_part = 0,
-         total = 0;
+         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, total = 0;
   int32_t p_max = 0, n_split = 0;
 };
 
@@ -65,14 +64,12 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
                             int32_t keep_num, int32_t keep_den, int32_t keep_abs, int32_t p_max,
                             int32_t* kept, int32_t* kept_count, uint32_t* status,
                             hipStream_t stream);
-// kept_mask non-NULL (128-bit codes): the kept pages come as mask words and
-// are written to kept; else kept is read.
 hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
-                           const int32_t* seq_len, int32_t* kept, const uint64_t* kept_mask,
+                           const int32_t* seq_len, const int32_t* kept,
                            const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
                            uint16_t* cum, hipStream_t stream);
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
-                               const int32_t* seq_len, int32_t* kept, const uint64_t* kept_mask,
+                               const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
                                int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* chist,
                                uint32_t* status, hipStream_t stream);
@@ -97,7 +94,6 @@ struct CompositeBuffers {
   uint32_t* q_codes;
   int32_t* kept;
   int32_t* kept_count;
-  uint64_t* kept_mask;  // kept pages as words of 64 (one-launch coarse stage)
   uint16_t* dist;
   int* chist;
   uint16_t* cum;  // per-block cumulative H histograms (hhr_decode's pick)
@@ -112,13 +108,12 @@ struct AppendArgs {
 
 // The coarse stage (S2..S4): kept pages, counts and query codes into buf;
 // with app, the appended keys are encoded first.  One launch (k_score_topp)
-// when one_launch_select(s), else staged launches.  mask (one launch only):
-// the kept pages go to buf.kept_mask as words instead of to buf.kept.
+// when one_launch_select(s), else staged launches.
 hipError_t launch_score_topp(const hhr_shape& s, const float* q, const int32_t* seq_len,
                              const float* R, const float* W, const void* meta, int32_t keep_num,
                              int32_t keep_den, int32_t keep_abs, int32_t p_max,
                              const CompositeBuffers& buf, hipStream_t stream,
-                             const AppendArgs* app = nullptr, bool mask = false);
+                             const AppendArgs* app = nullptr);
 // True when the coarse stage runs as one launch (k_score_topp): the scoring
 // grid is at most two rounds of one workgroup per CU and codes are 128-bit.
 bool one_launch_select(const hhr_shape& s);

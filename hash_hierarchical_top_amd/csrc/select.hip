@@ -81,19 +81,17 @@ __device__ __forceinline__ int kept_pages(const int32_t* kept_count, int bg, int
 
 // Distances of one 64-page chunk of one (b, g) for NW-word codes: grid
 // (chunks, B*Hkv).
-// MASK: the kept pages come as mask words (kept_mask) and are written to kept.
-template <int NW, bool MASK>
+template <int NW>
 __global__ __launch_bounds__(kHamDistThreads) void k_ham_dist(
     const uint32_t* __restrict__ q_codes, const uint32_t* __restrict__ codes,
-    const int32_t* __restrict__ seq_len, int32_t* __restrict__ kept,
-    const uint64_t* __restrict__ kept_mask, const int32_t* __restrict__ kept_count, int p_max,
-    int Hq, int Hkv, int Lcap, uint16_t* __restrict__ dist, int* __restrict__ hist,
-    uint16_t* __restrict__ cum) {
+    const int32_t* __restrict__ seq_len, const int32_t* __restrict__ kept,
+    const int32_t* __restrict__ kept_count, int p_max, int Hq, int Hkv, int Lcap,
+    uint16_t* __restrict__ dist, int* __restrict__ hist, uint16_t* __restrict__ cum) {
   __shared__ HamDistSmem<NW> sm;
   const int bg = blockIdx.y;
-  ham_dist_chunk<kHamDistThreads, false, NW, MASK>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, blockIdx.x,
-                                                   p_max, seq_len, kept_count, q_codes, codes,
-                                                   kept, kept_mask, dist, hist, cum, sm);
+  ham_dist_chunk<kHamDistThreads, false, NW>(bg / Hkv, bg % Hkv, Hq, Hkv, Lcap, blockIdx.x, p_max,
+                                         seq_len, kept_count, q_codes, codes, kept, dist, hist,
+                                         cum, sm);
 }
 
 // Exact top-k of one (b, g) from its distances and chunk histograms.
@@ -139,35 +137,31 @@ hipError_t launch_top_pages(const hhr_shape& s, const float* scores, const int32
 }
 
 hipError_t launch_ham_dist(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
-                           const int32_t* seq_len, int32_t* kept, const uint64_t* kept_mask,
+                           const int32_t* seq_len, const int32_t* kept,
                            const int32_t* kept_count, int32_t p_max, uint16_t* dist, int* hist,
                            uint16_t* cum, hipStream_t stream) {
   const dim3 grid(ham_chunks(p_max), s.batch * s.n_kv_heads);
-#define HHR_HAM_DIST(NW, M)                                                                   \
-  hipLaunchKernelGGL((k_ham_dist<NW, M>), grid, dim3(kHamDistThreads), 0, stream, q_codes,    \
-                     codes, seq_len, kept, kept_mask, kept_count, p_max, s.n_q_heads,         \
-                     s.n_kv_heads, s.max_ctx, dist, hist, cum)
-  if (kept_mask != nullptr) {  // 128-bit codes only (the one-launch coarse stage)
-    if (s.code_bits != 32 * kNW) return hipErrorInvalidValue;
-    HHR_HAM_DIST(4, true);
-    return hipGetLastError();
-  }
+#define HHR_HAM_DIST(NW)                                                                      \
+  hipLaunchKernelGGL(k_ham_dist<NW>, grid, dim3(kHamDistThreads), 0, stream, q_codes, codes, \
+                     seq_len, kept, kept_count, p_max, s.n_q_heads, s.n_kv_heads, s.max_ctx, \
+                     dist, hist, cum)
   switch (s.code_bits) {
-    case 64: HHR_HAM_DIST(2, false); break;
-    case 256: HHR_HAM_DIST(8, false); break;
-    default: HHR_HAM_DIST(4, false); break;
+    case 64: HHR_HAM_DIST(2); break;
+    case 256: HHR_HAM_DIST(8); break;
+    default: HHR_HAM_DIST(4); break;
   }
 #undef HHR_HAM_DIST
   return hipGetLastError();
 }
 
 hipError_t launch_hamming_topk(const hhr_shape& s, const uint32_t* q_codes, const uint32_t* codes,
-                               const int32_t* seq_len, int32_t* kept, const uint64_t* kept_mask,
+                               const int32_t* seq_len, const int32_t* kept,
                                const int32_t* kept_count, int32_t p_max, int32_t top_k,
                                int32_t* sel_idx, int32_t* sel_count, uint16_t* dist, int* hist,
                                uint32_t* status, hipStream_t stream) {
-  hipError_t e = launch_ham_dist(s, q_codes, codes, seq_len, kept, kept_mask, kept_count, p_max,
-                                 dist, hist, nullptr, stream);
+  hipError_t e =
+      launch_ham_dist(s, q_codes, codes, seq_len, kept, kept_count, p_max, dist, hist, nullptr,
+                      stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_ham_select, dim3(s.batch * s.n_kv_heads), dim3(kHamSelThreads), 0, stream,
                      seq_len, kept, kept_count, p_max, top_k, s.n_q_heads, s.n_kv_heads,

@@ -298,16 +298,12 @@ __device__ void score_batch(int b, int g, int Hq, int Hkv, int NpCap, int Np, in
 // values are used, so that work of the caller's with loads of its own shares
 // their round trip.  sbuf (kMaxCtx / kPS floats, LDS) serves only the radix
 // fallback.  emit(pos, page) with pos ascending in page.
-// MASK: emit(e, m) with the kept pages as 64-bit words (top_largest_strided).
-template <int NT, bool COH, bool MASK = false, typename Emit, typename Mid = NoMid>
+template <int NT, bool COH, typename Emit, typename Mid = NoMid>
 __device__ __forceinline__ int top_pages_strided(const float* sc, int Np, int P, float lo, float hi, float* sbuf,
                                  TopScratch& sh, Emit emit, Mid mid = Mid()) {
   static_assert(16 * NT >= kMaxCtx / kPS, "16 pages per thread cover the largest context");
-  return top_strided<NT, COH, MASK>(sc, Np, Np, P, AllPresent(), lo, hi, sbuf, sh, emit, mid);
+  return top_strided<NT, COH>(sc, Np, Np, P, AllPresent(), lo, hi, sbuf, sh, emit, mid);
 }
-
-// Words of a kept-page mask: bit i of word e = page 64 e + i.
-__host__ __device__ constexpr int kept_mask_words(int NpCap) { return (NpCap + 63) / 64; }
 
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
   if (Np <= 0) return 0;
@@ -344,7 +340,6 @@ struct HamDistSmem {
   int hist[kHistCopies][ham_bins_max<NW>()];
   int skept[kHamChunkPages];
   __attribute__((aligned(16))) uint32_t sq[kMaxG * NW];
-  int scan[kCumBlock / kWave + 1];
 };
 
 // 16-byte load; the coherent form is four agent-scope dword loads.
@@ -365,15 +360,12 @@ __device__ __forceinline__ u32x4 ld_u32x4(const uint32_t* p) {
 // Item j of every thread lies in block 4k + j of 256 candidates, whose
 // histogram is LDS copy j (fewer conflicting adds); the copies are summed
 // before the global adds.  Codes are NW 32-bit words.  All threads call.
-// MASK: the kept pages come as the words of kept_mask ([B][Hkv][words]); the
-// chunk finds its 64 by a prefix over the words' bit counts and writes them
-// to kept for the later stages.
-template <int NT, bool COH, int NW = kNW, bool MASK = false>
+template <int NT, bool COH, int NW = kNW>
 __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, int p_max,
                                const int32_t* seq_len, const int32_t* kept_count,
                                const uint32_t* q_codes, const uint32_t* __restrict__ codes,
-                               int32_t* kept, const uint64_t* kept_mask, uint16_t* dist,
-                               int* hist, uint16_t* cum, HamDistSmem<NW>& sm) {
+                               const int32_t* kept, uint16_t* dist, int* hist, uint16_t* cum,
+                               HamDistSmem<NW>& sm) {
   constexpr int kItems = kHamChunk / NT;
   static_assert(NT == kCumBlock && kItems == kHistCopies, "item j = block j = LDS copy j");
   static_assert(NW == 2 || NW == 4 || NW == 8, "64-, 128- or 256-bit codes");
@@ -385,15 +377,9 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   // kept pages and query codes are loaded before the kept count is known
   // (addresses clamped into the buffers), so they share its round trip
   int kp = 0;
-  uint64_t mword = 0ull;
   uint32_t qw = 0u;
-  const int nwords = kept_mask_words(Lcap / kPS);
-  if constexpr (MASK) {
-    static_assert(kMaxCtx / kPS / 64 <= NT, "one mask word per thread");
-    mword = Mem<COH>::ld(kept_mask + (size_t)bg * nwords + min(tid, nwords - 1));
-  } else if (tid < kHamChunkPages) {
+  if (tid < kHamChunkPages)
     kp = Mem<COH>::ld(kept + (size_t)bg * p_max + min(page0 + tid, p_max - 1));
-  }
   if (tid < G * NW) qw = Mem<COH>::ld(q_codes + ((size_t)b * Hq + (size_t)g * G) * NW + tid);
   const int L0 = seq_len[b];
   const int L = (L0 < 0 || L0 > Lcap) ? 0 : L0;
@@ -402,31 +388,10 @@ __device__ void ham_dist_chunk(int b, int g, int Hq, int Hkv, int Lcap, int k, i
   const int Np = (L + kPS - 1) / kPS;
   const int npg = min(kHamChunkPages, P - page0);
   const int ncl = npg * kPS;  // candidates in this chunk
-  if constexpr (MASK) {
-    // word tid holds pages [64 tid, 64 tid + 64); its first kept page has rank
-    // base.  The words that reach into ranks [page0, page0 + npg) place theirs.
-    const uint64_t m = tid < (Np + 63) / 64 ? mword : 0ull;
-    const int pc = popc64(m);
-    int tot;
-    const int base = block_exclusive_scan<NT, int>(pc, sm.scan, &tot);
-    if (base < page0 + npg && base + pc > page0) {
-      uint64_t mm = m;
-      int r = base;
-      for (; r < page0; ++r) mm &= mm - 1ull;
-      for (; mm != 0ull && r < page0 + npg; ++r) {
-        sm.skept[r - page0] = tid * 64 + __builtin_ctzll(mm);
-        mm &= mm - 1ull;
-      }
-    }
-  } else {
-    if (tid < npg) sm.skept[tid] = kp;
-  }
+  if (tid < npg) sm.skept[tid] = kp;
   if (tid < G * NW) sm.sq[tid] = qw;
   for (int i = tid; i < kHistCopies * nbins; i += NT) sm.hist[i / nbins][i % nbins] = 0;
   __syncthreads();
-  if constexpr (MASK) {
-    if (tid < npg) kept[(size_t)bg * p_max + page0 + tid] = sm.skept[tid];
-  }
 
   const uint32_t* cb = codes + (size_t)bg * Lcap * NW;
   const int lastc = max(ncl - 1, 0);

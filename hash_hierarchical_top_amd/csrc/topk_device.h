@@ -45,7 +45,6 @@ struct TopScratch {
   int bstar, above, digit;
   uint32_t T;
   int need_eq;
-  int n_eq;  // keys equal to T (linear mode 2 only)
   int scan[17];
   uint32_t uscan[17];
 };
@@ -183,11 +182,7 @@ __device__ __forceinline__ void emit_ordered(int cls, int c, int need_eq, int& g
 // score <= vmax.  sh.hist and sh.list_n must be zero behind a barrier; sbuf
 // (NT NV floats in LDS) is used only by the radix fallback.  Returns
 // min(P, n_valid).  All NT threads call.
-// MASK: instead of positions, emit(e, m) gives the taken set as 64-bit words,
-// bit i of word e = candidate 64 e + i (word e is slot e / NWAVES of wave
-// e % NWAVES, so one ballot makes it; words past n hold no bits).  Unless some
-// keys equal to the cut value are left out, this skips every rank and prefix.
-template <int NT, int NV, bool MASK = false, typename Present, typename Emit>
+template <int NT, int NV, typename Present, typename Emit>
 __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Present present,
                                    int P, float vmin, float vmax, float* sbuf, TopScratch& sh,
                                    Emit& emit) {
@@ -220,7 +215,6 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Pre
   // cut-off: mode 0 = every present candidate, 1 = bin >= bstar, 2 = bin >
   // bstar or (bin == bstar and key >= T, ties by need_eq), 3 = key >= T
   int mode = 0, need_eq = 0, bstar = 0;
-  bool ties_all = true;  // every key equal to T is taken (not known in mode 3)
   uint32_t T = 0u;
   if (!all) {
     __syncthreads();
@@ -278,13 +272,11 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Pre
         if (gtr < need && need <= gtr + eql) {  // all equal copies agree
           sh.T = orderable_key(vj);
           sh.need_eq = need - gtr;
-          sh.n_eq = eql;
         }
       }
       __syncthreads();
       T = sh.T;
       need_eq = sh.need_eq;
-      ties_all = need_eq == sh.n_eq;
     } else {
       mode = 3;  // radix over the keys of the whole set, read back from LDS
 #pragma unroll
@@ -298,26 +290,6 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Pre
           NV, Pe, sh);
       T = sh.T;
       need_eq = sh.need_eq;
-      ties_all = false;
-    }
-  }
-
-  // the taken set as words when no tie is left out (block-uniform)
-  auto taken_fast = [&](int j) -> bool {
-    if (bin[j] < 0) return false;
-    if (mode == 0) return true;
-    if (mode == 1) return bin[j] >= bstar;
-    if (mode == 2 && bin[j] != bstar) return bin[j] > bstar;
-    return orderable_key(x[j]) >= T;
-  };
-  if constexpr (MASK) {
-    if (ties_all) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const uint64_t m = __ballot(taken_fast(j));
-        if (l == 0 && (j * NWAVES + w) * kWave < n) emit(j * NWAVES + w, m);
-      }
-      return Pe;
     }
   }
 
@@ -375,13 +347,7 @@ __device__ int top_largest_strided(const float (&x)[NV], int n, int n_valid, Pre
       if (r == i) p = pre[i];
     const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)p, e / PER) + rank[j];
     const int gb = (int)(base & 0xFFFFu), eb = (int)(base >> 16);
-    const bool tk = cls[j] == 1 || (cls[j] == 2 && eb < need_eq);
-    if constexpr (MASK) {
-      const uint64_t m = __ballot(tk);
-      if (l == 0 && e * kWave < n) emit(e, m);
-    } else {
-      if (tk) emit(gb + min(eb, need_eq), j * NT + tid);
-    }
+    if (cls[j] == 1 || (cls[j] == 2 && eb < need_eq)) emit(gb + min(eb, need_eq), j * NT + tid);
   }
   return Pe;
 }
@@ -402,7 +368,7 @@ struct AllPresent {
 // of the present candidates (below n, with the given pieces lo, hi) and their
 // count in one barrier, and selects with top_largest_strided.  The caller
 // must have zeroed sh.hist and sh.list_n.
-template <int NT, int NV, bool COH, bool MASK, typename Present, typename Emit, typename Mid>
+template <int NT, int NV, bool COH, typename Present, typename Emit, typename Mid>
 __device__ int top_strided_nv(const float* src, int n_load, int n, int P, Present& present,
                               float lo, float hi, float* sbuf, TopScratch& sh, Emit& emit,
                               Mid& mid) {
@@ -438,16 +404,13 @@ __device__ int top_strided_nv(const float* src, int n_load, int n, int P, Presen
     vmax = fmaxf(vmax, sh.w_max[k]);
     n_valid += sh.w_n[k];
   }
-  return top_largest_strided<NT, NV, MASK>(x, n, n_valid, present, P, vmin, vmax, sbuf, sh,
-                                           emit);
+  return top_largest_strided<NT, NV>(x, n, n_valid, present, P, vmin, vmax, sbuf, sh, emit);
 }
 
 // The P largest of src[0 .. n) (those present), ties to the lower index,
-// emitted in ascending index (MASK: as words, see top_largest_strided).
-// n_load (>= n, <= 16 NT, block-uniform and known before n may be) bounds the
-// loads, so they need not wait for n.
-template <int NT, bool COH, bool MASK = false, typename Present, typename Emit,
-          typename Mid = NoMid>
+// emitted in ascending index.  n_load (>= n, <= 16 NT, block-uniform and
+// known before n may be) bounds the loads, so they need not wait for n.
+template <int NT, bool COH, typename Present, typename Emit, typename Mid = NoMid>
 __device__ __forceinline__ int top_strided(const float* src, int n_load, int n, int P, Present present, float lo,
                            float hi, float* sbuf, TopScratch& sh, Emit emit, Mid mid = Mid()) {
   const int tid = threadIdx.x;
@@ -455,8 +418,7 @@ __device__ __forceinline__ int top_strided(const float* src, int n_load, int n, 
   if (tid == 0) sh.list_n = 0;
   const int nv = (n_load + NT - 1) / NT;
 #define HHR_TOP_STRIDED(V) \
-  return top_strided_nv<NT, V, COH, MASK>(src, n_load, n, P, present, lo, hi, sbuf, sh, emit, \
-                                          mid)
+  return top_strided_nv<NT, V, COH>(src, n_load, n, P, present, lo, hi, sbuf, sh, emit, mid)
   if (nv <= 1) HHR_TOP_STRIDED(1);
   if (nv <= 2) HHR_TOP_STRIDED(2);
   if (nv <= 4) HHR_TOP_STRIDED(4);

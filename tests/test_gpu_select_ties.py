@@ -73,10 +73,10 @@ def test_top_pages_exact_on_constructed_scores(gpu_lib):
 def test_duplicate_pages_composite_equals_stages(gpu_lib, group):
     """Keys copied page by page in runs of `group` pages give equal page bounds in runs,
     so the cut of the top-P falls inside a run of ties (group 8192: every page equal).
-    The one-launch coarse stage of hhr_decode and hhr_select (kept pages handed to the
-    distance launch as bit words) must keep the same pages as the staged top-P, which
-    breaks ties to the lower page: the selections and outputs are bit-identical, and the
-    staged kept pages equal the oracle's top-P of the GPU's own bounds."""
+    The one-launch coarse stage of hhr_decode and hhr_select (top-P in the last scoring
+    workgroup) must keep the same pages as the staged top-P, both breaking ties to the
+    lower page: the selections and outputs are bit-identical, and the staged kept pages
+    equal the oracle's top-P of the GPU's own bounds."""
     print(f"\n[gpu duplicate pages] group={group}", flush=True)
     from hash_hierarchical_top_amd import synth
 
