@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void k_attn_pick(
   if (tid < kCh && k0 + tid < top_k) sel_idx[(size_t)bg * top_k + k0 + tid] = sm.sidx[tid];
   if (blockIdx.x == 0 && tid == 0) sel_count[bg] = count;
   if (k0 >= count) return;  // block-uniform
-  attn_chunk<KF32, false>(b, g, Hq, Hkv, Lcap, top_k, k0, min(kCh, count - k0), scale, q, kcache,
+  attn_chunk<KF32, true>(b, g, Hq, Hkv, Lcap, top_k, k0, min(kCh, count - k0), scale, q, kcache,
                           vcache, nullptr,
                           part + ((size_t)bg * n_split + blockIdx.x) * kMaxG * kPartStride,
                           status, sm, 0, kMaxG, true);
