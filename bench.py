@@ -384,7 +384,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16 K/V, f32 accumulate",
         "data": "synthetic (seeded; Llama-3.1-8B shape, planted-key queries)",
         "config": {"workload": args.workload, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "ctx": int(seq_np.max()), "page_size": 16, "code_bits": 128,
+                   "ctx": int(seq_np.max()), "max_ctx": Lcap, "page_size": 16, "code_bits": 128,
                    "keep": f"{keep[0]}/{keep[1]}" if keep[2] == 0 else keep[2], "top_k": top_k,
                    "meta_dtype": args.meta,
                    "layers_rotated": args.layers, "hip_graph": bool(graph is not None),

@@ -98,6 +98,7 @@ class HHRWorkload:
     top_k: int
     seed: int
     min_len: Optional[int] = None  # ragged lengths ~ U{min_len..max_ctx}; None -> all max_ctx
+    fixed_len: Optional[int] = None  # every sequence this long (a partly filled cache)
     head_dim: int = HEAD_DIM
     code_bits: int = CODE_BITS
     page_size: int = PAGE_SIZE
@@ -112,6 +113,10 @@ WORKLOADS: Dict[str, HHRWorkload] = {
     "llama8b_128k": HHRWorkload("llama8b_128k", 1, 32, 8, 131072, "bf16", 1, 8, 0, 4096, 1002),
     # same shape at 64K context (a test size between the two: 4096 pages per KV head)
     "llama8b_64k": HHRWorkload("llama8b_64k", 1, 32, 8, 65536, "bf16", 1, 8, 0, 4096, 1005),
+    # a 16K sequence in a 128K cache (the one-launch path on a partly filled cache: only
+    # the sequence's own pages are read), keep 25% of pages
+    "llama8b_16k_in_128k": HHRWorkload("llama8b_16k_in_128k", 1, 32, 8, 131072, "bf16", 1, 4, 0,
+                                       2048, 1006, fixed_len=16384),
     # batched ragged decode, 16 sequences of 8K..64K
     "llama8b_ragged_b16": HHRWorkload("llama8b_ragged_b16", 16, 32, 8, 65536, "bf16", 1, 4, 0,
                                       2048, 1003, min_len=8192),
@@ -120,6 +125,8 @@ WORKLOADS: Dict[str, HHRWorkload] = {
 
 def seq_lens_for(w: HHRWorkload) -> np.ndarray:
     """Per-sequence context lengths (seeded; ragged when min_len is set)."""
+    if w.fixed_len is not None:
+        return np.full(w.batch, w.fixed_len, dtype=np.int32)
     if w.min_len is None:
         return np.full(w.batch, w.max_ctx, dtype=np.int32)
     rng = np.random.Generator(np.random.PCG64(w.seed + 7919))
