@@ -228,6 +228,7 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.q_codes = take(BHq * (size_t)(s.code_bits / 32) * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
   w.wave_range = take(BHkv * (NpCap / 16) * sizeof(float2));
+  w.wg_thr = take(BHkv * (size_t)((NpCap + 63) / 64) * sizeof(float));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));
   w.attn_part = take(attn_part_bytes(s, w.n_split));
@@ -448,6 +449,7 @@ static hhr_status composite_buffers(const hhr_shape& shape, int32_t keep_num, in
   buf->scores = reinterpret_cast<float*>(base + ws->scores);
   buf->q_rot = reinterpret_cast<float*>(base + ws->q_rot);
   buf->wave_range = reinterpret_cast<float2*>(base + ws->wave_range);
+  buf->wg_thr = reinterpret_cast<float*>(base + ws->wg_thr);
   buf->q_codes = reinterpret_cast<uint32_t*>(base + ws->q_codes);
   buf->kept = reinterpret_cast<int32_t*>(base + ws->kept);
   buf->kept_count = reinterpret_cast<int32_t*>(base + ws->kept_count);

@@ -21,7 +21,8 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // holds the device status word at offset 0.
 struct Workspace {
   size_t ctrl = 0, counters = 0, ham_dist = 0, ham_hist = 0, ham_cum = 0, q_rot = 0, q_codes = 0,
-         scores = 0, wave_range = 0, kept = 0, kept_count = 0, attn_part = 0, total = 0;
+         scores = 0, wave_range = 0, wg_thr = 0, kept = 0, kept_count = 0, attn_part = 0,
+         total = 0;
   int32_t p_max = 0, n_split = 0;
 };
 
@@ -91,6 +92,7 @@ struct CompositeBuffers {
   float* scores;
   float* q_rot;
   float2* wave_range;
+  float* wg_thr;  // each scoring workgroup's lower bound of the top-P cut
   uint32_t* q_codes;
   int32_t* kept;
   int32_t* kept_count;

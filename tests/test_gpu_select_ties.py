@@ -69,19 +69,24 @@ def test_top_pages_exact_on_constructed_scores(gpu_lib):
     print(f"checked {checked} selections")
 
 
-@pytest.mark.parametrize("group", [4, 3, 8192])
-def test_duplicate_pages_composite_equals_stages(gpu_lib, group):
+@pytest.mark.parametrize("group,Lcap,lens", [(4, 8192, [8192, 5000]), (3, 8192, [8192, 5000]),
+                                             (8192, 8192, [8192, 5000]),
+                                             (1, 98304, [98304, 80000]),
+                                             (3, 98304, [98304, 80000]),
+                                             (98304, 98304, [98304, 80000])])
+def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens):
     """Keys copied page by page in runs of `group` pages give equal page bounds in runs,
-    so the cut of the top-P falls inside a run of ties (group 8192: every page equal).
+    so the cut of the top-P falls inside a run of ties (group = Lcap: every page equal).
     The one-launch coarse stage of hhr_decode and hhr_select (top-P in the last scoring
     workgroup) must keep the same pages as the staged top-P, both breaking ties to the
     lower page: the selections and outputs are bit-identical, and the staged kept pages
-    equal the oracle's top-P of the GPU's own bounds."""
-    print(f"\n[gpu duplicate pages] group={group}", flush=True)
+    equal the oracle's top-P of the GPU's own bounds.  The 98304-key cache (6144 and 5000
+    pages) takes the one-launch top-P through its lower-bound pre-filter, the second
+    sequence with a partly filled last scoring workgroup."""
+    print(f"\n[gpu duplicate pages] group={group} Lcap={Lcap}", flush=True)
     from hash_hierarchical_top_amd import synth
 
-    B, Hq, Hkv, Lcap = 2, 8, 2, 8192
-    lens = [8192, 5000]
+    B, Hq, Hkv = 2, 8, 2
     inp = synth.make_hhr_inputs(B, Hq, Hkv, lens, Lcap, "bf16", seed=77)
     K = inp["K"].reshape(B, Hkv, Lcap // 16, 16, 128)
     src = (np.arange(Lcap // 16) // group) * group
@@ -111,4 +116,6 @@ def test_duplicate_pages_composite_equals_stages(gpu_lib, group):
     assert torch.equal(out, p.out)
     sel2, sc2 = p.select()
     assert torch.equal(sc2, p.sel_count) and torch.equal(sel2, p.sel)
+    kept, kc, _ = p.select_pages()
+    assert torch.equal(kc, p.kept_count) and torch.equal(kept, p.kept)
     assert p.status() == 0
