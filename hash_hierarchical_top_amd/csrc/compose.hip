@@ -56,7 +56,7 @@ struct ScoreTopSmem {
 };
 
 // A lower bound of the top-P cut from the scoring workgroups (see
-// top_pages_prefiltered): while it pays, every workgroup holding pages
+// top_prefiltered): while it pays, every workgroup holding pages
 // publishes a value that q = ceil(P / (J - 1)) of its bounds reach (all of
 // them when it holds fewer), J = the workgroups holding pages.  It pays when
 // the top-P would otherwise hold more than 4 bounds per thread: at 128K
@@ -224,40 +224,17 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     s_wlo[tid >> 6] = __builtin_huge_valf();
     s_whi[tid >> 6] = -__builtin_huge_valf();
   }
-  if (quota > 0 && wg_has) {  // block-uniform
-    // a value that min(quota, pages here) of this workgroup's bounds reach: the
-    // smallest bound of the 64-bin histogram bin (over the workgroup's range)
-    // in which the count from the top reaches the quota
-    if (tid < 64) {
-      s_bcnt[tid] = 0;
-      s_bmin[tid] = 0xFFFFFFFFu;
-    }
-    __syncthreads();
+  if (quota > 0 && wg_has) {  // block-uniform: this workgroup's lower bound of the cut
+    lower_bound_init(s_bcnt, s_bmin);
+    __syncthreads();  // s_wlo, s_whi and the histogram words
     float wlo = __builtin_huge_valf(), whi = -__builtin_huge_valf();
 #pragma unroll
     for (int k = 0; k < kScoreThreads / kWave; ++k) {
       wlo = fminf(wlo, s_wlo[k]);
       whi = fmaxf(whi, s_whi[k]);
     }
-    const float inv = whi > wlo ? 64.f / (whi - wlo) : 0.f;
-    if (pf_lane) {
-      const float f = (mine - wlo) * inv;
-      const int bin = f < 64.f ? max((int)f, 0) : 63;
-      atomicAdd(&s_bcnt[bin], 1);
-      atomicMin(&s_bmin[bin], orderable_key(mine));
-    }
-    __syncthreads();
-    if (tid < 64) {  // wave 0: bins from the top
-      const int c = s_bcnt[63 - tid];
-      const int inc = wave_inclusive_scan(c);
-      const uint64_t hit = __ballot(inc >= quota && inc - c < quota);
-      float t = wlo;  // fewer than the quota here: every bound counts
-      if (hit != 0ull) {
-        const uint32_t key = s_bmin[63 - __builtin_ctzll(hit)];
-        t = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-      }
-      if (tid == 0) Mem<true>::st(wg_thr + (size_t)bg * gridDim.x + blockIdx.x, t);
-    }
+    publish_lower_bound(mine, pf_lane, wlo, whi, quota, s_bcnt, s_bmin,
+                        wg_thr + (size_t)bg * gridDim.x + blockIdx.x);
   }
   // The code bits of the queries (and of the appended key, as row G) need W's
   // columns in registers, which would not fit beside the metadata; the first
@@ -284,10 +261,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   for (int i = P + tid; i < p_max; i += kScoreThreads) out[i] = -1;
   if (tid == 0) kept_count[bg] = P;
   if (quota > 0) {  // block-uniform: the pages below the published lower bound are out
-    top_pages_prefiltered<kScoreThreads>(
-        scores + (size_t)bg * NpCap, Np, P, wg_thr + (size_t)bg * gridDim.x,
-        (Np + ppw - 1) / ppw, wr, (Np + kScorePagesPerWave - 1) / kScorePagesPerWave,
-        sm.sel.sbuf, sm.sel.cidx, sm.sel.top, [&](int pos, int c) { out[pos] = c; });
+    top_prefiltered<kScoreThreads>(scores + (size_t)bg * NpCap, Np, Np, P, AllPresent(),
+                                   wg_thr + (size_t)bg * gridDim.x, (Np + ppw - 1) / ppw,
+                                   sm.sel.sbuf, sm.sel.cidx, sm.sel.top,
+                                   [&](int pos, int c) { out[pos] = c; });
   } else if (P > 0) {
     // the range of all bounds from the waves' published {lo, hi}, one per thread
     static_assert(kMaxCtx / kPS / kScorePagesPerWave <= kScoreThreads,

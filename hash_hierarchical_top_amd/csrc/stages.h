@@ -305,116 +305,6 @@ __device__ __forceinline__ int top_pages_strided(const float* sc, int Np, int P,
   return top_strided<NT, COH>(sc, Np, Np, P, AllPresent(), lo, hi, sbuf, sh, emit, mid);
 }
 
-// The same top-P of Np <= kPrefilterMaxPages bounds when a lower bound lb of
-// the cut is known (k_score_topp: each scoring workgroup publishes a value
-// that at least q of its own bounds reach, with (workgroups - 1) q >= P, so
-// the P largest bounds are all >= the smallest published value).  Pages
-// below lb cannot be kept: the rest are compacted into LDS in page order
-// (ballots, one prefix over the (slot, wave) counts) and the top-P is taken
-// among them with top_largest_strided, on a quarter of the registers per
-// thread when about a quarter survive.  thr[j < J] are the published values,
-// wr[w < n_his] the scoring waves' {smallest, largest} bounds; sbuf holds the compacted
-// bounds (and serves the radix fallback), cidx their pages.  emit(pos, page)
-// with pos ascending in page.  All NT threads call; returns min(P, Np).
-constexpr int kPrefilterMaxPages = 8192;
-
-template <int NT, int NV2, typename Emit>
-__device__ __forceinline__ int top_compacted(int n, int P, float lb, float vmax, float* sbuf,
-                                             const uint16_t* cidx, TopScratch& sh, Emit& emit) {
-  const int tid = threadIdx.x;
-  float x2[NV2];
-#pragma unroll
-  for (int j = 0; j < NV2; ++j) x2[j] = sbuf[min(j * NT + tid, n - 1)];
-  auto emit2 = [&](int pos, int c) { emit(pos, (int)cidx[c]); };
-  return top_largest_strided<NT, NV2>(x2, n, n, AllPresent(), P, lb, vmax, sbuf, sh, emit2);
-}
-
-template <int NT, typename Emit>
-__device__ __forceinline__ int top_pages_prefiltered(const float* sc, int Np, int P,
-                                                     const float* thr, int J, const float2* wr,
-                                                     int n_his, float* sbuf, uint16_t* cidx,
-                                                     TopScratch& sh, Emit emit) {
-  constexpr int NV = kPrefilterMaxPages / NT;
-  constexpr int NWAVES = NT / kWave;
-  constexpr int NE = NV * NWAVES;
-  constexpr int PER = (NE + kWave - 1) / kWave;
-  static_assert(NE <= kStridedCnt && PER <= 4, "slot counts fit TopScratch::cnt");
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int l = tid % kWave;
-  const int last = max(Np - 1, 0);
-  float x[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) x[j] = Mem<true>::ld(sc + min(j * NT + tid, last));
-  const float t = Mem<true>::ld(thr + min(tid, J - 1));
-  const float h = Mem<true>::ld(reinterpret_cast<const float*>(wr + min(tid, n_his - 1)) + 1);
-  issue_loads_here();
-  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // for the selection below
-  if (tid == 0) sh.list_n = 0;
-  float tm = wave_min(tid < J ? t : __builtin_huge_valf());
-  float hm = wave_max(tid < n_his ? h : -__builtin_huge_valf());
-  if (l == 0) {
-    sh.w_min[w] = tm;
-    sh.w_max[w] = hm;
-  }
-  __syncthreads();
-  float lb = __builtin_huge_valf(), vmax = -__builtin_huge_valf();
-#pragma unroll
-  for (int k = 0; k < NWAVES; ++k) {
-    lb = fminf(lb, sh.w_min[k]);
-    vmax = fmaxf(vmax, sh.w_max[k]);
-  }
-  // compaction of the survivors (bound >= lb) in page order
-  uint32_t rank[NV];
-  bool keep[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    keep[j] = j * NT + tid < Np && x[j] >= lb;
-    const uint64_t m = __ballot(keep[j]);
-    rank[j] = mbcnt64(m);
-    if (l == 0) sh.cnt[j * NWAVES + w] = (uint32_t)popc64(m);
-  }
-  __syncthreads();
-  uint32_t pre[PER], tot;
-  {
-    uint32_t v[PER], local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = PER * l + i;
-      v[i] = e < NE ? sh.cnt[e] : 0u;
-      local += v[i];
-    }
-    const uint32_t inc = wave_inclusive_scan(local);
-    tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
-    uint32_t run = inc - local;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      pre[i] = run;
-      run += v[i];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int e = j * NWAVES + w;  // wave-uniform
-    const int r = e % PER;
-    uint32_t p = pre[0];
-#pragma unroll
-    for (int i = 1; i < PER; ++i)
-      if (r == i) p = pre[i];
-    const uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)p, e / PER) + rank[j];
-    if (keep[j]) {
-      sbuf[pos] = x[j];
-      cidx[pos] = (uint16_t)(j * NT + tid);
-    }
-  }
-  __syncthreads();
-  const int n = (int)tot;  // >= P by the choice of the published values
-  if (n <= NT) return top_compacted<NT, 1>(n, P, lb, vmax, sbuf, cidx, sh, emit);
-  if (n <= 2 * NT) return top_compacted<NT, 2>(n, P, lb, vmax, sbuf, cidx, sh, emit);
-  if (n <= 4 * NT) return top_compacted<NT, 4>(n, P, lb, vmax, sbuf, cidx, sh, emit);
-  return top_compacted<NT, 8>(n, P, lb, vmax, sbuf, cidx, sh, emit);
-}
-
 __device__ __forceinline__ int keep_count_dev(int Np, int keep_num, int keep_den, int keep_abs) {
   if (Np <= 0) return 0;
   if (keep_abs > 0) return min(Np, keep_abs);

@@ -427,4 +427,157 @@ __device__ __forceinline__ int top_strided(const float* src, int n_load, int n, 
 #undef HHR_TOP_STRIDED
 }
 
+// ---------------------------------------------------------------------------
+// Exact top-P of n <= kPrefilterMaxPages candidates when a lower bound lb of
+// the cut is known: each of the J producing workgroups has published (thr) a
+// value that q of its own candidates reach, with (J - 1) q >= P, so the P
+// largest candidates are all >= the smallest published value.  Candidates
+// below it cannot be taken: the rest are compacted into LDS in candidate
+// order (ballots, one prefix over the (slot, wave) counts) and the top-P is
+// taken among them with top_largest_strided, with a quarter of the registers
+// per thread when about a quarter survive.  sc[c] is loaded with agent-scope
+// loads (c < n_load, clamped); present(v) says whether candidate c < n takes
+// part; sbuf holds the compacted values (and serves the radix fallback), cidx
+// their candidate indices.  emit(pos, c) with pos ascending in c.  All NT
+// threads call; returns min(P, present candidates).
+constexpr int kPrefilterMaxPages = 8192;
+
+template <int NT, int NV2, typename Emit>
+__device__ __forceinline__ int top_compacted(int n, int P, float lb, float vmax, float* sbuf,
+                                             const uint16_t* cidx, TopScratch& sh, Emit& emit) {
+  const int tid = threadIdx.x;
+  float x2[NV2];
+#pragma unroll
+  for (int j = 0; j < NV2; ++j) x2[j] = sbuf[min(j * NT + tid, n - 1)];
+  auto emit2 = [&](int pos, int c) { emit(pos, (int)cidx[c]); };
+  return top_largest_strided<NT, NV2>(x2, n, n, AllPresent(), P, lb, vmax, sbuf, sh, emit2);
+}
+
+template <int NT, typename Present, typename Emit>
+__device__ __forceinline__ int top_prefiltered(const float* sc, int n_load, int n, int P,
+                                               Present present, const float* thr, int J,
+                                               float* sbuf, uint16_t* cidx, TopScratch& sh,
+                                               Emit emit) {
+  constexpr int NV = kPrefilterMaxPages / NT;
+  constexpr int NWAVES = NT / kWave;
+  constexpr int NE = NV * NWAVES;
+  constexpr int PER = (NE + kWave - 1) / kWave;
+  static_assert(NE <= kStridedCnt && PER <= 4, "slot counts fit TopScratch::cnt");
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = tid % kWave;
+  const int last = max(n_load - 1, 0);
+  float x[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) x[j] = Mem<true>::ld(sc + min(j * NT + tid, last));
+  const float t = Mem<true>::ld(thr + min(tid, J - 1));
+  issue_loads_here();
+  for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // for the selection below
+  if (tid == 0) sh.list_n = 0;
+  const float tm = wave_min(tid < J ? t : __builtin_huge_valf());
+  if (l == 0) sh.w_min[w] = tm;
+  __syncthreads();
+  float lb = __builtin_huge_valf();
+#pragma unroll
+  for (int k = 0; k < NWAVES; ++k) lb = fminf(lb, sh.w_min[k]);
+  // compaction of the survivors (present, >= lb) in candidate order, and their maximum
+  uint32_t rank[NV];
+  bool keep[NV];
+  float hm = -__builtin_huge_valf();
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    keep[j] = j * NT + tid < n && present(x[j]) && x[j] >= lb;
+    const uint64_t m = __ballot(keep[j]);
+    rank[j] = mbcnt64(m);
+    if (l == 0) sh.cnt[j * NWAVES + w] = (uint32_t)popc64(m);
+    if (keep[j]) hm = fmaxf(hm, x[j]);
+  }
+  hm = wave_max(hm);
+  if (l == 0) sh.w_max[w] = hm;
+  __syncthreads();
+  float vmax = -__builtin_huge_valf();
+#pragma unroll
+  for (int k = 0; k < NWAVES; ++k) vmax = fmaxf(vmax, sh.w_max[k]);
+  uint32_t pre[PER], tot;
+  {
+    uint32_t v[PER], local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = PER * l + i;
+      v[i] = e < NE ? sh.cnt[e] : 0u;
+      local += v[i];
+    }
+    const uint32_t inc = wave_inclusive_scan(local);
+    tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+    uint32_t run = inc - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      pre[i] = run;
+      run += v[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = j * NWAVES + w;  // wave-uniform
+    const int r = e % PER;
+    uint32_t p = pre[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i)
+      if (r == i) p = pre[i];
+    const uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)p, e / PER) + rank[j];
+    if (keep[j]) {
+      sbuf[pos] = x[j];
+      cidx[pos] = (uint16_t)(j * NT + tid);
+    }
+  }
+  __syncthreads();
+  const int nc = (int)tot;  // >= min(P, present) by the choice of the published values
+  if (nc <= 0) return 0;
+  if (nc <= NT) return top_compacted<NT, 1>(nc, P, lb, vmax, sbuf, cidx, sh, emit);
+  if (nc <= 2 * NT) return top_compacted<NT, 2>(nc, P, lb, vmax, sbuf, cidx, sh, emit);
+  if (nc <= 4 * NT) return top_compacted<NT, 4>(nc, P, lb, vmax, sbuf, cidx, sh, emit);
+  return top_compacted<NT, 8>(nc, P, lb, vmax, sbuf, cidx, sh, emit);
+}
+
+// The lower bound a producing workgroup publishes for top_prefiltered: a
+// value that min(q, its present candidates) of its candidates reach, namely
+// the smallest candidate of the bin of a 64-bin histogram over its
+// candidates' range (wlo, whi) in which the count from the top reaches q (its
+// smallest candidate when it has fewer than q).  Thread t holds candidate v
+// when has; s_cnt and s_min are 64 words of LDS that the caller has set to
+// 0 and 0xFFFFFFFF behind a barrier (lower_bound_init).  Every thread of the
+// workgroup calls (one barrier); thread 0 stores the value to *dst.
+__device__ __forceinline__ void lower_bound_init(int* s_cnt, uint32_t* s_min) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    s_cnt[tid] = 0;
+    s_min[tid] = 0xFFFFFFFFu;
+  }
+}
+
+__device__ __forceinline__ void publish_lower_bound(float v, bool has, float wlo, float whi,
+                                                    int q, int* s_cnt, uint32_t* s_min,
+                                                    float* dst) {
+  const int tid = threadIdx.x;
+  const float inv = whi > wlo ? 64.f / (whi - wlo) : 0.f;
+  if (has) {
+    const float f = (v - wlo) * inv;
+    const int bin = f < 64.f ? max((int)f, 0) : 63;
+    atomicAdd(&s_cnt[bin], 1);
+    atomicMin(&s_min[bin], orderable_key(v));
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: bins from the top
+    const int c = s_cnt[63 - tid];
+    const int inc = wave_inclusive_scan(c);
+    const uint64_t hit = __ballot(inc >= q && inc - c < q);
+    float t = wlo;  // fewer than q here: every candidate counts
+    if (hit != 0ull) {
+      const uint32_t key = s_min[63 - __builtin_ctzll(hit)];
+      t = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+    }
+    if (tid == 0) Mem<true>::st(dst, t);
+  }
+}
+
 }  // namespace hhr
