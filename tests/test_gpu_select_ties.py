@@ -69,12 +69,14 @@ def test_top_pages_exact_on_constructed_scores(gpu_lib):
     print(f"checked {checked} selections")
 
 
-@pytest.mark.parametrize("group,Lcap,lens", [(4, 8192, [8192, 5000]), (3, 8192, [8192, 5000]),
-                                             (8192, 8192, [8192, 5000]),
-                                             (1, 98304, [98304, 80000]),
-                                             (3, 98304, [98304, 80000]),
-                                             (98304, 98304, [98304, 80000])])
-def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens):
+@pytest.mark.parametrize("group,Lcap,lens,ramp", [(4, 8192, [8192, 5000], False),
+                                                  (3, 8192, [8192, 5000], False),
+                                                  (8192, 8192, [8192, 5000], False),
+                                                  (1, 98304, [98304, 80000], False),
+                                                  (3, 98304, [98304, 80000], False),
+                                                  (98304, 98304, [98304, 80000], False),
+                                                  (1, 98304, [98304, 80000], True)])
+def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens, ramp):
     """Keys copied page by page in runs of `group` pages give equal page bounds in runs,
     so the cut of the top-P falls inside a run of ties (group = Lcap: every page equal).
     The one-launch coarse stage of hhr_decode and hhr_select (top-P in the last scoring
@@ -82,8 +84,10 @@ def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens):
     lower page: the selections and outputs are bit-identical, and the staged kept pages
     equal the oracle's top-P of the GPU's own bounds.  The 98304-key cache (6144 and 5000
     pages) takes the one-launch top-P through its lower-bound pre-filter, the second
-    sequence with a partly filled last scoring workgroup."""
-    print(f"\n[gpu duplicate pages] group={group} Lcap={Lcap}", flush=True)
+    sequence with a partly filled last scoring workgroup.  ramp: keys scaled up with their
+    page index, so the largest bounds crowd into the last scoring workgroups and the
+    pre-filter keeps most pages (its widest compaction)."""
+    print(f"\n[gpu duplicate pages] group={group} Lcap={Lcap} ramp={ramp}", flush=True)
     from hash_hierarchical_top_amd import synth
 
     B, Hq, Hkv = 2, 8, 2
@@ -91,6 +95,11 @@ def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens):
     K = inp["K"].reshape(B, Hkv, Lcap // 16, 16, 128)
     src = (np.arange(Lcap // 16) // group) * group
     inp["K"] = np.ascontiguousarray(K[:, :, src].reshape(B, Hkv, Lcap, 128))
+    if ramp:  # bf16 keys times 1 + 3 p / pages, truncated back to bf16
+        Kf = (inp["K"].astype(np.uint32) << 16).view(np.float32)
+        scale = 1.0 + 3.0 * (np.arange(Lcap) // 16) / (Lcap // 16)
+        Kf = (Kf * scale[None, None, :, None].astype(np.float32)).astype(np.float32)
+        inp["K"] = np.ascontiguousarray((Kf.view(np.uint32) >> 16).astype(np.uint16))
     for b, L in enumerate(lens):
         inp["K"][b, :, L:] = 0
     p = U.Pipeline(gpu_lib, inp, "bf16", Hq, Hkv, Lcap, 1, 8, 0, 256)
