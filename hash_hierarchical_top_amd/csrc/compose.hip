@@ -138,6 +138,11 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 // {min, max} (or starts the page with it) in registers before the bound, and
 // stores the page's metadata back.  Nothing else touches that page, so no
 // other workgroup can see it half-updated.
+//
+// While the pre-filter pays (prefilter_quota), every workgroup holding pages
+// also publishes a lower bound of the cut (publish_lower_bound, into wg_thr
+// [B*Hkv][gridDim.x]) before it arrives, and the last one takes the top-P
+// among the pages at or above the smallest of them (top_prefiltered).
 template <bool MBF, bool APPEND>
 __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
     const float* __restrict__ q, const int32_t* __restrict__ seq_len,
