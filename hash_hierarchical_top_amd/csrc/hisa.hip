@@ -360,6 +360,7 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
 // scores (agent-scope stores) and counts in on its row's counter; the last to
 // arrive takes the row's exact top-k as k_hisa_topk does, with its 16 waves.
 typedef long fp8x8;
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 constexpr int kTsWaves = 8;      // the plain variant
 constexpr int kTsTopWaves = 16;  // with H5: k_hisa_topk's width
 
@@ -419,7 +420,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_token_scores(
   if (tid < kMaxIndexHeads) swsq[tid] = tid < Hi ? wv_ * sv_ : 0.f;
   __syncthreads();
   // A: head 16 ht + lrow (zero past Hi); this lane's 16 heads for the
-  // epilogue: 16 ht + 4 lgrp + j
+  // epilogue: 16 ht + 4 lgrp + j.  The k-step ks of lane group lgrp takes dims
+  // 32 lgrp + 8 ks .. + 7 (in A as in B), so that a lane's four key fragments
+  // are 32 contiguous bytes of its row, two 16-byte loads.
   fp8x8 aq[4][4];
   float wsq[4][4];
 #pragma unroll
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_token_scores(
     const bool hv = 16 * ht + lrow < Hi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      aq[ht][ks] = hv ? *(const fp8x8*)&sq8[16 * ht + lrow][32 * ks + 8 * lgrp] : 0;
+      aq[ht][ks] = hv ? *(const fp8x8*)&sq8[16 * ht + lrow][32 * lgrp + 8 * ks] : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) wsq[ht][j] = swsq[16 * ht + 4 * lgrp + j];
   }
@@ -442,56 +445,136 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_token_scores(
   auto tile_token = [&](int i) {
     return skb[i / tiles_per_block] * block + 16 * (i % tiles_per_block) + lrow;
   };
-  // key fragments and scale of tile i (token row of this lane; rows past L
-  // read row 0), all issued together
-  auto load_tile = [&](int i, fp8x8 (&kf)[4], float& ks) {
+  // key fragments of tile i (token row of this lane; rows past L read row 0)
+  auto load_keys = [&](int i, fp8x8 (&kf)[4]) {
     const int t = tile_token(i);
     const size_t row = (t >= 0 && t < L) ? (size_t)t : 0;
+    const u64x2* src = (const u64x2*)(kb + row * kD + 32 * lgrp);
+    const u64x2 lo = src[0], hi = src[1];
+    kf[0] = (fp8x8)lo[0];
+    kf[1] = (fp8x8)lo[1];
+    kf[2] = (fp8x8)hi[0];
+    kf[3] = (fp8x8)hi[1];
+  };
+  // The wave's tiles i, i + W, ... go in groups of four, tile j of a group in
+  // key buffer j, loaded two tiles ahead.  While every load of a group is in
+  // range (all but the last group or two) the group runs without guards: a
+  // guarded load leaves the compiler a join after which it can only wait for
+  // every load in flight.  Lane group lgrp loads the key scale of its row of
+  // the group's tile lgrp and stores that tile's score (after the lane-swap
+  // sums every lane holds its row's sum), so that a group costs one scale load
+  // and one store instead of four each.
+  constexpr int W = kTsWavesT;
+  fp8x8 kf[4][4];
+  // this lane's tile of the group at i, and its token (-1 past the tiles)
+  auto lane_token = [&](int i) {
+    const int ti = i + lgrp * W;
+    return ti < ntiles ? tile_token(ti) : -1;
+  };
+  auto scale_at = [&](int i) {  // issued a group ahead of its use
+    const int tt = lane_token(i);
+    return ksb[(tt >= 0 && tt < L) ? tt : 0];
+  };
+  auto run_group = [&](int i, float skr, auto guarded) {
+    constexpr bool kGuard = decltype(guarded)::value;
+    float out = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) kf[k] = *(const fp8x8*)(kb + row * kD + 32 * k + 8 * lgrp);
-    ks = ksb[row];
+    for (int j = 0; j < 4; ++j) {
+      if (!kGuard || i + (j + 2) * W < ntiles) load_keys(i + (j + 2) * W, kf[(j + 2) % 4]);
+      if (!kGuard || i + j * W < ntiles) {  // wave-uniform
+        floatx4 acc[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          acc[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aq[ht][ks], kf[j][ks], acc[ht],
+                                                                 0, 0, 0);
+        }
+        const float inf = opaque_inf();
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            part = fmaf(wsq[ht][jj], med_max(acc[ht][jj], 0.f, inf), part);
+        part = add_swap16(add_swap32(part));
+        if (lgrp == j) out = part;
+      }
+    }
+    const int ti = i + lgrp * W;
+    if (ti < ntiles) {
+      const int tt = tile_token(ti);
+      const int slot = slot0 + ti / tiles_per_block;
+      Mem<TOPK>::st(
+          token_scores + ((size_t)b * keep_blocks + slot) * block + 16 * (ti % tiles_per_block) +
+              lrow,
+          tt >= 0 && tt < L ? out * skr : -__builtin_huge_valf());
+    }
   };
   int i = wv;
-  fp8x8 kf[4], k1[4];
-  float s0 = 0.f, s1 = 0.f;
-  if (i < ntiles) load_tile(i, kf, s0);
-  if (i + kTsWavesT < ntiles) load_tile(i + kTsWavesT, k1, s1);
-  for (; i < ntiles; i += kTsWavesT) {
-    fp8x8 k2[4];
-    float s2 = 0.f;
-    if (i + 2 * kTsWavesT < ntiles) load_tile(i + 2 * kTsWavesT, k2, s2);
-    floatx4 acc[4];
+  if constexpr (TOPK) {
+    // a decode row: a tile or two per wave, each tile's keys and scale loaded
+    // together two tiles ahead
+    auto load_tile = [&](int i, fp8x8 (&k)[4], float& sc) {
+      load_keys(i, k);
+      const int t = tile_token(i);
+      sc = ksb[(t >= 0 && t < L) ? t : 0];
+    };
+    fp8x8 k0[4], k1[4];
+    float s0 = 0.f, s1 = 0.f;
+    if (i < ntiles) load_tile(i, k0, s0);
+    if (i + W < ntiles) load_tile(i + W, k1, s1);
+    for (; i < ntiles; i += W) {
+      fp8x8 k2[4];
+      float s2 = 0.f;
+      if (i + 2 * W < ntiles) load_tile(i + 2 * W, k2, s2);
+      floatx4 acc[4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      acc[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < 4; ++ht) {
+        acc[ht] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aq[ht][ks], kf[ks], acc[ht], 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks)
+          acc[ht] =
+              __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(aq[ht][ks], k0[ks], acc[ht], 0, 0, 0);
+      }
+      const int t = tile_token(i);
+      const bool valid = t >= 0 && t < L;
+      const float inf = opaque_inf();
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          part = fmaf(wsq[ht][jj], med_max(acc[ht][jj], 0.f, inf), part);
+      part = add_swap16(add_swap32(part)) * (valid ? s0 : 0.f);
+      if (lgrp == 0)
+        Mem<TOPK>::st(token_scores + ((size_t)b * keep_blocks + slot0 + i / tiles_per_block) *
+                                         block +
+                          16 * (i % tiles_per_block) + lrow,
+                      valid ? part : -__builtin_huge_valf());
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        k0[ks] = k1[ks];
+        k1[ks] = k2[ks];
+      }
+      s0 = s1;
+      s1 = s2;
     }
-    const int t = tile_token(i);
-    const bool valid = t >= 0 && t < L;
-    const float sk = valid ? s0 : 0.f;
-    const float inf = opaque_inf();
-    float part = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part = fmaf(wsq[ht][j], med_max(acc[ht][j], 0.f, inf), part);
-    part = add_swap16(add_swap32(part)) * sk;
-    if (lgrp == 0) {
-      const int slot = slot0 + i / tiles_per_block;
-      Mem<TOPK>::st(
-          token_scores + ((size_t)b * keep_blocks + slot) * block + 16 * (i % tiles_per_block) +
-              lrow,
-          valid ? part : -__builtin_huge_valf());
+  } else {
+    if (i < ntiles) load_keys(i, kf[0]);
+    if (i + W < ntiles) load_keys(i + W, kf[1]);
+    float skr = scale_at(i);
+    for (; i + 5 * W < ntiles; i += 4 * W) {
+      const float next = scale_at(i + 4 * W);
+      run_group(i, skr, std::false_type{});
+      skr = next;
     }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      kf[ks] = k1[ks];
-      k1[ks] = k2[ks];
+    for (; i < ntiles; i += 4 * W) {
+      const float next = scale_at(i + 4 * W);
+      run_group(i, skr, std::true_type{});
+      skr = next;
     }
-    s0 = s1;
-    s1 = s2;
   }
   }
   if constexpr (TOPK) {
