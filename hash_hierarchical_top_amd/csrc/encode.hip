@@ -56,11 +56,9 @@ __device__ __forceinline__ void enc_load_b(const float* R, const float* W, int g
       u32x4 hv, lv;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(raw[ks][2 * jj], h0, l0);
-        split_bf16(raw[ks][2 * jj + 1], h1, l1);
-        hv[jj] = h0 | (h1 << 16);
-        lv[jj] = l0 | (l1 << 16);
+        const u32x2 hl = split_bf16x2(raw[ks][2 * jj], raw[ks][2 * jj + 1]);
+        hv[jj] = hl[0];
+        lv[jj] = hl[1];
       }
       bhi[nt][ks] = as_bf16x8(hv);
       blo[nt][ks] = as_bf16x8(lv);
@@ -225,11 +223,8 @@ __global__ __launch_bounds__((enc_threads<NW, 4>())) void k_append_encode_f32(
         const int grow = row0 + r;
         floatx4 v = {0.f, 0.f, 0.f, 0.f};
         if (grow < e) v = *(const floatx4*)(Kf + (size_t)grow * kD + cc * 4);
-        uint32_t h[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split_bf16(v[j], h[j], lo[j]);
-        u32x2 hv = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        u32x2 lv = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        const u32x2 a = split_bf16x2(v[0], v[1]), c = split_bf16x2(v[2], v[3]);
+        const u32x2 hv = {a[0], c[0]}, lv = {a[1], c[1]};
         *(u32x2*)(a_hi + r * kLdsStride + cc * 4) = hv;
         *(u32x2*)(a_lo + r * kLdsStride + cc * 4) = lv;
       }

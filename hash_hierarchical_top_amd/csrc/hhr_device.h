@@ -19,17 +19,30 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// f32 -> bf16 bits, round to nearest even (finite inputs).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// f32 -> bf16 bits of a (low half) and b (high half), rounded to nearest
+// even: one v_cvt_pk_bf16_f32 (finite inputs).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return f32x2_to_bf16x2_rne(x, 0.f) & 0xFFFFu;
 }
 
-// Split x into bf16 hi + lo with x - hi - lo within 2^-17 |x|.
+// Split x into bf16 hi + lo with x - hi - lo within 2^-17 |x| (x - hi is
+// exact in f32).
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
   hi = f32_to_bf16_rne(x);
   lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+}
+// The same for a pair, packed as the MFMA operands hold them (a low, b high):
+// {hi, lo}.
+__device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
+  const uint32_t hi = f32x2_to_bf16x2_rne(a, b);
+  return u32x2{hi, f32x2_to_bf16x2_rne(a - __uint_as_float(hi << 16),
+                                       b - __uint_as_float(hi & 0xFFFF0000u))};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

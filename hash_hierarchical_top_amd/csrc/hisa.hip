@@ -282,11 +282,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_block_scores(
       u32x4 hv, lv;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16(jj < 2 ? x0[ks][2 * jj] : x1[ks][2 * jj - 4], h0, l0);
-        split_bf16(jj < 2 ? x0[ks][2 * jj + 1] : x1[ks][2 * jj - 3], h1, l1);
-        hv[jj] = h0 | (h1 << 16);
-        lv[jj] = l0 | (l1 << 16);
+        const u32x2 hl = split_bf16x2(jj < 2 ? x0[ks][2 * jj] : x1[ks][2 * jj - 4],
+                                      jj < 2 ? x0[ks][2 * jj + 1] : x1[ks][2 * jj - 3]);
+        hv[jj] = hl[0];
+        lv[jj] = hl[1];
       }
       bhi[ks] = as_bf16x8(hv);
       blo[ks] = as_bf16x8(lv);

@@ -1078,11 +1078,9 @@ __device__ void attn_chunk(int b, int g, int Hq, int Hkv, int Lcap, int top_k, i
       }
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf16(p[i], hi[i], lo[i]);
-      *(u32x2*)&sm.ab.p.h[h][k4] = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-      *(u32x2*)&sm.ab.p.l[h][k4] = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      const u32x2 a = split_bf16x2(p[0], p[1]), c = split_bf16x2(p[2], p[3]);
+      *(u32x2*)&sm.ab.p.h[h][k4] = u32x2{a[0], c[0]};
+      *(u32x2*)&sm.ab.p.l[h][k4] = u32x2{a[1], c[1]};
       if ((tq & 15) == 0) {
         sm.sm[h] = m;
         sm.sl[h] = s;
