@@ -323,6 +323,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_block_scores(
 }
 
 // H3: exact top keep_blocks blocks of one query (thread tid takes a run of consecutive blocks).
+template <int NVMAX>
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
     const float* __restrict__ block_scores, const int32_t* __restrict__ seq_len,
     int keep_blocks, int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
@@ -335,10 +336,11 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_top_blocks(
   const int tid = threadIdx.x;
   int32_t* out = kept + (size_t)b * keep_blocks;
   const float* sc = block_scores + (size_t)b * NbCap;
-  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];  // radix fallback only
-  const int cnt = top_strided<kHisaThreads, false>(sc, Nb, Nb, keep_blocks, AllPresent(),
-                                                   __builtin_huge_valf(), -__builtin_huge_valf(),
-                                                   sbuf, sh, [&](int pos, int c) { out[pos] = c; });
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaThreads * NVMAX];  // radix fallback only
+  auto emit = [&](int pos, int c) { out[pos] = c; };
+  const int cnt = top_strided<kHisaThreads, false, AllPresent, decltype(emit), NoMid, NVMAX>(
+      sc, Nb, Nb, keep_blocks, AllPresent(), __builtin_huge_valf(), -__builtin_huge_valf(), sbuf,
+      sh, emit);
   for (int i = cnt + tid; i < keep_blocks; i += kHisaThreads) out[i] = -1;
   if (tid == 0) kept_count[b] = cnt;
 }
@@ -601,6 +603,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_token_scores(
 // candidate c = (kept slot c / block, row c % block).  Kept blocks are
 // ascending, so candidate order is position order and ties go to the lower
 // position.
+template <int NVMAX>
 __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
     const float* __restrict__ token_scores, const int32_t* __restrict__ seq_len,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ kept_count, int keep_blocks,
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
   const int ncand = kc * block;
   const int tid = threadIdx.x;
   const float* ts = token_scores + (size_t)b * keep_blocks * block;
-  __shared__ __attribute__((aligned(16))) float sbuf[kHisaMaxCand];  // radix fallback only
+  __shared__ __attribute__((aligned(16))) float sbuf[kHisaThreads * NVMAX];  // radix fallback only
   // the kept blocks (for the output positions) load with the scores; the
   // scores load before the kept count is known (clamped to the buffer), and
   // only the first ncand are candidates.  The token-score pass wrote -inf for
@@ -625,10 +628,11 @@ __global__ __launch_bounds__(kHisaThreads) void k_hisa_topk(
   };
   auto present = [](float v) { return v != -__builtin_huge_valf(); };
   int32_t* out = sel_idx + (size_t)b * top_k;
-  const int cnt = top_strided<kHisaThreads, false>(
-      ts, keep_blocks * block, ncand, top_k, present, __builtin_huge_valf(),
-      -__builtin_huge_valf(), sbuf, sh,
-      [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; }, load_kept);
+  auto emit = [&](int pos, int c) { out[pos] = skept[c / block] * block + c % block; };
+  const int cnt =
+      top_strided<kHisaThreads, false, decltype(present), decltype(emit), decltype(load_kept),
+                  NVMAX>(ts, keep_blocks * block, ncand, top_k, present, __builtin_huge_valf(),
+                         -__builtin_huge_valf(), sbuf, sh, emit, load_kept);
   for (int i = cnt + tid; i < top_k; i += kHisaThreads) out[i] = -1;
   if (tid == 0) sel_count[b] = cnt;
 }
@@ -686,7 +690,10 @@ hipError_t launch_hisa_block_scores(const hhr_hisa_shape& s, const uint8_t* q8,
 hipError_t launch_hisa_top_blocks(const hhr_hisa_shape& s, const float* block_scores,
                                   const int32_t* seq_len, int32_t keep_blocks, int32_t* kept,
                                   int32_t* kept_count, uint32_t* status, hipStream_t stream) {
-  hipLaunchKernelGGL(k_hisa_top_blocks, dim3(s.batch), dim3(kHisaThreads), 0, stream,
+  // register-resident blocks per thread: 1 up to 1024 blocks (two workgroups
+  // then fit on a CU), else up to 16
+  auto kern = s.max_ctx / s.block <= kHisaThreads ? k_hisa_top_blocks<1> : k_hisa_top_blocks<16>;
+  hipLaunchKernelGGL(kern, dim3(s.batch), dim3(kHisaThreads), 0, stream,
                      block_scores, seq_len, keep_blocks, kept, kept_count, status, s.max_ctx,
                      s.block);
   return hipGetLastError();
@@ -726,7 +733,10 @@ hipError_t launch_hisa_token_topk(const hhr_hisa_shape& s, const uint8_t* q8,
                      shared ? 1 : 0, nslot, s.batch, xcd_rows, 0, nullptr, nullptr, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_hisa_topk, dim3(s.batch), dim3(kHisaThreads), 0, stream, token_scores,
+  // register-resident candidates per thread: up to 8 (two workgroups then fit
+  // on a CU), else up to 16
+  auto topk = keep_blocks * s.block <= 8 * kHisaThreads ? k_hisa_topk<8> : k_hisa_topk<16>;
+  hipLaunchKernelGGL(topk, dim3(s.batch), dim3(kHisaThreads), 0, stream, token_scores,
                      seq_len, kept, kept_count, keep_blocks, top_k, sel_idx, sel_count,
                      s.max_ctx, s.block);
   return hipGetLastError();

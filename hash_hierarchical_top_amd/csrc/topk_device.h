@@ -408,22 +408,25 @@ __device__ int top_strided_nv(const float* src, int n_load, int n, int P, Presen
 }
 
 // The P largest of src[0 .. n) (those present), ties to the lower index,
-// emitted in ascending index.  n_load (>= n, <= 16 NT, block-uniform and
+// emitted in ascending index.  n_load (>= n, <= NVMAX NT, block-uniform and
 // known before n may be) bounds the loads, so they need not wait for n.
-template <int NT, bool COH, typename Present, typename Emit, typename Mid = NoMid>
+// NVMAX (1, 2, 4, 8 or 16) caps the registers a caller reserves for it.
+template <int NT, bool COH, typename Present, typename Emit, typename Mid = NoMid,
+          int NVMAX = 16>
 __device__ __forceinline__ int top_strided(const float* src, int n_load, int n, int P, Present present, float lo,
                            float hi, float* sbuf, TopScratch& sh, Emit emit, Mid mid = Mid()) {
+  static_assert(NVMAX == 1 || NVMAX == 2 || NVMAX == 4 || NVMAX == 8 || NVMAX == 16, "NVMAX");
   const int tid = threadIdx.x;
   for (int i = tid; i < kLinBins; i += NT) sh.hist[i] = 0;  // ready after the range barrier
   if (tid == 0) sh.list_n = 0;
   const int nv = (n_load + NT - 1) / NT;
 #define HHR_TOP_STRIDED(V) \
   return top_strided_nv<NT, V, COH>(src, n_load, n, P, present, lo, hi, sbuf, sh, emit, mid)
-  if (nv <= 1) HHR_TOP_STRIDED(1);
-  if (nv <= 2) HHR_TOP_STRIDED(2);
-  if (nv <= 4) HHR_TOP_STRIDED(4);
-  if (nv <= 8) HHR_TOP_STRIDED(8);
-  HHR_TOP_STRIDED(16);
+  if (NVMAX == 1 || nv <= 1) HHR_TOP_STRIDED(1);
+  if (NVMAX == 2 || nv <= 2) HHR_TOP_STRIDED(NVMAX < 2 ? NVMAX : 2);
+  if (NVMAX == 4 || nv <= 4) HHR_TOP_STRIDED(NVMAX < 4 ? NVMAX : 4);
+  if (NVMAX == 8 || nv <= 8) HHR_TOP_STRIDED(NVMAX < 8 ? NVMAX : 8);
+  HHR_TOP_STRIDED(NVMAX);
 #undef HHR_TOP_STRIDED
 }
 
