@@ -692,8 +692,9 @@ def main_hisa_prefill(args, torch, hhr, synth, dev):
                 "kernel": "hhr_hisa_prefill_select (k_hisa_pool_tail, k_hisa_block_scores, "
                           "k_hisa_top_blocks, k_hisa_token_scores, k_hisa_topk)",
                 "flops_per_launch": flops, "avg_launch_us": round(ms * 1e3, 3),
-                "note": "each row re-reads its 64 kept blocks (1 MiB of fp8 keys) from L2 and "
-                        "the last-level cache: bound by cache bandwidth and latency, not HBM"}
+                "note": "each row re-reads its 64 kept blocks (1 MiB of fp8 keys), mostly from "
+                        "L2 and the last-level cache: bound by on-chip cache work and latency, "
+                        "not HBM"}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_prefill(rows, src, w, L, args.cpu_seconds)
