@@ -499,6 +499,43 @@ def test_prefill_select(gpu_lib, keep_all, n_rand):
 
 
 @pytest.mark.slow
+def test_prefill_wide_selection(gpu_lib):
+    """More than 64 rows over a cache of more than 1024 blocks, keeping more than 8192
+    candidates per row: the many-row selections then hold up to 16 blocks and 16
+    candidates per thread (the wide forms of k_hisa_top_blocks and k_hisa_topk).  Sampled
+    rows equal the decode path at their q_len bit for bit and match the oracle's causal
+    prefill selection within the band."""
+    H = gpu_lib
+    Hi, blk, Lcap, L, keep, top_k = 16, 16, 32768, 30000, 600, 1000
+    rng = np.random.default_rng(71)
+    pos = np.unique(np.concatenate([[0, 15, 16, 9599, 9600, 17000, L - 1],
+                                    rng.integers(16384, L, 70)]))
+    q_len = (pos + 1).astype(np.int32)
+    M = q_len.size
+    assert M > 64 and keep * blk > 8192 and Lcap // blk > 1024
+    src = synth.make_hisa_inputs(Hi, L, Lcap, 4, 72, block=blk, make_kv=False)
+    qs = [synth.make_hisa_inputs(Hi, 1, 16, 4, 300 + r, block=16, make_kv=False)
+          for r in range(M)]
+    q8 = np.stack([x["q8"] for x in qs])
+    q_scale = np.stack([x["q_scale"] for x in qs])
+    wt = np.stack([x["w"] for x in qs])
+    mid = np.flatnonzero(q_len % blk != 0)
+    sample = np.unique(np.concatenate([[0, 1, 2, 3, 4, M - 1], rng.choice(mid, 4, replace=False)]))
+    print(f"\n[gpu hisa prefill wide] M={M} keep={keep} block={blk} sampled rows "
+          f"{sample.tolist()}", flush=True)
+    run = PrefillRun(H, src["k8"], src["k_scale"], q8, q_scale, wt, q_len, blk, keep, top_k,
+                     copy_rows=sample)
+    run.check_decode_identity()
+    n_blk = n_tok = 0
+    for i in range(sample.size):
+        b_, t_ = run.check_row(i)
+        n_blk += b_
+        n_tok += t_
+    print(f"excused blocks {n_blk}, tokens {n_tok} over {sample.size} rows", flush=True)
+    U.record_excused("hisa_prefill_32k_wide_sampled", rows=int(sample.size), blocks=n_blk,
+                     tokens=n_tok)
+
+
 def test_prefill_bench_shape_sampled_rows(gpu_lib):
     """The bench's prefill shape: 512 rows at positions drawn over a 131072-key prompt
     (64 fp8 index heads, blocks of 128, 64 kept blocks, top-2048), in one call.  Sampled
