@@ -22,17 +22,12 @@ constexpr int kHisaThreads = 1024;
 constexpr int kHisaItems = 16;  // candidates per thread: <= 16384 per query
 constexpr int kHisaMaxCand = kHisaThreads * kHisaItems;
 
-// OCP fp8 e4m3fn -> f32: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
-// 2..0; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN; no infinities.
+// OCP fp8 e4m3fn -> f32 (exact): sign bit 7, exponent bits 6..3 (bias 7), mantissa
+// bits 2..0; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN; no infinities.
+// On gfx950 v_cvt_f32_fp8 decodes this format: one instruction for the field decode
+// (the same bits for all 256 codes).  v holds the code in its low byte.
 __device__ __forceinline__ float e4m3fn_to_f32(uint32_t v) {
-  const uint32_t sign = (v & 0x80u) << 24;
-  const uint32_t e = (v >> 3) & 0xFu;
-  const uint32_t m = v & 0x7u;
-  float mag;
-  if (e == 0) mag = (float)m * 0.001953125f;  // m * 2^-9, exact
-  else if (e == 15 && m == 7) mag = __builtin_nanf("");
-  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return __uint_as_float(__float_as_uint(mag) | sign);
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, 0);
 }
 
 __device__ __forceinline__ int checked_len(const int32_t* seq_len, int b, int Lcap,
@@ -245,8 +240,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_hisa_block_scores(
     u32x2 pk;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t lo = __float_as_uint(e4m3fn_to_f32((qv[k] >> (16 * kk)) & 0xFFu)) >> 16;
-      const uint32_t hi = __float_as_uint(e4m3fn_to_f32((qv[k] >> (16 * kk + 8)) & 0xFFu)) >> 16;
+      const uint32_t lo = __float_as_uint(e4m3fn_to_f32(qv[k] >> (16 * kk))) >> 16;
+      const uint32_t hi = __float_as_uint(e4m3fn_to_f32(qv[k] >> (16 * kk + 8))) >> 16;
       pk[kk] = lo | (hi << 16);
     }
     *(u32x2*)&sq[h][d] = pk;
