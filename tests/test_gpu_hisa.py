@@ -499,6 +499,45 @@ def test_prefill_select(gpu_lib, keep_all, n_rand):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("n_cap", [1024, 4096], ids=["blocks1024", "blocks4096"])
+def test_top_blocks_exact_on_constructed_scores(gpu_lib, n_cap):
+    """hhr_hisa_top_blocks on constructed block scores (the page top-P tests' patterns:
+    ties at the cut, all equal, few values, an outlier, signed zeros) for several rows
+    at once: one block per thread (up to 1024 blocks) and up to 16 per thread, each row
+    equal to the oracle's (score descending, block ascending) order."""
+    from tests.test_gpu_select_ties import PATTERNS, _scores
+    H = gpu_lib
+    dv = U.dev()
+    blk = 16
+    shape = H.make_hisa_shape(4, 8, blk, n_cap * blk)
+    rng = np.random.Generator(np.random.PCG64(77))
+    sizes = [1, 5, 777, n_cap] if n_cap == 1024 else [1, 1000, n_cap]
+    checked = 0
+    for pattern in PATTERNS:
+        for P in (1, 5, 64, 1023):
+            ns = rng.permutation(sizes * 2)[:4]
+            scores = np.zeros((4, n_cap), np.float32)
+            for r, n in enumerate(ns):
+                scores[r, :n] = _scores(pattern, int(n), min(P, int(n)), rng)
+            seq = torch.tensor(ns * blk, dtype=torch.int32, device=dv)
+            kept = torch.full((4, P), 12345, dtype=torch.int32, device=dv)
+            kc = torch.full((4,), -3, dtype=torch.int32, device=dv)
+            status = torch.zeros(1, dtype=torch.int32, device=dv)
+            H.hhr_hisa_top_blocks(shape, torch.from_numpy(scores).to(dv), seq, P, kept, kc,
+                                  status)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0
+            for r, n in enumerate(ns):
+                want = O.top_largest(scores[r, :n].astype(np.float64), np.arange(n), P)
+                got = kept[r].cpu().numpy()
+                cnt = int(kc[r])
+                assert cnt == min(P, n), (pattern, n, P)
+                assert got[:cnt].tolist() == want.tolist(), (pattern, n, P)
+                assert (got[cnt:] == -1).all(), (pattern, n, P)
+                checked += 1
+    print(f"checked {checked} rows", flush=True)
+
+
 def test_prefill_wide_selection(gpu_lib):
     """More than 64 rows over a cache of more than 1024 blocks, keeping more than 8192
     candidates per row: the many-row selections then hold up to 16 blocks and 16
