@@ -227,7 +227,7 @@ bool make_workspace(const hhr_shape& s, int32_t keep_num, int32_t keep_den, int3
   w.q_rot = take(BHq * kD * sizeof(float));
   w.q_codes = take(BHq * (size_t)(s.code_bits / 32) * sizeof(uint32_t));
   w.scores = take(BHkv * NpCap * sizeof(float));
-  w.wave_range = take(BHkv * (NpCap / 16) * sizeof(float2));
+  w.wave_range = take(BHkv * (size_t)((NpCap + 15) / 16) * sizeof(float2));  // per 16-page block
   w.wg_thr = take(BHkv * (size_t)((NpCap + 63) / 64) * sizeof(float));
   w.kept = take(BHkv * (size_t)w.p_max * sizeof(int32_t));
   w.kept_count = take(BHkv * sizeof(int32_t));

@@ -56,21 +56,49 @@ struct ScoreTopSmem {
 };
 
 // A lower bound of the top-P cut from the scoring workgroups (see
-// top_prefiltered): while it pays, every workgroup holding pages
-// publishes a value that q = ceil(P / (J - 1)) of its bounds reach (all of
-// them when it holds fewer), J = the workgroups holding pages.  It pays when
-// the top-P would otherwise hold more than 4 bounds per thread: at 128K
-// (8192 pages) the step takes 42.6 instead of 43.2 us, while at 32K (2048
-// pages, 2 per thread) the workgroups' extra histogram pass cost 1 us more
-// than the smaller selection saved.
+// top_prefiltered): while it pays, every workgroup holding pages publishes a
+// value that q = ceil(P / (J - 1)) of its bounds reach (all of them when it
+// holds fewer), J = the workgroups holding pages.  The P largest bounds are
+// then all at or above the smallest published value as long as every holding
+// workgroup but one holds at least q pages: with contiguous runs all but the
+// last hold ppw pages; round robin, each holds at least max(floor(nblk /
+// Jg), 1) blocks, all whole but the sequence's last.  It pays when the top-P
+// would otherwise hold more than 4 bounds per thread: at 128K (8192 pages)
+// the step takes 42.6 instead of 43.2 us, while at 32K (2048 pages, 2 per
+// thread) the workgroups' extra histogram pass cost 1 us more than the
+// smaller selection saved.
 constexpr int kPrefilterMinPages = 4 * kScoreThreads;
 
-__device__ __forceinline__ int prefilter_quota(int Np, int P, int ppw) {
-  const int J = (Np + ppw - 1) / ppw;
+// J: the workgroups holding pages (ScoreBlocks::holders).
+__device__ __forceinline__ int prefilter_quota(int Np, int P, int ppw, int J, int held) {
   if (Np <= kPrefilterMinPages || Np > kPrefilterMaxPages || J < 2 || P <= 0) return 0;
   const int q = (P + J - 2) / (J - 1);
-  return q <= ppw / 2 ? q : 0;  // 0: off (no pages would be dropped)
+  return q <= ppw / 2 && q <= held ? q : 0;  // 0: off (nothing dropped, or no valid bound)
 }
+
+// The 16-page blocks of one (b, g) that the scoring waves read: wave w < nwv
+// (the waves with pages) of workgroup x reads block x * nwv + w (contiguous
+// runs), or x + Jg w (round robin over the grid's Jg workgroups); nbc or more:
+// none.  Either way each of the cache's nbc blocks has one wave.
+struct ScoreBlocks {
+  int nbc, nwv, Jg;
+  bool rr;
+  __device__ __forceinline__ int block(int x, int w) const {
+    return w < nwv ? (rr ? x + Jg * w : x * nwv + w) : nbc;
+  }
+  // The workgroups holding some of nblk blocks: x < holders(nblk).
+  __device__ __forceinline__ int holders(int nblk) const {
+    return rr ? min(Jg, nblk) : (nblk + nwv - 1) / nwv;
+  }
+  // Pages that every holding workgroup but one holds at least.
+  __device__ __forceinline__ int held(int nblk) const {
+    return rr ? kScorePagesPerWave * max(nblk / Jg, 1) : kScorePagesPerWave * nwv;
+  }
+  // Whether block blk (in [0, nbc)) is workgroup x's.
+  __device__ __forceinline__ bool holds(int x, int blk) const {
+    return rr ? blk % Jg == x && blk / Jg < nwv : blk / nwv == x;
+  }
+};
 
 // Folds the appended key's rotation x (LDS, 128 dims) into page pn's metadata
 // held by this wave (score_load's lane layout), or makes it the page's only row
@@ -125,7 +153,14 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 
 // S2 + S3 + S4.  grid (ceil(NpCap / ppw), B*Hkv), 1024 threads: the first
 // ppw / 16 of the 16 waves score 16 pages each (ppw = 256, or 128 or 64 when
-// the grid would not cover the chip).  Each workgroup rotates its group's
+// the grid would not cover the chip).  Which 16-page blocks a wave scores
+// depends on how full the sequence's cache is (ScoreBlocks): a sequence
+// filling more than half of it is read in one contiguous run of blocks per
+// workgroup, a shorter one round robin over the workgroups, so that its pages
+// spread over all of them (a 16K sequence in a 128K cache: 11.3 instead of
+// 14.3 us for this kernel; for a full cache the round robin measured 25.4
+// against 22.2 us, and a multiplicative block permutation 27.0 us).  Each
+// workgroup rotates its group's
 // queries itself (64 KiB of R from L2, issued after its metadata loads so both
 // are in flight together); workgroup 0 of each (b, g) also writes the query
 // codes, once its bounds are done (the sign bits need W's columns in
@@ -164,19 +199,24 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
   const int NpCap = Lcap / kPS;
-  const int pb = blockIdx.x * ppw + (tid >> 6) * kScorePagesPerWave;
   // a wave loads its pages' metadata only once the sequence length says they
   // exist (clamped to the last one), so a short sequence in a long cache reads
   // only its own pages
-  const bool wave_in = (tid >> 6) * kScorePagesPerWave < ppw && pb < NpCap;  // wave-uniform
   const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
   const int Np = (L + kPS - 1) / kPS;
-  const bool wave_has = wave_in && pb < Np;          // wave-uniform
+  const int nblk = (Np + kScorePagesPerWave - 1) / kScorePagesPerWave;
+  const ScoreBlocks sb{(NpCap + kScorePagesPerWave - 1) / kScorePagesPerWave,
+                       ppw / kScorePagesPerWave, (int)gridDim.x, 2 * Np <= NpCap};
+  const int wv = tid >> 6;
+  const int blk = sb.block(blockIdx.x, wv);  // wave-uniform
+  const int pb = blk * kScorePagesPerWave;
+  const bool wave_has = blk < nblk;          // wave-uniform
   PageLoads<1> pl;
   if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
-  const bool wg_has = (int)blockIdx.x * ppw < Np;  // block-uniform
+  const int J = sb.holders(nblk);
+  const bool wg_has = (int)blockIdx.x < J;  // block-uniform
   // the workgroup holding the last page, when a key was appended (block-uniform)
-  const bool owner = APPEND && L > 0 && (int)blockIdx.x == (Np - 1) / ppw;
+  const bool owner = APPEND && L > 0 && sb.holds(blockIdx.x, nblk - 1);
   const void* key = nullptr;  // the appended key's row
   uint32_t* crow = nullptr;   // and its code
   if (APPEND && L > 0) {
@@ -201,9 +241,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       merge_appended_row<MBF>(bg, NpCap, Np - 1, pb, (L - 1) % kPS == 0, sm.rot.xnew, meta, pl);
   }
   uint32_t* ctl = counters + (size_t)bg * kCountersPerGroup;
-  float2* wr = wave_range + (size_t)bg * (NpCap / kScorePagesPerWave);
+  float2* wr = wave_range + (size_t)bg * ((NpCap + kScorePagesPerWave - 1) / kScorePagesPerWave);
   const int P = keep_count_dev(Np, keep_num, keep_den, keep_abs);
-  const int quota = prefilter_quota(Np, P, ppw);  // block-uniform
+  const int quota = prefilter_quota(Np, P, ppw, J, sb.held(nblk));  // block-uniform
   float mine = 0.f;                                 // this lane's bound (pf_lane)
   bool pf_lane = false;
   if (wave_has) {
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   if (tid == 0) kept_count[bg] = P;
   if (quota > 0) {  // block-uniform: the pages below the published lower bound are out
     top_prefiltered<kScoreThreads>(scores + (size_t)bg * NpCap, Np, Np, P, AllPresent(),
-                                   wg_thr + (size_t)bg * gridDim.x, (Np + ppw - 1) / ppw,
+                                   wg_thr + (size_t)bg * gridDim.x, J,
                                    sm.sel.sbuf, sm.sel.cidx, sm.sel.top,
                                    [&](int pos, int c) { out[pos] = c; });
   } else if (P > 0) {

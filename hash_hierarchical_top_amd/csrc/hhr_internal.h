@@ -85,7 +85,7 @@ hipError_t launch_sparse_decode(const hhr_shape& s, const float* q, const void* 
 // hhr_decode, S6 + S7 with every attention workgroup picking its own keys).
 // counters: kCountersPerGroup words per (b, g) (zero before and after every
 // call): word kScoreCounter counts k_score_topp's arrivals.  wave_range:
-// {smallest, largest} bound of each 16-page wave, [B*Hkv][NpCap/16].
+// {smallest, largest} bound of each 16-page block, [B*Hkv][ceil(NpCap/16)].
 struct CompositeBuffers {
   uint32_t* status;
   uint32_t* counters;

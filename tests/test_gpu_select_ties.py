@@ -75,7 +75,9 @@ def test_top_pages_exact_on_constructed_scores(gpu_lib):
                                                   (1, 98304, [98304, 80000], False),
                                                   (3, 98304, [98304, 80000], False),
                                                   (98304, 98304, [98304, 80000], False),
-                                                  (1, 98304, [98304, 80000], True)])
+                                                  (1, 98304, [98304, 80000], True),
+                                                  (1, 163840, [80000, 66000], False),
+                                                  (3, 163840, [80000, 66000], True)])
 def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens, ramp):
     """Keys copied page by page in runs of `group` pages give equal page bounds in runs,
     so the cut of the top-P falls inside a run of ties (group = Lcap: every page equal).
@@ -86,7 +88,9 @@ def test_duplicate_pages_composite_equals_stages(gpu_lib, group, Lcap, lens, ram
     pages) takes the one-launch top-P through its lower-bound pre-filter, the second
     sequence with a partly filled last scoring workgroup.  ramp: keys scaled up with their
     page index, so the largest bounds crowd into the last scoring workgroups and the
-    pre-filter keeps most pages (its widest compaction)."""
+    pre-filter keeps most pages (its widest compaction).  The 163840-key cache (10240
+    pages) holds sequences of 5000 and 4125 pages, under half of it: the scoring
+    workgroups take their 16-page blocks round robin, and the pre-filter still runs."""
     print(f"\n[gpu duplicate pages] group={group} Lcap={Lcap} ramp={ramp}", flush=True)
     from hash_hierarchical_top_amd import synth
 
