@@ -158,13 +158,13 @@ __device__ __forceinline__ void merge_appended_row(int bg, int NpCap, int pn, in
 // filling more than half of it is read in one contiguous run of blocks per
 // workgroup, a shorter one round robin over the workgroups, so that its pages
 // spread over all of them (a 16K sequence in a 128K cache: 11.3 instead of
-// 14.3 us for this kernel; for a full cache the round robin measured 25.4
-// against 22.2 us, and a multiplicative block permutation 27.0 us).  Each
-// workgroup rotates its group's
-// queries itself (64 KiB of R from L2, issued after its metadata loads so both
-// are in flight together); workgroup 0 of each (b, g) also writes the query
-// codes, once its bounds are done (the sign bits need W's columns in
-// registers, which would not fit beside the metadata).
+// 14.3 us for this kernel; on a full cache round robin measured 25.4
+// against 22.2 us, and blocks permuted by an odd multiplier 22.3 against
+// 22.0 us).  Each workgroup rotates its group's queries itself (64 KiB of R
+// from L2, issued after its metadata loads so both are in flight together);
+// the first workgroup of each (b, g) to finish its bounds also writes the
+// query codes (the sign bits need W's columns in registers, which would not
+// fit beside the metadata).
 //
 // APPEND: row L - 1 of every sequence is a key appended since the last encode
 // (its K row is in kcache).  The workgroup that holds the last page encodes
