@@ -193,7 +193,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   __shared__ float s_wlo[kScoreThreads / kWave], s_whi[kScoreThreads / kWave];
   __shared__ int s_bcnt[64];
   __shared__ uint32_t s_bmin[64];
-  const int bg = blockIdx.y;
+  // Workgroups go to the 8 XCDs round robin by linear id; the ids are regrouped
+  // so that the workgroups sharing an XCD take consecutive (b, g, x): a (b, g)
+  // whose workgroups fill an XCD then reads its R through one L2.  Any
+  // bijection is correct; this one only chooses which L2 serves which R.
+  const int nwg = (int)(gridDim.x * gridDim.y);
+  const int id = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  const int lin = nwg % 8 == 0 ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int wx = lin % (int)gridDim.x;
+  const int bg = lin / (int)gridDim.x;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
   const int G = Hq / Hkv;
@@ -202,21 +210,21 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
   // a wave loads its pages' metadata only once the sequence length says they
   // exist (clamped to the last one), so a short sequence in a long cache reads
   // only its own pages
-  const int L = clamped_len(seq_len, b, Lcap, blockIdx.x == 0 && g == 0 ? status : nullptr);
+  const int L = clamped_len(seq_len, b, Lcap, wx == 0 && g == 0 ? status : nullptr);
   const int Np = (L + kPS - 1) / kPS;
   const int nblk = (Np + kScorePagesPerWave - 1) / kScorePagesPerWave;
   const ScoreBlocks sb{(NpCap + kScorePagesPerWave - 1) / kScorePagesPerWave,
                        ppw / kScorePagesPerWave, (int)gridDim.x, 2 * Np <= NpCap};
   const int wv = tid >> 6;
-  const int blk = sb.block(blockIdx.x, wv);  // wave-uniform
+  const int blk = sb.block(wx, wv);  // wave-uniform
   const int pb = blk * kScorePagesPerWave;
   const bool wave_has = blk < nblk;          // wave-uniform
   PageLoads<1> pl;
   if (wave_has) score_load<MBF, 1>(bg, NpCap, Np, pb, meta, pl);
   const int J = sb.holders(nblk);
-  const bool wg_has = (int)blockIdx.x < J;  // block-uniform
+  const bool wg_has = wx < J;  // block-uniform
   // the workgroup holding the last page, when a key was appended (block-uniform)
-  const bool owner = APPEND && L > 0 && sb.holds(blockIdx.x, nblk - 1);
+  const bool owner = APPEND && L > 0 && sb.holds(wx, nblk - 1);
   const void* key = nullptr;  // the appended key's row
   uint32_t* crow = nullptr;   // and its code
   if (APPEND && L > 0) {
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score_topp(
       whi = fmaxf(whi, s_whi[k]);
     }
     publish_lower_bound(mine, pf_lane, wlo, whi, quota, s_bcnt, s_bmin,
-                        wg_thr + (size_t)bg * gridDim.x + blockIdx.x);
+                        wg_thr + (size_t)bg * gridDim.x + wx);
   }
   // The code bits of the queries (and of the appended key, as row G) need W's
   // columns in registers, which would not fit beside the metadata; the first
